@@ -1,0 +1,347 @@
+"""Plain float64 CPU oracle for gated, no-position MLA (test infrastructure only).
+
+Sources (cited by page title and section):
+  [MLA]  "Kimi K3 · Gated MLA · OpenModelAtlas": the 20-step equation list
+         (query heads, key and value heads, causal attention, gate), the
+         ``KimiMLAAttention`` constructor/forward excerpts and the
+         ``eager_attention_forward`` excerpt (fp32 softmax, scaling = q_head_dim^-1/2).
+  [FR]   "Gated MLA et NoPE" (mkdocs.reaper.mx): cache row of 512 + 64 values,
+         sigmoid output gate, no position encoding.
+  [CLIP] "SOTA-131" practice page (anthology-of-the-sota): QK-Clip rescales a
+         head's query and key projection weights when its maximum logit exceeds
+         a threshold.
+  [FW]   "Kimi Qkclip" (Fireworks blog): training materialises K, inference
+         skips the K up-projection (the absorbed form).
+
+Conventions shared with the library's C ABI (layouts, not arithmetic):
+  q [Ntok, H, D] with D = N + S (first N = q^C, last S = q^R), c^KV [Ntok, R],
+  k^S [Ntok, S], kv_b_proj.weight [H*(N+V), R] (head h: N rows of W_UK_h^T then
+  V rows of W_UV_h^T), gate logits [Ntok, H*V], output [Ntok, H*V] head-major.
+
+Everything is computed in float64 from the exact values of the inputs. No
+function here is blocked, fused or reordered beyond splitting independent
+query rows into blocks to bound memory; each query row is computed from its
+full masked score row exactly as the equations define it.
+"""
+from __future__ import annotations
+
+import collections
+import math
+
+import numpy as np
+
+Dims = collections.namedtuple("Dims", "heads kv_rank shared_dim nope_dim v_dim")
+
+f64 = np.float64
+
+
+def _dims(d) -> Dims:
+    return Dims(int(d.heads), int(d.kv_rank), int(d.shared_dim), int(d.nope_dim), int(d.v_dim))
+
+
+def scale_of(d) -> float:
+    """The score scale 1/sqrt(q_head_dim), q_head_dim = nope + shared ([MLA]
+    constructor: ``self.scaling = self.q_head_dim ** (-0.5)``; equation S <- S/sqrt(192))."""
+    d = _dims(d)
+    return 1.0 / math.sqrt(d.nope_dim + d.shared_dim)
+
+
+def sigmoid(x):
+    """sigma(x) = 1 / (1 + e^{-x})  ([MLA] gate step o = sigma(g) . o~)."""
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-np.asarray(x, dtype=f64)))
+
+
+# ---------------------------------------------------------------------------
+# Key and value heads ([MLA] steps "[k^C v] = c^KV W_UKV", K^C_h = cols 1:128,
+# V_h = cols 129:256, K_h = [K^C_h k^S])
+# ---------------------------------------------------------------------------
+
+
+def expand_latent(ckv, w_kv_b, dims, head: int):
+    """K^C_h and V_h of one head from the latent c^KV.
+
+    [k^C v] = c^KV W_UKV with W_UKV = kv_b_proj.weight^T; head h's block of 256
+    output columns splits into its first N (K^C_h) and its last V (V_h).
+    Returns (K^C_h [T, N], V_h [T, V]) in float64.
+    """
+    d = _dims(dims)
+    w = np.asarray(w_kv_b, dtype=f64)
+    blk = w[head * (d.nope_dim + d.v_dim):(head + 1) * (d.nope_dim + d.v_dim), :]   # [N+V, R]
+    kv = np.asarray(ckv, dtype=f64) @ blk.T                                          # [T, N+V]
+    return kv[:, :d.nope_dim], kv[:, d.nope_dim:]
+
+
+def key_of_head(kc_h, ks):
+    """K_h = [K^C_h, k^S]: the shared k^S is the same for every head."""
+    return np.concatenate([np.asarray(kc_h, dtype=f64), np.asarray(ks, dtype=f64)], axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Causal attention ([MLA] steps S = Q K^T, S <- S/sqrt(192), causal softmax,
+# O~ = A V, reshape, gate)
+# ---------------------------------------------------------------------------
+
+
+def _attend_sequence(Q, K, Vv, scale, block):
+    """One sequence and one head: rows of A over s <= t, then A V.
+
+    Returns (O~ [L, V], lse [L], max unmasked scaled logit).
+    """
+    L = Q.shape[0]
+    out = np.zeros((L, Vv.shape[1]), dtype=f64)
+    lse = np.full(L, -np.inf, dtype=f64)
+    smax = -np.inf
+    for t0 in range(0, L, block):
+        t1 = min(L, t0 + block)
+        S = (Q[t0:t1] @ K[:t1].T) * scale               # S = Q K^T / sqrt(D)
+        t = np.arange(t0, t1)[:, None]
+        s = np.arange(t1)[None, :]
+        visible = s <= t                                # causal: s <= t
+        S = np.where(visible, S, -np.inf)
+        smax = max(smax, float(S.max()))
+        m = S.max(axis=1, keepdims=True)
+        e = np.exp(S - m)                               # exp S_{t,s}; exactly 0 where s > t
+        den = e.sum(axis=1, keepdims=True)              # sum_{u <= t} exp S_{t,u}
+        A = e / den
+        out[t0:t1] = A @ Vv[:t1]                        # O~ = A V
+        lse[t0:t1] = (m + np.log(den))[:, 0]
+    return out, lse, smax
+
+
+def prefill(q, ckv, ks, w_kv_b, gate, cu_seqlens, dims, block: int = 512, heads=None):
+    """Training-form gated MLA over packed sequences.
+
+    For every head h and every sequence [a, b) of ``cu_seqlens``:
+    K^C_h, V_h from c^KV (expansion), K_h = [K^C_h, k^S], S = Q_h K_h^T / sqrt(D),
+    causal softmax (A = 0 for s > t), O~ = A V_h. Sequences never attend to
+    each other. Then o~ = reshape(O~) head-major and o = sigma(g) . o~ (no gate
+    when ``gate`` is None).
+
+    Returns (out [Ntok, H*V], lse [H, Ntok] natural log, max_logit [H]) in
+    float64; max_logit[h] is the largest scaled logit S_{t,s} over every
+    unmasked pair of every sequence (-inf when there is none).
+    """
+    d = _dims(dims)
+    H, N, V = d.heads, d.nope_dim, d.v_dim
+    cu = [int(x) for x in cu_seqlens]
+    n = cu[-1]
+    scale = scale_of(d)
+    q = np.asarray(q)
+    out = np.zeros((n, H * V), dtype=f64)
+    lse = np.full((H, n), -np.inf, dtype=f64)
+    smax = np.full(H, -np.inf, dtype=f64)
+    for h in (range(H) if heads is None else heads):
+        kc, vv = expand_latent(ckv, w_kv_b, d, h)
+        K = key_of_head(kc, ks)
+        Q = np.asarray(q[:, h, :], dtype=f64)
+        for a, b in zip(cu[:-1], cu[1:]):
+            if b <= a:
+                continue
+            o, l, m = _attend_sequence(Q[a:b], K[a:b], vv[a:b], scale, block)
+            out[a:b, h * V:(h + 1) * V] = o
+            lse[h, a:b] = l
+            smax[h] = max(smax[h], m)
+    if gate is not None:
+        out = sigmoid(gate) * out
+    return out, lse, smax
+
+
+def max_logit_head(q, ckv, ks, w_kv_b, cu_seqlens, dims, head: int, block: int = 1024):
+    """Largest scaled causal logit of one head over all sequences (no softmax)."""
+    d = _dims(dims)
+    scale = scale_of(d)
+    kc, _ = expand_latent(ckv, w_kv_b, d, head)
+    K = key_of_head(kc, ks)
+    Q = np.asarray(np.asarray(q)[:, head, :], dtype=f64)
+    cu = [int(x) for x in cu_seqlens]
+    best = -np.inf
+    for a, b in zip(cu[:-1], cu[1:]):
+        for t0 in range(a, b, block):
+            t1 = min(b, t0 + block)
+            S = (Q[t0:t1] @ K[a:t1].T) * scale
+            t = np.arange(t0, t1)[:, None]
+            s = np.arange(a, t1)[None, :]
+            S = np.where(s <= t, S, -np.inf)
+            best = max(best, float(S.max()))
+    return best
+
+
+def prefill_rows(q, ckv, ks, w_kv_b, gate, cu_seqlens, dims, head: int, rows):
+    """Selected output rows of one head (for spot checks at sizes the full
+    oracle cannot finish). ``rows`` are global token indices.
+
+    Returns (o [len(rows), V] gated, lse [len(rows)]).
+    """
+    d = _dims(dims)
+    V = d.v_dim
+    scale = scale_of(d)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    kc, vv = expand_latent(ckv, w_kv_b, d, head)
+    K = key_of_head(kc, ks)
+    qq = np.asarray(q)
+    out = np.zeros((len(rows), V), dtype=f64)
+    lse = np.zeros(len(rows), dtype=f64)
+    for i, t in enumerate(rows):
+        s_idx = int(np.searchsorted(cu, t, side="right") - 1)
+        a = int(cu[s_idx])
+        S = (K[a:t + 1] @ np.asarray(qq[t, head, :], dtype=f64)) * scale   # s = a..t
+        m = S.max()
+        e = np.exp(S - m)
+        den = e.sum()
+        o = (e / den) @ vv[a:t + 1]
+        if gate is not None:
+            o = sigmoid(np.asarray(gate)[t, head * V:(head + 1) * V]) * o
+        out[i] = o
+        lse[i] = m + math.log(den)
+    return out, lse
+
+
+def dense_prefill(q, ckv, ks, w_kv_b, gate, cu_seqlens, dims):
+    """Brute force for tiny inputs, in the style of ``eager_attention_forward``.
+
+    Materialises every head's full K and V with one einsum, builds the whole
+    Ntok x Ntok score matrix per head, adds an additive mask (0 where the key is
+    in the same sequence and not after the query, -inf elsewhere), and applies
+    a textbook softmax. Returns (out [Ntok, H*V], probs [H, Ntok, Ntok],
+    max_logit [H]).
+    """
+    d = _dims(dims)
+    H, N, V, S_ = d.heads, d.nope_dim, d.v_dim, d.shared_dim
+    n = int(cu_seqlens[-1])
+    w = np.asarray(w_kv_b, dtype=f64).reshape(H, N + V, -1)                 # [H, N+V, R]
+    kv = np.einsum("tr,hcr->htc", np.asarray(ckv, dtype=f64), w)           # [H, T, N+V]
+    kc, vv = kv[..., :N], kv[..., N:]
+    ksb = np.broadcast_to(np.asarray(ks, dtype=f64)[None], (H, n, S_))
+    key = np.concatenate([kc, ksb], axis=-1)                               # [H, T, D]
+    qh = np.asarray(q, dtype=f64).transpose(1, 0, 2)                       # [H, T, D]
+    seq_id = np.repeat(np.arange(len(cu_seqlens) - 1), np.diff(np.asarray(cu_seqlens)))
+    pos = np.arange(n)
+    allowed = (seq_id[:, None] == seq_id[None, :]) & (pos[None, :] <= pos[:, None])
+    mask = np.where(allowed, 0.0, -np.inf)
+    scores = np.einsum("hqd,hkd->hqk", qh, key) * scale_of(d) + mask[None]
+    smax = np.where(allowed[None], scores, -np.inf).reshape(H, -1).max(axis=1)
+    ex = np.exp(scores - scores.max(axis=-1, keepdims=True))
+    probs = ex / ex.sum(axis=-1, keepdims=True)
+    o = np.einsum("hqk,hkd->qhd", probs, vv).reshape(n, H * V)
+    if gate is not None:
+        o = o / (1.0 + np.exp(-np.asarray(gate, dtype=f64)))
+    return o, probs, smax
+
+
+# ---------------------------------------------------------------------------
+# Absorbed (inference) form ([FW] "the projection is skipped" at decode; the
+# cache row [c^KV | k^S] of [FR]). By associativity of the [MLA] equations:
+#   q^C . K^C_s = c_s . (W_UK_h q^C)   and   sum_s p_s V_s = (sum_s p_s c_s) W_UV_h
+# ---------------------------------------------------------------------------
+
+
+def absorb_query(q_h, w_kv_b, dims, head: int):
+    """q_abs = [W_UK_h q^C_h, q^R_h] (length R + S) for one head and one token."""
+    d = _dims(dims)
+    N, V = d.nope_dim, d.v_dim
+    w = np.asarray(w_kv_b, dtype=f64)
+    wk = w[head * (N + V):head * (N + V) + N, :]             # [N, R] = W_UK_h^T
+    q_h = np.asarray(q_h, dtype=f64)
+    return np.concatenate([wk.T @ q_h[:N], q_h[N:]])
+
+
+def absorbed(q, cache_rows, w_kv_b, gate, dims):
+    """Absorbed-form gated MLA over a latent cache.
+
+    q [B, Tq, H, D]; ``cache_rows[b]`` holds the valid rows [c^KV | k^S] of
+    sequence b ([L_b, R+S]); gate [B, Tq, H*V] or None. Query i of Tq sees rows
+    j <= L_b - Tq + i (the Tq queries are the last Tq positions of the
+    sequence). Scores use the same 1/sqrt(N+S) scale as the training form.
+
+    Returns (out [B, Tq, H*V], max_logit [H]).
+    """
+    d = _dims(dims)
+    H, R, N, V = d.heads, d.kv_rank, d.nope_dim, d.v_dim
+    scale = scale_of(d)
+    q = np.asarray(q)
+    B, Tq = q.shape[0], q.shape[1]
+    w = np.asarray(w_kv_b, dtype=f64)
+    out = np.zeros((B, Tq, H * V), dtype=f64)
+    smax = np.full(H, -np.inf, dtype=f64)
+    for b in range(B):
+        rows = np.asarray(cache_rows[b], dtype=f64)          # [L, R+S]
+        L = rows.shape[0]
+        for i in range(Tq):
+            vis = L - Tq + i + 1
+            if vis <= 0:
+                continue
+            for h in range(H):
+                qa = absorb_query(q[b, i, h], w, d, h)
+                s = (rows[:vis] @ qa) * scale
+                smax[h] = max(smax[h], float(s.max()))
+                m = s.max()
+                e = np.exp(s - m)
+                p = e / e.sum()
+                o_lat = p @ rows[:vis, :R]                   # sum_s p_s c_s
+                wv = w[h * (N + V) + N:(h + 1) * (N + V), :]  # [V, R] = W_UV_h^T
+                out[b, i, h * V:(h + 1) * V] = wv @ o_lat    # (o_lat) W_UV_h
+    if gate is not None:
+        out = sigmoid(gate) * out
+    return out, smax
+
+
+def absorbed_rows_selected(q, cache_rows, w_kv_b, gate, dims, batches):
+    """``absorbed`` restricted to the listed sequences (spot checks)."""
+    qs = np.asarray(q)[list(batches)]
+    gs = None if gate is None else np.asarray(gate)[list(batches)]
+    return absorbed(qs, [cache_rows[b] for b in batches], w_kv_b, gs, dims)
+
+
+# ---------------------------------------------------------------------------
+# Query projection ([MLA] "q = c^Q W_UQ") and QK-Clip ([CLIP])
+# ---------------------------------------------------------------------------
+
+
+def q_projection(cq, w_q_b, dims):
+    """q = c^Q W_UQ with W_UQ = q_b_proj.weight^T, viewed [Ntok, H, D]."""
+    d = _dims(dims)
+    q = np.asarray(cq, dtype=f64) @ np.asarray(w_q_b, dtype=f64).T
+    return q.reshape(q.shape[0], d.heads, d.nope_dim + d.shared_dim)
+
+
+def qk_clip(w_q_b, w_kv_b, max_logit, tau, dims):
+    """QK-Clip: for each head whose maximum logit exceeds tau, rescale that
+    head's query and key projection weights so the maximum becomes tau.
+
+    gamma_h = tau / S_max[h] when S_max[h] > tau, else 1. Every logit of head h
+    is q^C.K^C + q^R.k^S (then scaled); k^S is shared by all heads and is left
+    untouched, so the head's q^R rows take the whole factor gamma_h, and the
+    head-specific nope parts take sqrt(gamma_h) on each side (q^C rows of
+    q_b_proj and K^C rows of kv_b_proj). Then every logit of head h is exactly
+    gamma_h times its old value. V rows of kv_b_proj are untouched.
+
+    Returns (w_q_b' , w_kv_b', clipped mask [H] bool, gamma [H]) in float64.
+    """
+    d = _dims(dims)
+    H, N, V, S_ = d.heads, d.nope_dim, d.v_dim, d.shared_dim
+    D = N + S_
+    wq = np.array(w_q_b, dtype=f64, copy=True)
+    wk = np.array(w_kv_b, dtype=f64, copy=True)
+    sm = np.asarray(max_logit, dtype=f64)
+    mask = sm > tau
+    gamma = np.where(mask, tau / np.where(mask, sm, 1.0), 1.0)
+    for h in np.nonzero(mask)[0]:
+        g = gamma[h]
+        r = math.sqrt(g)
+        wq[h * D:h * D + N, :] *= r            # q^C rows
+        wq[h * D + N:(h + 1) * D, :] *= g      # q^R rows
+        wk[h * (N + V):h * (N + V) + N, :] *= r  # K^C rows (W_UK_h)
+    return wq, wk, mask, gamma
+
+
+def round_to(x, dtype: str):
+    """Round float64 values to the nearest 'f32' or 'bf16' value, ties to even."""
+    x = np.asarray(x, dtype=f64)
+    if dtype == "f32":
+        return x.astype(np.float32).astype(f64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    m, e = np.frexp(x)                       # x = m * 2^e, 0.5 <= |m| < 1
+    r = np.rint(m * 256.0)                   # 8 significant bits, half to even
+    return np.ldexp(r, e - 8)

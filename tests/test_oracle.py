@@ -1,0 +1,367 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself (closed forms, a library routine, brute force, invariants, the pages'
+printed numbers), chosen so that a dropped term, a wrong sign or index, or a
+transposed operand in the oracle fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._util import rel_err
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()
+                vals[k] = int(v)
+    return vals
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _id_weights(dims, uv_of_head, uk_of_head=None):
+    """kv_b_proj.weight [H*(N+V), R] built from per-head blocks (rows = output features)."""
+    H, R, N, V = dims.heads, dims.kv_rank, dims.nope_dim, dims.v_dim
+    w = np.zeros((H * (N + V), R))
+    for h in range(H):
+        w[h * (N + V):h * (N + V) + N] = np.eye(N, R) if uk_of_head is None else uk_of_head(h)
+        w[h * (N + V) + N:(h + 1) * (N + V)] = uv_of_head(h)
+    return w
+
+
+# ---------------------------------------------------------------------------
+# generator and rounding
+# ---------------------------------------------------------------------------
+
+
+def test_generator_is_deterministic():
+    a = synth.prefill_inputs(synth.TINY, [5, 7], seed=3, bf16=True)
+    b = synth.prefill_inputs(synth.TINY, [5, 7], seed=3, bf16=True)
+    c = synth.prefill_inputs(synth.TINY, [5, 7], seed=4, bf16=True)
+    for x, y in [(a.q, b.q), (a.ckv, b.ckv), (a.w_kv_b, b.w_kv_b), (a.gate, b.gate)]:
+        assert np.array_equal(x, y)
+    assert not np.array_equal(a.q, c.q)
+    assert list(a.cu_seqlens) == [0, 5, 12]
+    d = synth.decode_inputs(synth.TINY, [3, 9], cap=16, tq=1, seed=5, bf16=True)
+    assert np.array_equal(d.cache_rows(1), d.cache_rows(1))
+    assert d.cache_rows(0).shape == (3, 48)
+
+
+def test_bf16_rounding_two_implementations_agree():
+    # synth rounds float32 with integer bit arithmetic; the oracle rounds float64
+    # with frexp/rint. Both are round-to-nearest-even to 8 significant bits.
+    one = 1.0
+    assert oracle.round_to(one + 2.0 ** -8, "bf16") == 1.0                       # tie -> even
+    assert oracle.round_to(one + 3 * 2.0 ** -8, "bf16") == one + 2.0 ** -6       # tie -> even
+    assert oracle.round_to(one + 2.0 ** -8 + 2.0 ** -20, "bf16") == one + 2.0 ** -7
+    assert synth.round_bf16(np.float32([one + 2.0 ** -8]))[0] == 1.0
+    assert synth.round_bf16(np.float32([one + 3 * 2.0 ** -8]))[0] == one + 2.0 ** -6
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 37
+    assert np.array_equal(synth.round_bf16(x).astype(np.float64), oracle.round_to(x.astype(np.float64), "bf16"))
+    bits = synth.bf16_bits(synth.round_bf16(x))
+    assert np.array_equal(synth.from_bf16_bits(bits), synth.round_bf16(x))
+
+
+# ---------------------------------------------------------------------------
+# the pages' printed numbers
+# ---------------------------------------------------------------------------
+
+
+def test_layer_parameter_accounting_matches_page():
+    """The weight layouts used here (q_b_proj [H*D, q_in], kv_b_proj [H*(N+V), R],
+    a joint down-projection of width R + S) reproduce the page's exact counts."""
+    g = _golden("k3_mla_parameters.txt")
+    d = synth.K3
+    hidden, q_in = 7168, synth.K3_Q_LORA_RANK
+    D = d.nope_dim + d.shared_dim
+    w_dq = hidden * q_in
+    q_norm = q_in
+    w_q_b = (d.heads * D) * q_in
+    w_dkv = hidden * (d.kv_rank + d.shared_dim)
+    kv_norm = d.kv_rank
+    w_kv_b = (d.heads * (d.nope_dim + d.v_dim)) * d.kv_rank
+    w_g = hidden * d.heads * d.v_dim
+    w_o = d.heads * d.v_dim * hidden
+    assert w_dq + q_norm + w_q_b == g["query_heads"]
+    assert w_dkv + kv_norm + w_kv_b == g["key_and_value_heads"]
+    assert w_g == g["output_gate_projection"]
+    assert w_o == g["output_projection"]
+    total = w_dq + q_norm + w_q_b + w_dkv + kv_norm + w_kv_b + w_g + w_o
+    assert total == g["per_instance_total"]
+    assert total * 24 == g["all_24_layers"]
+
+
+def test_cache_row_width_matches_page():
+    g = _golden("k3_cache_widths.txt")
+    d = synth.K3
+    assert 2 * d.heads * d.v_dim == g["classic_values"]
+    assert d.kv_rank == g["mla_latent"] and d.shared_dim == g["mla_shared"]
+    assert round(g["classic_values"] / (d.kv_rank + d.shared_dim)) == g["ratio_rounded"]
+
+
+# ---------------------------------------------------------------------------
+# materialised (training) form
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("gate", [True, False])
+def test_blocked_oracle_equals_brute_force(gate):
+    p = synth.prefill_inputs(synth.TINY, [23, 1, 0, 40], seed=11, bf16=False, gate=gate)
+    out, lse, sm = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims, block=7)
+    out2, probs, sm2 = oracle.dense_prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims)
+    assert rel_err(out, out2) < 1e-12
+    assert np.allclose(sm, sm2, rtol=1e-13, atol=0)
+    # lse brackets the row maximum: max_s S <= lse <= max_s S + log(#visible)
+    assert np.all(np.isfinite(lse))
+
+
+def test_softmax_rows_sum_to_one_and_masked_weights_are_zero():
+    p = synth.prefill_inputs(synth.TINY, [9, 14], seed=2, bf16=False)
+    _, probs, _ = oracle.dense_prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims)
+    assert np.allclose(probs.sum(axis=-1), 1.0, atol=1e-14)
+    n = int(p.cu_seqlens[-1])
+    seq = np.repeat([0, 1], [9, 14])
+    pos = np.arange(n)
+    forbidden = (seq[:, None] != seq[None, :]) | (pos[None, :] > pos[:, None])
+    assert np.all(probs[:, forbidden] == 0.0)
+    assert np.all(probs[:, ~forbidden] > 0.0)
+
+
+def test_single_token_returns_gated_value_row():
+    """T = 1: the only weight is 1, so o = sigma(g) . V_0 with V_0 = c_0 W_UV_h.
+    With W_UV_h = (h+1) I (and random W_UK_h) this is (h+1) sigma(g) c_0."""
+    dims = oracle.Dims(3, 8, 4, 8, 8)
+    rng = np.random.default_rng(0)
+    w = _id_weights(dims, lambda h: (h + 1) * np.eye(8), lambda h: rng.standard_normal((8, 8)))
+    q, ckv, ks, g = _rand(rng, 1, 3, 12), _rand(rng, 1, 8), _rand(rng, 1, 4), _rand(rng, 1, 24)
+    out, lse, sm = oracle.prefill(q, ckv, ks, w, g, [0, 1], dims)
+    expect = np.concatenate([(h + 1) * ckv[0] for h in range(3)]) / (1 + np.exp(-g[0]))
+    assert rel_err(out[0], expect) < 1e-14
+    assert np.allclose(lse[:, 0], sm)          # one visible key: lse = its logit
+
+
+def test_zero_query_gives_prefix_mean_per_sequence():
+    """q = 0: every visible logit is 0, A_{t,s} = 1/(t+1), so O~_t is the running
+    mean of V over its own sequence."""
+    dims = oracle.Dims(2, 6, 3, 6, 6)
+    rng = np.random.default_rng(1)
+    w = _id_weights(dims, lambda h: (2 * h - 1.5) * np.eye(6), lambda h: rng.standard_normal((6, 6)))
+    lens = [5, 8]
+    n = sum(lens)
+    ckv, ks = _rand(rng, n, 6), _rand(rng, n, 3)
+    q = np.zeros((n, 2, 9))
+    out, lse, sm = oracle.prefill(q, ckv, ks, w, None, [0, 5, 13], dims)
+    expect = np.zeros((n, 12))
+    for a, b in [(0, 5), (5, 13)]:
+        cm = np.cumsum(ckv[a:b], axis=0) / np.arange(1, b - a + 1)[:, None]
+        for h in range(2):
+            expect[a:b, h * 6:(h + 1) * 6] = (2 * h - 1.5) * cm
+    assert rel_err(out, expect) < 1e-14
+    assert np.all(sm == 0.0)
+    pos = np.array([0, 1, 2, 3, 4, 0, 1, 2, 3, 4, 5, 6, 7])
+    assert np.allclose(lse, np.log(pos + 1)[None], atol=1e-15)
+
+
+def test_gate_zero_halves_and_saturated_gate_selects_heads():
+    p = synth.prefill_inputs(synth.TINY, [17], seed=5, bf16=False)
+    ungated, _, _ = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, None, p.cu_seqlens, p.dims)
+    half, _, _ = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, np.zeros_like(p.gate), p.cu_seqlens, p.dims)
+    assert rel_err(half, ungated / 2) < 1e-15
+    V = p.dims.v_dim
+    g = np.full_like(p.gate, -800.0)
+    g[:, 2 * V:3 * V] = 800.0                  # open head 2 only
+    sel, _, _ = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, g, p.cu_seqlens, p.dims)
+    assert np.array_equal(sel[:, 2 * V:3 * V], ungated[:, 2 * V:3 * V])
+    assert np.all(sel[:, :2 * V] == 0) and np.all(sel[:, 3 * V:] == 0)
+
+
+def test_matches_torch_causal_sdpa_in_identity_special_case():
+    """R = N, W_UK_h = I, W_UV_h = a permutation P_h: then K_h = [c, k^S] and
+    V_h = c P_h^T, so each head is textbook causal scaled-dot-product attention
+    with the default scale 1/sqrt(q width) = 1/sqrt(N+S)."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    H, N, S = 3, 16, 8
+    dims = oracle.Dims(H, N, S, N, N)
+    rng = np.random.default_rng(7)
+    perms = [rng.permutation(N) for _ in range(H)]
+    w = _id_weights(dims, lambda h: np.eye(N)[perms[h]])
+    T = 37
+    q, ckv, ks = _rand(rng, T, H, N + S), _rand(rng, T, N), _rand(rng, T, S)
+    out, _, _ = oracle.prefill(q, ckv, ks, w, None, [0, T], dims, block=8)
+    for h in range(H):
+        qt = torch.from_numpy(q[:, h, :])[None, None]
+        kt = torch.from_numpy(np.concatenate([ckv, ks], axis=1))[None, None]
+        vt = torch.from_numpy(ckv[:, perms[h]])[None, None]
+        ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True)[0, 0].numpy()
+        assert rel_err(out[:, h * N:(h + 1) * N], ref) < 1e-12
+
+
+def test_max_logit_closed_form_respects_causality():
+    """q_t = (T-1-t) e_1, c_s = s e_1, k^S = 0, W_UK = I: logit(t, s) =
+    (T-1-t) s / sqrt(D) for s <= t, largest at t = floor((T-1)/2) with value
+    t (T-1-t) / sqrt(D). Without the mask it would be (T-1)^2 / sqrt(D)."""
+    dims = oracle.Dims(1, 4, 2, 4, 4)
+    D = 6
+    lens = [64, 9]
+    qs, cs = [], []
+    for T in lens:
+        q = np.zeros((T, 1, D))
+        q[:, 0, 0] = np.arange(T - 1, -1, -1)
+        c = np.zeros((T, 4))
+        c[:, 0] = np.arange(T)
+        qs.append(q)
+        cs.append(c)
+    q = np.concatenate(qs)
+    c = np.concatenate(cs)
+    ks = np.zeros((sum(lens), 2))
+    w = _id_weights(dims, lambda h: np.eye(4))
+    _, _, sm = oracle.prefill(q, c, ks, w, None, [0, 64, 73], dims, block=16)
+    assert sm[0] == pytest.approx(31 * 32 / math.sqrt(D), rel=1e-15)
+    assert oracle.max_logit_head(q, c, ks, w, [0, 64, 73], dims, 0) == pytest.approx(31 * 32 / math.sqrt(D), rel=1e-15)
+    _, _, sm2 = oracle.dense_prefill(q, c, ks, w, None, [0, 64, 73], dims)
+    assert sm2[0] == pytest.approx(31 * 32 / math.sqrt(D), rel=1e-15)
+
+
+def test_lse_brackets_row_max_and_rows_are_independent():
+    p = synth.prefill_inputs(synth.TINY, [30], seed=9, bf16=False)
+    out, lse, sm = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims, block=4)
+    for h in range(p.dims.heads):
+        rows = [0, 7, 29]
+        o, l = oracle.prefill_rows(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims, h, rows)
+        V = p.dims.v_dim
+        assert rel_err(o, out[rows, h * V:(h + 1) * V]) < 1e-13
+        assert np.allclose(l, lse[h, rows], rtol=1e-14)
+    assert np.all(lse.max(axis=1) >= sm - 1e-12)
+    assert np.all(lse[:, 0] <= sm + 1e-12)   # row 0 has a single key
+
+
+# ---------------------------------------------------------------------------
+# absorbed (inference) form
+# ---------------------------------------------------------------------------
+
+
+def test_absorbed_equals_materialised_on_tiny_fp32_workload():
+    p, q4, cache, lens, g4 = synth.tiny_fp32_absorbed()
+    ref, _, sm_ref = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims)
+    out, sm = oracle.absorbed(q4, [cache[0]], p.w_kv_b, g4, p.dims)
+    assert rel_err(out[0], ref) < 1e-10
+    assert np.allclose(sm, sm_ref, rtol=1e-12)
+
+
+@pytest.mark.parametrize("tq", [1, 3])
+def test_absorbed_decode_is_last_rows_of_prefill(tq):
+    dims = synth.TINY
+    p = synth.prefill_inputs(dims, [21, 40], seed=4, bf16=True)
+    ref, _, _ = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims)
+    rows = [np.concatenate([p.ckv[a:b], p.ks[a:b]], axis=1) for a, b in [(0, 21), (21, 61)]]
+    q = np.stack([p.q[21 - tq:21], p.q[61 - tq:61]])
+    g = np.stack([p.gate[21 - tq:21], p.gate[61 - tq:61]])
+    out, sm = oracle.absorbed(q, rows, p.w_kv_b, g, dims)
+    assert rel_err(out[0], ref[21 - tq:21]) < 1e-10
+    assert rel_err(out[1], ref[61 - tq:61]) < 1e-10
+    sm_rows = oracle.absorbed_rows_selected(q, rows, p.w_kv_b, g, dims, [0, 1])[1]
+    assert np.array_equal(sm_rows, sm)
+
+
+def test_absorbed_max_logit_matches_materialised_last_rows():
+    dims = synth.TINY
+    p = synth.prefill_inputs(dims, [33], seed=8, bf16=True)
+    tq = 5
+    rows = [np.concatenate([p.ckv, p.ks], axis=1)]
+    _, sm = oracle.absorbed(p.q[None, 33 - tq:], rows, p.w_kv_b, None, dims)
+    # the same logits from the materialised side: K_h = [K^C_h, k^S], scaled dot
+    for h in range(dims.heads):
+        kc, _ = oracle.expand_latent(p.ckv, p.w_kv_b, dims, h)
+        K = np.concatenate([kc, p.ks], axis=1)
+        best = -np.inf
+        for t in range(33 - tq, 33):
+            best = max(best, float((K[:t + 1] @ p.q[t, h].astype(np.float64)).max()) * oracle.mla_oracle.scale_of(dims))
+        assert sm[h] == pytest.approx(best, rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# QK-Clip
+# ---------------------------------------------------------------------------
+
+
+def _tiny_clip_case(T=24):
+    dims = oracle.Dims(4, 16, 8, 16, 16)
+    rng = np.random.default_rng(21)
+    q_in = 20
+    cq = rng.standard_normal((T, q_in))
+    wq = rng.standard_normal((4 * 24, q_in)) / math.sqrt(q_in)
+    ckv = rng.standard_normal((T, 16))
+    ks = rng.standard_normal((T, 8))
+    w = rng.standard_normal((4 * 32, 16)) / 4.0
+    wq[1 * 24:2 * 24] *= 40.0
+    w[1 * 32:1 * 32 + 16] *= 40.0
+    return dims, cq, wq, ckv, ks, w
+
+
+def test_qk_clip_scales_every_logit_of_a_clipped_head_by_gamma():
+    dims, cq, wq, ckv, ks, w = _tiny_clip_case()
+    T = cq.shape[0]
+    q = oracle.q_projection(cq, wq, dims)
+    _, probs0, sm = oracle.dense_prefill(q, ckv, ks, w, None, [0, T], dims)
+    tau = 3.0 * np.sort(sm)[-2]     # only head 1 (x40) exceeds tau
+    wq2, w2, mask, gamma = oracle.qk_clip(wq, w, sm, tau, dims)
+    assert list(mask) == [False, True, False, False]
+    assert gamma[1] == pytest.approx(tau / sm[1], rel=1e-15) and np.all(gamma[[0, 2, 3]] == 1.0)
+    q2 = oracle.q_projection(cq, wq2, dims)
+    # raw scaled logits before and after, for every head
+    for h in range(4):
+        kc, _ = oracle.expand_latent(ckv, w, dims, h)
+        kc2, _ = oracle.expand_latent(ckv, w2, dims, h)
+        S1 = q[:, h] @ np.concatenate([kc, ks], 1).T
+        S2 = q2[:, h] @ np.concatenate([kc2, ks], 1).T
+        assert np.allclose(S2, gamma[h] * S1, rtol=1e-12, atol=1e-12 * np.abs(S1).max())
+    _, _, sm2 = oracle.prefill(q2, ckv, ks, w2, None, [0, T], dims)
+    assert sm2[1] == pytest.approx(tau, rel=1e-12)
+    # unclipped heads: same logits up to the BLAS's rounding order
+    assert np.allclose(sm2[[0, 2, 3]], sm[[0, 2, 3]], rtol=1e-14, atol=0)
+    # untouched: unclipped heads' rows, every V row
+    for h in (0, 2, 3):
+        assert np.array_equal(wq2[h * 24:(h + 1) * 24], wq[h * 24:(h + 1) * 24])
+        assert np.array_equal(w2[h * 32:(h + 1) * 32], w[h * 32:(h + 1) * 32])
+    assert np.array_equal(w2[32 + 16:64], w[32 + 16:64])
+
+
+def test_qk_clip_threshold_is_strict():
+    dims = oracle.Dims(5, 4, 2, 4, 4)
+    rng = np.random.default_rng(3)
+    wq = rng.standard_normal((5 * 6, 7))
+    w = rng.standard_normal((5 * 8, 4))
+    tau = 10.0
+    sm = np.array([tau - 1e-9, tau, tau * (1 + 1e-12), -np.inf, 1e6])
+    wq2, w2, mask, gamma = oracle.qk_clip(wq, w, sm, tau, dims)
+    assert list(mask) == [False, False, True, False, True]
+    assert gamma[4] == tau / 1e6 and gamma[3] == 1.0
+    assert np.array_equal(wq2[:12], wq[:12])
+    assert np.allclose(wq2[4 * 6:4 * 6 + 4], wq[4 * 6:4 * 6 + 4] * math.sqrt(1e-5), rtol=1e-15)
+    assert np.allclose(wq2[4 * 6 + 4:5 * 6], wq[4 * 6 + 4:5 * 6] * 1e-5, rtol=1e-15)
+
+
+def test_clip_stress_recipe_clips_exactly_the_scaled_heads():
+    """The QK-Clip stress recipe at reduced length: the x40 heads reach logits
+    above 1000 and are the only ones above tau = 100 (unscaled heads stay near 5)."""
+    p = synth.clip_stress_inputs(synth.K3, 96, seed=3)
+    q = synth.round_bf16(oracle.q_projection(p.cq, p.w_q_b, p.dims).astype(np.float32))
+    sm = np.array([oracle.max_logit_head(q, p.ckv, p.ks, p.w_kv_b, p.cu_seqlens, p.dims, h)
+                   for h in range(96)])
+    mask = sm > synth.TAU
+    assert list(np.nonzero(mask)[0]) == list(synth.CLIP_HEADS)
+    assert sm[mask].min() > 1000.0
+    assert sm[~mask].max() < 10.0
