@@ -1,0 +1,220 @@
+"""Benchmark of the gated-MLA hot path on one MI355X.
+
+One step = the whole path on seeded synthetic inputs shaped like Kimi K3's MLA
+layers, inputs resident in HBM:
+  1. mla_prefill  : training-form gated prefill, B=1, T=4096, H=96, bf16 in,
+                    fp32 out, with the fused per-head max logit;
+  2. mla_qk_clip  : QK-Clip on q_b_proj / kv_b_proj from that max logit (tau=100);
+  3. mla_absorbed : absorbed decode, 64 sequences x 1 query over a latent cache
+                    of up to 32768 rows x 576 bf16 per sequence.
+
+``value`` is the prefill's algorithmic TFLOP/s (expansion + QK^T + PV over the
+causal pairs) from HIP events around the prefill calls; the decode's cache
+GB/s and the per-kernel roofline figures are reported beside it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "MLA prefill TFLOP/s (%MFMA peak); absorbed decode cache GB/s (%HBM peak)"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_flops(T: int, H: int, R: int = 512, D: int = 192, V: int = 128):
+    pairs = T * (T + 1) // 2
+    qk = 2.0 * H * pairs * D
+    pv = 2.0 * H * pairs * V
+    expand = 2.0 * T * H * 256 * R
+    return qk, pv, expand
+
+
+def cpu_baseline(p, budget_s: float = 12.0):
+    """The oracle (fp64 NumPy) on a bounded sample of the same prefill: whole
+    heads, one after another, until about ``budget_s`` seconds have passed."""
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    T, H = p.ntok, p.dims.heads
+    qk, pv, ex = prefill_flops(T, H)
+    per_head = (qk + pv + ex) / H
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < H:
+        oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims, heads=[heads])
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": per_head * heads / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {H} heads of the T={T} prefill (fp64 NumPy), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mla_qk_clip_amd as m
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+
+    def up(x, dt=torch.bfloat16):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(dt)
+
+    log("generating the prefill workload (T=4096, H=96)")
+    p = synth.k3_prefill()
+    dims = m.Dims()
+    q, ckv, ks = up(p.q), up(p.ckv), up(p.ks)
+    w_kv_b, gate = up(p.w_kv_b), up(p.gate)
+    w_q_b = up(synth.k3_q_weight())
+    cu = torch.from_numpy(p.cu_seqlens).to(dev)
+    T = p.ntok
+    out = torch.empty((T, 96 * 128), dtype=torch.float32, device=dev)
+    ml = torch.empty(96, dtype=torch.float32, device=dev)
+    ws = torch.empty(m.mla_prefill_workspace_size(dims, m.MLA_BF16, T, 1), dtype=torch.uint8, device=dev)
+    clipped = torch.empty(96, dtype=torch.uint8, device=dev)
+    gamma = torch.empty(96, dtype=torch.float32, device=dev)
+
+    decode = not args.no_decode
+    if decode:
+        log("generating the decode workload (64 x <=32768 rows x 576)")
+        d = synth.k3_decode()
+        cache = torch.full((d.batch, d.cap, 576), float("nan"), dtype=torch.bfloat16, device=dev)
+        for b in range(d.batch):
+            rows = d.cache_rows(b)
+            cache[b, :rows.shape[0]] = up(rows)
+        dq, dg, dw = up(d.q), up(d.gate), up(d.w_kv_b)
+        lens = torch.from_numpy(d.lens).to(dev)
+        dout = torch.empty((d.batch, 1, 96 * 128), dtype=torch.bfloat16, device=dev)
+        dml = torch.empty(96, dtype=torch.float32, device=dev)
+        dws = torch.empty(m.mla_absorbed_workspace_size(dims, m.MLA_BF16, d.batch, 1), dtype=torch.uint8,
+                          device=dev)
+        cache_bytes = float(d.lens.astype(np.int64).sum()) * 576 * 2
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        m.mla_prefill(dims, q, ckv, ks, w_kv_b, gate, cu, out=out, max_logit=ml, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        m.mla_qk_clip(dims, w_q_b, w_kv_b, ml, synth.TAU, clipped=clipped, gamma=gamma)
+        if ev is not None:
+            ev[2].record(stream)
+        if decode:
+            m.mla_absorbed(dims, dq, cache, lens, dw, dg, out=dout, max_logit=dml, workspace=dws)
+        if ev is not None:
+            ev[3].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    pre_ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    clip_ms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+    dec_ms = float(np.median([e[2].elapsed_time(e[3]) for e in evs])) if decode else None
+
+    # per-kernel averages, measured in a second pass with per-launch events
+    log("per-kernel timing pass")
+    m.mla_timing_enable(True)
+    for _ in range(min(args.steps, 10)):
+        step()
+    torch.cuda.synchronize()
+    kern = {}
+    for k in ("prefill_plan", "prefill_expand", "prefill_attn", "qk_clip", "absorbed_prefix", "absorb_q",
+              "absorbed_split", "absorbed_combine", "fill"):
+        tot, n = m.mla_timing_read(k)
+        if n:
+            kern[k] = tot / n
+    m.mla_timing_enable(False)
+
+    qk, pv, ex = prefill_flops(T, 96)
+    pre_tflops = (qk + pv + ex) / (pre_ms * 1e-3) / 1e12
+    attn_tflops = (qk + pv) / (kern["prefill_attn"] * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Kimi K3 gated MLA prefill B=1 T=4096 H=96 bf16 (step also runs QK-Clip and "
+                               "absorbed decode B=64 cache<=32768x576)",
+                   "heads": 96, "kv_rank": 512, "shared": 64, "nope": 128, "v": 128, "seq_len": T},
+        "prefill": {"ms": round(pre_ms, 4), "tflops": round(pre_tflops, 2),
+                    "frac_mfma_peak": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+                    "gflop": round((qk + pv + ex) / 1e9, 1)},
+        "qk_clip": {"ms": round(clip_ms, 4)},
+        "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "roofline": {"kernel": "prefill_attn", "bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "algorithmic": f"{(qk + pv) / 1e9:.1f} GFLOP per launch (QK^T + PV)"},
+    }
+    if decode:
+        gbps = cache_bytes / (dec_ms * 1e-3) / 1e9
+        split_gbps = cache_bytes / (kern["absorbed_split"] * 1e-3) / 1e9
+        res["decode"] = {"ms": round(dec_ms, 4), "cache_gbps": round(gbps, 1),
+                         "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4), "cache_bytes": int(cache_bytes),
+                         "sum_lens": int(d.lens.sum())}
+        res["decode_roofline"] = {"kernel": "absorbed_split", "bound": "hbm", "achieved": round(split_gbps, 1),
+                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(split_gbps / PEAK_HBM_GBPS, 4),
+                                  "traffic": None}
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(p)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

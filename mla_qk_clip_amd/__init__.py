@@ -1,0 +1,212 @@
+"""Python binding of libmla (gated no-position MLA, per-head max logit, QK-Clip)
+for AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libmla.so``. PyTorch provides device memory and the current HIP stream.
+Names match the C ABI in ``include/mla.h``. The library must have been built
+(``python mla_qk_clip_amd/build.py``); importing this package without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_OK, MLA_ERR_INVALID, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
+MLA_F32, MLA_BF16 = 0, 1
+
+EXPORTED = (
+    "mla_prefill_workspace_size", "mla_prefill", "mla_absorbed_workspace_size", "mla_absorbed",
+    "mla_qk_clip", "mla_status_string", "mla_last_error", "mla_version", "mla_timing_enable",
+    "mla_timing_read",
+)
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libmla status {status}: {msg}")
+        self.status = status
+
+
+class mla_dims(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("kv_rank", ctypes.c_int32), ("shared_dim", ctypes.c_int32),
+                ("nope_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+@dataclass(frozen=True)
+class Dims:
+    heads: int = 96
+    kv_rank: int = 512
+    shared_dim: int = 64
+    nope_dim: int = 128
+    v_dim: int = 128
+    scale: float = 0.0   # 0 -> (nope + shared) ** -0.5
+
+    def c(self) -> mla_dims:
+        return mla_dims(self.heads, self.kv_rank, self.shared_dim, self.nope_dim, self.v_dim, self.scale)
+
+    @property
+    def qk_dim(self) -> int:
+        return self.nope_dim + self.shared_dim
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python mla_qk_clip_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    D = ctypes.POINTER(mla_dims)
+    lib.mla_prefill_workspace_size.argtypes = [D, I32, I64, I32]
+    lib.mla_prefill_workspace_size.restype = SZ
+    lib.mla_prefill.argtypes = [D, I32, I32, P, P, P, P, P, P, I32, I64, P, P, P, I32, P, SZ, P]
+    lib.mla_prefill.restype = I32
+    lib.mla_absorbed_workspace_size.argtypes = [D, I32, I32, I32]
+    lib.mla_absorbed_workspace_size.restype = SZ
+    lib.mla_absorbed.argtypes = [D, I32, I32, P, P, I64, P, I32, I32, P, P, P, P, I32, P, SZ, P]
+    lib.mla_absorbed.restype = I32
+    lib.mla_qk_clip.argtypes = [D, I32, P, I32, P, P, F, P, P, P]
+    lib.mla_qk_clip.restype = I32
+    lib.mla_status_string.argtypes = [I32]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_version.argtypes = []
+    lib.mla_version.restype = ctypes.c_char_p
+    lib.mla_timing_enable.argtypes = [I32]
+    lib.mla_timing_enable.restype = None
+    lib.mla_timing_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]
+    lib.mla_timing_read.restype = I32
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != MLA_OK:
+        raise MlaError(status, f"{lib.mla_status_string(status).decode()}: {lib.mla_last_error().decode()}")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    if t.dtype == torch.float32:
+        return MLA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _torch_dt(code: int):
+    return torch.bfloat16 if code == MLA_BF16 else torch.float32
+
+
+def mla_prefill_workspace_size(dims: Dims, in_dtype: int, total_tokens: int, nseq: int) -> int:
+    return int(lib.mla_prefill_workspace_size(ctypes.byref(dims.c()), in_dtype, total_tokens, nseq))
+
+
+def mla_absorbed_workspace_size(dims: Dims, in_dtype: int, batch: int, tq: int) -> int:
+    return int(lib.mla_absorbed_workspace_size(ctypes.byref(dims.c()), in_dtype, batch, tq))
+
+
+def mla_prefill(dims: Dims, q, ckv, ks, w_kv_b, gate, cu_seqlens, *, out_dtype=None, out=None, lse=None,
+                max_logit=None, accumulate=False, workspace=None, want_lse=False, stream=None):
+    """Training-form gated MLA over packed sequences (see ``mla_prefill`` in include/mla.h).
+
+    q [T, H, N+S], ckv [T, R], ks [T, S], w_kv_b [H*(N+V), R], gate [T, H*V] or None,
+    cu_seqlens int32 [nseq+1] on the device. Returns (out [T, H*V], lse or None, max_logit [H]).
+    """
+    in_dt = _dt(q)
+    out_dt = MLA_F32 if out_dtype is None else (MLA_BF16 if out_dtype == torch.bfloat16 else MLA_F32)
+    T = q.shape[0]
+    nseq = cu_seqlens.numel() - 1
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, dims.heads * dims.v_dim), dtype=_torch_dt(out_dt), device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((dims.heads, T), dtype=torch.float32, device=dev)
+    if max_logit is None:
+        max_logit = torch.empty(dims.heads, dtype=torch.float32, device=dev)
+    need = mla_prefill_workspace_size(dims, in_dt, T, nseq)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.mla_prefill(ctypes.byref(dims.c()), in_dt, out_dt, _ptr(q), _ptr(ckv), _ptr(ks), _ptr(w_kv_b),
+                         _ptr(gate), _ptr(cu_seqlens), nseq, T, _ptr(out), _ptr(lse), _ptr(max_logit),
+                         1 if accumulate else 0, _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st)
+    return out, lse, max_logit
+
+
+def mla_absorbed(dims: Dims, q, cache, lens, w_kv_b, gate, *, out_dtype=None, out=None, max_logit=None,
+                 accumulate=False, workspace=None, stream=None):
+    """Absorbed-form gated MLA over the latent cache (see ``mla_absorbed`` in include/mla.h).
+
+    q [B, Tq, H, N+S], cache [B, cap, R+S], lens int32 [B] on the device, w_kv_b [H*(N+V), R],
+    gate [B, Tq, H*V] or None. Returns (out [B, Tq, H*V], max_logit [H]).
+    """
+    in_dt = _dt(q)
+    out_dt = in_dt if out_dtype is None else (MLA_BF16 if out_dtype == torch.bfloat16 else MLA_F32)
+    B, Tq = q.shape[0], q.shape[1]
+    cap = cache.shape[1]
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Tq, dims.heads * dims.v_dim), dtype=_torch_dt(out_dt), device=dev)
+    if max_logit is None:
+        max_logit = torch.empty(dims.heads, dtype=torch.float32, device=dev)
+    need = mla_absorbed_workspace_size(dims, in_dt, B, Tq)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.mla_absorbed(ctypes.byref(dims.c()), in_dt, out_dt, _ptr(q), _ptr(cache), cap, _ptr(lens), B, Tq,
+                          _ptr(w_kv_b), _ptr(gate), _ptr(out), _ptr(max_logit), 1 if accumulate else 0,
+                          _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st)
+    return out, max_logit
+
+
+def mla_qk_clip(dims: Dims, w_q_b, w_kv_b, max_logit, tau: float, *, clipped=None, gamma=None, stream=None):
+    """QK-Clip in place on q_b_proj.weight [H*D, q_in] and kv_b_proj.weight [H*(N+V), R].
+
+    Returns (clipped uint8 [H], gamma fp32 [H]).
+    """
+    dev = w_q_b.device
+    if clipped is None:
+        clipped = torch.empty(dims.heads, dtype=torch.uint8, device=dev)
+    if gamma is None:
+        gamma = torch.empty(dims.heads, dtype=torch.float32, device=dev)
+    st = lib.mla_qk_clip(ctypes.byref(dims.c()), _dt(w_q_b), _ptr(w_q_b), w_q_b.shape[1], _ptr(w_kv_b),
+                         _ptr(max_logit), float(tau), _ptr(clipped), _ptr(gamma), _stream(stream))
+    _check(st)
+    return clipped, gamma
+
+
+def mla_timing_enable(on: bool) -> None:
+    lib.mla_timing_enable(1 if on else 0)
+
+
+def mla_timing_read(kernel: str):
+    """(total milliseconds, launches) of one kernel since timing was enabled."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    lib.mla_timing_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n))
+    return ms.value, n.value
+
+
+def default_scale(dims: Dims) -> float:
+    return dims.scale if dims.scale > 0 else 1.0 / math.sqrt(dims.qk_dim)

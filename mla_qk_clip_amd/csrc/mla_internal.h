@@ -1,0 +1,99 @@
+// Host-side launch helpers shared between the C ABI front end and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Kimi K3 head shape compiled into the bf16 MFMA kernels.
+constexpr int kR = 512;   // kv_rank
+constexpr int kS = 64;    // shared key width
+constexpr int kN = 128;   // nope width
+constexpr int kV = 128;   // value width
+constexpr int kD = kN + kS;
+
+// Prefill (bf16) tiling.
+constexpr int kPrefBM = 128;  // queries per workgroup
+constexpr int kPrefBN = 64;   // keys per inner tile
+constexpr int kSeqPad = 64;   // per-sequence padding of the expanded K^C / V^T
+
+// Absorbed (bf16) split-K.
+constexpr int kDecSplits = 256;  // workgroups of the split kernel
+constexpr int kDecRows = 32;     // cache rows per inner tile
+constexpr int kDecMaxHeads = 128;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace layout of the bf16 prefill.
+struct PrefillWs {
+  size_t kc, vt, pcu, order, toff, hdr, total;
+  int64_t npad_max;
+};
+inline PrefillWs prefill_ws_layout(int heads, int64_t ntok, int nseq) {
+  PrefillWs w{};
+  w.npad_max = static_cast<int64_t>(align_up(static_cast<size_t>(ntok + static_cast<int64_t>(kSeqPad) * nseq), 128));
+  size_t off = 0;
+  w.kc = off; off = align_up(off + static_cast<size_t>(heads) * w.npad_max * kN * 2, 256);
+  w.vt = off; off = align_up(off + static_cast<size_t>(heads) * w.npad_max * kV * 2, 256);
+  w.pcu = off; off = align_up(off + static_cast<size_t>(nseq + 1) * 4, 256);
+  w.order = off; off = align_up(off + static_cast<size_t>(nseq + 1) * 4, 256);
+  w.toff = off; off = align_up(off + static_cast<size_t>(nseq + 1) * 4, 256);
+  w.hdr = off; off = align_up(off + 64, 256);
+  w.total = off;
+  return w;
+}
+
+// Workspace layout of the fp32 prefill: K^C [H][Ntok][N], V [H][Ntok][V].
+inline size_t prefill_f32_ws(int heads, int64_t ntok, int N, int V) {
+  return align_up(static_cast<size_t>(heads) * ntok * (N + V) * 4, 256);
+}
+
+// Workspace layout of the bf16 absorbed path.
+struct AbsorbedWs {
+  size_t qabs, prefix, part_o, part_ml, total;
+  int64_t slots;
+};
+inline AbsorbedWs absorbed_ws_layout(int heads, int batch, int tq) {
+  AbsorbedWs w{};
+  const int64_t bt = static_cast<int64_t>(batch) * tq;
+  w.slots = kDecSplits + bt;
+  size_t off = 0;
+  w.qabs = off; off = align_up(off + static_cast<size_t>(bt) * heads * (kR + kS) * 2, 256);
+  w.prefix = off; off = align_up(off + static_cast<size_t>(bt + 1) * 8, 256);
+  w.part_o = off; off = align_up(off + static_cast<size_t>(w.slots) * heads * kR * 4, 256);
+  w.part_ml = off; off = align_up(off + static_cast<size_t>(w.slots) * heads * 2 * 4, 256);
+  w.total = off;
+  return w;
+}
+
+// ---- launchers (defined next to their kernels) ----
+
+hipError_t launch_fill(float* p, int n, float v, hipStream_t st);
+
+hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16,
+                               const void* q, const void* ckv, const void* ks, const void* w_kv_b,
+                               const void* gate, const int32_t* cu, int nseq, int64_t ntok,
+                               void* out, float* lse, float* max_logit, void* ws, hipStream_t st);
+
+hipError_t launch_prefill_f32(int heads, int R, int S, int N, int V, float scale,
+                              const float* q, const float* ckv, const float* ks, const float* w_kv_b,
+                              const float* gate, const int32_t* cu, int nseq, int64_t ntok,
+                              float* out, float* lse, float* max_logit, void* ws, hipStream_t st);
+
+hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16,
+                                const void* q, const void* cache, int64_t cap, const int32_t* lens,
+                                int batch, int tq, const void* w_kv_b, const void* gate, void* out,
+                                float* max_logit, void* ws, hipStream_t st);
+
+hipError_t launch_absorbed_f32(int heads, int R, int S, int N, int V, float scale,
+                               const float* q, const float* cache, int64_t cap, const int32_t* lens,
+                               int batch, int tq, const float* w_kv_b, const float* gate, float* out,
+                               float* max_logit, hipStream_t st);
+
+hipError_t launch_qk_clip(int heads, int S, int N, int V, bool bf16, void* w_q_b, int q_in, int R,
+                          void* w_kv_b, const float* max_logit, float tau, uint8_t* clipped,
+                          float* gamma, hipStream_t st);
+
+}  // namespace mla

@@ -282,3 +282,9 @@ def k3_clip_stress(seed: int = 3, seqlen: int = 2048) -> PrefillInputs:
 def k3_varlen(seed: int = 4, seqlens=VARLEN_SEQLENS) -> PrefillInputs:
     """Long-context packed varlen prefill: 32768 + 16384 + 8192 + 2048 tokens."""
     return prefill_inputs(K3, list(seqlens), seed, bf16=True)
+
+
+def k3_q_weight(seed: int = 11, q_in: int = K3_Q_LORA_RANK) -> np.ndarray:
+    """q_b_proj.weight [96*192, 1536] ~ N(0,1)/sqrt(1536), bf16 (for a clip step without clipped heads)."""
+    rng = np.random.default_rng(seed)
+    return round_bf16(_normal(rng, (K3.heads * K3.qk_dim, q_in), 1.0 / math.sqrt(q_in)))

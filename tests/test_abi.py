@@ -1,0 +1,109 @@
+"""The C-ABI library loads, exports every symbol include/mla.h declares, and
+rejects bad arguments with status codes before launching anything (no GPU
+needed: every case here fails validation on the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    import mla_qk_clip_amd
+    return mla_qk_clip_amd
+
+
+def test_every_declared_symbol_is_exported(m):
+    names = _declared()
+    assert "mla_prefill" in names and "mla_absorbed" in names and "mla_qk_clip" in names
+    for n in names:
+        assert hasattr(m.lib, n), n
+    assert set(names) == set(m.EXPORTED)
+
+
+def test_version_and_status_strings(m):
+    assert b"gfx950" in m.lib.mla_version()
+    for s in range(5):
+        assert m.lib.mla_status_string(s)
+
+
+def _prefill(m, dims, **kw):
+    args = dict(in_dt=m.MLA_BF16, out_dt=m.MLA_F32, q=16, ckv=16, ks=16, w=16, gate=None, cu=16, nseq=1, ntok=10,
+                out=16, lse=None, ml=16, acc=0, ws=16, wsb=1 << 40)
+    args.update(kw)
+    d = dims.c()
+    return m.lib.mla_prefill(ctypes.byref(d), args["in_dt"], args["out_dt"], args["q"], args["ckv"], args["ks"],
+                             args["w"], args["gate"], args["cu"], args["nseq"], args["ntok"], args["out"],
+                             args["lse"], args["ml"], args["acc"], args["ws"], args["wsb"], None)
+
+
+def test_prefill_validation(m):
+    K3 = m.Dims()
+    assert _prefill(m, K3, ml=None) == m.MLA_ERR_INVALID
+    assert b"max_logit" in m.lib.mla_last_error()
+    assert _prefill(m, K3, q=None) == m.MLA_ERR_INVALID
+    assert _prefill(m, K3, q=24) == m.MLA_ERR_INVALID            # misaligned
+    assert b"aligned" in m.lib.mla_last_error()
+    assert _prefill(m, K3, ws=16, wsb=10) == m.MLA_ERR_WORKSPACE
+    assert _prefill(m, K3, acc=2) == m.MLA_ERR_INVALID
+    assert _prefill(m, K3, nseq=0) == m.MLA_ERR_INVALID
+    assert _prefill(m, K3, ntok=-1) == m.MLA_ERR_INVALID
+    assert _prefill(m, K3, in_dt=7) == m.MLA_ERR_INVALID
+    assert _prefill(m, K3, in_dt=m.MLA_F32, out_dt=m.MLA_BF16) == m.MLA_ERR_UNSUPPORTED
+    assert _prefill(m, m.Dims(96, 256, 64, 128, 128)) == m.MLA_ERR_UNSUPPORTED   # bf16 shape not compiled
+    assert _prefill(m, m.Dims(0, 512, 64, 128, 128)) == m.MLA_ERR_INVALID
+    assert _prefill(m, m.Dims(4, 2048, 16, 32, 32), in_dt=m.MLA_F32) == m.MLA_ERR_UNSUPPORTED
+    assert m.lib.mla_prefill(None, 1, 0, None, None, None, None, None, None, 1, 1, None, None, None, 0, None, 0,
+                             None) == m.MLA_ERR_INVALID
+
+
+def test_absorbed_validation(m):
+    K3 = m.Dims()
+    d = K3.c()
+    f = m.lib.mla_absorbed
+    good = dict(q=16, cache=16, cap=100, lens=16, B=2, tq=1, w=16, gate=None, out=16, ml=16, acc=0, ws=16,
+                wsb=1 << 40)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return f(ctypes.byref(d), m.MLA_BF16, m.MLA_BF16, a["q"], a["cache"], a["cap"], a["lens"], a["B"], a["tq"],
+                 a["w"], a["gate"], a["out"], a["ml"], a["acc"], a["ws"], a["wsb"], None)
+    assert call(tq=0) == m.MLA_ERR_INVALID
+    assert call(cap=0) == m.MLA_ERR_INVALID
+    assert call(lens=None) == m.MLA_ERR_INVALID
+    assert call(wsb=5) == m.MLA_ERR_WORKSPACE
+    assert call(gate=8) == m.MLA_ERR_INVALID
+    big = m.Dims(200).c()
+    assert f(ctypes.byref(big), m.MLA_BF16, m.MLA_BF16, 16, 16, 100, 16, 1, 1, 16, None, 16, 16, 0, 16, 1 << 40,
+             None) == m.MLA_ERR_UNSUPPORTED
+
+
+def test_qk_clip_validation(m):
+    K3 = m.Dims()
+    d = K3.c()
+    f = m.lib.mla_qk_clip
+    assert f(ctypes.byref(d), m.MLA_BF16, 16, 1536, 16, 16, 0.0, None, None, None) == m.MLA_ERR_INVALID
+    assert f(ctypes.byref(d), m.MLA_BF16, 16, 1536, 16, 16, float("nan"), None, None, None) == m.MLA_ERR_INVALID
+    assert f(ctypes.byref(d), m.MLA_BF16, 16, 1530, 16, 16, 100.0, None, None, None) == m.MLA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(d), m.MLA_BF16, None, 1536, 16, 16, 100.0, None, None, None) == m.MLA_ERR_INVALID
+    assert f(ctypes.byref(d), m.MLA_BF16, 16, 1536, 16, None, 100.0, None, None, None) == m.MLA_ERR_INVALID
+
+
+def test_workspace_sizes(m):
+    K3 = m.Dims()
+    a = m.mla_prefill_workspace_size(K3, m.MLA_BF16, 4096, 1)
+    b = m.mla_prefill_workspace_size(K3, m.MLA_BF16, 59392, 4)
+    # expanded K^C and V^T of every head dominate: 96 heads x 256 values x 2 bytes per padded row
+    assert a >= 96 * 256 * 2 * 4096 and b >= 96 * 256 * 2 * 59392
+    assert m.mla_absorbed_workspace_size(K3, m.MLA_BF16, 64, 1) > 0
+    assert m.mla_prefill_workspace_size(m.Dims(0), m.MLA_BF16, 10, 1) == 0

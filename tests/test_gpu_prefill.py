@@ -1,0 +1,136 @@
+"""GPU parity of the training-form prefill (mla_prefill) against the CPU oracle.
+
+Tolerances: bf16 path max|x - ref| / max|ref| <= 2e-2 (normwise), fp32 path
+<= 1e-4, per-head max logit <= 1e-3 relative.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._util import rel_err
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+SMAX_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def lib(gpu_available):
+    import mla_qk_clip_amd as m
+    return m
+
+
+def _check(p, out, lse, ml, ref, ref_lse, ref_sm, tol, heads=None):
+    from tests._gpu import host
+    V = p.dims.v_dim
+    o = host(out)
+    if heads is None:
+        assert rel_err(o, ref) <= tol, rel_err(o, ref)
+        if lse is not None:
+            n = p.ntok
+            lse_h = host(lse)[:, :n]
+            assert np.max(np.abs(lse_h - ref_lse)) <= 1e-2
+    else:
+        for h in heads:
+            e = rel_err(o[:, h * V:(h + 1) * V], ref[:, h * V:(h + 1) * V])
+            assert e <= tol, (h, e)
+    sm = host(ml)
+    rel = np.abs(sm - ref_sm) / np.abs(ref_sm)
+    assert np.all(rel <= SMAX_TOL), rel.max()
+
+
+def test_tiny_fp32_matches_oracle(lib):
+    from tests._gpu import log, run_prefill
+    p = synth.tiny_fp32_prefill()
+    log("tiny fp32 prefill")
+    out, lse, ml = run_prefill(p)
+    ref, ref_lse, ref_sm = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims)
+    _check(p, out, lse, ml, ref, ref_lse, ref_sm, F32_TOL)
+    from tests._gpu import host
+    assert np.max(np.abs(host(lse) - ref_lse)) <= 1e-4
+
+
+def test_fp32_varlen_ragged_matches_oracle(lib):
+    from tests._gpu import log, run_prefill
+    p = synth.prefill_inputs(synth.TINY, [1, 0, 37, 64, 5], seed=21, bf16=False)
+    log("fp32 varlen prefill")
+    out, lse, ml = run_prefill(p)
+    ref, ref_lse, ref_sm = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims)
+    _check(p, out, lse, ml, ref, ref_lse, ref_sm, F32_TOL)
+
+
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_bf16_varlen_ragged_tiles(lib, out_bf16):
+    """Several sequences that start mid-tile, end mid-tile, are shorter than
+    one key tile, empty, or span several 128-query tiles."""
+    import torch
+    from tests._gpu import log, run_prefill
+    dims = synth.Dims(8, 512, 64, 128, 128)
+    p = synth.prefill_inputs(dims, [1, 63, 64, 65, 0, 130, 300, 7], seed=5, bf16=True)
+    log(f"bf16 ragged varlen prefill out_bf16={out_bf16}")
+    out, lse, ml = run_prefill(p, out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    ref, ref_lse, ref_sm = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims)
+    _check(p, out, lse, ml, ref, ref_lse, ref_sm, BF16_TOL)
+
+
+def test_bf16_no_gate_and_accumulate(lib):
+    import torch
+    from tests._gpu import host, log, run_prefill
+    dims = synth.Dims(4, 512, 64, 128, 128)
+    p = synth.prefill_inputs(dims, [200], seed=6, bf16=True, gate=False)
+    p2 = synth.prefill_inputs(dims, [90, 33], seed=7, bf16=True, gate=False)
+    log("bf16 no gate + accumulate")
+    out, _, ml = run_prefill(p)
+    ref, _, sm1 = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, None, p.cu_seqlens, dims)
+    assert rel_err(host(out), ref) <= BF16_TOL
+    # second call folds into the same max_logit buffer
+    _, _, ml2 = run_prefill(p2, max_logit=ml, accumulate=True)
+    _, _, sm2 = oracle.prefill(p2.q, p2.ckv, p2.ks, p2.w_kv_b, None, p2.cu_seqlens, dims)
+    both = np.maximum(sm1, sm2)
+    assert np.all(np.abs(host(ml2) - both) / np.abs(both) <= SMAX_TOL)
+    assert ml2.data_ptr() == ml.data_ptr()
+    del torch
+
+
+def test_bf16_k3_medium_all_heads(lib):
+    from tests._gpu import log, run_prefill
+    p = synth.prefill_inputs(synth.K3, [512], seed=8, bf16=True)
+    log("bf16 K3 T=512 H=96")
+    out, lse, ml = run_prefill(p)
+    ref, ref_lse, ref_sm = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims)
+    _check(p, out, lse, ml, ref, ref_lse, ref_sm, BF16_TOL)
+
+
+def test_bf16_k3_prefill_4096_sampled(lib):
+    """The K3 prefill workload at full size (T=4096, H=96): every head's max
+    logit against the oracle, full outputs for three heads."""
+    from tests._gpu import host, log, run_prefill
+    p = synth.k3_prefill()
+    log("bf16 K3 T=4096 H=96: GPU")
+    out, lse, ml = run_prefill(p)
+    heads = [0, 47, 95]
+    log("oracle rows")
+    ref, ref_lse, _ = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims, heads=heads)
+    o = host(out)
+    V = p.dims.v_dim
+    for h in heads:
+        assert rel_err(o[:, h * V:(h + 1) * V], ref[:, h * V:(h + 1) * V]) <= BF16_TOL
+        assert np.max(np.abs(host(lse)[h] - ref_lse[h])) <= 1e-2
+    log("oracle max logits")
+    ref_sm = np.array([oracle.max_logit_head(p.q, p.ckv, p.ks, p.w_kv_b, p.cu_seqlens, p.dims, h)
+                       for h in range(p.dims.heads)])
+    sm = host(ml)
+    assert np.all(np.abs(sm - ref_sm) / np.abs(ref_sm) <= SMAX_TOL)
+
+
+def test_bf16_bitwise_deterministic(lib):
+    from tests._gpu import log, run_prefill
+    dims = synth.Dims(16, 512, 64, 128, 128)
+    p = synth.prefill_inputs(dims, [700, 300], seed=9, bf16=True)
+    log("determinism")
+    o1, l1, m1 = run_prefill(p)
+    o2, l2, m2 = run_prefill(p)
+    assert bool((o1 == o2).all()) and bool((l1 == l2).all()) and bool((m1 == m2).all())
