@@ -166,8 +166,9 @@ def main():
         step()
     torch.cuda.synchronize()
     kern = {}
-    for k in ("prefill_plan", "prefill_expand", "prefill_attn", "qk_clip", "absorbed_prefix", "absorb_q",
-              "absorbed_split", "absorbed_combine", "fill"):
+    for k in ("fill", "prefill_aux_init", "prefill_plan", "prefill_expand", "prefill_attn", "prefill_refine_scan",
+              "prefill_refine_exact", "qk_clip", "absorbed_prefix", "absorb_q", "absorbed_split",
+              "absorbed_fixup", "absorbed_combine"):
         tot, n = m.mla_timing_read(k)
         if n:
             kern[k] = tot / n

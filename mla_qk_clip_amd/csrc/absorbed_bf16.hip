@@ -36,187 +36,312 @@ __global__ void __launch_bounds__(64) absorbed_prefix_kernel(const int32_t* __re
   P[static_cast<int64_t>(batch) * tq] = acc;
 }
 
-// q_abs[v][h][r] = sum_k w_kv_b[h*256 + k][r] * q[v][h][k]  (r < 512),
-// q_abs[v][h][512 + s] = q[v][h][128 + s].  Grid (heads, 2): 256 columns r per block.
-constexpr int kAbsQChunk = 32;
+// q_abs[v][h][r] = sum_k w_kv_b[h*256 + k][r] * q[v][h][k]  (r < 512) as a
+// bf16 MFMA product [64 v x 128 k] x [128 k x 128 r] per workgroup; the W_UK_h
+// tile sits row-major in LDS and is read as the k-major operand with the
+// LDS transpose read. q_abs[v][h][512 + s] = q[v][h][128 + s].
+// Grid (heads, 4 column chunks of 128); 4 waves; virtual sequences in chunks of 64.
+constexpr int kAqLd = 128 + 8;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// Transpose read (gfx950 ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i passes the address of element (k0 + i/4, m0 + 4*(i%4)) of a
+// row-major [k][m] tile and receives the column m0 + i at rows k0 .. k0+3.
+__device__ __forceinline__ v4s lds_tr4(const lds_u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+}
+__device__ __forceinline__ bf16x8 cat_bf16(v4s lo, v4s hi) {
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  const v8s x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, x);
+}
+
 __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ w, int bt, int heads,
                                                        uint16_t* __restrict__ qabs) {
-  __shared__ float qc[kAbsQChunk][kN];
-  const int h = blockIdx.x;
-  const int r = blockIdx.y * 256 + threadIdx.x;
-  const uint16_t* wk = w + static_cast<size_t>(h) * 256 * kR + r;
-  for (int v0 = 0; v0 < bt; v0 += kAbsQChunk) {
-    const int nv = min(kAbsQChunk, bt - v0);
-    __syncthreads();
-    for (int e = threadIdx.x; e < nv * kN; e += 256) {
-      const int v = e / kN, k = e - v * kN;
-      qc[v][k] = bf16_to_f32(q[(static_cast<size_t>(v0 + v) * heads + h) * kD + k]);
-    }
-    __syncthreads();
-    float acc[kAbsQChunk];
+  __shared__ __align__(16) uint16_t Wt[kN * kAqLd];
+  const int h = blockIdx.x, rc = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  // W_UK_h rows k (128) x columns r in [128 rc, 128 rc + 128)
+  for (int c = tid; c < kN * 16; c += 256) {
+    const int k = c >> 4, part = c & 15;
+    *reinterpret_cast<uint4*>(Wt + k * kAqLd + 8 * part) =
+        ldg16(w + (static_cast<size_t>(h) * 256 + k) * kR + 128 * rc + 8 * part);
+  }
+  __syncthreads();
+  const lds_u16* wl = (const lds_u16*)(Wt);
+  const int vb = wave & 1;          // which 32 virtual sequences of the 64-chunk
+  const int rb0 = 2 * (wave >> 1);  // two 32-column blocks
+  for (int v0 = 0; v0 < bt; v0 += 64) {
+    const int v = v0 + 32 * vb + l32;
+    const bool vv = v < bt;
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int v = 0; v < kAbsQChunk; ++v) acc[v] = 0.0f;
-    for (int k = 0; k < kN; ++k) {
-      const float wv = bf16_to_f32(wk[static_cast<size_t>(k) * kR]);
+    for (int kk = 0; kk < kN / 16; ++kk) {
+      const bf16x8 a = as_bf16x8(vv ? ldg16(q + (static_cast<size_t>(v) * heads + h) * kD + 16 * kk + 8 * g)
+                                    : make_uint4(0, 0, 0, 0));
 #pragma unroll
-      for (int v = 0; v < kAbsQChunk; ++v) acc[v] = fmaf(wv, qc[v][k], acc[v]);
+      for (int j = 0; j < 2; ++j) {
+        const int mb = 32 * (rb0 + j) + 16 * ((lane >> 4) & 1);
+        const int i = lane & 15;
+        const lds_u16* p0 = wl + (16 * kk + 8 * g + (i >> 2)) * kAqLd + mb + 4 * (i & 3);
+        const bf16x8 b = cat_bf16(lds_tr4(p0), lds_tr4(p0 + 4 * kAqLd));
+        acc[j] = mfma32(a, b, acc[j]);
+      }
     }
-    for (int v = 0; v < nv; ++v) qabs[(static_cast<size_t>(v0 + v) * heads + h) * kW + r] = f32_to_bf16(acc[v]);
-    if (blockIdx.y == 0 && threadIdx.x < kS) {
-      for (int v = 0; v < nv; ++v)
-        qabs[(static_cast<size_t>(v0 + v) * heads + h) * kW + kR + threadIdx.x] =
-            q[(static_cast<size_t>(v0 + v) * heads + h) * kD + kN + threadIdx.x];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int vr = v0 + 32 * vb + acc_row(e, g);
+        if (vr < bt)
+          qabs[(static_cast<size_t>(vr) * heads + h) * kW + 128 * rc + 32 * (rb0 + j) + l32] = f32_to_bf16(acc[j][e]);
+      }
+    if (rc == 0) {
+      for (int e = tid; e < 64 * kS; e += 256) {
+        const int vr = v0 + e / kS, s = e % kS;
+        if (vr < bt) qabs[(static_cast<size_t>(vr) * heads + h) * kW + kR + s] = q[(static_cast<size_t>(vr) * heads + h) * kD + kN + s];
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Split kernel. 4 waves; wave w < ceil(H/32) owns heads 32w .. 32w+31: it keeps
-// their q_abs as MFMA operands in registers, forms S^T = C Q^T for each tile
-// of 32 rows (each lane owns one head column), runs the online softmax and
-// accumulates O_lat^T = C^T P^T (512 x 32) in registers. All 256 threads load
-// each tile once from HBM into LDS twice: row-major (score operand) and
-// transposed with the value-operand row permutation (latent operand).
-// Partials: part_ml[slot][h] = {raw row max, denominator}, part_o[slot][h][r]
-// = unnormalised o_lat, slot = workgroup + virtual sequence.
+// Split kernel. Workgroup = 4 waves; waves 0-2 each own 32 heads (head block
+// 3*blockIdx.y + wave). The workgroup's rows are visited in tiles of 32 rows,
+// segment by segment. Every wave streams a quarter of each tile straight from
+// HBM into LDS (global_load_lds, 16 bytes per lane, no registers), three tiles
+// ahead of the compute, into a ring of 4 LDS stages; one barrier per tile.
+// LDS tile layout: [32 rows][73 chunks of 8 bf16] (72 data chunks and one pad
+// chunk per row, so rows are 36 banks apart and both read patterns below are
+// free of bank conflicts). A wave-wide copy fills 64 consecutive chunk slots;
+// lanes that land on a pad slot fetch a harmless valid chunk. A compute wave keeps its heads' q_abs as MFMA operands in
+// registers, forms S^T = C Q^T (each lane owns one head column; rows of C read
+// as b128) and accumulates O_lat^T = C^T P^T with C^T read through the LDS
+// transpose read. The softmax uses a lazily updated reference max: the
+// accumulators are rescaled only when a head's max grows by more than a
+// factor 2^8 in probability, so p <= 256.
+// Partials per (workgroup, virtual sequence) slot and head:
+//   part_o[slot][h][r] = sum_j p_j c_j[r] (relative to the reference max),
+//   part_ml[slot][h] = {reference max (raw), denominator, true raw max, 0}.
 // ---------------------------------------------------------------------------
-constexpr int kCsLd = kW + 8;            // 584
-constexpr int kCtLd = kDecRows + 8;      // 40
+constexpr int kChunks = kW / 8;                       // 72 data chunks of 16 bytes per row
+constexpr int kRowSlots = kChunks + 1;                // 73 slots per LDS row (one pad)
+constexpr int kTileSlots = kDecRows * kRowSlots;      // 2336
+constexpr int kDmaCopies = (kTileSlots + 63) / 64;    // 37 wave-wide 1 KB copies per tile
+constexpr int kTileBytes = kDmaCopies * 1024;         // 37888 bytes per stage
+constexpr int kStages = 3;
 
-__global__ void __launch_bounds__(256) absorbed_split_kernel(
-    const uint16_t* __restrict__ cache, int64_t cap, int tq, int heads, int64_t bt,
-    const int64_t* __restrict__ P, const uint16_t* __restrict__ qabs, float scale,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ __align__(16) uint16_t Cs[kDecRows * kCsLd];
-  __shared__ __align__(16) uint16_t Ct[kR * kCtLd];
+struct TileCursor {
+  int64_t vs;       // virtual sequence of the current tile
+  int64_t pos;      // global start row of the current tile
+  int64_t seg_end;  // global end of the current segment (within the workgroup range)
+  int64_t hi;
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int G = gridDim.x;
-  const int64_t total = P[bt];
-  int64_t lo = total * blockIdx.x / G;
-  const int64_t hi = total * (blockIdx.x + 1) / G;
-  if (lo >= hi) return;
-
-  const int head = 32 * wave + l32;
-  const bool hvalid = head < heads;
-  const bool active = 32 * wave < heads;   // this wave owns some heads
-  const float c2 = scale * kLog2e;
-
-  // virtual sequence holding row lo
+__device__ __forceinline__ void cursor_init(TileCursor& c, const int64_t* P, int64_t bt, int64_t lo, int64_t hi) {
   int64_t vlo = 0, vhi = bt - 1;
   while (vlo < vhi) {
     const int64_t mid = (vlo + vhi + 1) >> 1;
     if (P[mid] <= lo) vlo = mid; else vhi = mid - 1;
   }
-  int64_t vs = vlo;
+  while (P[vlo + 1] <= lo) ++vlo;
+  c.vs = vlo;
+  c.pos = lo;
+  c.hi = hi;
+  c.seg_end = min(hi, P[vlo + 1]);
+}
+__device__ __forceinline__ void cursor_next(TileCursor& c, const int64_t* P) {
+  c.pos = min(c.pos + kDecRows, c.seg_end);
+  if (c.pos >= c.seg_end && c.pos < c.hi) {
+    while (P[c.vs + 1] <= c.pos) ++c.vs;
+    c.seg_end = min(c.hi, P[c.vs + 1]);
+  }
+}
 
-  while (lo < hi) {
-    while (P[vs + 1] <= lo) ++vs;
-    const int64_t seg_end = min(hi, P[vs + 1]);
-    const int b = static_cast<int>(vs / tq);
-    const int r0 = static_cast<int>(lo - P[vs]);
-    const int r1 = static_cast<int>(seg_end - P[vs]);
-    const uint16_t* cb = cache + static_cast<size_t>(b) * cap * kW;
+// vmcnt-only wait (expcnt and lgkmcnt left at their maxima), gfx9 encoding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
-    bf16x8 qf[kW / 16];
+struct SplitState {
+  bf16x8 qf[kW / 16];
+  f32x16 oacc[kR / 32];
+  float m_ref, m_true, l_part;
+  bool overflow, first;
+};
+
+// Scores, softmax weights and the latent accumulation for one tile in `tile`.
+__device__ __forceinline__ void split_compute(const uint16_t* tile, int nrows, int lane, float c2, SplitState& S) {
+  const int g = lane >> 5, l32 = lane & 31;
+  const int i16 = lane & 15;
+  const int mhalf = 16 * ((lane >> 4) & 1);
+  const char* tb = reinterpret_cast<const char*>(tile);
+  const lds_u16* tl = (const lds_u16*)(tile);
+  f32x16 sacc = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < kW / 16; ++kk) {
+    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(tb + 16 * (l32 * kRowSlots + 2 * kk + g)));
+    sacc = mfma32(a, S.qf[kk], sacc);
+  }
+  if (nrows < kDecRows) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (acc_row(e, g) >= nrows) sacc[e] = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (S.first) S.m_ref = mx;
+  S.m_true = fmaxf(S.m_true, mx);
+  S.overflow = S.overflow || (mx - S.m_ref) * c2 > 64.0f;
+  const float moff = -S.m_ref * c2;
+  uint32_t pk[8];
+  float psum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) {
+    const float p0 = fast_exp2(fmaf(sacc[e], c2, moff));
+    const float p1 = fast_exp2(fmaf(sacc[e + 1], c2, moff));
+    psum += p0 + p1;
+    pk[e >> 1] = pack_bf16x2(p0, p1);
+  }
+  S.l_part += psum;
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const bf16x8 bp = as_bf16x8(make_uint4(pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]));
+    const int rA = 16 * jj + 4 * g + (i16 >> 2);
+    const lds_u16* rowp = tl + rA * (8 * kRowSlots) + mhalf + 4 * (i16 & 3);
+#pragma unroll
+    for (int cbk = 0; cbk < kR / 32; ++cbk) {
+      const lds_u16* p0 = rowp + 32 * cbk;
+      const bf16x8 a = cat_bf16(lds_tr4(p0), lds_tr4(p0 + 8 * (8 * kRowSlots)));
+      S.oacc[cbk] = mfma32(a, bp, S.oacc[cbk]);
+    }
+  }
+}
+
+// Wave 3 streams every tile of the workgroup into a ring of kStages LDS stages
+// with direct global->LDS copies (37 wave-wide 1 KB copies per tile), two
+// tiles ahead of the compute waves. It never reads LDS, and the compute waves
+// never copy, so neither code path has to wait on the other's memory ops
+// except through the explicit vmcnt wait and the barrier.
+__device__ __forceinline__ void split_issue(uint16_t* ring, int stage, TileCursor& lc, const int64_t* P,
+                                            const uint16_t* cache, int64_t cap, int tq, int lane) {
+  const int b = static_cast<int>(lc.vs / tq);
+  const int64_t row0 = lc.pos - P[lc.vs];
+  const int64_t left = lc.seg_end - lc.pos;
+  const int nrows = left < kDecRows ? static_cast<int>(left) : kDecRows;
+  const uint16_t* src = cache + (static_cast<size_t>(b) * cap + row0) * kW;
+  char* dst = reinterpret_cast<char*>(ring) + stage * kTileBytes;
+#pragma unroll
+  for (int kc = 0; kc < kDmaCopies; ++kc) {
+    const int slot = 64 * kc + lane;
+    int r = slot / kRowSlots;
+    int c = slot - r * kRowSlots;
+    // pad slots, slots past the tile and rows past the segment fetch a valid
+    // chunk of the tile's first row (finite; never used or masked)
+    if (r >= nrows || c >= kChunks) {
+      r = 0;
+      c = 0;
+    }
+    __builtin_amdgcn_global_load_lds(src + r * kW + 8 * c,
+                                     (__attribute__((address_space(3))) void*)(dst + 1024 * kc), 16, 0, 0);
+  }
+  cursor_next(lc, P);
+}
+
+__global__ void __launch_bounds__(256) absorbed_split_kernel(
+    const uint16_t* __restrict__ cache, int64_t cap, int tq, int heads, int64_t bt,
+    const int64_t* __restrict__ P, const uint16_t* __restrict__ qabs, float scale,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ __align__(16) uint16_t ring[kStages * kTileBytes / 2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int G = gridDim.x;
+  const int64_t total = P[bt];
+  const int64_t lo = total * blockIdx.x / G;
+  const int64_t hi = total * (blockIdx.x + 1) / G;
+  if (lo >= hi) return;
+
+  int ntiles = 0;
+  {
+    TileCursor c;
+    cursor_init(c, P, bt, lo, hi);
+    while (c.pos < hi) {
+      ++ntiles;
+      cursor_next(c, P);
+    }
+  }
+
+  if (wave == 3) {
+    // ---------------- loader ----------------
+    TileCursor lc;
+    cursor_init(lc, P, bt, lo, hi);
+    split_issue(ring, 0, lc, P, cache, cap, tq, lane);
+    if (ntiles > 1) split_issue(ring, 1, lc, P, cache, cap, tq, lane);
+    if (ntiles > 1) wait_vmcnt<kDmaCopies>(); else wait_vmcnt<0>();   // tile 0 landed
+    __syncthreads();
+    for (int i = 0; i < ntiles; ++i) {
+      if (i + 2 < ntiles) split_issue(ring, (i + 2) % kStages, lc, P, cache, cap, tq, lane);
+      // tile i+1 must have landed before the barrier that ends tile i
+      if (i + 2 < ntiles) wait_vmcnt<kDmaCopies>(); else wait_vmcnt<0>();
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------- compute waves ----------------
+  const int hb = 3 * blockIdx.y + wave;
+  const int head = 32 * hb + l32;
+  const bool active = 32 * hb < heads;
+  const bool hvalid = active && head < heads;
+  const float c2 = scale * kLog2e;
+  __syncthreads();   // tile 0
+
+  TileCursor cur;
+  cursor_init(cur, P, bt, lo, hi);
+  int i = 0;   // global tile index of this workgroup
+  SplitState S;
+  while (cur.pos < hi) {
+    // ---- one segment: the rows of virtual sequence cur.vs inside [lo, hi) ----
+    const int64_t vs = cur.vs;
+    const int64_t seg_end = cur.seg_end;
     {
       const uint16_t* qrow = qabs + (static_cast<size_t>(vs) * heads + (hvalid ? head : 0)) * kW + 8 * g;
 #pragma unroll
       for (int kk = 0; kk < kW / 16; ++kk)
-        qf[kk] = as_bf16x8(hvalid ? ldg16(qrow + 16 * kk) : make_uint4(0, 0, 0, 0));
+        S.qf[kk] = as_bf16x8(hvalid ? ldg16(qrow + 16 * kk) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+      for (int j = 0; j < kR / 32; ++j) S.oacc[j] = f32x16{};
     }
-    f32x16 oacc[kR / 32];
-#pragma unroll
-    for (int i = 0; i < kR / 32; ++i) oacc[i] = f32x16{};
-    float m_raw = -INFINITY, l_part = 0.0f;
-
-    for (int t0 = r0; t0 < r1; t0 += kDecRows) {
-      const int nrows = min(kDecRows, r1 - t0);
-      // ---- load the tile as 8x8 blocks (8 rows x 8 features) ----
+    // Fixed reference max per segment (the first tile's): probabilities
+    // relative to it may exceed 1 but stay far inside the bf16 / fp32 range
+    // unless a later logit exceeds it by more than 64 / c2 (p > 2^64; flagged,
+    // and such segments are recomputed by the fix-up kernel).
+    S.m_ref = 0.0f;
+    S.m_true = -INFINITY;
+    S.l_part = 0.0f;
+    S.overflow = false;
+    S.first = true;
+    do {
+      const int64_t left = seg_end - cur.pos;
+      const int nrows = left < kDecRows ? static_cast<int>(left) : kDecRows;
+      if (active) split_compute(ring + (i % kStages) * (kTileBytes / 2), nrows, lane, c2, S);
+      S.first = false;
       __syncthreads();
-      for (int blkid = tid; blkid < 4 * (kW / 8); blkid += 256) {
-        const int rg = blkid / (kW / 8);
-        const int dg = blkid - rg * (kW / 8);
-        const int base = 16 * (rg >> 1) + 4 * (rg & 1);
-        uint4 rows[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int rr = base + (e & 3) + ((e >> 2) << 3);
-          rows[e] = rr < nrows ? ldg16(cb + static_cast<size_t>(t0 + rr) * kW + 8 * dg) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int rr = base + (e & 3) + ((e >> 2) << 3);
-          *reinterpret_cast<uint4*>(Cs + rr * kCsLd + 8 * dg) = rows[e];
-        }
-        if (dg < kR / 8) {
-          const int pos = 16 * (rg >> 1) + 8 * (rg & 1);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            uint32_t wd[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t a = (&rows[2 * k].x)[c >> 1];
-              const uint32_t bb = (&rows[2 * k + 1].x)[c >> 1];
-              wd[k] = (c & 1) ? ((a >> 16) | (bb & 0xffff0000u)) : ((a & 0xffffu) | (bb << 16));
-            }
-            *reinterpret_cast<uint4*>(Ct + (8 * dg + c) * kCtLd + pos) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-          }
-        }
-      }
-      __syncthreads();
-      if (!active) continue;
+      cursor_next(cur, P);
+      ++i;
+    } while (cur.pos < seg_end);
 
-      // ---- S^T (32 rows x 32 heads), raw scores ----
-      f32x16 sacc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < kW / 16; ++kk) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Cs + l32 * kCsLd + 16 * kk + 8 * g));
-        sacc = mfma32(a, qf[kk], sacc);
-      }
-      if (nrows < kDecRows) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (acc_row(e, g) >= nrows) sacc[e] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_raw, mx);
-      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-      const float corr = fast_exp2((m_raw - m_use) * c2);
-      const float moff = -m_use * c2;
-      m_raw = m_new;
-      uint32_t pk[8];
-      float psum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const float p0 = fast_exp2(fmaf(sacc[e], c2, moff));
-        const float p1 = fast_exp2(fmaf(sacc[e + 1], c2, moff));
-        psum += p0 + p1;
-        pk[e >> 1] = pack_bf16x2(p0, p1);
-      }
-      l_part = l_part * corr + psum;
-#pragma unroll
-      for (int i = 0; i < kR / 32; ++i) oacc[i] *= corr;
-
-      // ---- O_lat^T (512 x 32 heads) += C^T P^T ----
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const bf16x8 bp = as_bf16x8(make_uint4(pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]));
-#pragma unroll
-        for (int cbk = 0; cbk < kR / 32; ++cbk) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Ct + (32 * cbk + l32) * kCtLd + 16 * jj + 8 * g));
-          oacc[cbk] = mfma32(a, bp, oacc[cbk]);
-        }
-      }
-    }
-
-    // ---- partial for (this workgroup, vs) ----
-    if (active && hvalid) {
+    // ---- the segment's partial ----
+    if (hvalid) {
       const size_t slot = static_cast<size_t>(blockIdx.x) + static_cast<size_t>(vs);
       float* po = part_o + (slot * heads + head) * kR;
 #pragma unroll
@@ -224,16 +349,88 @@ __global__ void __launch_bounds__(256) absorbed_split_kernel(
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
           const int r = 32 * cbk + 8 * grp + 4 * g;
-          *reinterpret_cast<float4*>(po + r) =
-              make_float4(oacc[cbk][4 * grp], oacc[cbk][4 * grp + 1], oacc[cbk][4 * grp + 2], oacc[cbk][4 * grp + 3]);
+          *reinterpret_cast<float4*>(po + r) = make_float4(S.oacc[cbk][4 * grp], S.oacc[cbk][4 * grp + 1],
+                                                           S.oacc[cbk][4 * grp + 2], S.oacc[cbk][4 * grp + 3]);
         }
-      const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
-      if (g == 0) {
-        part_ml[(slot * heads + head) * 2] = m_raw;
-        part_ml[(slot * heads + head) * 2 + 1] = l_tot;
+      const float l_tot = S.l_part + __shfl_xor(S.l_part, 32, 64);
+      if (g == 0)
+        *reinterpret_cast<float4*>(part_ml + (slot * heads + head) * 4) =
+            make_float4(S.m_ref, l_tot, S.m_true, S.overflow ? 1.0f : 0.0f);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fix-up for segments whose logits outgrew the split kernel's fixed reference
+// (a later logit above the first tile's max by more than 64 / c2, i.e. far
+// outside normal attention statistics): recompute those (segment, head)
+// partials with a plain online softmax that rescales as it goes. One
+// workgroup per split workgroup; one wavefront per flagged head at a time.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) absorbed_fixup_kernel(
+    const uint16_t* __restrict__ cache, int64_t cap, int tq, int heads, int64_t bt, int G,
+    const int64_t* __restrict__ P, const uint16_t* __restrict__ qabs, float scale, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t total = P[bt];
+  const int64_t lo = total * blockIdx.x / G;
+  const int64_t hi = total * (blockIdx.x + 1) / G;
+  if (lo >= hi) return;
+  const float c2 = scale * kLog2e;
+  TileCursor cur;
+  cursor_init(cur, P, bt, lo, hi);
+  while (cur.pos < hi) {
+    const int64_t vs = cur.vs;
+    const int64_t seg_beg = cur.pos, seg_end = cur.seg_end;
+    const size_t slot = static_cast<size_t>(blockIdx.x) + static_cast<size_t>(vs);
+    const int b = static_cast<int>(vs / tq);
+    const uint16_t* cb = cache + static_cast<size_t>(b) * cap * kW;
+    for (int h = wave; h < heads; h += 4) {
+      float* ml = part_ml + (slot * heads + h) * 4;
+      if (ml[3] == 0.0f) continue;
+      // q_abs of this head, 9 features per lane
+      float qa[kW / 64];
+      const uint16_t* qrow = qabs + (static_cast<size_t>(vs) * heads + h) * kW;
+#pragma unroll
+      for (int j = 0; j < kW / 64; ++j) qa[j] = bf16_to_f32(qrow[lane + 64 * j]);
+      float o[kR / 64];
+#pragma unroll
+      for (int j = 0; j < kR / 64; ++j) o[j] = 0.0f;
+      float m = -INFINITY, l = 0.0f;
+      for (int64_t r = seg_beg - P[vs]; r < seg_end - P[vs]; ++r) {
+        const uint16_t* row = cb + static_cast<size_t>(r) * kW;
+        float part = 0.0f;
+        float cv[kR / 64];
+#pragma unroll
+        for (int j = 0; j < kW / 64; ++j) {
+          const float x = bf16_to_f32(row[lane + 64 * j]);
+          if (j < kR / 64) cv[j] = x;
+          part = fmaf(qa[j], x, part);
+        }
+        const float sraw = wave_sum(part);
+        const float m_new = fmaxf(m, sraw);
+        const float corr = fast_exp2((m - m_new) * c2);
+        const float p = fast_exp2((sraw - m_new) * c2);
+        l = l * corr + p;
+#pragma unroll
+        for (int j = 0; j < kR / 64; ++j) o[j] = o[j] * corr + p * cv[j];
+        m = m_new;
+      }
+      float* po = part_o + (slot * heads + h) * kR;
+#pragma unroll
+      for (int j = 0; j < kR / 64; ++j) po[lane + 64 * j] = o[j];
+      if (lane == 0) {
+        ml[0] = m;
+        ml[1] = l;
+        ml[2] = m;
+        ml[3] = 0.0f;
       }
     }
-    lo = seg_end;
+    cur.pos = seg_end;
+    if (cur.pos < hi) {
+      while (P[cur.vs + 1] <= cur.pos) ++cur.vs;
+      cur.seg_end = min(hi, P[cur.vs + 1]);
+    }
   }
 }
 
@@ -273,15 +470,20 @@ __global__ void __launch_bounds__(256) absorbed_combine_kernel(
     const int wa = split_of_row(total, G, P[vs]);
     const int wb = split_of_row(total, G, P[vs + 1] - 1);
     float M = -INFINITY;
-    for (int wg = wa; wg <= wb; ++wg) M = fmaxf(M, part_ml[((static_cast<size_t>(wg) + vs) * heads + h) * 2]);
+    float Mt = -INFINITY;
+    for (int wg = wa; wg <= wb; ++wg) {
+      const float4 ml = *reinterpret_cast<const float4*>(part_ml + ((static_cast<size_t>(wg) + vs) * heads + h) * 4);
+      M = fmaxf(M, ml.x);
+      Mt = fmaxf(Mt, ml.z);
+    }
     float den = 0.0f;
     float acc[kR / 16];
 #pragma unroll
     for (int e = 0; e < kR / 16; ++e) acc[e] = 0.0f;
     for (int wg = wa; wg <= wb; ++wg) {
       const size_t s = (static_cast<size_t>(wg) + vs) * heads + h;
-      const float f = fast_exp2((part_ml[s * 2] - M) * c2);
-      den += f * part_ml[s * 2 + 1];
+      const float f = fast_exp2((part_ml[s * 4] - M) * c2);
+      den += f * part_ml[s * 4 + 1];
       const float* po = part_o + s * kR + sub * (kR / 16);
 #pragma unroll
       for (int e = 0; e < kR / 16; e += 4) {
@@ -292,7 +494,7 @@ __global__ void __launch_bounds__(256) absorbed_combine_kernel(
     const float inv = 1.0f / den;
 #pragma unroll
     for (int e = 0; e < kR / 16; ++e) olat[vl][sub * (kR / 16) + e] = acc[e] * inv;
-    mmax = M;
+    mmax = Mt;
   } else {
 #pragma unroll
     for (int e = 0; e < kR / 16; ++e) olat[vl][sub * (kR / 16) + e] = 0.0f;
@@ -354,15 +556,23 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
   if (e != hipSuccess) return e;
   {
     TimedScope ts_("absorb_q", st);
-    hipLaunchKernelGGL(absorb_q_kernel, dim3(heads, kR / 256), dim3(256), 0, st, static_cast<const uint16_t*>(q),
+    hipLaunchKernelGGL(absorb_q_kernel, dim3(heads, kR / 128), dim3(256), 0, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(w_kv_b), static_cast<int>(bt), heads, qabs);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     TimedScope ts_("absorbed_split", st);
-    hipLaunchKernelGGL(absorbed_split_kernel, dim3(kDecSplits), dim3(256), 0, st,
+    hipLaunchKernelGGL(absorbed_split_kernel, dim3(kDecSplits, (heads + kDecHeadsPerWg - 1) / kDecHeadsPerWg), dim3(256), 0, st,
                        static_cast<const uint16_t*>(cache), cap, tq, heads, bt, P, qabs, scale, part_o, part_ml);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    TimedScope ts_("absorbed_fixup", st);
+    hipLaunchKernelGGL(absorbed_fixup_kernel, dim3(kDecSplits), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(cache), cap, tq, heads, bt, kDecSplits, P, qabs, scale, part_o,
+                       part_ml);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

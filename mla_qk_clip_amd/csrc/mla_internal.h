@@ -22,15 +22,25 @@ constexpr int kSeqPad = 64;   // per-sequence padding of the expanded K^C / V^T
 // Absorbed (bf16) split-K.
 constexpr int kDecSplits = 256;  // workgroups of the split kernel
 constexpr int kDecRows = 32;     // cache rows per inner tile
+constexpr int kDecHeadsPerWg = 96;  // 3 compute waves x 32 heads
 constexpr int kDecMaxHeads = 128;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace layout of the bf16 prefill.
 struct PrefillWs {
-  size_t kc, vt, pcu, order, toff, hdr, total;
+  size_t kc, vt, pcu, order, toff, hdr, rowmax, aux, cand, total;
   int64_t npad_max;
 };
+// aux[h][0] = approximate (raw, unscaled) head max logit, aux[h][1] = max |q_t|^2,
+// aux[h][2] = max |K^C_s|^2 (bf16 values), aux[h][3] unused; aux[H][0] = max |k^S_s|^2.
+constexpr int kAuxStride = 4;
+// Max-logit refinement candidates per head: int count, int overflow flag, then
+// kRefKeys (query row, key) pairs.
+constexpr int kRefRows = 64;
+constexpr int kRefKeys = 256;
+constexpr int kRefSlices = 8;
+constexpr int kCandStride = 2 + 2 * kRefKeys;
 inline PrefillWs prefill_ws_layout(int heads, int64_t ntok, int nseq) {
   PrefillWs w{};
   w.npad_max = static_cast<int64_t>(align_up(static_cast<size_t>(ntok + static_cast<int64_t>(kSeqPad) * nseq), 128));
@@ -41,6 +51,9 @@ inline PrefillWs prefill_ws_layout(int heads, int64_t ntok, int nseq) {
   w.order = off; off = align_up(off + static_cast<size_t>(nseq + 1) * 4, 256);
   w.toff = off; off = align_up(off + static_cast<size_t>(nseq + 1) * 4, 256);
   w.hdr = off; off = align_up(off + 64, 256);
+  w.rowmax = off; off = align_up(off + static_cast<size_t>(heads) * ntok * 4, 256);
+  w.aux = off; off = align_up(off + static_cast<size_t>(heads + 1) * kAuxStride * 4, 256);
+  w.cand = off; off = align_up(off + static_cast<size_t>(heads) * kCandStride * 4, 256);
   w.total = off;
   return w;
 }
@@ -63,7 +76,7 @@ inline AbsorbedWs absorbed_ws_layout(int heads, int batch, int tq) {
   w.qabs = off; off = align_up(off + static_cast<size_t>(bt) * heads * (kR + kS) * 2, 256);
   w.prefix = off; off = align_up(off + static_cast<size_t>(bt + 1) * 8, 256);
   w.part_o = off; off = align_up(off + static_cast<size_t>(w.slots) * heads * kR * 4, 256);
-  w.part_ml = off; off = align_up(off + static_cast<size_t>(w.slots) * heads * 2 * 4, 256);
+  w.part_ml = off; off = align_up(off + static_cast<size_t>(w.slots) * heads * 4 * 4, 256);
   w.total = off;
   return w;
 }

@@ -74,9 +74,11 @@ constexpr int kExBM = 128, kExBN = 128, kExBK = 64, kExLd = kExBK + 8, kExOutLd 
 __global__ void __launch_bounds__(256) prefill_expand_kernel(
     const uint16_t* __restrict__ ckv, const uint16_t* __restrict__ w, const int32_t* __restrict__ cu,
     int nseq, const int32_t* __restrict__ pcu, const int32_t* __restrict__ hdr, int64_t npad_max,
-    uint16_t* __restrict__ kc, uint16_t* __restrict__ vt) {
+    const uint16_t* __restrict__ ks, uint16_t* __restrict__ kc, uint16_t* __restrict__ vt,
+    float* __restrict__ aux) {
   __shared__ __align__(16) uint16_t smem[2 * kExBM * kExLd];
   __shared__ int src_row[kExBM];
+  __shared__ float red[4];
   static_assert(kExBM * kExOutLd <= 2 * kExBM * kExLd, "staging must fit");
 
   const int npad = hdr[1];
@@ -169,6 +171,34 @@ __global__ void __launch_bounds__(256) prefill_expand_kernel(
         else st[n * kExOutLd + ((m & ~15) | vperm16(m & 15))] = v;
       }
   __syncthreads();
+  if (half == 0) {
+    // largest squared norm of a stored K^C row (and, once, of a k^S row): the
+    // error bound of the max-logit refinement
+    const int row = tid >> 1, part = tid & 1;
+    float n2 = 0.0f;
+#pragma unroll 8
+    for (int e = 0; e < 64; e += 2) {
+      const uint32_t w2 = *reinterpret_cast<const uint32_t*>(st + row * kExOutLd + 64 * part + e);
+      n2 = fmaf(bf16lo(w2), bf16lo(w2), fmaf(bf16hi(w2), bf16hi(w2), n2));
+    }
+    n2 += __shfl_xor(n2, 1, 64);
+    float s2 = 0.0f;
+    if (head == 0 && part == 0 && src_row[row] >= 0) {
+      const uint16_t* kr = ks + static_cast<size_t>(src_row[row]) * kS;
+      for (int e = 0; e < kS; e += 8) {
+        const uint4 w4 = ldg16(kr + e);
+        const uint32_t* x = &w4.x;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s2 = fmaf(bf16lo(x[u]), bf16lo(x[u]), fmaf(bf16hi(x[u]), bf16hi(x[u]), s2));
+      }
+    }
+    n2 = wave_max(n2);
+    s2 = wave_max(s2);
+    if (lane == 0) red[wave] = n2;
+    __syncthreads();
+    if (tid == 0) atomic_max_float(aux + head * kAuxStride + 2, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    if (head == 0 && lane == 0) atomic_max_float(aux + static_cast<size_t>(gridDim.x / 2) * kAuxStride, s2);
+  }
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const int id = tid + 256 * c;
@@ -198,10 +228,12 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ pcu, const int32_t* __restrict__ order,
     const int32_t* __restrict__ toff, const int32_t* __restrict__ hdr, int nseq, int heads,
     int64_t ntok, int64_t npad_max, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt,
-    float scale, void* __restrict__ out, float* __restrict__ lse, float* __restrict__ max_logit) {
+    float scale, void* __restrict__ out, float* __restrict__ lse, float* __restrict__ rowmax,
+    float* __restrict__ aux) {
   __shared__ __align__(16) uint16_t Ks[kPrefBN * kKsLd];
   __shared__ __align__(16) uint16_t Vs[kV * kVsLd];
   __shared__ float red[4];
+  __shared__ float redq[4];
 
   // ---- work item: blocks that share a head run on the same XCD ----
   const int ntiles = hdr[0];
@@ -387,15 +419,187 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(
           *reinterpret_cast<float4*>(orow) = make_float4(o[0], o[1], o[2], o[3]);
         }
       }
-    if (lse && g == 0) lse[static_cast<size_t>(head) * ntok + t] = m_raw * scale + __logf(l_tot);
+    if (g == 0) {
+      if (lse) lse[static_cast<size_t>(head) * ntok + t] = m_raw * scale + __logf(l_tot);
+      rowmax[static_cast<size_t>(head) * ntok + t] = m_raw;
+    }
   }
+  // block maxima of the raw row max and of |q_t|^2 for the max-logit refinement
+  float qn2 = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < kD / 16; ++kk)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = static_cast<float>(qf[kk][e]);
+      qn2 = fmaf(x, x, qn2);
+    }
+  qn2 += __shfl_xor(qn2, 32, 64);
   float v = qvalid ? m_raw : -INFINITY;
   v = wave_max(v);
-  if (lane == 0) red[wave] = v;
+  qn2 = wave_max(qvalid ? qn2 : 0.0f);
+  if (lane == 0) {
+    red[wave] = v;
+    redq[wave] = qn2;
+  }
   __syncthreads();
   if (tid == 0) {
     const float mm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if (mm > -INFINITY) atomic_max_float(max_logit + head, mm * scale);
+    if (mm > -INFINITY) atomic_max_float(aux + head * kAuxStride, mm);
+    atomic_max_float(aux + head * kAuxStride + 1, fmaxf(fmaxf(redq[0], redq[1]), fmaxf(redq[2], redq[3])));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Max-logit refinement. The attention kernel's logits carry the bf16 rounding
+// of K^C (relative error up to 2^-8 per element: 8 significant bits), so
+// its maximum can be off by ~1e-3.
+// Every logit satisfies |approx - exact| <= delta with
+//   delta = (2^-8 * 1.01 + 3e-5) * max_t |q_t| * max_s |K_s|
+// (bf16 rounding of K^C plus fp32 accumulation), hence the exact maximum E
+// lies in [M - delta, M + delta] for the approximate maximum M, and its pair
+// has an approximate logit >= M - 2 delta. The scan kernel (heads x key
+// slices) re-scores the candidate rows (row max >= M - 2 delta) against their
+// keys with the stored bf16 K^C and lists the candidate pairs; the exact
+// kernel recomputes those pairs in fp32 from c^KV and kv_b_proj
+// (K^C_s = c_s W_UK_h). Too many candidates (near-ties, e.g. q = 0) fall back
+// to M, which is then within delta of E.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float refine_threshold(const float* aux, int h, int heads, float* M_out) {
+  const float M = aux[h * kAuxStride];
+  const float qn = sqrtf(aux[h * kAuxStride + 1]);
+  const float kn = sqrtf(aux[h * kAuxStride + 2] + aux[static_cast<size_t>(heads) * kAuxStride]);
+  *M_out = M;
+  return M - 2.0f * (1.01f / 256.0f + 3e-5f) * qn * kn;
+}
+
+__global__ void __launch_bounds__(256) prefill_refine_scan_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ks, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ pcu, int nseq, int heads, int64_t ntok, int64_t npad_max,
+    const uint16_t* __restrict__ kc, const float* __restrict__ rowmax, const float* __restrict__ aux,
+    int32_t* __restrict__ cand) {
+  __shared__ int rows[kRefRows];
+  __shared__ int nrows;
+  __shared__ float qrow[kD];
+  const int h = blockIdx.x, slice = blockIdx.y;
+  const int tid = threadIdx.x;
+  float M;
+  const float thr = refine_threshold(aux, h, heads, &M);
+  if (!(M > -INFINITY)) return;
+  int32_t* c = cand + static_cast<size_t>(h) * kCandStride;
+  if (tid == 0) nrows = 0;
+  __syncthreads();
+  for (int64_t t = tid; t < ntok; t += 256) {
+    if (rowmax[static_cast<size_t>(h) * ntok + t] >= thr) {
+      const int k = atomicAdd(&nrows, 1);
+      if (k < kRefRows) rows[k] = static_cast<int>(t);
+    }
+  }
+  __syncthreads();
+  if (nrows > kRefRows) {
+    if (tid == 0) c[1] = 1;
+    return;
+  }
+  for (int r = 0; r < nrows; ++r) {
+    const int t = rows[r];
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int a = cu[lo];
+    const int nkeys = t - a + 1;
+    const int per = (nkeys + kRefSlices - 1) / kRefSlices;
+    const int s0 = a + slice * per, s1 = min(t + 1, s0 + per);
+    __syncthreads();
+    if (tid < kD) qrow[tid] = bf16_to_f32(q[(static_cast<size_t>(t) * heads + h) * kD + tid]);
+    __syncthreads();
+    const uint16_t* kch = kc + (static_cast<size_t>(h) * npad_max + pcu[lo]) * kN;
+    for (int s = s0 + tid; s < s1; s += 256) {
+      uint4 x[kD / 8];
+      const uint16_t* kr = kch + static_cast<size_t>(s - a) * kN;
+      const uint16_t* sr = ks + static_cast<size_t>(s) * kS;
+#pragma unroll
+      for (int e = 0; e < kN / 8; ++e) x[e] = ldg16(kr + 8 * e);
+#pragma unroll
+      for (int e = 0; e < kS / 8; ++e) x[kN / 8 + e] = ldg16(sr + 8 * e);
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kD / 8; ++e) {
+        const uint32_t* w4 = &x[e].x;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc = fmaf(qrow[8 * e + 2 * u], bf16lo(w4[u]), fmaf(qrow[8 * e + 2 * u + 1], bf16hi(w4[u]), acc));
+      }
+      if (acc >= thr) {
+        const int k = atomicAdd(&c[0], 1);
+        if (k < kRefKeys) {
+          c[2 + 2 * k] = t;
+          c[3 + 2 * k] = s;
+        } else {
+          c[1] = 1;
+        }
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) prefill_refine_exact_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ckv, const uint16_t* __restrict__ ks,
+    const uint16_t* __restrict__ w, int heads, const float* __restrict__ aux, const int32_t* __restrict__ cand,
+    float scale, float* __restrict__ max_logit) {
+  __shared__ float qrow[kD];
+  __shared__ float crow[kR];
+  __shared__ float red[8];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float M;
+  refine_threshold(aux, h, heads, &M);
+  if (!(M > -INFINITY)) return;
+  const int32_t* c = cand + static_cast<size_t>(h) * kCandStride;
+  const int nk = c[0];
+  float best = -INFINITY;
+  if (c[1] == 0 && nk <= kRefKeys) {
+    for (int k = 0; k < nk; ++k) {
+      const int t = c[2 + 2 * k], s = c[3 + 2 * k];
+      __syncthreads();
+      if (tid < kD) qrow[tid] = bf16_to_f32(q[(static_cast<size_t>(t) * heads + h) * kD + tid]);
+      for (int e = tid; e < kR; e += 256) crow[e] = bf16_to_f32(ckv[static_cast<size_t>(s) * kR + e]);
+      __syncthreads();
+      // K^C_s[n] = sum_r c_s[r] * w[h*256 + n][r] in fp32; two threads per feature n
+      const int n = tid >> 1, part = tid & 1;
+      const uint16_t* wr = w + (static_cast<size_t>(h) * 256 + n) * kR + part * (kR / 2);
+      uint4 x[kR / 16];
+#pragma unroll
+      for (int e = 0; e < kR / 16; ++e) x[e] = ldg16(wr + 8 * e);
+      float kcn = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kR / 16; ++e) {
+        const uint32_t* w4 = &x[e].x;
+        const float* cr = crow + part * (kR / 2) + 8 * e;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kcn = fmaf(cr[2 * u], bf16lo(w4[u]), fmaf(cr[2 * u + 1], bf16hi(w4[u]), kcn));
+      }
+      kcn += __shfl_xor(kcn, 1, 64);
+      float pr = part == 0 ? qrow[n] * kcn : 0.0f;
+      if (tid < kS) pr += qrow[kN + tid] * bf16_to_f32(ks[static_cast<size_t>(s) * kS + tid]);
+      pr = wave_sum(pr);
+      if (lane == 0) red[wave] = pr;
+      __syncthreads();
+      best = fmaxf(best, (red[0] + red[1]) + (red[2] + red[3]));
+    }
+  }
+  if (tid == 0) {
+    const float e = (c[1] != 0 || nk > kRefKeys || !(best > -INFINITY)) ? M : best;
+    atomic_max_float(max_logit + h, e * scale);
+  }
+}
+
+__global__ void prefill_aux_init_kernel(float* aux, int32_t* cand, int heads) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < (heads + 1) * kAuxStride) aux[i] = ((i % kAuxStride) == 0 && i < heads * kAuxStride) ? -INFINITY : 0.0f;
+  if (i < heads) {
+    cand[static_cast<size_t>(i) * kCandStride] = 0;
+    cand[static_cast<size_t>(i) * kCandStride + 1] = 0;
   }
 }
 
@@ -411,7 +615,15 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
   int32_t* order = reinterpret_cast<int32_t*>(base + L.order);
   int32_t* toff = reinterpret_cast<int32_t*>(base + L.toff);
   int32_t* hdr = reinterpret_cast<int32_t*>(base + L.hdr);
+  float* rowmax = reinterpret_cast<float*>(base + L.rowmax);
+  float* aux = reinterpret_cast<float*>(base + L.aux);
+  int32_t* cand = reinterpret_cast<int32_t*>(base + L.cand);
 
+  {
+    TimedScope ts_("prefill_aux_init", st);
+    hipLaunchKernelGGL(prefill_aux_init_kernel, dim3((heads + 1) * kAuxStride / 256 + 1), dim3(256), 0, st, aux,
+                       cand, heads);
+  }
   {
     TimedScope ts_("prefill_plan", st);
     hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(256), 0, st, cu, nseq, pcu, order, toff, hdr);
@@ -423,7 +635,8 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
   {
     TimedScope ts_("prefill_expand", st);
     hipLaunchKernelGGL(prefill_expand_kernel, eg, dim3(256), 0, st, static_cast<const uint16_t*>(ckv),
-                       static_cast<const uint16_t*>(w_kv_b), cu, nseq, pcu, hdr, L.npad_max, kc, vt);
+                       static_cast<const uint16_t*>(w_kv_b), cu, nseq, pcu, hdr, L.npad_max,
+                       static_cast<const uint16_t*>(ks), kc, vt, aux);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -439,7 +652,7 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
       hipLaunchKernelGGL(prefill_attn_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(ks),
                          static_cast<const uint16_t*>(gate), cu, pcu, order, toff, hdr, nseq, heads, ntok,
-                         L.npad_max, kc, vt, scale, out, lse, max_logit);
+                         L.npad_max, kc, vt, scale, out, lse, rowmax, aux);
     }
   } else {
     {
@@ -447,8 +660,24 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
       hipLaunchKernelGGL(prefill_attn_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(ks),
                          static_cast<const uint16_t*>(gate), cu, pcu, order, toff, hdr, nseq, heads, ntok,
-                         L.npad_max, kc, vt, scale, out, lse, max_logit);
+                         L.npad_max, kc, vt, scale, out, lse, rowmax, aux);
     }
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    TimedScope ts_("prefill_refine_scan", st);
+    hipLaunchKernelGGL(prefill_refine_scan_kernel, dim3(heads, kRefSlices), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(ks), cu, pcu, nseq, heads, ntok,
+                       L.npad_max, kc, rowmax, aux, cand);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    TimedScope ts_("prefill_refine_exact", st);
+    hipLaunchKernelGGL(prefill_refine_exact_kernel, dim3(heads), dim3(256), 0, st, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(ckv), static_cast<const uint16_t*>(ks),
+                       static_cast<const uint16_t*>(w_kv_b), heads, aux, cand, scale, max_logit);
   }
   return hipGetLastError();
 }

@@ -114,4 +114,4 @@ def test_clip_stress_workload_end_to_end(lib):
     assert np.all(np.abs(sm2[list(synth.CLIP_HEADS)] - tau) <= 2e-2 * tau)
     others = [h for h in range(dims.heads) if h not in synth.CLIP_HEADS]
     assert np.array_equal(sm2[others], sm[others])
-    del math, gamma, mask, gm
+    del gamma, mask, gm
