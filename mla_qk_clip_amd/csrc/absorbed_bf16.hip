@@ -183,11 +183,26 @@ __device__ __forceinline__ void split_compute(const uint16_t* tile, int nrows, i
   const int mhalf = 16 * ((lane >> 4) & 1);
   const char* tb = reinterpret_cast<const char*>(tile);
   const lds_u16* tl = (const lds_u16*)(tile);
+  // S^T = C Q^T with the LDS operand reads issued kPf k-steps ahead of their MFMA
+  constexpr int kPf = 6;
+  const uint4* arow = reinterpret_cast<const uint4*>(tb + 16 * (l32 * kRowSlots + g));
+  uint4 af[kPf];
+#pragma unroll
+  for (int kk = 0; kk < kPf; ++kk) af[kk] = arow[2 * kk];
   f32x16 sacc = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < kW / 16; ++kk) {
-    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(tb + 16 * (l32 * kRowSlots + 2 * kk + g)));
+    const bf16x8 a = as_bf16x8(af[kk % kPf]);
+    if (kk + kPf < kW / 16) af[kk % kPf] = arow[2 * (kk + kPf)];
     sacc = mfma32(a, S.qf[kk], sacc);
+  }
+  // keep the reads kPf MFMAs ahead (the scheduler would otherwise sink them
+  // next to their uses and expose the LDS latency on every MFMA)
+  __builtin_amdgcn_sched_group_barrier(0x100, kPf, 0);
+#pragma unroll
+  for (int kk = 0; kk < kW / 16; ++kk) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   if (nrows < kDecRows) {
 #pragma unroll
@@ -212,17 +227,33 @@ __device__ __forceinline__ void split_compute(const uint16_t* tile, int nrows, i
     pk[e >> 1] = pack_bf16x2(p0, p1);
   }
   S.l_part += psum;
+  // O_lat^T += C^T P^T: 32 MFMAs (2 row halves x 16 latent blocks); the two
+  // transpose reads of each operand are issued kPv MFMAs ahead
+  constexpr int kPv = 4;
+  const bf16x8 bp0 = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+  const bf16x8 bp1 = as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7]));
+  const lds_u16* rowp = tl + (4 * g + (i16 >> 2)) * (8 * kRowSlots) + mhalf + 4 * (i16 & 3);
+  auto pv_ptr = [&](int m) { return rowp + (m >> 4) * 16 * (8 * kRowSlots) + 32 * (m & 15); };
+  v4s t0[kPv], t1[kPv];
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const bf16x8 bp = as_bf16x8(make_uint4(pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]));
-    const int rA = 16 * jj + 4 * g + (i16 >> 2);
-    const lds_u16* rowp = tl + rA * (8 * kRowSlots) + mhalf + 4 * (i16 & 3);
+  for (int m = 0; m < kPv; ++m) {
+    t0[m] = lds_tr4(pv_ptr(m));
+    t1[m] = lds_tr4(pv_ptr(m) + 8 * (8 * kRowSlots));
+  }
 #pragma unroll
-    for (int cbk = 0; cbk < kR / 32; ++cbk) {
-      const lds_u16* p0 = rowp + 32 * cbk;
-      const bf16x8 a = cat_bf16(lds_tr4(p0), lds_tr4(p0 + 8 * (8 * kRowSlots)));
-      S.oacc[cbk] = mfma32(a, bp, S.oacc[cbk]);
+  for (int m = 0; m < 2 * (kR / 32); ++m) {
+    const bf16x8 a = cat_bf16(t0[m % kPv], t1[m % kPv]);
+    if (m + kPv < 2 * (kR / 32)) {
+      t0[m % kPv] = lds_tr4(pv_ptr(m + kPv));
+      t1[m % kPv] = lds_tr4(pv_ptr(m + kPv) + 8 * (8 * kRowSlots));
     }
+    S.oacc[m & 15] = mfma32(a, (m >> 4) ? bp1 : bp0, S.oacc[m & 15]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPv, 1);
+#pragma unroll
+  for (int m = 0; m < 2 * (kR / 32); ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
   }
 }
 

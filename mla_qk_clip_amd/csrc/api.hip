@@ -8,7 +8,7 @@
 
 #include <string>
 
-#include "../../include/mla.h"
+#include "mla.h"
 #include "mla_internal.h"
 
 namespace {

@@ -20,6 +20,13 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D = A x B + C with A: 16x32 (lane l holds row l%16, k-slots 8*(l/16)..+7),
+// B: 32x16 (lane l holds column l%16, the same k-slots) and C/D: 16x16 with
+// lane l holding column l%16, rows 4*(l/16) + i for i = 0..3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Row index (within a 32x32 accumulator block) of accumulator element i in a lane of half g.
 __device__ __forceinline__ int acc_row(int i, int g) { return ((i >> 2) << 3) + (g << 2) + (i & 3); }
 

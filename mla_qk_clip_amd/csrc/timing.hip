@@ -4,7 +4,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/mla.h"
+#include "mla.h"
 #include "timing.h"
 
 namespace mla {
