@@ -163,11 +163,6 @@ __device__ __forceinline__ void cursor_next(TileCursor& c, const int64_t* P) {
 }
 
 // vmcnt-only wait (expcnt and lgkmcnt left at their maxima), gfx9 encoding
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 struct SplitState {
   bf16x8 qf[kW / 16];

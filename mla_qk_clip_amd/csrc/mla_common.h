@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -37,11 +39,10 @@ __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w <
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Round two floats to bf16 (nearest-even) and pack them (a in the low half).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 ha = static_cast<__bf16>(a);
-  __bf16 hb = static_cast<__bf16>(b);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ha)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hb)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 __device__ __forceinline__ uint16_t f32_to_bf16(float a) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
@@ -51,7 +52,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float sigmoidf_(float x) {
   // 1 / (1 + e^-x); e^-x overflows to +inf for very negative x, giving 0.
-  return 1.0f / (1.0f + fast_exp2(-x * kLog2e));
+  return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
 }
 
 // Order-preserving float max through integer atomics: non-negative floats
@@ -76,6 +77,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Max / sum of a value and the same value in the lane 32 apart (one
+// cross-half swap, no LDS traffic).
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1, so
+// that register arrays are always indexed by constants.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -87,6 +109,20 @@ __device__ __forceinline__ void stg16(void* p, uint4 v) { *reinterpret_cast<uint
 // rows {4-7, 12-15} as 8 consecutive elements, matching the rows it holds in
 // the score accumulator.
 __device__ __forceinline__ int vperm16(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (global loads, including the ones that write LDS directly).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Copy 16 bytes per lane from global memory straight into LDS: lane i's
+// bytes land at lds + 16 i (lds must be the same for the whole wave).
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
 
 __global__ void fill_f32_kernel(float* p, int n, float v);
 

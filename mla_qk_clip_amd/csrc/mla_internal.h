@@ -15,7 +15,7 @@ constexpr int kV = 128;   // value width
 constexpr int kD = kN + kS;
 
 // Prefill (bf16) tiling.
-constexpr int kPrefBM = 128;  // queries per workgroup
+constexpr int kPrefBM = 256;  // queries per workgroup
 constexpr int kPrefBN = 64;   // keys per inner tile
 constexpr int kSeqPad = 64;   // per-sequence padding of the expanded K^C / V^T
 
@@ -27,11 +27,19 @@ constexpr int kDecMaxHeads = 128;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace layout of the bf16 prefill.
+// Workspace layout of the bf16 prefill. Sequences are padded to multiples of
+// 64 rows; padded row p belongs to 64-row key tile p / 64 and the expanded
+// operands are stored tile-blocked in the order the attention kernel copies
+// them into LDS (1 KB = 64 x 16 bytes per block, padding rows zero):
+//   kc [H][tile][16 units][64 rows][8]   K^C, unit u = features 8u..8u+7
+//   vt [H][tile][8 units][128 d][8]      V^T, unit u = keys at permuted
+//                                        positions 8u..8u+7 of the tile
+//   ksp[tile][8 units][64 rows][8]       k^S (shared by all heads)
 struct PrefillWs {
-  size_t kc, vt, pcu, order, toff, hdr, rowmax, aux, cand, total;
+  size_t kc, vt, ksp, pcu, order, toff, hdr, rowmax, aux, cand, total;
   int64_t npad_max;
 };
+constexpr int kTileElems = kPrefBN * kN;  // elements of one K^C (or V^T) tile of one head
 // aux[h][0] = approximate (raw, unscaled) head max logit, aux[h][1] = max |q_t|^2,
 // aux[h][2] = max |K^C_s|^2 (bf16 values), aux[h][3] unused; aux[H][0] = max |k^S_s|^2.
 constexpr int kAuxStride = 4;
@@ -47,6 +55,7 @@ inline PrefillWs prefill_ws_layout(int heads, int64_t ntok, int nseq) {
   size_t off = 0;
   w.kc = off; off = align_up(off + static_cast<size_t>(heads) * w.npad_max * kN * 2, 256);
   w.vt = off; off = align_up(off + static_cast<size_t>(heads) * w.npad_max * kV * 2, 256);
+  w.ksp = off; off = align_up(off + static_cast<size_t>(w.npad_max) * kS * 2, 256);
   w.pcu = off; off = align_up(off + static_cast<size_t>(nseq + 1) * 4, 256);
   w.order = off; off = align_up(off + static_cast<size_t>(nseq + 1) * 4, 256);
   w.toff = off; off = align_up(off + static_cast<size_t>(nseq + 1) * 4, 256);

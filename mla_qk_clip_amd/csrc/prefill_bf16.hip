@@ -9,6 +9,8 @@
 //
 // Three launches: a one-workgroup plan (per-sequence padded offsets and a
 // longest-first tile order), the expansion GEMM, and the attention kernel.
+#include <type_traits>
+
 #include "mla_common.h"
 #include "mla_internal.h"
 #include "timing.h"
@@ -65,9 +67,11 @@ __global__ void __launch_bounds__(256) prefill_plan_kernel(const int32_t* __rest
 
 // ---------------------------------------------------------------------------
 // Expansion: C[p, j] = sum_k c^KV[src(p), k] * w_kv_b[j, k] over padded rows p.
-// One workgroup = 128 padded rows x one 128-wide half of one head (even half:
-// K^C_h, odd half: V_h). K^C goes to kc[h][p][d]; V goes transposed to
-// vt[h][d][p'] with p' the value-operand permutation inside each 16-row group.
+// One workgroup = 128 padded rows (two key tiles) x one 128-wide half of one
+// head (even half: K^C_h, odd half: V_h), written tile-blocked (see
+// PrefillWs). V is stored transposed with the keys of each 16-row group in the
+// value-operand order (vperm16). The head-0 K^C blocks also write the padded
+// k^S copy.
 // ---------------------------------------------------------------------------
 constexpr int kExBM = 128, kExBN = 128, kExBK = 64, kExLd = kExBK + 8, kExOutLd = 128 + 8;
 
@@ -75,7 +79,7 @@ __global__ void __launch_bounds__(256) prefill_expand_kernel(
     const uint16_t* __restrict__ ckv, const uint16_t* __restrict__ w, const int32_t* __restrict__ cu,
     int nseq, const int32_t* __restrict__ pcu, const int32_t* __restrict__ hdr, int64_t npad_max,
     const uint16_t* __restrict__ ks, uint16_t* __restrict__ kc, uint16_t* __restrict__ vt,
-    float* __restrict__ aux) {
+    uint16_t* __restrict__ ksp, float* __restrict__ aux) {
   __shared__ __align__(16) uint16_t smem[2 * kExBM * kExLd];
   __shared__ int src_row[kExBM];
   __shared__ float red[4];
@@ -199,41 +203,76 @@ __global__ void __launch_bounds__(256) prefill_expand_kernel(
     if (tid == 0) atomic_max_float(aux + head * kAuxStride + 2, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
     if (head == 0 && lane == 0) atomic_max_float(aux + static_cast<size_t>(gridDim.x / 2) * kAuxStride, s2);
   }
+  const size_t tile0 = static_cast<size_t>(head) * (npad_max / kPrefBN) + m0 / kPrefBN;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const int id = tid + 256 * c;
-    const int row = id >> 4, part = id & 15;
-    const uint4 v = *reinterpret_cast<const uint4*>(st + row * kExOutLd + 8 * part);
     if (half == 0) {
-      stg16(kc + (static_cast<size_t>(head) * npad_max + m0 + row) * kN + 8 * part, v);
+      const int r = id & 63, u = (id >> 6) & 15, tl = id >> 10;
+      const uint4 v = *reinterpret_cast<const uint4*>(st + (tl * kPrefBN + r) * kExOutLd + 8 * u);
+      stg16(kc + (tile0 + tl) * kTileElems + (u * kPrefBN + r) * 8, v);
     } else {
-      stg16(vt + (static_cast<size_t>(head) * kV + row) * npad_max + m0 + 8 * part, v);
+      const int d = id & 127, u = (id >> 7) & 7, tl = id >> 10;
+      const uint4 v = *reinterpret_cast<const uint4*>(st + d * kExOutLd + tl * kPrefBN + 8 * u);
+      stg16(vt + (tile0 + tl) * kTileElems + (u * kV + d) * 8, v);
+    }
+  }
+  if (half == 0 && head == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int id = tid + 256 * c;
+      const int r = id & 63, u = (id >> 6) & 7, tl = id >> 9;
+      const int src = src_row[tl * kPrefBN + r];
+      const uint4 v = src >= 0 ? ldg16(ks + static_cast<size_t>(src) * kS + 8 * u) : make_uint4(0, 0, 0, 0);
+      stg16(ksp + (static_cast<size_t>(m0 / kPrefBN + tl) * (kS / 8) + u) * (kPrefBN * 8) + r * 8, v);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Attention. One workgroup = one head x 128 queries of one sequence; 4 waves
-// of 32 queries. Scores are formed transposed (S^T = K Q^T) so that each lane
-// owns one query column: the row max/sum and the output rescale stay in the
-// lane. Keys are visited in tiles of 64 up to the diagonal (tiles above it
-// are skipped); only the diagonal tiles are masked.
+// Attention. One workgroup = one head x 256 queries of one sequence; 8 waves
+// (two per SIMD) of 32 queries. Scores are formed transposed (S^T = K Q^T) so
+// that each lane owns one query column: the row max/sum and the output
+// rescale stay in the lane. Keys are visited in tiles of 64 up to the
+// diagonal (tiles above it are skipped); a wave's last tile is its only
+// masked one.
+//
+// K tiles ([24 units][64 keys]: K^C units then k^S units) and V^T tiles
+// ([8 units][128 d]) live in two double-buffered LDS rings, copied straight
+// from the tile-blocked workspace (no register staging) one tile ahead; a
+// wave's 16-lane group reads 16 consecutive 16-byte units (no bank
+// conflicts). Software pipeline per wave and tile j:
+//   [B] S(j+1) = K(j+1) Q^T on the matrix cores while the VALU turns S(j)
+//       into bf16 probabilities;
+//   [C] O^T += V(j)^T P(j)^T on the matrix cores while the VALU masks and
+//       takes the row max of S(j+1).
+// The softmax keeps a per-query reference max that moves only when a tile's
+// max exceeds it by more than 2^8 (in exp2 units), so the output rescale is
+// rare; probabilities stay <= 2^8, exact in fp32 and bf16 range.
 // ---------------------------------------------------------------------------
-constexpr int kKsLd = kD + 8;       // 200 bf16 per key row in LDS
-constexpr int kVsLd = kPrefBN + 8;  // 72 bf16 per value-transposed row in LDS
+constexpr int kAttnThreads = 512;
+constexpr int kAttnWaves = kAttnThreads / 64;
+constexpr int kKUnits = kD / 8;                          // 16-byte units per key row (24)
+constexpr int kKTile = kPrefBN * kKUnits;                // 1536 units = 24 KB
+constexpr int kVTile = kV * (kPrefBN / 8);               // 1024 units = 16 KB
+static_assert(kN / 8 == 2 * kAttnWaves && kS / 8 == kAttnWaves && kVTile / 64 == 2 * kAttnWaves,
+              "each wave copies two K^C blocks, one k^S block and two V^T blocks per tile");
+constexpr float kRescaleLog2 = 8.0f;
 
 template <bool OUT_BF16>
-__global__ void __launch_bounds__(256) prefill_attn_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ks, const uint16_t* __restrict__ gate,
+__global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ksp, const uint16_t* __restrict__ gate,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ pcu, const int32_t* __restrict__ order,
     const int32_t* __restrict__ toff, const int32_t* __restrict__ hdr, int nseq, int heads,
     int64_t ntok, int64_t npad_max, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt,
     float scale, void* __restrict__ out, float* __restrict__ lse, float* __restrict__ rowmax,
     float* __restrict__ aux) {
-  __shared__ __align__(16) uint16_t Ks[kPrefBN * kKsLd];
-  __shared__ __align__(16) uint16_t Vs[kV * kVsLd];
-  __shared__ float red[4];
-  __shared__ float redq[4];
+  __shared__ uint4 K0[kKTile];
+  __shared__ uint4 K1[kKTile];
+  __shared__ uint4 V0[kVTile];
+  __shared__ uint4 V1[kVTile];
+  __shared__ float red[kAttnWaves];
+  __shared__ float redq[kAttnWaves];
 
   // ---- work item: blocks that share a head run on the same XCD ----
   const int ntiles = hdr[0];
@@ -261,10 +300,12 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int q0 = qt * kPrefBM;
-  const int qi = q0 + 32 * wave + l32;           // this lane's query (sequence-local)
+  const int qw = q0 + 32 * wave;                 // first query of this wave
+  const int qi = qw + l32;                       // this lane's query (sequence-local)
   const bool qvalid = qi < L;
   const int nkv = min(L, q0 + kPrefBM);
-  const int nkt = (nkv + kPrefBN - 1) / kPrefBN;
+  const int nkt = (nkv + kPrefBN - 1) / kPrefBN;                     // tiles staged by the workgroup
+  const int nkt_w = qw < L ? min(nkt, (qw + 31) / kPrefBN + 1) : 0;  // tiles this wave uses
 
   // ---- queries, held as MFMA B operands for the whole loop ----
   bf16x8 qf[kD / 16];
@@ -275,119 +316,208 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(
       qf[kk] = as_bf16x8(qvalid ? ldg16(qrow + 16 * kk) : make_uint4(0, 0, 0, 0));
   }
 
-  const uint16_t* kc_h = kc + (static_cast<size_t>(head) * npad_max + pbase) * kN;
-  const uint16_t* vt_h = vt + static_cast<size_t>(head) * kV * npad_max + pbase;
+  // tile-blocked operands of this head and sequence (tile index = padded row / 64)
+  const size_t tb = static_cast<size_t>(pbase / kPrefBN);
+  const uint16_t* kc_h = kc + (static_cast<size_t>(head) * (npad_max / kPrefBN) + tb) * kTileElems;
+  const uint16_t* vt_h = vt + (static_cast<size_t>(head) * (npad_max / kPrefBN) + tb) * kTileElems;
+  const uint16_t* ks_t = ksp + tb * (kPrefBN * kS);
 
-  uint4 rk[6], rv[4];
-  auto load_tile = [&](int j) {
+  // ---- tile copies: 1 KB blocks, lane i's 16 bytes at block + 16 i ----
+  auto dma_k = [&](uint4* dst, int j) {
+    const uint16_t* kcj = kc_h + static_cast<size_t>(j) * kTileElems;
+    dma16(kcj + (2 * wave) * 512 + 8 * lane, dst + (2 * wave) * 64);
+    dma16(kcj + (2 * wave + 1) * 512 + 8 * lane, dst + (2 * wave + 1) * 64);
+    dma16(ks_t + static_cast<size_t>(j) * (kPrefBN * kS) + wave * 512 + 8 * lane, dst + (kN / 8 + wave) * 64);
+  };
+  auto dma_v = [&](uint4* dst, int j) {
+    const uint16_t* vtj = vt_h + static_cast<size_t>(j) * kTileElems;
+    dma16(vtj + (2 * wave) * 512 + 8 * lane, dst + (2 * wave) * 64);
+    dma16(vtj + (2 * wave + 1) * 512 + 8 * lane, dst + (2 * wave + 1) * 64);
+  };
+
+  // LDS operand addresses: K unit (2kk + g) * 64 + 32 blk + l32, V^T unit
+  // (2jj + g) * 128 + 32 db + l32 (a 16-lane group reads 16 consecutive units)
+  auto kfrag = [&](const uint4* kt, int f) {   // f = 2 kk + blk
+    return as_bf16x8(kt[(2 * (f >> 1) + g) * kPrefBN + 32 * (f & 1) + l32]);
+  };
+  auto vfrag = [&](const uint4* vtile, int f) {   // f = 4 jj + db
+    return as_bf16x8(vtile[(2 * (f >> 2) + g) * kV + 32 * (f & 3) + l32]);
+  };
+  constexpr int kQkMfma = 2 * (kD / 16);   // 24
+  constexpr int kPvMfma = 4 * (kV / 32);   // 16
+  constexpr int kPfK = 4, kPfV = 4;        // LDS fragments in flight
+
+  // S^T for the 64 keys of a K tile: two 32x32 blocks (chains interleaved)
+  auto qk = [&](const uint4* kt, f32x16 (&s)[2]) {
+    bf16x8 kb[kPfK];
+#pragma unroll
+    for (int f = 0; f < kPfK; ++f) kb[f] = kfrag(kt, f);
+#pragma unroll
+    for (int f = 0; f < kQkMfma; ++f) {
+      s[f & 1] = mfma32(kb[f % kPfK], qf[f >> 1], f < 2 ? f32x16{} : s[f & 1]);
+      if (f + kPfK < kQkMfma) kb[f % kPfK] = kfrag(kt, f + kPfK);
+    }
+  };
+  auto mask_tile = [&](int j, f32x16 (&s)[2]) {
     const int kv0 = j * kPrefBN;
 #pragma unroll
-    for (int c = 0; c < 6; ++c) {
-      const int id = tid + 256 * c;          // 64 rows x 24 chunks
-      const int row = id / 24, part = id - row * 24;
-      const int kv = kv0 + row;
-      if (part < 16) {
-        rk[c] = ldg16(kc_h + static_cast<size_t>(kv) * kN + 8 * part);
-      } else {
-        rk[c] = kv < L ? ldg16(ks + static_cast<size_t>(a0 + kv) * kS + 8 * (part - 16)) : make_uint4(0, 0, 0, 0);
-      }
-    }
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int id = tid + 256 * c;          // 128 rows x 8 chunks
-      const int d = id >> 3, part = id & 7;
-      rv[c] = ldg16(vt_h + static_cast<size_t>(d) * npad_max + kv0 + 8 * part);
-    }
+      for (int e = 0; e < 16; ++e)
+        if (kv0 + 32 * blk + acc_row(e, g) > qi) s[blk][e] = -INFINITY;
+  };
+  auto tile_max = [&](const f32x16 (&s)[2]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[blk][e]);
+    return xor32_max(mx);
   };
 
   f32x16 oacc[kV / 32];
 #pragma unroll
   for (int i = 0; i < kV / 32; ++i) oacc[i] = f32x16{};
-  float m_raw = -INFINITY;   // running max of raw (unscaled) scores of this lane's query
-  float l_part = 0.0f;       // this lane half's share of the softmax denominator
+  float m_ref = -INFINITY;   // reference max (raw score units) the probabilities are taken against
+  float m_true = -INFINITY;  // running max of this lane's query's raw scores
+  float l_part = 0.0f;       // this lane half's share of the softmax denominator (w.r.t. m_ref)
+  float mx_cur = -INFINITY;  // max of the current tile's scores
   const float c2 = scale * kLog2e;
 
-  load_tile(0);
-  for (int j = 0; j < nkt; ++j) {
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < 6; ++c) {
-      const int id = tid + 256 * c;
-      const int row = id / 24, part = id - row * 24;
-      *reinterpret_cast<uint4*>(Ks + row * kKsLd + 8 * part) = rk[c];
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int id = tid + 256 * c;
-      const int d = id >> 3, part = id & 7;
-      *reinterpret_cast<uint4*>(Vs + d * kVsLd + 8 * part) = rv[c];
-    }
-    __syncthreads();
-    if (j + 1 < nkt) load_tile(j + 1);
-
-    // S^T for the 64 keys of this tile: two 32x32 blocks
-    f32x16 sacc[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < kD / 16; ++kk) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + (32 * blk + l32) * kKsLd + 16 * kk + 8 * g));
-        acc = mfma32(a, qf[kk], acc);
-      }
-      sacc[blk] = acc;
-    }
-
-    // causal mask on the diagonal tiles
-    const int kv0 = j * kPrefBN;
-    if (kv0 + kPrefBN - 1 > q0 + 32 * wave) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kv = kv0 + 32 * blk + acc_row(e, g);
-          if (kv > qi) sacc[blk][e] = -INFINITY;
-        }
-    }
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[blk][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_raw, mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float corr = fast_exp2((m_raw - m_use) * c2);
-    const float moff = -m_use * c2;
-    m_raw = m_new;
-
-    uint32_t pk[2][8];
+  // probability pair i (elements 2i, 2i+1 of the 32 scores a lane holds)
+  auto prob_pair = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8], float moff, float& psum, int i) {
+    const int blk = i >> 3, e = 2 * (i & 7);
+    const float p0 = fast_exp2(fmaf(s[blk][e], c2, moff));
+    const float p1 = fast_exp2(fmaf(s[blk][e + 1], c2, moff));
+    psum += p0 + p1;
+    pk[blk][i & 7] = pack_bf16x2(p0, p1);
+  };
+  auto pv_operand = [&](const uint32_t (&pk)[2][8], int jj) {
+    const uint32_t* src = &pk[jj >> 1][4 * (jj & 1)];
+    return as_bf16x8(make_uint4(src[0], src[1], src[2], src[3]));
+  };
+  auto probs = [&](const f32x16 (&s)[2], uint32_t (&pk)[2][8], float moff) {
     float psum = 0.0f;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int i = 0; i < 16; ++i) prob_pair(s, pk, moff, psum, i);
+    l_part += psum;
+  };
+  auto pv = [&](const uint4* vtile, const uint32_t (&pk)[2][8]) {
+    bf16x8 vb[kPfV];
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const float p0 = fast_exp2(fmaf(sacc[blk][e], c2, moff));
-        const float p1 = fast_exp2(fmaf(sacc[blk][e + 1], c2, moff));
-        psum += p0 + p1;
-        pk[blk][e >> 1] = pack_bf16x2(p0, p1);
+    for (int f = 0; f < kPfV; ++f) vb[f] = vfrag(vtile, f);
+#pragma unroll
+    for (int f = 0; f < kPvMfma; ++f) {
+      oacc[f & 3] = mfma32(vb[f % kPfV], pv_operand(pk, f >> 2), oacc[f & 3]);
+      if (f + kPfV < kPvMfma) vb[f % kPfV] = vfrag(vtile, f + kPfV);
+    }
+  };
+  // S(j+1) = K(j+1) Q^T interleaved with the probabilities of S(j), then
+  // O^T += V(j)^T P(j)^T interleaved with the row max of S(j+1); the issue
+  // order is pinned with scheduling groups (MFMA 0x008, DS read 0x100, VALU 0x002).
+  auto overlapped = [&](const uint4* kt, const uint4* vtile, const f32x16 (&cur)[2], f32x16 (&nxt)[2],
+                        float moff) {
+    uint32_t pk[2][8];
+    float psum = 0.0f;
+    bf16x8 kb[kPfK];
+    static_for<0, kPfK>([&](auto F) { kb[F] = kfrag(kt, F); });
+    static_for<0, kQkMfma>([&](auto F) {
+      constexpr int f = decltype(F)::value;
+      if constexpr (f < 2) {
+        nxt[f & 1] = mfma32(kb[f % kPfK], qf[f >> 1], f32x16{});
+      } else {
+        nxt[f & 1] = mfma32(kb[f % kPfK], qf[f >> 1], nxt[f & 1]);
       }
-    l_part = l_part * corr + psum;
-#pragma unroll
-    for (int i = 0; i < kV / 32; ++i) oacc[i] *= corr;
+      if constexpr (f + kPfK < kQkMfma) kb[f % kPfK] = kfrag(kt, f + kPfK);
+      if constexpr (f < 16) prob_pair(cur, pk, moff, psum, f);
+    });
+    l_part += psum;
+    bf16x8 vb[kPfV];
+    static_for<0, kPfV>([&](auto F) { vb[F] = vfrag(vtile, F); });
+    float mx = -INFINITY;
+    static_for<0, kPvMfma>([&](auto F) {
+      constexpr int f = decltype(F)::value;
+      oacc[f & 3] = mfma32(vb[f % kPfV], pv_operand(pk, f >> 2), oacc[f & 3]);
+      if constexpr (f + kPfV < kPvMfma) vb[f % kPfV] = vfrag(vtile, f + kPfV);
+      mx = fmaxf(mx, fmaxf(nxt[f >> 3][2 * (f & 7)], nxt[f >> 3][2 * (f & 7) + 1]));
+    });
+    mx_cur = xor32_max(mx);
+    static_for<0, kPfK>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
+    static_for<0, kQkMfma>([&](auto F) {
+      constexpr int f = decltype(F)::value;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (f + kPfK < kQkMfma) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if constexpr (f < 16) __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    });
+    static_for<0, kPfV>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
+    static_for<0, kPvMfma>([&](auto F) {
+      constexpr int f = decltype(F)::value;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (f + kPfV < kPvMfma) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+    });
+  };
 
-    // O^T += V^T P^T, 16 keys per MFMA
+  f32x16 sA[2], sB[2];
+
+  // one tile step; P = j & 1 picks the ring buffers and the score registers
+  auto step = [&](auto par, int j) {
+    constexpr int P = decltype(par)::value;
+    uint4* kdst = P ? K1 : K0;            // K(j+2) replaces K(j)
+    uint4* vdst = P ? V0 : V1;            // V(j+1) replaces V(j-1)
+    const uint4* kread = P ? K0 : K1;     // K(j+1)
+    const uint4* vread = P ? V1 : V0;     // V(j)
+    f32x16 (&cur)[2] = P ? sB : sA;
+    f32x16 (&nxt)[2] = P ? sA : sB;
+    if (j + 2 < nkt) dma_k(kdst, j + 2);
+    if (j + 1 < nkt) dma_v(vdst, j + 1);
+    if (j < nkt_w) {
+      // [A] move the reference max when S(j) exceeds it by more than 2^8
+      const bool need = (mx_cur - m_ref) * c2 > kRescaleLog2;
+      if (__ballot(need)) {
+        const float m_new = need ? mx_cur : m_ref;
+        const float corr = need ? fast_exp2((m_ref - m_new) * c2) : 1.0f;
+        m_ref = m_new;
+        l_part *= corr;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const uint32_t* src = &pk[jj >> 1][4 * (jj & 1)];
-      const bf16x8 bp = as_bf16x8(make_uint4(src[0], src[1], src[2], src[3]));
-#pragma unroll
-      for (int db = 0; db < kV / 32; ++db) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Vs + (32 * db + l32) * kVsLd + 16 * jj + 8 * g));
-        oacc[db] = mfma32(a, bp, oacc[db]);
+        for (int i = 0; i < kV / 32; ++i) oacc[i] *= corr;
+      }
+      m_true = fmaxf(m_true, mx_cur);
+      const float moff = -m_ref * c2;
+      if (j + 2 < nkt_w) {
+        overlapped(kread, vread, cur, nxt, moff);
+      } else {
+        // the wave's last two tiles: the next one (if any) is the masked diagonal tile
+        uint32_t pk[2][8];
+        probs(cur, pk, moff);
+        pv(vread, pk);
+        if (j + 1 < nkt_w) {
+          qk(kread, nxt);
+          mask_tile(j + 1, nxt);
+          mx_cur = tile_max(nxt);
+        }
       }
     }
+    wait_vmcnt<0>();
+    __syncthreads();
+  };
+
+  // ---- prologue: K(0), K(1), V(0) in LDS; S(0) ----
+  dma_k(K0, 0);
+  dma_v(V0, 0);
+  if (nkt > 1) dma_k(K1, 1);
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (nkt_w > 0) {
+    qk(K0, sA);
+    if (nkt_w == 1) mask_tile(0, sA);
+    mx_cur = tile_max(sA);
+  }
+  __syncthreads();   // K0 is refilled by the first step
+
+  for (int j = 0; j < nkt; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < nkt) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
   // ---- epilogue: normalise, gate, store; log-sum-exp; per-head max logit ----
@@ -420,8 +550,8 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(
         }
       }
     if (g == 0) {
-      if (lse) lse[static_cast<size_t>(head) * ntok + t] = m_raw * scale + __logf(l_tot);
-      rowmax[static_cast<size_t>(head) * ntok + t] = m_raw;
+      if (lse) lse[static_cast<size_t>(head) * ntok + t] = m_ref * scale + __logf(l_tot);
+      rowmax[static_cast<size_t>(head) * ntok + t] = m_true;
     }
   }
   // block maxima of the raw row max and of |q_t|^2 for the max-logit refinement
@@ -434,7 +564,7 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(
       qn2 = fmaf(x, x, qn2);
     }
   qn2 += __shfl_xor(qn2, 32, 64);
-  float v = qvalid ? m_raw : -INFINITY;
+  float v = qvalid ? m_true : -INFINITY;
   v = wave_max(v);
   qn2 = wave_max(qvalid ? qn2 : 0.0f);
   if (lane == 0) {
@@ -443,9 +573,13 @@ __global__ void __launch_bounds__(256) prefill_attn_kernel(
   }
   __syncthreads();
   if (tid == 0) {
-    const float mm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float mm = red[0], mq = redq[0];
+    for (int w = 1; w < kAttnWaves; ++w) {
+      mm = fmaxf(mm, red[w]);
+      mq = fmaxf(mq, redq[w]);
+    }
     if (mm > -INFINITY) atomic_max_float(aux + head * kAuxStride, mm);
-    atomic_max_float(aux + head * kAuxStride + 1, fmaxf(fmaxf(redq[0], redq[1]), fmaxf(redq[2], redq[3])));
+    atomic_max_float(aux + head * kAuxStride + 1, mq);
   }
 }
 
@@ -513,13 +647,14 @@ __global__ void __launch_bounds__(256) prefill_refine_scan_kernel(
     __syncthreads();
     if (tid < kD) qrow[tid] = bf16_to_f32(q[(static_cast<size_t>(t) * heads + h) * kD + tid]);
     __syncthreads();
-    const uint16_t* kch = kc + (static_cast<size_t>(h) * npad_max + pcu[lo]) * kN;
+    const uint16_t* kch = kc + (static_cast<size_t>(h) * (npad_max / kPrefBN) + pcu[lo] / kPrefBN) * kTileElems;
     for (int s = s0 + tid; s < s1; s += 256) {
       uint4 x[kD / 8];
-      const uint16_t* kr = kch + static_cast<size_t>(s - a) * kN;
+      const int pl = s - a;   // sequence-local row: tile pl / 64, row pl % 64 of the tile-blocked K^C
+      const uint16_t* kr = kch + static_cast<size_t>(pl / kPrefBN) * kTileElems + (pl % kPrefBN) * 8;
       const uint16_t* sr = ks + static_cast<size_t>(s) * kS;
 #pragma unroll
-      for (int e = 0; e < kN / 8; ++e) x[e] = ldg16(kr + 8 * e);
+      for (int e = 0; e < kN / 8; ++e) x[e] = ldg16(kr + e * (kPrefBN * 8));
 #pragma unroll
       for (int e = 0; e < kS / 8; ++e) x[kN / 8 + e] = ldg16(sr + 8 * e);
       float acc = 0.0f;
@@ -611,6 +746,7 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
   char* base = static_cast<char*>(ws);
   uint16_t* kc = reinterpret_cast<uint16_t*>(base + L.kc);
   uint16_t* vt = reinterpret_cast<uint16_t*>(base + L.vt);
+  uint16_t* ksp = reinterpret_cast<uint16_t*>(base + L.ksp);
   int32_t* pcu = reinterpret_cast<int32_t*>(base + L.pcu);
   int32_t* order = reinterpret_cast<int32_t*>(base + L.order);
   int32_t* toff = reinterpret_cast<int32_t*>(base + L.toff);
@@ -636,7 +772,7 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
     TimedScope ts_("prefill_expand", st);
     hipLaunchKernelGGL(prefill_expand_kernel, eg, dim3(256), 0, st, static_cast<const uint16_t*>(ckv),
                        static_cast<const uint16_t*>(w_kv_b), cu, nseq, pcu, hdr, L.npad_max,
-                       static_cast<const uint16_t*>(ks), kc, vt, aux);
+                       static_cast<const uint16_t*>(ks), kc, vt, ksp, aux);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -649,16 +785,16 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
   if (out_bf16) {
     {
       TimedScope ts_("prefill_attn", st);
-      hipLaunchKernelGGL(prefill_attn_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
-                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(ks),
+      hipLaunchKernelGGL(prefill_attn_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0, st,
+                         static_cast<const uint16_t*>(q), ksp,
                          static_cast<const uint16_t*>(gate), cu, pcu, order, toff, hdr, nseq, heads, ntok,
                          L.npad_max, kc, vt, scale, out, lse, rowmax, aux);
     }
   } else {
     {
       TimedScope ts_("prefill_attn", st);
-      hipLaunchKernelGGL(prefill_attn_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
-                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(ks),
+      hipLaunchKernelGGL(prefill_attn_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0, st,
+                         static_cast<const uint16_t*>(q), ksp,
                          static_cast<const uint16_t*>(gate), cu, pcu, order, toff, hdr, nseq, heads, ntok,
                          L.npad_max, kc, vt, scale, out, lse, rowmax, aux);
     }
