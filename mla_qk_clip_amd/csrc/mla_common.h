@@ -79,9 +79,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Max / sum of a value and the same value in the lane 32 apart (one
 // cross-half swap, no LDS traffic).
+// max(a, b, c) with NaN propagation (IEEE maximum: no operand quieting needed)
+__device__ __forceinline__ float fmax3_(float a, float b, float c) {
+  return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+}
 __device__ __forceinline__ float xor32_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+  return fmax3_(v, __uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -116,6 +120,19 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Raw buffer resource over [base, base + bytes) (reads past the end return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// Buffer load of 16 bytes per lane (at byte offset voff + soff of the
+// resource) straight into LDS: lane i's bytes land at lds + 16 i (lds must be
+// the same for the whole wave).
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
 // Copy 16 bytes per lane from global memory straight into LDS: lane i's

@@ -322,17 +322,23 @@ __global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
   const uint16_t* vt_h = vt + (static_cast<size_t>(head) * (npad_max / kPrefBN) + tb) * kTileElems;
   const uint16_t* ks_t = ksp + tb * (kPrefBN * kS);
 
-  // ---- tile copies: 1 KB blocks, lane i's 16 bytes at block + 16 i ----
+  // ---- tile copies: 1 KB blocks, lane i's 16 bytes at block + 16 i. Buffer
+  // loads (not flat/global ones) keep the compiler's LDS-read waits partial.
+  const uint32_t seq_tiles = static_cast<uint32_t>((L + kPrefBN - 1) / kPrefBN);
+  const auto rs_kc = make_rsrc(kc_h, seq_tiles * kTileElems * 2);
+  const auto rs_vt = make_rsrc(vt_h, seq_tiles * kTileElems * 2);
+  const auto rs_ks = make_rsrc(ks_t, seq_tiles * kPrefBN * kS * 2);
+  const uint32_t lane16 = 16u * lane;
   auto dma_k = [&](uint4* dst, int j) {
-    const uint16_t* kcj = kc_h + static_cast<size_t>(j) * kTileElems;
-    dma16(kcj + (2 * wave) * 512 + 8 * lane, dst + (2 * wave) * 64);
-    dma16(kcj + (2 * wave + 1) * 512 + 8 * lane, dst + (2 * wave + 1) * 64);
-    dma16(ks_t + static_cast<size_t>(j) * (kPrefBN * kS) + wave * 512 + 8 * lane, dst + (kN / 8 + wave) * 64);
+    const uint32_t so = static_cast<uint32_t>(j) * (kTileElems * 2);
+    dma16_buf(rs_kc, lane16 + (2 * wave) * 1024, so, dst + (2 * wave) * 64);
+    dma16_buf(rs_kc, lane16 + (2 * wave + 1) * 1024, so, dst + (2 * wave + 1) * 64);
+    dma16_buf(rs_ks, lane16 + wave * 1024, static_cast<uint32_t>(j) * (kPrefBN * kS * 2), dst + (kN / 8 + wave) * 64);
   };
   auto dma_v = [&](uint4* dst, int j) {
-    const uint16_t* vtj = vt_h + static_cast<size_t>(j) * kTileElems;
-    dma16(vtj + (2 * wave) * 512 + 8 * lane, dst + (2 * wave) * 64);
-    dma16(vtj + (2 * wave + 1) * 512 + 8 * lane, dst + (2 * wave + 1) * 64);
+    const uint32_t so = static_cast<uint32_t>(j) * (kTileElems * 2);
+    dma16_buf(rs_vt, lane16 + (2 * wave) * 1024, so, dst + (2 * wave) * 64);
+    dma16_buf(rs_vt, lane16 + (2 * wave + 1) * 1024, so, dst + (2 * wave + 1) * 64);
   };
 
   // LDS operand addresses: K unit (2kk + g) * 64 + 32 blk + l32, V^T unit
@@ -371,7 +377,7 @@ __global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[blk][e]);
+      for (int e = 0; e < 16; e += 2) mx = fmax3_(mx, s[blk][e], s[blk][e + 1]);
     return xor32_max(mx);
   };
 
@@ -413,8 +419,7 @@ __global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
     }
   };
   // S(j+1) = K(j+1) Q^T interleaved with the probabilities of S(j), then
-  // O^T += V(j)^T P(j)^T interleaved with the row max of S(j+1); the issue
-  // order is pinned with scheduling groups (MFMA 0x008, DS read 0x100, VALU 0x002).
+  // O^T += V(j)^T P(j)^T interleaved with the row max of S(j+1).
   auto overlapped = [&](const uint4* kt, const uint4* vtile, const f32x16 (&cur)[2], f32x16 (&nxt)[2],
                         float moff) {
     uint32_t pk[2][8];
@@ -439,23 +444,9 @@ __global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
       constexpr int f = decltype(F)::value;
       oacc[f & 3] = mfma32(vb[f % kPfV], pv_operand(pk, f >> 2), oacc[f & 3]);
       if constexpr (f + kPfV < kPvMfma) vb[f % kPfV] = vfrag(vtile, f + kPfV);
-      mx = fmaxf(mx, fmaxf(nxt[f >> 3][2 * (f & 7)], nxt[f >> 3][2 * (f & 7) + 1]));
+      mx = fmax3_(mx, nxt[f >> 3][2 * (f & 7)], nxt[f >> 3][2 * (f & 7) + 1]);
     });
     mx_cur = xor32_max(mx);
-    static_for<0, kPfK>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
-    static_for<0, kQkMfma>([&](auto F) {
-      constexpr int f = decltype(F)::value;
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if constexpr (f + kPfK < kQkMfma) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if constexpr (f < 16) __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-    });
-    static_for<0, kPfV>([&](auto) { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); });
-    static_for<0, kPvMfma>([&](auto F) {
-      constexpr int f = decltype(F)::value;
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if constexpr (f + kPfV < kPvMfma) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
-    });
   };
 
   f32x16 sA[2], sB[2];
