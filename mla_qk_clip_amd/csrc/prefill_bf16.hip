@@ -259,6 +259,27 @@ static_assert(kN / 8 == 2 * kAttnWaves && kS / 8 == kAttnWaves && kVTile / 64 ==
               "each wave copies two K^C blocks, one k^S block and two V^T blocks per tile");
 constexpr float kRescaleLog2 = 8.0f;
 
+// Issue order of the overlapped tile body. qk: score MFMA idx = 12 blk + kk
+// (else value MFMA idx = 4 jj + db); pair: probability pair formed with it;
+// mx: group of four elements of score block 0 folded into the row max.
+struct Ovl {
+  bool qk;
+  int8_t idx, pair, mx;
+};
+constexpr Ovl kOvl[] = {
+    {true, 0, 0, -1},   {true, 1, 1, -1},   {true, 2, 2, -1},   {true, 3, 3, -1},   {true, 4, -1, -1},
+    {true, 5, -1, -1},  {true, 6, 4, -1},   {false, 0, -1, -1}, {true, 7, 5, -1},   {false, 1, -1, -1},
+    {true, 8, 6, -1},   {false, 2, -1, -1}, {true, 9, 7, -1},   {false, 3, -1, -1}, {true, 10, 8, -1},
+    {false, 4, -1, -1}, {true, 11, 9, -1},  {false, 5, -1, -1}, {true, 12, 10, -1}, {false, 6, -1, -1},
+    {true, 13, 11, -1}, {false, 7, -1, -1}, {true, 14, 12, -1}, {false, 8, -1, 0},  {true, 15, 13, -1},
+    {false, 9, -1, 1},  {true, 16, 14, -1}, {false, 10, -1, 2}, {true, 17, 15, -1}, {false, 11, -1, 3},
+    {true, 18, -1, -1}, {false, 12, -1, -1}, {true, 19, -1, -1}, {false, 13, -1, -1}, {true, 20, -1, -1},
+    {false, 14, -1, -1}, {true, 21, -1, -1}, {false, 15, -1, -1}, {true, 22, -1, -1}, {true, 23, -1, -1},
+};
+constexpr int kOvlLen = sizeof(kOvl) / sizeof(kOvl[0]);
+constexpr int kRing = 4;   // LDS operand fragments in flight
+static_assert(kOvlLen == 40, "24 score + 16 value MFMAs");
+
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ksp, const uint16_t* __restrict__ gate,
@@ -418,35 +439,47 @@ __global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
       if (f + kPfV < kPvMfma) vb[f % kPfV] = vfrag(vtile, f + kPfV);
     }
   };
-  // S(j+1) = K(j+1) Q^T interleaved with the probabilities of S(j), then
-  // O^T += V(j)^T P(j)^T interleaved with the row max of S(j+1).
+  // Overlapped tile body: the 24 score MFMAs of S(j+1) = K(j+1) Q^T and the
+  // 16 value MFMAs of O^T += V(j)^T P(j)^T are issued in one interleaved
+  // sequence (kOvl), each with one LDS operand read kRing MFMAs ahead and a
+  // share of the VALU work: the probabilities of S(j) (pair p = elements 2p,
+  // 2p+1 of the 32 scores a lane holds; the value MFMAs of 16 keys jj need
+  // pairs 4jj..4jj+3) and the row max of S(j+1). Scheduling barriers keep
+  // the issue order.
   auto overlapped = [&](const uint4* kt, const uint4* vtile, const f32x16 (&cur)[2], f32x16 (&nxt)[2],
                         float moff) {
     uint32_t pk[2][8];
     float psum = 0.0f;
-    bf16x8 kb[kPfK];
-    static_for<0, kPfK>([&](auto F) { kb[F] = kfrag(kt, F); });
-    static_for<0, kQkMfma>([&](auto F) {
-      constexpr int f = decltype(F)::value;
-      if constexpr (f < 2) {
-        nxt[f & 1] = mfma32(kb[f % kPfK], qf[f >> 1], f32x16{});
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+    bf16x8 ring[kRing];
+    auto fetch = [&](auto C) {
+      constexpr int c = decltype(C)::value;
+      if constexpr (kOvl[c].qk) return kfrag(kt, 2 * (kOvl[c].idx % 12) + kOvl[c].idx / 12);
+      else return vfrag(vtile, kOvl[c].idx);
+    };
+    static_for<0, kRing>([&](auto C) { ring[C] = fetch(C); });
+    static_for<0, kOvlLen>([&](auto C) {
+      constexpr int c = decltype(C)::value;
+      constexpr Ovl o = kOvl[c];
+      if constexpr (o.qk) {
+        constexpr int blk = o.idx / 12, kk = o.idx % 12;
+        if constexpr (kk == 0) nxt[blk] = mfma32(ring[c % kRing], qf[kk], f32x16{});
+        else nxt[blk] = mfma32(ring[c % kRing], qf[kk], nxt[blk]);
       } else {
-        nxt[f & 1] = mfma32(kb[f % kPfK], qf[f >> 1], nxt[f & 1]);
+        oacc[o.idx & 3] = mfma32(ring[c % kRing], pv_operand(pk, o.idx >> 2), oacc[o.idx & 3]);
       }
-      if constexpr (f + kPfK < kQkMfma) kb[f % kPfK] = kfrag(kt, f + kPfK);
-      if constexpr (f < 16) prob_pair(cur, pk, moff, psum, f);
+      if constexpr (c + kRing < kOvlLen) ring[c % kRing] = fetch(std::integral_constant<int, c + kRing>{});
+      if constexpr (o.pair >= 0) prob_pair(cur, pk, moff, psum, o.pair);
+      if constexpr (o.mx >= 0) {
+        mx0 = fmax3_(mx0, nxt[0][4 * o.mx], nxt[0][4 * o.mx + 1]);
+        mx0 = fmax3_(mx0, nxt[0][4 * o.mx + 2], nxt[0][4 * o.mx + 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     });
     l_part += psum;
-    bf16x8 vb[kPfV];
-    static_for<0, kPfV>([&](auto F) { vb[F] = vfrag(vtile, F); });
-    float mx = -INFINITY;
-    static_for<0, kPvMfma>([&](auto F) {
-      constexpr int f = decltype(F)::value;
-      oacc[f & 3] = mfma32(vb[f % kPfV], pv_operand(pk, f >> 2), oacc[f & 3]);
-      if constexpr (f + kPfV < kPvMfma) vb[f % kPfV] = vfrag(vtile, f + kPfV);
-      mx = fmax3_(mx, nxt[f >> 3][2 * (f & 7)], nxt[f >> 3][2 * (f & 7) + 1]);
-    });
-    mx_cur = xor32_max(mx);
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) mx1 = fmax3_(mx1, nxt[1][e], nxt[1][e + 1]);
+    mx_cur = xor32_max(__builtin_elementwise_maximum(mx0, mx1));
   };
 
   f32x16 sA[2], sB[2];
