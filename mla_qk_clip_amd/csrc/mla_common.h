@@ -112,7 +112,9 @@ __device__ __forceinline__ void stg16(void* p, uint4 v) { *reinterpret_cast<uint
 // trade places, so that lane half 0 finds rows {0-3, 8-11} and half 1 finds
 // rows {4-7, 12-15} as 8 consecutive elements, matching the rows it holds in
 // the score accumulator.
-__device__ __forceinline__ int vperm16(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+__host__ __device__ constexpr int vperm16(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+// The same exchange applied inside every aligned group of 16.
+__host__ __device__ constexpr int kperm(int n) { return (n & ~15) | vperm16(n & 15); }
 
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (global loads, including the ones that write LDS directly).

@@ -31,7 +31,8 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // 64 rows; padded row p belongs to 64-row key tile p / 64 and the expanded
 // operands are stored tile-blocked in the order the attention kernel copies
 // them into LDS (1 KB = 64 x 16 bytes per block, padding rows zero):
-//   kc [H][tile][16 units][64 rows][8]   K^C, unit u = features 8u..8u+7
+//   kc [H][tile][16 units][64 rows][8]   K^C, unit u = features kperm(8u..8u+7),
+//                                        kperm(n) = (n & ~15) | vperm16(n & 15)
 //   vt [H][tile][8 units][128 d][8]      V^T, unit u = keys at permuted
 //                                        positions 8u..8u+7 of the tile
 //   ksp[tile][8 units][64 rows][8]       k^S (shared by all heads)
@@ -43,15 +44,16 @@ constexpr int kTileElems = kPrefBN * kN;  // elements of one K^C (or V^T) tile o
 // aux[h][0] = approximate (raw, unscaled) head max logit, aux[h][1] = max |q_t|^2,
 // aux[h][2] = max |K^C_s|^2 (bf16 values), aux[h][3] unused; aux[H][0] = max |k^S_s|^2.
 constexpr int kAuxStride = 4;
-// Max-logit refinement candidates per head: int count, int overflow flag, then
-// kRefKeys (query row, key) pairs.
+// Max-logit refinement candidates per head: [0] pair count, [1] overflow flag,
+// [2] row count, then kRefRows (row, sequence start) and kRefKeys (row, key) pairs.
 constexpr int kRefRows = 64;
 constexpr int kRefKeys = 256;
-constexpr int kRefSlices = 8;
-constexpr int kCandStride = 2 + 2 * kRefKeys;
+constexpr int kCandRows = 4;
+constexpr int kCandPairs = kCandRows + 2 * kRefRows;
+constexpr int kCandStride = kCandPairs + 2 * kRefKeys;
 inline PrefillWs prefill_ws_layout(int heads, int64_t ntok, int nseq) {
   PrefillWs w{};
-  w.npad_max = static_cast<int64_t>(align_up(static_cast<size_t>(ntok + static_cast<int64_t>(kSeqPad) * nseq), 128));
+  w.npad_max = static_cast<int64_t>(align_up(static_cast<size_t>(ntok + static_cast<int64_t>(kSeqPad) * nseq), 256));
   size_t off = 0;
   w.kc = off; off = align_up(off + static_cast<size_t>(heads) * w.npad_max * kN * 2, 256);
   w.vt = off; off = align_up(off + static_cast<size_t>(heads) * w.npad_max * kV * 2, 256);

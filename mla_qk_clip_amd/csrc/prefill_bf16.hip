@@ -66,34 +66,66 @@ __global__ void __launch_bounds__(256) prefill_plan_kernel(const int32_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// Expansion: C[p, j] = sum_k c^KV[src(p), k] * w_kv_b[j, k] over padded rows p.
-// One workgroup = 128 padded rows (two key tiles) x one 128-wide half of one
-// head (even half: K^C_h, odd half: V_h), written tile-blocked (see
-// PrefillWs). V is stored transposed with the keys of each 16-row group in the
-// value-operand order (vperm16). The head-0 K^C blocks also write the padded
-// k^S copy.
+// Expansion: [K^C_h | V_h][p] = c^KV[src(p)] W_UKV[:, 256h : 256h+256] over
+// padded rows p. One workgroup = 256 padded rows (four key tiles) x the 256
+// columns of one head; 8 waves, wave w owns rows 64 (w & 3) .. +63 of the
+// K^C half (w < 4) or of the V half. K = 512 in 16 steps of 32 through a
+// double-buffered LDS tile staged through registers one step ahead.
+//
+// LDS tile layout (one operand, 256 rows x four 16-byte k-units): unit (r, c)
+// at (r / 16) * 64 + c * 16 + r % 16: a wave's staging store of 64 units
+// covers 16 whole row segments, and a 16-lane group of a fragment read
+// touches 16 consecutive units.
+//
+// Both halves are stored straight from the accumulators with 16-byte stores:
+// V is formed as C = c^KV W_V (accumulator lane = feature d, its rows = keys)
+// and lands in V^T units of eight keys in value-operand order (vperm16); K^C
+// is formed transposed, C^T = W_K c^KV^T (lane = key, rows = features), and
+// lands in units of eight features in that same order: unit u of a K^C row
+// holds features kperm(8u .. 8u+7), kperm(n) = (n & ~15) | vperm16(n & 15).
+// The attention kernel loads q^C in that feature order. The head-0 workgroups
+// also write the padded k^S copy.
 // ---------------------------------------------------------------------------
-constexpr int kExBM = 128, kExBN = 128, kExBK = 64, kExLd = kExBK + 8, kExOutLd = 128 + 8;
+constexpr int kExRows = 256;      // padded rows per workgroup
+constexpr int kExThreads = 512;
+constexpr int kExSteps = kR / 32;  // k-steps of 32
+constexpr int kExUnits = kExRows * 4;  // 16-byte units per operand slot
+constexpr int kExGroupRows = 2, kExGroupHeads = 16, kExGroup = kExGroupRows * kExGroupHeads;
 
-__global__ void __launch_bounds__(256) prefill_expand_kernel(
+__global__ void __launch_bounds__(kExThreads) prefill_expand_kernel(
     const uint16_t* __restrict__ ckv, const uint16_t* __restrict__ w, const int32_t* __restrict__ cu,
-    int nseq, const int32_t* __restrict__ pcu, const int32_t* __restrict__ hdr, int64_t npad_max,
-    const uint16_t* __restrict__ ks, uint16_t* __restrict__ kc, uint16_t* __restrict__ vt,
+    int nseq, const int32_t* __restrict__ pcu, const int32_t* __restrict__ hdr, int64_t npad_max, int64_t ntok,
+    int heads, const uint16_t* __restrict__ ks, uint16_t* __restrict__ kc, uint16_t* __restrict__ vt,
     uint16_t* __restrict__ ksp, float* __restrict__ aux) {
-  __shared__ __align__(16) uint16_t smem[2 * kExBM * kExLd];
-  __shared__ int src_row[kExBM];
-  __shared__ float red[4];
-  static_assert(kExBM * kExOutLd <= 2 * kExBM * kExLd, "staging must fit");
+  __shared__ uint4 Cs[2][kExUnits];   // c^KV slots
+  __shared__ uint4 Ws[2][kExUnits];   // W_UKV slots
+  __shared__ int src_row[kExRows];
+  __shared__ float red[8];
 
+  // ---- work item: groups of kExGroupRows row tiles x kExGroupHeads heads,
+  // consecutive groups on the same XCD ----
   const int npad = hdr[1];
-  const int m0 = blockIdx.y * kExBM;
+  const int nrt = static_cast<int>(npad_max / kExRows);
+  const int nrg = (nrt + kExGroupRows - 1) / kExGroupRows, nhg = (heads + kExGroupHeads - 1) / kExGroupHeads;
+  const int per_xcd = (nrg * nhg * kExGroup + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per_xcd) return;
+  const int item = (blockIdx.x & 7) * per_xcd + slot;
+  const int grp = item / kExGroup, gi = item - grp * kExGroup;
+  if (grp >= nrg * nhg) return;
+  const int rg = grp / nhg, hg = grp - rg * nhg;
+  const int rt = rg * kExGroupRows + gi % kExGroupRows;
+  const int head = hg * kExGroupHeads + gi / kExGroupRows;
+  if (rt >= nrt || head >= heads) return;
+  const int m0 = rt * kExRows;
   if (m0 >= npad) return;
-  const int head = blockIdx.x >> 1, half = blockIdx.x & 1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int wm = wave >> 1, wn = wave & 1;
 
-  if (tid < kExBM) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar branches)
+  const int g = lane >> 5, l32 = lane & 31;
+  const int wm = wave & 3, half = wave >> 2;
+
+  if (tid < kExRows) {
     const int p = m0 + tid;
     int src = -1;
     if (p < npad) {
@@ -109,123 +141,153 @@ __global__ void __launch_bounds__(256) prefill_expand_kernel(
   }
   __syncthreads();
 
-  uint16_t* As = smem;
-  uint16_t* Bs = smem + kExBM * kExLd;
-  const uint16_t* wrow = w + (static_cast<size_t>(head) * 256 + half * 128) * kR;
-
-  uint4 ra[4], rb[4];
-  auto load = [&](int k0) {
+  // ---- staging: thread (wave w, lane i) carries unit (row 16 b + i % 16,
+  // k-unit i / 16) of blocks b = 2w, 2w+1 of both operands ----
+  const uint16_t* csrc[2];
+  const uint16_t* wsrc[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int id = tid + 256 * c;
-      const int row = id >> 3, part = id & 7;
-      const int src = src_row[row];
-      ra[c] = src >= 0 ? ldg16(ckv + static_cast<size_t>(src) * kR + k0 + 8 * part) : make_uint4(0, 0, 0, 0);
-      rb[c] = ldg16(wrow + static_cast<size_t>(row) * kR + k0 + 8 * part);
+  for (int bb = 0; bb < 2; ++bb) {
+    const int r = 16 * (2 * wave + bb) + (lane & 15), c = lane >> 4;
+    const int src = src_row[r];
+    csrc[bb] = src >= 0 ? ckv + static_cast<size_t>(src) * kR + 8 * c : nullptr;   // padding rows: zeros
+    wsrc[bb] = w + (static_cast<size_t>(head) * 256 + r) * kR + 8 * c;
+  }
+  uint4 rc[2], rw[2];
+  auto gload = [&](int st) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      rc[bb] = csrc[bb] ? ldg16(csrc[bb] + 32 * st) : make_uint4(0, 0, 0, 0);
+      rw[bb] = ldg16(wsrc[bb] + 32 * st);
     }
   };
-
-  f32x16 acc[2][2];
+  auto sstore = [&](int sl) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-  load(0);
-  for (int kt = 0; kt < kR / kExBK; ++kt) {
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int id = tid + 256 * c;
-      const int row = id >> 3, part = id & 7;
-      *reinterpret_cast<uint4*>(As + row * kExLd + 8 * part) = ra[c];
-      *reinterpret_cast<uint4*>(Bs + row * kExLd + 8 * part) = rb[c];
+    for (int bb = 0; bb < 2; ++bb) {
+      Cs[sl][64 * (2 * wave + bb) + lane] = rc[bb];
+      Ws[sl][64 * (2 * wave + bb) + lane] = rw[bb];
     }
-    __syncthreads();
-    if (kt + 1 < kR / kExBK) load((kt + 1) * kExBK);
-#pragma unroll
-    for (int ks = 0; ks < kExBK / 16; ++ks) {
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = as_bf16x8(*reinterpret_cast<const uint4*>(As + (wm * 64 + 32 * i + l32) * kExLd + 16 * ks + 8 * g));
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = as_bf16x8(*reinterpret_cast<const uint4*>(Bs + (wn * 64 + 32 * j + l32) * kExLd + 16 * ks + 8 * g));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-    }
-  }
+  };
+  auto frag = [&](const uint4* t, int r0, int kh) {   // rows r0 .. r0+31, k-units 2 kh + g
+    const int r = r0 + l32;
+    return as_bf16x8(t[(r >> 4) * 64 + (2 * kh + g) * 16 + (r & 15)]);
+  };
 
-  // stage the 128 x 128 tile as bf16 in its final orientation
-  __syncthreads();
-  uint16_t* st = smem;
+  // acc: K half (transposed C^T): acc[2 fb + kb], fb = feature block (4), kb = key block (2);
+  //      V half: acc[4 kb + fb]. Each half runs its own copy of the loop (no
+  //      register joins between the two operand orders).
+  const size_t tiles_h = static_cast<size_t>(head) * (npad_max / kPrefBN);
+  float n2 = 0.0f;   // |K^C_key|^2 of this lane's keys (bf16 values), K half only
+  auto run = [&](auto HALF) {
+    constexpr int H = decltype(HALF)::value;
+    f32x16 acc[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+
+    gload(0);
+    sstore(0);
+    gload(1);
+    __syncthreads();
+    for (int st = 0; st < kExSteps; ++st) {
+      const uint4* cs = Cs[st & 1];
+      const uint4* ws = Ws[st & 1];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int kh = 0; kh < 2; ++kh) {
+        bf16x8 cf[2], wf[4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = wm * 64 + 32 * i + acc_row(e, g);   // padded row within the tile
-        const int n = wn * 64 + 32 * j + l32;             // feature within the half
-        const uint16_t v = f32_to_bf16(acc[i][j][e]);
-        if (half == 0) st[m * kExOutLd + n] = v;
-        else st[n * kExOutLd + ((m & ~15) | vperm16(m & 15))] = v;
+        for (int kb = 0; kb < 2; ++kb) cf[kb] = frag(cs, 64 * wm + 32 * kb, kh);
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb) wf[fb] = frag(ws, 128 * H + 32 * fb, kh);
+        if constexpr (H == 0) {
+#pragma unroll
+          for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) acc[2 * fb + kb] = mfma32(wf[fb], cf[kb], acc[2 * fb + kb]);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb) acc[4 * kb + fb] = mfma32(cf[kb], wf[fb], acc[4 * kb + fb]);
+        }
       }
-  __syncthreads();
-  if (half == 0) {
-    // largest squared norm of a stored K^C row (and, once, of a k^S row): the
-    // error bound of the max-logit refinement
-    const int row = tid >> 1, part = tid & 1;
-    float n2 = 0.0f;
-#pragma unroll 8
-    for (int e = 0; e < 64; e += 2) {
-      const uint32_t w2 = *reinterpret_cast<const uint32_t*>(st + row * kExOutLd + 64 * part + e);
-      n2 = fmaf(bf16lo(w2), bf16lo(w2), fmaf(bf16hi(w2), bf16hi(w2), n2));
+      if (st + 1 < kExSteps) sstore((st + 1) & 1);   // slot last read by step st - 1
+      if (st + 2 < kExSteps) gload(st + 2);
+      __syncthreads();
     }
-    n2 += __shfl_xor(n2, 1, 64);
-    float s2 = 0.0f;
-    if (head == 0 && part == 0 && src_row[row] >= 0) {
-      const uint16_t* kr = ks + static_cast<size_t>(src_row[row]) * kS;
-      for (int e = 0; e < kS; e += 8) {
-        const uint4 w4 = ldg16(kr + e);
-        const uint32_t* x = &w4.x;
+
+    // ---- store: 16-byte units straight from the accumulators ----
+    if constexpr (H == 0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) s2 = fmaf(bf16lo(x[u]), bf16lo(x[u]), fmaf(bf16hi(x[u]), bf16hi(x[u]), s2));
+      for (int kb = 0; kb < 2; ++kb) {
+        const int p = m0 + 64 * wm + 32 * kb + l32;          // this lane's key (padded row)
+        uint16_t* dst = kc + (tiles_h + p / kPrefBN) * kTileElems + (p % kPrefBN) * 8;
+        float s2 = 0.0f;
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const f32x16& a = acc[2 * fb + kb];
+            uint32_t wv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              wv[e] = pack_bf16x2(a[8 * hh + 2 * e], a[8 * hh + 2 * e + 1]);
+              s2 = fmaf(bf16lo(wv[e]), bf16lo(wv[e]), fmaf(bf16hi(wv[e]), bf16hi(wv[e]), s2));
+            }
+            const int u = 4 * fb + 2 * hh + g;                  // features kperm(8u .. 8u+7)
+            stg16(dst + u * (kPrefBN * 8), make_uint4(wv[0], wv[1], wv[2], wv[3]));
+          }
+        n2 = fmaxf(n2, xor32_sum(s2));
       }
-    }
-    n2 = wave_max(n2);
-    s2 = wave_max(s2);
-    if (lane == 0) red[wave] = n2;
-    __syncthreads();
-    if (tid == 0) atomic_max_float(aux + head * kAuxStride + 2, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
-    if (head == 0 && lane == 0) atomic_max_float(aux + static_cast<size_t>(gridDim.x / 2) * kAuxStride, s2);
-  }
-  const size_t tile0 = static_cast<size_t>(head) * (npad_max / kPrefBN) + m0 / kPrefBN;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int id = tid + 256 * c;
-    if (half == 0) {
-      const int r = id & 63, u = (id >> 6) & 15, tl = id >> 10;
-      const uint4 v = *reinterpret_cast<const uint4*>(st + (tl * kPrefBN + r) * kExOutLd + 8 * u);
-      stg16(kc + (tile0 + tl) * kTileElems + (u * kPrefBN + r) * 8, v);
     } else {
-      const int d = id & 127, u = (id >> 7) & 7, tl = id >> 10;
-      const uint4 v = *reinterpret_cast<const uint4*>(st + d * kExOutLd + tl * kPrefBN + 8 * u);
-      stg16(vt + (tile0 + tl) * kTileElems + (u * kV + d) * 8, v);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const f32x16& a = acc[4 * kb + fb];
+            const int p0 = m0 + 64 * wm + 32 * kb + 16 * hh;    // first key of the 16-key group
+            const int d = 32 * fb + l32;
+            const int u = ((p0 % kPrefBN) >> 3) + g;            // keys at value-operand positions 8u .. 8u+7
+            uint16_t* dst = vt + (tiles_h + p0 / kPrefBN) * kTileElems + (u * kV + d) * 8;
+            stg16(dst, make_uint4(pack_bf16x2(a[8 * hh], a[8 * hh + 1]), pack_bf16x2(a[8 * hh + 2], a[8 * hh + 3]),
+                                  pack_bf16x2(a[8 * hh + 4], a[8 * hh + 5]), pack_bf16x2(a[8 * hh + 6], a[8 * hh + 7])));
+          }
     }
-  }
-  if (half == 0 && head == 0) {
+  };
+  if (half == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
+  // largest squared norm of a stored K^C row (and, once, of a k^S row): the
+  // error bound of the max-logit refinement
+  n2 = wave_max(n2);
+  if (lane == 0) red[wave] = n2;
+  if (head == 0) {
+    // padded k^S copy (tile-blocked, zero rows past each sequence) and the largest |k^S_s|^2
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int id = tid + 256 * c;
+      const int id = tid + kExThreads * c;   // 256 rows x 8 units
       const int r = id & 63, u = (id >> 6) & 7, tl = id >> 9;
       const int src = src_row[tl * kPrefBN + r];
       const uint4 v = src >= 0 ? ldg16(ks + static_cast<size_t>(src) * kS + 8 * u) : make_uint4(0, 0, 0, 0);
       stg16(ksp + (static_cast<size_t>(m0 / kPrefBN + tl) * (kS / 8) + u) * (kPrefBN * 8) + r * 8, v);
     }
+    float s2 = 0.0f;
+    if (tid < kExRows && src_row[tid] >= 0) {
+#pragma unroll
+      for (int u = 0; u < kS / 8; ++u) {
+        const uint4 v = ldg16(ks + static_cast<size_t>(src_row[tid]) * kS + 8 * u);
+        const uint32_t* x = &v.x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s2 = fmaf(bf16lo(x[e]), bf16lo(x[e]), fmaf(bf16hi(x[e]), bf16hi(x[e]), s2));
+      }
+    }
+    s2 = wave_max(s2);
+    if (lane == 0 && wave < kExRows / 64) atomic_max_float(aux + static_cast<size_t>(heads) * kAuxStride, s2);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float mm = red[0];
+    for (int i = 1; i < 4; ++i) mm = fmaxf(mm, red[i]);
+    atomic_max_float(aux + head * kAuxStride + 2, mm);
   }
 }
 
@@ -328,13 +390,23 @@ __global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
   const int nkt = (nkv + kPrefBN - 1) / kPrefBN;                     // tiles staged by the workgroup
   const int nkt_w = qw < L ? min(nkt, (qw + 31) / kPrefBN + 1) : 0;  // tiles this wave uses
 
-  // ---- queries, held as MFMA B operands for the whole loop ----
+  // ---- queries, held as MFMA B operands for the whole loop; the q^C
+  // features in the stored K^C order kperm (two 8-byte halves per fragment) ----
   bf16x8 qf[kD / 16];
   {
-    const uint16_t* qrow = q + (static_cast<size_t>(a0 + (qvalid ? qi : 0)) * heads + head) * kD + 8 * g;
+    const uint16_t* qrow = q + (static_cast<size_t>(a0 + (qvalid ? qi : 0)) * heads + head) * kD;
 #pragma unroll
-    for (int kk = 0; kk < kD / 16; ++kk)
-      qf[kk] = as_bf16x8(qvalid ? ldg16(qrow + 16 * kk) : make_uint4(0, 0, 0, 0));
+    for (int kk = 0; kk < kN / 16; ++kk) {
+      uint2 lo = make_uint2(0, 0), hi = make_uint2(0, 0);
+      if (qvalid) {
+        lo = *reinterpret_cast<const uint2*>(qrow + 16 * kk + 4 * g);
+        hi = *reinterpret_cast<const uint2*>(qrow + 16 * kk + 8 + 4 * g);
+      }
+      qf[kk] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    }
+#pragma unroll
+    for (int kk = kN / 16; kk < kD / 16; ++kk)
+      qf[kk] = as_bf16x8(qvalid ? ldg16(qrow + 16 * kk + 8 * g) : make_uint4(0, 0, 0, 0));
   }
 
   // tile-blocked operands of this head and sequence (tile index = padded row / 64)
@@ -615,12 +687,14 @@ __global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
 //   delta = (2^-8 * 1.01 + 3e-5) * max_t |q_t| * max_s |K_s|
 // (bf16 rounding of K^C plus fp32 accumulation), hence the exact maximum E
 // lies in [M - delta, M + delta] for the approximate maximum M, and its pair
-// has an approximate logit >= M - 2 delta. The scan kernel (heads x key
-// slices) re-scores the candidate rows (row max >= M - 2 delta) against their
-// keys with the stored bf16 K^C and lists the candidate pairs; the exact
-// kernel recomputes those pairs in fp32 from c^KV and kv_b_proj
-// (K^C_s = c_s W_UK_h). Too many candidates (near-ties, e.g. q = 0) fall back
-// to M, which is then within delta of E.
+// has an approximate logit >= M - 2 delta. Three small launches:
+//   rows : rows whose approximate row max reaches M - 2 delta (per head);
+//   pairs: every key (one thread each) re-scored against those rows with the
+//          stored bf16 K^C; pairs reaching M - 2 delta are listed;
+//   exact: one workgroup per listed pair recomputes its logit in fp32 from
+//          c^KV and kv_b_proj (K^C_s = c_s W_UK_h) and takes the maximum.
+// Too many candidates (near-ties, e.g. q = 0) fall back to M, which is then
+// within delta of E.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float refine_threshold(const float* aux, int h, int heads, float* M_out) {
   const float M = aux[h * kAuxStride];
@@ -630,73 +704,100 @@ __device__ __forceinline__ float refine_threshold(const float* aux, int h, int h
   return M - 2.0f * (1.01f / 256.0f + 3e-5f) * qn * kn;
 }
 
-__global__ void __launch_bounds__(256) prefill_refine_scan_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ks, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ pcu, int nseq, int heads, int64_t ntok, int64_t npad_max,
-    const uint16_t* __restrict__ kc, const float* __restrict__ rowmax, const float* __restrict__ aux,
-    int32_t* __restrict__ cand) {
-  __shared__ int rows[kRefRows];
-  __shared__ int nrows;
-  __shared__ float qrow[kD];
-  const int h = blockIdx.x, slice = blockIdx.y;
-  const int tid = threadIdx.x;
+constexpr int kRefRowSplit = 8;     // workgroups per head scanning row maxima
+constexpr int kRefExactSplit = 16;  // workgroups per head recomputing listed pairs
+
+__device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int t) {
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(256) prefill_refine_rows_kernel(const int32_t* __restrict__ cu, int nseq,
+                                                                  int heads, int64_t ntok,
+                                                                  const float* __restrict__ rowmax,
+                                                                  const float* __restrict__ aux,
+                                                                  int32_t* __restrict__ cand) {
+  const int h = blockIdx.x;
   float M;
   const float thr = refine_threshold(aux, h, heads, &M);
   if (!(M > -INFINITY)) return;
   int32_t* c = cand + static_cast<size_t>(h) * kCandStride;
-  if (tid == 0) nrows = 0;
-  __syncthreads();
-  for (int64_t t = tid; t < ntok; t += 256) {
+  for (int64_t t = threadIdx.x + 256 * static_cast<int64_t>(blockIdx.y); t < ntok; t += 256 * gridDim.y) {
     if (rowmax[static_cast<size_t>(h) * ntok + t] >= thr) {
-      const int k = atomicAdd(&nrows, 1);
-      if (k < kRefRows) rows[k] = static_cast<int>(t);
+      const int k = atomicAdd(&c[2], 1);
+      if (k < kRefRows) {
+        c[kCandRows + 2 * k] = static_cast<int>(t);
+        c[kCandRows + 2 * k + 1] = cu[seq_of(cu, nseq, static_cast<int>(t))];
+      } else {
+        c[1] = 1;
+      }
     }
+  }
+}
+
+__global__ void __launch_bounds__(256) prefill_refine_pairs_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ks, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ pcu, int nseq, int heads, int64_t ntok, int64_t npad_max,
+    const uint16_t* __restrict__ kc, const float* __restrict__ aux, int32_t* __restrict__ cand) {
+  __shared__ float qs[kRefRows][kD];
+  __shared__ int rt[kRefRows], ra[kRefRows];
+  const int h = blockIdx.x;
+  float M;
+  const float thr = refine_threshold(aux, h, heads, &M);
+  if (!(M > -INFINITY)) return;
+  int32_t* c = cand + static_cast<size_t>(h) * kCandStride;
+  if (c[1] != 0) return;
+  const int nrows = min(c[2], kRefRows);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nrows * kD; i += 256) {
+    const int r = i / kD, e = i - r * kD;
+    qs[r][e] = bf16_to_f32(q[(static_cast<size_t>(c[kCandRows + 2 * r]) * heads + h) * kD + e]);
+  }
+  if (tid < nrows) {
+    rt[tid] = c[kCandRows + 2 * tid];
+    ra[tid] = c[kCandRows + 2 * tid + 1];
   }
   __syncthreads();
-  if (nrows > kRefRows) {
-    if (tid == 0) c[1] = 1;
-    return;
-  }
+  const int64_t s64 = static_cast<int64_t>(blockIdx.y) * 256 + tid;
+  if (s64 >= ntok) return;
+  const int s = static_cast<int>(s64);
+  bool any = false;
+  for (int r = 0; r < nrows; ++r) any |= (s >= ra[r] && s <= rt[r]);
+  if (!any) return;
+  // this key's stored [K^C | k^S] (tile-blocked K^C: unit u of row p at tile p/64, offset u*64*8 + (p%64)*8)
+  const int sq = seq_of(cu, nseq, s);
+  const int p = pcu[sq] + (s - cu[sq]);
+  const uint16_t* kr = kc + (static_cast<size_t>(h) * (npad_max / kPrefBN) + p / kPrefBN) * kTileElems + (p % kPrefBN) * 8;
+  uint4 x[kD / 8];
+#pragma unroll
+  for (int u = 0; u < kN / 8; ++u) x[u] = ldg16(kr + u * (kPrefBN * 8));
+#pragma unroll
+  for (int u = 0; u < kS / 8; ++u) x[kN / 8 + u] = ldg16(ks + static_cast<size_t>(s) * kS + 8 * u);
   for (int r = 0; r < nrows; ++r) {
-    const int t = rows[r];
-    int lo = 0, hi = nseq - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (cu[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int a = cu[lo];
-    const int nkeys = t - a + 1;
-    const int per = (nkeys + kRefSlices - 1) / kRefSlices;
-    const int s0 = a + slice * per, s1 = min(t + 1, s0 + per);
-    __syncthreads();
-    if (tid < kD) qrow[tid] = bf16_to_f32(q[(static_cast<size_t>(t) * heads + h) * kD + tid]);
-    __syncthreads();
-    const uint16_t* kch = kc + (static_cast<size_t>(h) * (npad_max / kPrefBN) + pcu[lo] / kPrefBN) * kTileElems;
-    for (int s = s0 + tid; s < s1; s += 256) {
-      uint4 x[kD / 8];
-      const int pl = s - a;   // sequence-local row: tile pl / 64, row pl % 64 of the tile-blocked K^C
-      const uint16_t* kr = kch + static_cast<size_t>(pl / kPrefBN) * kTileElems + (pl % kPrefBN) * 8;
-      const uint16_t* sr = ks + static_cast<size_t>(s) * kS;
+    if (s < ra[r] || s > rt[r]) continue;
+    float acc = 0.0f;
 #pragma unroll
-      for (int e = 0; e < kN / 8; ++e) x[e] = ldg16(kr + e * (kPrefBN * 8));
+    for (int u = 0; u < kD / 8; ++u) {
+      const uint32_t* w4 = &x[u].x;
 #pragma unroll
-      for (int e = 0; e < kS / 8; ++e) x[kN / 8 + e] = ldg16(sr + 8 * e);
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < kD / 8; ++e) {
-        const uint32_t* w4 = &x[e].x;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc = fmaf(qrow[8 * e + 2 * u], bf16lo(w4[u]), fmaf(qrow[8 * e + 2 * u + 1], bf16hi(w4[u]), acc));
+      for (int e = 0; e < 4; ++e) {
+        // K^C unit u holds features kperm(8u .. 8u+7); the k^S units are in natural order
+        const int f0 = u < kN / 8 ? kperm(8 * u + 2 * e) : 8 * u + 2 * e;
+        const int f1 = u < kN / 8 ? kperm(8 * u + 2 * e + 1) : 8 * u + 2 * e + 1;
+        acc = fmaf(qs[r][f0], bf16lo(w4[e]), fmaf(qs[r][f1], bf16hi(w4[e]), acc));
       }
-      if (acc >= thr) {
-        const int k = atomicAdd(&c[0], 1);
-        if (k < kRefKeys) {
-          c[2 + 2 * k] = t;
-          c[3 + 2 * k] = s;
-        } else {
-          c[1] = 1;
-        }
+    }
+    if (acc >= thr) {
+      const int k = atomicAdd(&c[0], 1);
+      if (k < kRefKeys) {
+        c[kCandPairs + 2 * k] = rt[r];
+        c[kCandPairs + 2 * k + 1] = s;
+      } else {
+        c[1] = 1;
       }
     }
   }
@@ -708,49 +809,49 @@ __global__ void __launch_bounds__(256) prefill_refine_exact_kernel(
     float scale, float* __restrict__ max_logit) {
   __shared__ float qrow[kD];
   __shared__ float crow[kR];
-  __shared__ float red[8];
-  const int h = blockIdx.x;
+  __shared__ float red[4];
+  const int h = blockIdx.x, pi = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float M;
   refine_threshold(aux, h, heads, &M);
   if (!(M > -INFINITY)) return;
   const int32_t* c = cand + static_cast<size_t>(h) * kCandStride;
   const int nk = c[0];
+  const bool fallback = c[1] != 0 || nk == 0 || nk > kRefKeys;
+  if (fallback) {
+    if (pi == 0 && tid == 0) atomic_max_float(max_logit + h, M * scale);
+    return;
+  }
   float best = -INFINITY;
-  if (c[1] == 0 && nk <= kRefKeys) {
-    for (int k = 0; k < nk; ++k) {
-      const int t = c[2 + 2 * k], s = c[3 + 2 * k];
-      __syncthreads();
-      if (tid < kD) qrow[tid] = bf16_to_f32(q[(static_cast<size_t>(t) * heads + h) * kD + tid]);
-      for (int e = tid; e < kR; e += 256) crow[e] = bf16_to_f32(ckv[static_cast<size_t>(s) * kR + e]);
-      __syncthreads();
-      // K^C_s[n] = sum_r c_s[r] * w[h*256 + n][r] in fp32; two threads per feature n
-      const int n = tid >> 1, part = tid & 1;
-      const uint16_t* wr = w + (static_cast<size_t>(h) * 256 + n) * kR + part * (kR / 2);
-      uint4 x[kR / 16];
+  for (int k = pi; k < nk; k += gridDim.y) {
+    const int t = c[kCandPairs + 2 * k], s = c[kCandPairs + 2 * k + 1];
+    __syncthreads();
+    if (tid < kD) qrow[tid] = bf16_to_f32(q[(static_cast<size_t>(t) * heads + h) * kD + tid]);
+    for (int e = tid; e < kR; e += 256) crow[e] = bf16_to_f32(ckv[static_cast<size_t>(s) * kR + e]);
+    __syncthreads();
+    // K^C_s[n] = sum_r c_s[r] * w[h*256 + n][r] in fp32; two threads per feature n
+    const int n = tid >> 1, part = tid & 1;
+    const uint16_t* wr = w + (static_cast<size_t>(h) * 256 + n) * kR + part * (kR / 2);
+    uint4 x[kR / 16];
 #pragma unroll
-      for (int e = 0; e < kR / 16; ++e) x[e] = ldg16(wr + 8 * e);
-      float kcn = 0.0f;
+    for (int e = 0; e < kR / 16; ++e) x[e] = ldg16(wr + 8 * e);
+    float kcn = 0.0f;
 #pragma unroll
-      for (int e = 0; e < kR / 16; ++e) {
-        const uint32_t* w4 = &x[e].x;
-        const float* cr = crow + part * (kR / 2) + 8 * e;
+    for (int e = 0; e < kR / 16; ++e) {
+      const uint32_t* w4 = &x[e].x;
+      const float* cr = crow + part * (kR / 2) + 8 * e;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) kcn = fmaf(cr[2 * u], bf16lo(w4[u]), fmaf(cr[2 * u + 1], bf16hi(w4[u]), kcn));
-      }
-      kcn += __shfl_xor(kcn, 1, 64);
-      float pr = part == 0 ? qrow[n] * kcn : 0.0f;
-      if (tid < kS) pr += qrow[kN + tid] * bf16_to_f32(ks[static_cast<size_t>(s) * kS + tid]);
-      pr = wave_sum(pr);
-      if (lane == 0) red[wave] = pr;
-      __syncthreads();
-      best = fmaxf(best, (red[0] + red[1]) + (red[2] + red[3]));
-    }
+      for (int u = 0; u < 4; ++u) kcn = fmaf(cr[2 * u], bf16lo(w4[u]), fmaf(cr[2 * u + 1], bf16hi(w4[u]), kcn));
   }
-  if (tid == 0) {
-    const float e = (c[1] != 0 || nk > kRefKeys || !(best > -INFINITY)) ? M : best;
-    atomic_max_float(max_logit + h, e * scale);
+    kcn += __shfl_xor(kcn, 1, 64);
+    float pr = part == 0 ? qrow[n] * kcn : 0.0f;
+    if (tid < kS) pr += qrow[kN + tid] * bf16_to_f32(ks[static_cast<size_t>(s) * kS + tid]);
+    pr = wave_sum(pr);
+    if (lane == 0) red[wave] = pr;
+    __syncthreads();
+    best = fmaxf(best, (red[0] + red[1]) + (red[2] + red[3]));
   }
+  if (tid == 0 && best > -INFINITY) atomic_max_float(max_logit + h, best * scale);
 }
 
 __global__ void prefill_aux_init_kernel(float* aux, int32_t* cand, int heads) {
@@ -759,6 +860,7 @@ __global__ void prefill_aux_init_kernel(float* aux, int32_t* cand, int heads) {
   if (i < heads) {
     cand[static_cast<size_t>(i) * kCandStride] = 0;
     cand[static_cast<size_t>(i) * kCandStride + 1] = 0;
+    cand[static_cast<size_t>(i) * kCandStride + 2] = 0;
   }
 }
 
@@ -791,12 +893,13 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const dim3 eg(2 * heads, static_cast<unsigned>(L.npad_max / kExBM));
   {
+    const int64_t ex_items = (L.npad_max / kExRows + kExGroupRows - 1) / kExGroupRows *
+                             ((heads + kExGroupHeads - 1) / kExGroupHeads) * kExGroup;
     TimedScope ts_("prefill_expand", st);
-    hipLaunchKernelGGL(prefill_expand_kernel, eg, dim3(256), 0, st, static_cast<const uint16_t*>(ckv),
-                       static_cast<const uint16_t*>(w_kv_b), cu, nseq, pcu, hdr, L.npad_max,
-                       static_cast<const uint16_t*>(ks), kc, vt, ksp, aux);
+    hipLaunchKernelGGL(prefill_expand_kernel, dim3(static_cast<unsigned>((ex_items + 7) / 8 * 8)), dim3(kExThreads), 0,
+                       st, static_cast<const uint16_t*>(ckv), static_cast<const uint16_t*>(w_kv_b), cu, nseq, pcu,
+                       hdr, L.npad_max, ntok, heads, static_cast<const uint16_t*>(ks), kc, vt, ksp, aux);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -826,18 +929,26 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    TimedScope ts_("prefill_refine_scan", st);
-    hipLaunchKernelGGL(prefill_refine_scan_kernel, dim3(heads, kRefSlices), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(ks), cu, pcu, nseq, heads, ntok,
-                       L.npad_max, kc, rowmax, aux, cand);
+    TimedScope ts_("prefill_refine_rows", st);
+    hipLaunchKernelGGL(prefill_refine_rows_kernel, dim3(heads, kRefRowSplit), dim3(256), 0, st, cu, nseq, heads, ntok,
+                       rowmax, aux, cand);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    TimedScope ts_("prefill_refine_pairs", st);
+    hipLaunchKernelGGL(prefill_refine_pairs_kernel, dim3(heads, static_cast<unsigned>((ntok + 255) / 256)), dim3(256),
+                       0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(ks), cu, pcu, nseq, heads,
+                       ntok, L.npad_max, kc, aux, cand);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     TimedScope ts_("prefill_refine_exact", st);
-    hipLaunchKernelGGL(prefill_refine_exact_kernel, dim3(heads), dim3(256), 0, st, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(ckv), static_cast<const uint16_t*>(ks),
-                       static_cast<const uint16_t*>(w_kv_b), heads, aux, cand, scale, max_logit);
+    hipLaunchKernelGGL(prefill_refine_exact_kernel, dim3(heads, kRefExactSplit), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(ckv),
+                       static_cast<const uint16_t*>(ks), static_cast<const uint16_t*>(w_kv_b), heads, aux, cand, scale,
+                       max_logit);
   }
   return hipGetLastError();
 }
