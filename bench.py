@@ -17,8 +17,10 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -42,6 +44,43 @@ def prefill_flops(T: int, H: int, R: int = 512, D: int = 192, V: int = 128):
     pv = 2.0 * H * pairs * V
     expand = 2.0 * T * H * 256 * R
     return qk, pv, expand
+
+
+def source_digest(files) -> str:
+    """sha256 over the kernel sources a counter table was taken with."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str, files):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    table (profiles/traffic_<kernel>.md: FETCH_SIZE + WRITE_SIZE per dispatch,
+    scaled by the copy-kernel calibration), or None when the table is missing
+    or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"^- (\w+): `?([^`\s]+)`?", line.strip())
+            if m:
+                rec[m.group(1)] = m.group(2)
+    if rec.get("source_sha256") != source_digest(files):
+        return None
+    try:
+        return int(float(rec["bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+PREFILL_SOURCES = ("mla_qk_clip_amd/csrc/prefill_bf16.hip", "mla_qk_clip_amd/csrc/mla_common.h",
+                   "mla_qk_clip_amd/csrc/mla_internal.h")
+DECODE_SOURCES = ("mla_qk_clip_amd/csrc/absorbed_bf16.hip", "mla_qk_clip_amd/csrc/mla_common.h",
+                  "mla_qk_clip_amd/csrc/mla_internal.h")
 
 
 def cpu_baseline(p, budget_s: float = 12.0):
@@ -76,6 +115,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first copy 512 MiB device-to-device once (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -124,6 +165,13 @@ def main():
         cache_bytes = float(d.lens.astype(np.int64).sum()) * 576 * 2
 
     stream = torch.cuda.current_stream()
+    if args.calib_copy:
+        # a plain copy of known size: reads and writes 512 MiB each
+        src = torch.ones(256 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         if ev is not None:
@@ -200,7 +248,8 @@ def main():
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
         "roofline": {"kernel": "prefill_attn", "bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "algorithmic": f"{(qk + pv) / 1e9:.1f} GFLOP per launch (QK^T + PV)"},
+                     "traffic": recorded_traffic("prefill_attn", PREFILL_SOURCES),
+                     "algorithmic": f"{(qk + pv) / 1e9:.1f} GFLOP per launch (QK^T + PV)"},
     }
     if decode:
         gbps = cache_bytes / (dec_ms * 1e-3) / 1e9
@@ -210,7 +259,8 @@ def main():
                          "sum_lens": int(d.lens.sum())}
         res["decode_roofline"] = {"kernel": "absorbed_split", "bound": "hbm", "achieved": round(split_gbps, 1),
                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(split_gbps / PEAK_HBM_GBPS, 4),
-                                  "traffic": None}
+                                  "traffic": recorded_traffic("absorbed_split", DECODE_SOURCES),
+                                  "algorithmic": f"{cache_bytes / 1e9:.4f} GB of cache rows per launch"}
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(p)
