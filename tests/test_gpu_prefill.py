@@ -126,6 +126,40 @@ def test_bf16_k3_prefill_4096_sampled(lib):
     assert np.all(np.abs(sm - ref_sm) / np.abs(ref_sm) <= SMAX_TOL)
 
 
+def test_bf16_k3_varlen_long_sampled(lib):
+    """The long packed varlen workload (32768 + 16384 + 8192 + 2048 tokens,
+    H=96) at full size: sampled output rows and LSE of two heads (first, last
+    and middle rows of every sequence plus random rows), the exact max logit of
+    one head, and finite outputs everywhere."""
+    from tests._gpu import host, log, run_prefill
+    p = synth.k3_varlen()
+    log("bf16 K3 varlen 32768+16384+8192+2048: GPU")
+    out, lse, ml = run_prefill(p)
+    assert bool(torch_isfinite_all(out)) and bool(torch_isfinite_all(lse)) and bool(torch_isfinite_all(ml))
+    cu = [int(x) for x in p.cu_seqlens]
+    rng = np.random.default_rng(5)
+    rows = []
+    for a, b in zip(cu[:-1], cu[1:]):
+        L = b - a
+        rows += [a, a + 1, a + L // 2, b - 2, b - 1] + sorted(int(x) for x in rng.integers(a, b, size=8))
+    V = p.dims.v_dim
+    lse_h = host(lse)
+    for h in (0, 95):
+        log(f"oracle rows, head {h}")
+        ref, ref_lse = oracle.prefill_rows(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims, h, rows)
+        got = host(out[rows, h * V:(h + 1) * V])
+        assert rel_err(got, ref) <= BF16_TOL
+        assert np.max(np.abs(lse_h[h, rows] - ref_lse)) <= 1e-2
+    log("oracle max logit, head 0")
+    ref_sm0 = oracle.max_logit_head(p.q, p.ckv, p.ks, p.w_kv_b, p.cu_seqlens, p.dims, 0)
+    assert abs(float(host(ml)[0]) - ref_sm0) / abs(ref_sm0) <= SMAX_TOL
+
+
+def torch_isfinite_all(t):
+    import torch
+    return torch.isfinite(t).all().item()
+
+
 def test_bf16_bitwise_deterministic(lib):
     from tests._gpu import log, run_prefill
     dims = synth.Dims(16, 512, 64, 128, 128)
