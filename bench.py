@@ -215,7 +215,7 @@ def main():
     torch.cuda.synchronize()
     kern = {}
     for k in ("fill", "prefill_aux_init", "prefill_plan", "prefill_expand", "prefill_attn", "prefill_refine_rows", "prefill_refine_pairs",
-              "prefill_refine_exact", "qk_clip", "absorbed_prefix", "absorb_q", "absorbed_split",
+              "prefill_refine_exact", "qk_clip", "absorb_q", "absorbed_split",
               "absorbed_fixup", "absorbed_combine"):
         tot, n = m.mla_timing_read(k)
         if n:

@@ -24,16 +24,35 @@ constexpr int kW = kR + kS;  // 576 values per cache row
 
 // P[v] = sum of visible rows of the virtual sequences before v; virtual
 // sequence v = b * tq + i sees rows 0 .. lens[b] - tq + i of cache[b].
-__global__ void __launch_bounds__(64) absorbed_prefix_kernel(const int32_t* __restrict__ lens, int batch, int tq,
-                                                             int64_t* __restrict__ P) {
-  if (threadIdx.x != 0) return;
-  int64_t acc = 0;
-  for (int b = 0; b < batch; ++b)
-    for (int i = 0; i < tq; ++i) {
-      P[static_cast<int64_t>(b) * tq + i] = acc;
-      acc += lens[b] - tq + i + 1;
+// One 256-thread block: per-thread chunk sums, a scan of the 256 sums in LDS,
+// then each thread writes its chunk's prefixes. Also clears the fix-up count.
+__device__ void absorbed_prefix_block(const int32_t* __restrict__ lens, int tq, int64_t bt,
+                                      int64_t* __restrict__ P, int32_t* __restrict__ nflag) {
+  __shared__ int64_t sums[256];
+  const int tid = threadIdx.x;
+  const int64_t chunk = (bt + 255) / 256;
+  const int64_t v0 = tid * chunk, v1 = min(bt, v0 + chunk);
+  auto rows_of = [&](int64_t v) { return static_cast<int64_t>(lens[v / tq] - tq + static_cast<int>(v % tq) + 1); };
+  int64_t s = 0;
+  for (int64_t v = v0; v < v1; ++v) s += rows_of(v);
+  sums[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    int64_t acc = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int64_t x = sums[i];
+      sums[i] = acc;
+      acc += x;
     }
-  P[static_cast<int64_t>(batch) * tq] = acc;
+    P[bt] = acc;
+    *nflag = 0;
+  }
+  __syncthreads();
+  int64_t acc = sums[tid];
+  for (int64_t v = v0; v < v1; ++v) {
+    P[v] = acc;
+    acc += rows_of(v);
+  }
 }
 
 // q_abs[v][h][r] = sum_k w_kv_b[h*256 + k][r] * q[v][h][k]  (r < 512) as a
@@ -60,9 +79,11 @@ __device__ __forceinline__ bf16x8 cat_bf16(v4s lo, v4s hi) {
 
 __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ w, int bt, int heads,
-                                                       uint16_t* __restrict__ qabs) {
+                                                       uint16_t* __restrict__ qabs, const int32_t* __restrict__ lens,
+                                                       int tq, int64_t* __restrict__ P, int32_t* __restrict__ nflag) {
   __shared__ __align__(16) uint16_t Wt[kN * kAqLd];
   const int h = blockIdx.x, rc = blockIdx.y;
+  if (h == 0 && rc == 0) absorbed_prefix_block(lens, tq, bt, P, nflag);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   // W_UK_h rows k (128) x columns r in [128 rc, 128 rc + 128)
@@ -111,22 +132,26 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
 
 // ---------------------------------------------------------------------------
 // Split kernel. Workgroup = 4 waves; waves 0-2 each own 32 heads (head block
-// 3*blockIdx.y + wave). The workgroup's rows are visited in tiles of 32 rows,
-// segment by segment. Every wave streams a quarter of each tile straight from
-// HBM into LDS (global_load_lds, 16 bytes per lane, no registers), three tiles
-// ahead of the compute, into a ring of 4 LDS stages; one barrier per tile.
+// 3*blockIdx.y + wave), wave 3 is the loader. The workgroup's rows are visited
+// in tiles of 32 rows, segment (virtual sequence) by segment. The loader
+// streams every tile straight from HBM into a ring of kStages LDS stages
+// (global_load_lds, 16 bytes per lane, no registers), two tiles ahead of the
+// compute; one barrier per tile.
 // LDS tile layout: [32 rows][73 chunks of 8 bf16] (72 data chunks and one pad
 // chunk per row, so rows are 36 banks apart and both read patterns below are
 // free of bank conflicts). A wave-wide copy fills 64 consecutive chunk slots;
-// lanes that land on a pad slot fetch a harmless valid chunk. A compute wave keeps its heads' q_abs as MFMA operands in
-// registers, forms S^T = C Q^T (each lane owns one head column; rows of C read
-// as b128) and accumulates O_lat^T = C^T P^T with C^T read through the LDS
-// transpose read. The softmax uses a lazily updated reference max: the
-// accumulators are rescaled only when a head's max grows by more than a
-// factor 2^8 in probability, so p <= 256.
+// lanes that land on a pad slot fetch a harmless valid chunk.
+// A compute wave keeps its heads' q_abs as MFMA operands in registers, forms
+// S^T = C Q^T (each lane owns one head column; rows of C read as b128) and
+// accumulates O_lat^T = C^T P^T with C^T read through the LDS transpose read.
+// The softmax takes every probability against a fixed reference, the first
+// tile's max of the segment, so the accumulators are never rescaled; a head
+// whose later logits exceed the reference by more than 64 in exp2 units is
+// flagged (and counted in nflag) and its segment is recomputed by the fix-up
+// kernel.
 // Partials per (workgroup, virtual sequence) slot and head:
 //   part_o[slot][h][r] = sum_j p_j c_j[r] (relative to the reference max),
-//   part_ml[slot][h] = {reference max (raw), denominator, true raw max, 0}.
+//   part_ml[slot][h] = {reference max (raw), denominator, true raw max, flag}.
 // ---------------------------------------------------------------------------
 constexpr int kChunks = kW / 8;                       // 72 data chunks of 16 bytes per row
 constexpr int kRowSlots = kChunks + 1;                // 73 slots per LDS row (one pad)
@@ -285,7 +310,7 @@ __device__ __forceinline__ void split_issue(uint16_t* ring, int stage, TileCurso
 __global__ void __launch_bounds__(256) absorbed_split_kernel(
     const uint16_t* __restrict__ cache, int64_t cap, int tq, int heads, int64_t bt,
     const int64_t* __restrict__ P, const uint16_t* __restrict__ qabs, float scale,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, int32_t* __restrict__ nflag) {
   __shared__ __align__(16) uint16_t ring[kStages * kTileBytes / 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -382,6 +407,7 @@ __global__ void __launch_bounds__(256) absorbed_split_kernel(
       if (g == 0)
         *reinterpret_cast<float4*>(part_ml + (slot * heads + head) * 4) =
             make_float4(S.m_ref, l_tot, S.m_true, S.overflow ? 1.0f : 0.0f);
+      if (__ballot(S.overflow) && lane == 0) atomicAdd(nflag, 1);
     }
   }
 }
@@ -396,7 +422,8 @@ __global__ void __launch_bounds__(256) absorbed_split_kernel(
 __global__ void __launch_bounds__(256) absorbed_fixup_kernel(
     const uint16_t* __restrict__ cache, int64_t cap, int tq, int heads, int64_t bt, int G,
     const int64_t* __restrict__ P, const uint16_t* __restrict__ qabs, float scale, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, const int32_t* __restrict__ nflag) {
+  if (*nflag == 0) return;   // nothing was flagged (the common case)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t total = P[bt];
   const int64_t lo = total * blockIdx.x / G;
@@ -574,23 +601,20 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
   float* part_ml = reinterpret_cast<float*>(base + L.part_ml);
   const int64_t bt = static_cast<int64_t>(batch) * tq;
 
-  {
-    TimedScope ts_("absorbed_prefix", st);
-    hipLaunchKernelGGL(absorbed_prefix_kernel, dim3(1), dim3(64), 0, st, lens, batch, tq, P);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  int32_t* nflag = reinterpret_cast<int32_t*>(base + L.nflag);
+  hipError_t e;
   {
     TimedScope ts_("absorb_q", st);
     hipLaunchKernelGGL(absorb_q_kernel, dim3(heads, kR / 128), dim3(256), 0, st, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(w_kv_b), static_cast<int>(bt), heads, qabs);
+                       static_cast<const uint16_t*>(w_kv_b), static_cast<int>(bt), heads, qabs, lens, tq, P, nflag);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     TimedScope ts_("absorbed_split", st);
     hipLaunchKernelGGL(absorbed_split_kernel, dim3(kDecSplits, (heads + kDecHeadsPerWg - 1) / kDecHeadsPerWg), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(cache), cap, tq, heads, bt, P, qabs, scale, part_o, part_ml);
+                       static_cast<const uint16_t*>(cache), cap, tq, heads, bt, P, qabs, scale, part_o, part_ml,
+                       nflag);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -598,7 +622,7 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
     TimedScope ts_("absorbed_fixup", st);
     hipLaunchKernelGGL(absorbed_fixup_kernel, dim3(kDecSplits), dim3(256), 0, st,
                        static_cast<const uint16_t*>(cache), cap, tq, heads, bt, kDecSplits, P, qabs, scale, part_o,
-                       part_ml);
+                       part_ml, nflag);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -76,7 +76,7 @@ inline size_t prefill_f32_ws(int heads, int64_t ntok, int N, int V) {
 
 // Workspace layout of the bf16 absorbed path.
 struct AbsorbedWs {
-  size_t qabs, prefix, part_o, part_ml, total;
+  size_t qabs, prefix, nflag, part_o, part_ml, total;
   int64_t slots;
 };
 inline AbsorbedWs absorbed_ws_layout(int heads, int batch, int tq) {
@@ -86,6 +86,7 @@ inline AbsorbedWs absorbed_ws_layout(int heads, int batch, int tq) {
   size_t off = 0;
   w.qabs = off; off = align_up(off + static_cast<size_t>(bt) * heads * (kR + kS) * 2, 256);
   w.prefix = off; off = align_up(off + static_cast<size_t>(bt + 1) * 8, 256);
+  w.nflag = off; off = align_up(off + 4, 256);   // count of segments the fix-up kernel must redo
   w.part_o = off; off = align_up(off + static_cast<size_t>(w.slots) * heads * kR * 4, 256);
   w.part_ml = off; off = align_up(off + static_cast<size_t>(w.slots) * heads * 4 * 4, 256);
   w.total = off;

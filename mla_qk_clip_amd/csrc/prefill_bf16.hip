@@ -312,13 +312,16 @@ __global__ void __launch_bounds__(kExThreads) prefill_expand_kernel(
 // max exceeds it by more than 2^8 (in exp2 units), so the output rescale is
 // rare; probabilities stay <= 2^8, exact in fp32 and bf16 range.
 // ---------------------------------------------------------------------------
-constexpr int kAttnThreads = 512;
-constexpr int kAttnWaves = kAttnThreads / 64;
+constexpr int kAttnWaves = kPrefBM / 32;                 // one wave per 32 queries
+constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kKUnits = kD / 8;                          // 16-byte units per key row (24)
 constexpr int kKTile = kPrefBN * kKUnits;                // 1536 units = 24 KB
 constexpr int kVTile = kV * (kPrefBN / 8);               // 1024 units = 16 KB
-static_assert(kN / 8 == 2 * kAttnWaves && kS / 8 == kAttnWaves && kVTile / 64 == 2 * kAttnWaves,
-              "each wave copies two K^C blocks, one k^S block and two V^T blocks per tile");
+constexpr int kKcCopies = (kN / 8) / kAttnWaves;         // 1 KB copies per wave per tile: K^C,
+constexpr int kKsCopies = (kS / 8) / kAttnWaves;         //   k^S
+constexpr int kVtCopies = (kVTile / 64) / kAttnWaves;    //   and V^T
+static_assert(kKcCopies * kAttnWaves == kN / 8 && kKsCopies * kAttnWaves == kS / 8 &&
+                  kVtCopies * kAttnWaves == kVTile / 64, "tile copies split evenly over the waves");
 constexpr float kRescaleLog2 = 8.0f;
 
 // Issue order of the overlapped tile body. qk: score MFMA idx = 12 blk + kk
@@ -354,8 +357,6 @@ __global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
   __shared__ uint4 K1[kKTile];
   __shared__ uint4 V0[kVTile];
   __shared__ uint4 V1[kVTile];
-  __shared__ float red[kAttnWaves];
-  __shared__ float redq[kAttnWaves];
 
   // ---- work item: blocks that share a head run on the same XCD ----
   const int ntiles = hdr[0];
@@ -424,14 +425,25 @@ __global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
   const uint32_t lane16 = 16u * lane;
   auto dma_k = [&](uint4* dst, int j) {
     const uint32_t so = static_cast<uint32_t>(j) * (kTileElems * 2);
-    dma16_buf(rs_kc, lane16 + (2 * wave) * 1024, so, dst + (2 * wave) * 64);
-    dma16_buf(rs_kc, lane16 + (2 * wave + 1) * 1024, so, dst + (2 * wave + 1) * 64);
-    dma16_buf(rs_ks, lane16 + wave * 1024, static_cast<uint32_t>(j) * (kPrefBN * kS * 2), dst + (kN / 8 + wave) * 64);
+#pragma unroll
+    for (int c = 0; c < kKcCopies; ++c) {
+      const int blk = kKcCopies * wave + c;
+      dma16_buf(rs_kc, lane16 + blk * 1024, so, dst + blk * 64);
+    }
+    const uint32_t sos = static_cast<uint32_t>(j) * (kPrefBN * kS * 2);
+#pragma unroll
+    for (int c = 0; c < kKsCopies; ++c) {
+      const int blk = kKsCopies * wave + c;
+      dma16_buf(rs_ks, lane16 + blk * 1024, sos, dst + (kN / 8 + blk) * 64);
+    }
   };
   auto dma_v = [&](uint4* dst, int j) {
     const uint32_t so = static_cast<uint32_t>(j) * (kTileElems * 2);
-    dma16_buf(rs_vt, lane16 + (2 * wave) * 1024, so, dst + (2 * wave) * 64);
-    dma16_buf(rs_vt, lane16 + (2 * wave + 1) * 1024, so, dst + (2 * wave + 1) * 64);
+#pragma unroll
+    for (int c = 0; c < kVtCopies; ++c) {
+      const int blk = kVtCopies * wave + c;
+      dma16_buf(rs_vt, lane16 + blk * 1024, so, dst + blk * 64);
+    }
   };
 
   // LDS operand addresses: K unit (2kk + g) * 64 + 32 blk + l32, V^T unit
@@ -663,6 +675,8 @@ __global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
   float v = qvalid ? m_true : -INFINITY;
   v = wave_max(v);
   qn2 = wave_max(qvalid ? qn2 : 0.0f);
+  float* red = reinterpret_cast<float*>(K0);   // the rings are idle after the loop
+  float* redq = red + kAttnWaves;
   if (lane == 0) {
     red[wave] = v;
     redq[wave] = qn2;
