@@ -24,8 +24,9 @@ constexpr int kW = kR + kS;  // 576 values per cache row
 
 // P[v] = sum of visible rows of the virtual sequences before v; virtual
 // sequence v = b * tq + i sees rows 0 .. lens[b] - tq + i of cache[b].
-// One 256-thread block: per-thread chunk sums, a scan of the 256 sums in LDS,
-// then each thread writes its chunk's prefixes. Also clears the fix-up count.
+// One 256-thread block: per-thread chunk sums, an inclusive Hillis-Steele
+// scan of the 256 sums in LDS (8 steps), then each thread writes its chunk's
+// prefixes. Also clears the fix-up count.
 __device__ void absorbed_prefix_block(const int32_t* __restrict__ lens, int tq, int64_t bt,
                                       int64_t* __restrict__ P, int32_t* __restrict__ nflag) {
   __shared__ int64_t sums[256];
@@ -37,18 +38,18 @@ __device__ void absorbed_prefix_block(const int32_t* __restrict__ lens, int tq, 
   for (int64_t v = v0; v < v1; ++v) s += rows_of(v);
   sums[tid] = s;
   __syncthreads();
-  if (tid == 0) {
-    int64_t acc = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int64_t x = sums[i];
-      sums[i] = acc;
-      acc += x;
-    }
-    P[bt] = acc;
+#pragma unroll
+  for (int off = 1; off < 256; off <<= 1) {
+    const int64_t t = tid >= off ? sums[tid - off] : 0;
+    __syncthreads();
+    sums[tid] += t;
+    __syncthreads();
+  }
+  if (tid == 255) {
+    P[bt] = sums[255];
     *nflag = 0;
   }
-  __syncthreads();
-  int64_t acc = sums[tid];
+  int64_t acc = sums[tid] - s;
   for (int64_t v = v0; v < v1; ++v) {
     P[v] = acc;
     acc += rows_of(v);
@@ -80,17 +81,31 @@ __device__ __forceinline__ bf16x8 cat_bf16(v4s lo, v4s hi) {
 __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ w, int bt, int heads,
                                                        uint16_t* __restrict__ qabs, const int32_t* __restrict__ lens,
-                                                       int tq, int64_t* __restrict__ P, int32_t* __restrict__ nflag) {
+                                                       int tq, int64_t* __restrict__ P, int32_t* __restrict__ nflag,
+                                                       float* __restrict__ ml_init) {
   __shared__ __align__(16) uint16_t Wt[kN * kAqLd];
   const int h = blockIdx.x, rc = blockIdx.y;
-  if (h == 0 && rc == 0) absorbed_prefix_block(lens, tq, bt, P, nflag);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  // W_UK_h rows k (128) x columns r in [128 rc, 128 rc + 128)
-  for (int c = tid; c < kN * 16; c += 256) {
-    const int k = c >> 4, part = c & 15;
-    *reinterpret_cast<uint4*>(Wt + k * kAqLd + 8 * part) =
-        ldg16(w + (static_cast<size_t>(h) * 256 + k) * kR + 128 * rc + 8 * part);
+  // W_UK_h rows k (128) x columns r in [128 rc, 128 rc + 128): all eight
+  // 16-byte loads of a thread in flight before the LDS stores
+  {
+    uint4 wv[kN * 16 / 256];
+#pragma unroll
+    for (int j = 0; j < kN * 16 / 256; ++j) {
+      const int c = tid + 256 * j, k = c >> 4, part = c & 15;
+      wv[j] = ldg16(w + (static_cast<size_t>(h) * 256 + k) * kR + 128 * rc + 8 * part);
+    }
+#pragma unroll
+    for (int j = 0; j < kN * 16 / 256; ++j) {
+      const int c = tid + 256 * j, k = c >> 4, part = c & 15;
+      *reinterpret_cast<uint4*>(Wt + k * kAqLd + 8 * part) = wv[j];
+    }
+  }
+  if (h == 0 && rc == 0) {
+    absorbed_prefix_block(lens, tq, bt, P, nflag);
+    // max-logit slots start at -inf unless the caller accumulates into them
+    if (ml_init && tid < heads) ml_init[tid] = -INFINITY;
   }
   __syncthreads();
   const lds_u16* wl = (const lds_u16*)(Wt);
@@ -100,10 +115,13 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
     const int v = v0 + 32 * vb + l32;
     const bool vv = v < bt;
     f32x16 acc[2] = {f32x16{}, f32x16{}};
+    uint4 qv[kN / 16];
+#pragma unroll
+    for (int kk = 0; kk < kN / 16; ++kk)
+      qv[kk] = vv ? ldg16(q + (static_cast<size_t>(v) * heads + h) * kD + 16 * kk + 8 * g) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int kk = 0; kk < kN / 16; ++kk) {
-      const bf16x8 a = as_bf16x8(vv ? ldg16(q + (static_cast<size_t>(v) * heads + h) * kD + 16 * kk + 8 * g)
-                                    : make_uint4(0, 0, 0, 0));
+      const bf16x8 a = as_bf16x8(qv[kk]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int mb = 32 * (rb0 + j) + 16 * ((lane >> 4) & 1);
@@ -489,70 +507,152 @@ __global__ void __launch_bounds__(256) absorbed_fixup_kernel(
 
 // ---------------------------------------------------------------------------
 // Combine: merge the partials of each (virtual sequence, head) by log-sum-exp,
-// then O~ = o_lat W_UV_h, gate, store, and the per-head max logit.
+// then O~ = o_lat W_UV_h^T, gate, store, and the per-head max logit.
 // Grid (heads, ceil(bt / 16)); 256 threads.
+// Phase 1: 16 threads per virtual sequence, thread `sub` owning the latent
+// columns 4 sub + 64 e + j (e < 8, j < 4), so that one load instruction reads
+// 256 contiguous bytes of a partial; partials are visited two at a time with
+// all of their loads in flight. Splits that hold no rows (fewer rows than
+// splits in total) wrote no partial and are skipped. o_lat goes to LDS as a
+// pair of bf16 parts, hi = bf16(o) and lo = bf16(o - hi), which together
+// carry about 16 significant bits.
+// Phase 2: O~^T [128 d x 16 v] = W_UV_h [128 x 512] o_lat^T with 16x16x32 bf16
+// MFMAs on both parts; wave w computes d in [32 w, 32 w + 32) and loads its
+// W_UV_h operands at kernel start, so they arrive during phase 1.
 // ---------------------------------------------------------------------------
 constexpr int kCmbV = 16;
+constexpr int kCmbLd = kR + 8;   // LDS row of the o_lat parts (16-byte pad)
 
-__device__ __forceinline__ int split_of_row(int64_t total, int G, int64_t row) {
-  // largest w with floor(total * w / G) <= row
-  int lo = 0, hi = G - 1;
+// First cache row of split workgroup w (the split kernel's partition).
+__device__ __forceinline__ int64_t split_lo(int64_t total, int w) { return total * w / kDecSplits; }
+
+// The split workgroup whose rows contain `row`: the largest w with split_lo(w) <= row.
+__device__ __forceinline__ int split_of_row(int64_t total, int64_t row) {
+  int lo = 0, hi = kDecSplits - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (total * mid / G <= row) lo = mid; else hi = mid - 1;
+    if (split_lo(total, mid) <= row) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
 
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256) absorbed_combine_kernel(
-    const int64_t* __restrict__ P, int64_t bt, int G, int heads, float scale,
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, const uint16_t* __restrict__ w,
-    const uint16_t* __restrict__ gate, void* __restrict__ out, float* __restrict__ max_logit) {
-  __shared__ float olat[kCmbV][kR];
+    const int64_t* __restrict__ P, int64_t bt, int heads, float scale, const float* __restrict__ part_o,
+    const float* __restrict__ part_ml, const uint16_t* __restrict__ w, const uint16_t* __restrict__ gate,
+    void* __restrict__ out, float* __restrict__ max_logit) {
+  __shared__ __align__(16) uint16_t ohi[kCmbV * kCmbLd];
+  __shared__ __align__(16) uint16_t olo[kCmbV * kCmbLd];
   __shared__ float red[kCmbV];
   const int h = blockIdx.x;
   const int64_t v0 = static_cast<int64_t>(blockIdx.y) * kCmbV;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, kq = lane >> 4;
+
+  // W_UV_h rows d = 32 wave + 16 b + i16, k-slots 8 kq .. +7 of every 32-wide
+  // step; the first half of the steps is loaded now (arriving during phase
+  // 1), the second half when phase 2 starts.
+  constexpr int kKs = kR / 32;
+  const uint16_t* wrow = w + (static_cast<size_t>(h) * 256 + kN + 32 * wave + i16) * kR + 8 * kq;
+  uint4 wop[2][kKs];
+  static_for<0, 2>([&](auto b) {
+    static_for<0, kKs / 2>([&](auto kk) { wop[b][kk] = ldg16(wrow + b * 16 * kR + 32 * kk); });
+  });
+
+  // ---- phase 1: o_lat of the workgroup's 16 virtual sequences ----
+  // Online merge: partials are visited two at a time (all their loads in
+  // flight together) against a running reference max M.
   const int vl = tid >> 4, sub = tid & 15;
   const int64_t vs = v0 + vl;
-  const int64_t total = P[bt];
   const float c2 = scale * kLog2e;
-  float mmax = -INFINITY;
+  float acc[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
+  float den = 1.0f, Mt = -INFINITY;
   if (vs < bt) {
-    const int wa = split_of_row(total, G, P[vs]);
-    const int wb = split_of_row(total, G, P[vs + 1] - 1);
+    const int64_t total = P[bt];
+    const int wa = split_of_row(total, P[vs]);
+    const int wb = split_of_row(total, P[vs + 1] - 1);
+    auto nonempty = [&](int s) { return split_lo(total, s) < split_lo(total, s + 1); };
     float M = -INFINITY;
-    float Mt = -INFINITY;
-    for (int wg = wa; wg <= wb; ++wg) {
-      const float4 ml = *reinterpret_cast<const float4*>(part_ml + ((static_cast<size_t>(wg) + vs) * heads + h) * 4);
-      M = fmaxf(M, ml.x);
-      Mt = fmaxf(Mt, ml.z);
-    }
-    float den = 0.0f;
-    float acc[kR / 16];
+    den = 0.0f;
+    const float* pb = part_o + static_cast<size_t>(h) * kR + 4 * sub;
+    // split wa holds the sequence's first row, so the first pair is never empty
+    for (int s = wa; s <= wb; s += 2) {
+      const bool e0 = nonempty(s);
+      const bool e1 = s + 1 <= wb && nonempty(s + 1);
+      const size_t slot0 = (static_cast<size_t>(s) + vs) * heads + h;
+      const size_t slot1 = slot0 + heads;
+      float4 m0 = make_float4(-INFINITY, 0.f, -INFINITY, 0.f), m1 = m0;
+      float4 x0[8], x1[8];
+      if (e0) {
+        m0 = *reinterpret_cast<const float4*>(part_ml + slot0 * 4);
+        const float* p0 = pb + (static_cast<size_t>(s) + vs) * heads * kR;
 #pragma unroll
-    for (int e = 0; e < kR / 16; ++e) acc[e] = 0.0f;
-    for (int wg = wa; wg <= wb; ++wg) {
-      const size_t s = (static_cast<size_t>(wg) + vs) * heads + h;
-      const float f = fast_exp2((part_ml[s * 4] - M) * c2);
-      den += f * part_ml[s * 4 + 1];
-      const float* po = part_o + s * kR + sub * (kR / 16);
+        for (int e = 0; e < 8; ++e) x0[e] = *reinterpret_cast<const float4*>(p0 + 64 * e);
+      }
+      if (e1) {
+        m1 = *reinterpret_cast<const float4*>(part_ml + slot1 * 4);
+        const float* p1 = pb + (static_cast<size_t>(s) + 1 + vs) * heads * kR;
 #pragma unroll
-      for (int e = 0; e < kR / 16; e += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(po + e);
-        acc[e] += f * x.x; acc[e + 1] += f * x.y; acc[e + 2] += f * x.z; acc[e + 3] += f * x.w;
+        for (int e = 0; e < 8; ++e) x1[e] = *reinterpret_cast<const float4*>(p1 + 64 * e);
+      }
+      Mt = fmaxf(Mt, fmaxf(m0.z, m1.z));
+      const float mnew = fmaxf(M, fmaxf(m0.x, m1.x));
+      if (mnew > M) {
+        const float corr = fast_exp2((M - mnew) * c2);   // 0 on the first pair (M = -inf)
+        den *= corr;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) acc[e] *= corr;
+        M = mnew;
+      }
+      if (e0) {
+        const float f = fast_exp2((m0.x - M) * c2);
+        den = fmaf(f, m0.y, den);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc[4 * e] = fmaf(f, x0[e].x, acc[4 * e]);
+          acc[4 * e + 1] = fmaf(f, x0[e].y, acc[4 * e + 1]);
+          acc[4 * e + 2] = fmaf(f, x0[e].z, acc[4 * e + 2]);
+          acc[4 * e + 3] = fmaf(f, x0[e].w, acc[4 * e + 3]);
+        }
+      }
+      if (e1) {
+        const float f = fast_exp2((m1.x - M) * c2);
+        den = fmaf(f, m1.y, den);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc[4 * e] = fmaf(f, x1[e].x, acc[4 * e]);
+          acc[4 * e + 1] = fmaf(f, x1[e].y, acc[4 * e + 1]);
+          acc[4 * e + 2] = fmaf(f, x1[e].z, acc[4 * e + 2]);
+          acc[4 * e + 3] = fmaf(f, x1[e].w, acc[4 * e + 3]);
+        }
       }
     }
-    const float inv = 1.0f / den;
-#pragma unroll
-    for (int e = 0; e < kR / 16; ++e) olat[vl][sub * (kR / 16) + e] = acc[e] * inv;
-    mmax = Mt;
-  } else {
-#pragma unroll
-    for (int e = 0; e < kR / 16; ++e) olat[vl][sub * (kR / 16) + e] = 0.0f;
   }
-  if (sub == 0) red[vl] = mmax;
+  {
+    const float inv = 1.0f / den;   // den >= 1: the partial holding M contributes f = 1 times its sum
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t hv[2], lv[2];
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const float a = acc[4 * e + j] * inv, b = acc[4 * e + j + 1] * inv;
+        hv[j >> 1] = pack_bf16x2(a, b);
+        lv[j >> 1] = pack_bf16x2(a - bf16lo(hv[j >> 1]), b - bf16hi(hv[j >> 1]));
+      }
+      const int off = vl * kCmbLd + 64 * e + 4 * sub;
+      *reinterpret_cast<uint2*>(ohi + off) = make_uint2(hv[0], hv[1]);
+      *reinterpret_cast<uint2*>(olo + off) = make_uint2(lv[0], lv[1]);
+    }
+  }
+  if (sub == 0) red[vl] = Mt;
   __syncthreads();
   if (tid == 0) {
     float mm = -INFINITY;
@@ -560,39 +660,46 @@ __global__ void __launch_bounds__(256) absorbed_combine_kernel(
     if (mm > -INFINITY) atomic_max_float(max_logit + h, mm * scale);
   }
 
-  // O~[v][d] = sum_r olat[v][r] * w_kv_b[h*256 + 128 + d][r]
-  const int d = tid & 127;
-  const int vh = tid >> 7;   // 8 virtual sequences each
-  const uint16_t* wv = w + (static_cast<size_t>(h) * 256 + kN + d) * kR;
-  float o[8];
+  // ---- phase 2: O~^T = W_UV_h o_lat^T ----
+  static_for<0, 2>([&](auto b) {
+    static_for<kKs / 2, kKs>([&](auto kk) { wop[b][kk] = ldg16(wrow + b * 16 * kR + 32 * kk); });
+  });
+  f32x4 oc[2] = {f32x4{}, f32x4{}};
+  static_for<0, kKs>([&](auto kk) {
+    const int off = i16 * kCmbLd + 32 * kk + 8 * kq;
+    const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(ohi + off));
+    const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(olo + off));
+    static_for<0, 2>([&](auto b) {
+      oc[b] = mfma16(as_bf16x8(wop[b][kk]), bh, oc[b]);
+      oc[b] = mfma16(as_bf16x8(wop[b][kk]), bl, oc[b]);
+    });
+  });
+  const int64_t v = v0 + i16;
+  if (v < bt) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = 0.0f;
-  for (int r = 0; r < kR; r += 8) {
-    const uint4 wq = ldg16(wv + r);
-    const float wf[8] = {bf16lo(wq.x), bf16hi(wq.x), bf16lo(wq.y), bf16hi(wq.y),
-                         bf16lo(wq.z), bf16hi(wq.z), bf16lo(wq.w), bf16hi(wq.w)};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float* ol = &olat[vh * 8 + i][r];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[i] = fmaf(ol[e], wf[e], o[i]);
+    for (int b = 0; b < 2; ++b) {
+      const size_t idx = (static_cast<size_t>(v) * heads + h) * kV + 32 * wave + 16 * b + 4 * kq;
+      float y[4] = {oc[b][0], oc[b][1], oc[b][2], oc[b][3]};
+      if (gate) {
+        const uint2 gv = *reinterpret_cast<const uint2*>(gate + idx);
+        y[0] *= sigmoidf_(bf16lo(gv.x));
+        y[1] *= sigmoidf_(bf16hi(gv.x));
+        y[2] *= sigmoidf_(bf16lo(gv.y));
+        y[3] *= sigmoidf_(bf16hi(gv.y));
+      }
+      if (OUT_BF16)
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) =
+            make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+      else
+        *reinterpret_cast<float4*>(static_cast<float*>(out) + idx) = make_float4(y[0], y[1], y[2], y[3]);
     }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t v = v0 + vh * 8 + i;
-    if (v >= bt) continue;
-    float y = o[i];
-    const size_t idx = (static_cast<size_t>(v) * heads + h) * kV + d;
-    if (gate) y *= sigmoidf_(bf16_to_f32(gate[idx]));
-    if (OUT_BF16) static_cast<uint16_t*>(out)[idx] = f32_to_bf16(y);
-    else static_cast<float*>(out)[idx] = y;
   }
 }
 
 hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const void* q, const void* cache,
                                 int64_t cap, const int32_t* lens, int batch, int tq, const void* w_kv_b,
-                                const void* gate, void* out, float* max_logit, void* ws, hipStream_t st) {
+                                const void* gate, void* out, float* max_logit, bool init_max_logit, void* ws,
+                                hipStream_t st) {
   const AbsorbedWs L = absorbed_ws_layout(heads, batch, tq);
   char* base = static_cast<char*>(ws);
   uint16_t* qabs = reinterpret_cast<uint16_t*>(base + L.qabs);
@@ -606,7 +713,8 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
   {
     TimedScope ts_("absorb_q", st);
     hipLaunchKernelGGL(absorb_q_kernel, dim3(heads, kR / 128), dim3(256), 0, st, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(w_kv_b), static_cast<int>(bt), heads, qabs, lens, tq, P, nflag);
+                       static_cast<const uint16_t*>(w_kv_b), static_cast<int>(bt), heads, qabs, lens, tq, P, nflag,
+                       init_max_logit ? max_logit : nullptr);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -630,14 +738,14 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
   if (out_bf16) {
     {
       TimedScope ts_("absorbed_combine", st);
-      hipLaunchKernelGGL(absorbed_combine_kernel<true>, cg, dim3(256), 0, st, P, bt, kDecSplits, heads, scale,
+      hipLaunchKernelGGL(absorbed_combine_kernel<true>, cg, dim3(256), 0, st, P, bt, heads, scale,
                          part_o, part_ml, static_cast<const uint16_t*>(w_kv_b),
                          static_cast<const uint16_t*>(gate), out, max_logit);
     }
   } else {
     {
       TimedScope ts_("absorbed_combine", st);
-      hipLaunchKernelGGL(absorbed_combine_kernel<false>, cg, dim3(256), 0, st, P, bt, kDecSplits, heads, scale,
+      hipLaunchKernelGGL(absorbed_combine_kernel<false>, cg, dim3(256), 0, st, P, bt, heads, scale,
                          part_o, part_ml, static_cast<const uint16_t*>(w_kv_b),
                          static_cast<const uint16_t*>(gate), out, max_logit);
     }

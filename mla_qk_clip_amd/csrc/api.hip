@@ -192,14 +192,16 @@ mla_status mla_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_
     }
   }
   hipError_t e = hipSuccess;
-  if (!accumulate) {
+  // the bf16 path clears the max-logit slots in its first kernel
+  const bool fused_init = in_dtype == MLA_BF16 && batch > 0;
+  if (!accumulate && !fused_init) {
     e = mla::launch_fill(max_logit, s.H, -INFINITY, stream);
     if (e != hipSuccess) return hip_fail(e, "max_logit init");
   }
   if (batch == 0) return MLA_OK;
   if (in_dtype == MLA_BF16) {
     e = mla::launch_absorbed_bf16(s.H, s.scale, out_dtype == MLA_BF16, q, cache, cap, lens, batch, tq, w_kv_b,
-                                  gate, out, max_logit, workspace, stream);
+                                  gate, out, max_logit, !accumulate, workspace, stream);
   } else {
     e = mla::launch_absorbed_f32(s.H, s.R, s.S, s.N, s.V, s.scale, static_cast<const float*>(q),
                                  static_cast<const float*>(cache), cap, lens, batch, tq,

@@ -110,7 +110,7 @@ hipError_t launch_prefill_f32(int heads, int R, int S, int N, int V, float scale
 hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16,
                                 const void* q, const void* cache, int64_t cap, const int32_t* lens,
                                 int batch, int tq, const void* w_kv_b, const void* gate, void* out,
-                                float* max_logit, void* ws, hipStream_t st);
+                                float* max_logit, bool init_max_logit, void* ws, hipStream_t st);
 
 hipError_t launch_absorbed_f32(int heads, int R, int S, int N, int V, float scale,
                                const float* q, const float* cache, int64_t cap, const int32_t* lens,
