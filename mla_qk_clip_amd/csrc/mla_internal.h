@@ -15,7 +15,7 @@ constexpr int kV = 128;   // value width
 constexpr int kD = kN + kS;
 
 // Prefill (bf16) tiling.
-constexpr int kPrefBM = 256;  // queries per workgroup
+constexpr int kPrefBM = 128;  // queries per attention workgroup (two workgroups per CU)
 constexpr int kPrefBN = 64;   // keys per inner tile
 constexpr int kSeqPad = 64;   // per-sequence padding of the expanded K^C / V^T
 

@@ -292,8 +292,11 @@ __global__ void __launch_bounds__(kExThreads) prefill_expand_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Attention. One workgroup = one head x 256 queries of one sequence; 8 waves
-// (two per SIMD) of 32 queries. Scores are formed transposed (S^T = K Q^T) so
+// Attention. One workgroup = one head x 128 queries of one sequence; 4 waves
+// of 32 queries, two workgroups per CU (80 KB of LDS and at most 256 VGPRs
+// each), so that one workgroup's prologue (query and first tile loads) and
+// epilogue (output stores) overlap the other's tile loop. Scores are formed
+// transposed (S^T = K Q^T) so
 // that each lane owns one query column: the row max/sum and the output
 // rescale stay in the lane. Keys are visited in tiles of 64 up to the
 // diagonal (tiles above it are skipped); a wave's last tile is its only
@@ -346,7 +349,7 @@ constexpr int kRing = 4;   // LDS operand fragments in flight
 static_assert(kOvlLen == 40, "24 score + 16 value MFMAs");
 
 template <bool OUT_BF16>
-__global__ void __launch_bounds__(kAttnThreads) prefill_attn_kernel(
+__global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) prefill_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ksp, const uint16_t* __restrict__ gate,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ pcu, const int32_t* __restrict__ order,
     const int32_t* __restrict__ toff, const int32_t* __restrict__ hdr, int nseq, int heads,
