@@ -449,6 +449,24 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
     }
   };
 
+  // copy c of this wave's share of a step: K^C blocks, then k^S blocks (tile
+  // jk into kdst), then V^T blocks (tile jv into vdst)
+  constexpr int kStepCopies = kKcCopies + kKsCopies + kVtCopies;
+  auto dma_one = [&](int c, uint4* kdst, int jk, uint4* vdst, int jv) {
+    // (the block offset goes into the scalar offset: one address VGPR for all copies)
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    if (c < kKcCopies) {
+      const int blk = kKcCopies * w + c;
+      dma16_buf(rs_kc, lane16, static_cast<uint32_t>(jk) * (kTileElems * 2) + blk * 1024, kdst + blk * 64);
+    } else if (c < kKcCopies + kKsCopies) {
+      const int blk = kKsCopies * w + (c - kKcCopies);
+      dma16_buf(rs_ks, lane16, static_cast<uint32_t>(jk) * (kPrefBN * kS * 2) + blk * 1024, kdst + (kN / 8 + blk) * 64);
+    } else {
+      const int blk = kVtCopies * w + (c - kKcCopies - kKsCopies);
+      dma16_buf(rs_vt, lane16, static_cast<uint32_t>(jv) * (kTileElems * 2) + blk * 1024, vdst + blk * 64);
+    }
+  };
+
   // LDS operand addresses: K unit (2kk + g) * 64 + 32 blk + l32, V^T unit
   // (2jj + g) * 128 + 32 db + l32 (a 16-lane group reads 16 consecutive units)
   auto kfrag = [&](const uint4* kt, int f) {   // f = 2 kk + blk
@@ -534,7 +552,7 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
   // pairs 4jj..4jj+3) and the row max of S(j+1). Scheduling barriers keep
   // the issue order.
   auto overlapped = [&](const uint4* kt, const uint4* vtile, const f32x16 (&cur)[2], f32x16 (&nxt)[2],
-                        float moff) {
+                        float moff, auto&& issue_copy) {
     uint32_t pk[2][8];
     float psum = 0.0f;
     float mx0 = -INFINITY, mx1 = -INFINITY;
@@ -556,6 +574,7 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
         oacc[o.idx & 3] = mfma32(ring[c % kRing], pv_operand(pk, o.idx >> 2), oacc[o.idx & 3]);
       }
       if constexpr (c + kRing < kOvlLen) ring[c % kRing] = fetch(std::integral_constant<int, c + kRing>{});
+      if constexpr (c % 4 == 0 && c / 4 < kStepCopies) issue_copy(c / 4);
       if constexpr (o.pair >= 0) prob_pair(cur, pk, moff, psum, o.pair);
       if constexpr (o.mx >= 0) {
         mx0 = fmax3_(mx0, nxt[0][4 * o.mx], nxt[0][4 * o.mx + 1]);
@@ -580,8 +599,14 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
     const uint4* vread = P ? V1 : V0;     // V(j)
     f32x16 (&cur)[2] = P ? sB : sA;
     f32x16 (&nxt)[2] = P ? sA : sB;
-    if (j + 2 < nkt) dma_k(kdst, j + 2);
-    if (j + 1 < nkt) dma_v(vdst, j + 1);
+    const bool cp_k = j + 2 < nkt, cp_v = j + 1 < nkt;
+    // the step's copies are spread over the overlapped body (one per four
+    // MFMAs) so that their issue hides behind the matrix work
+    const bool spread = j < nkt_w && j + 2 < nkt_w;
+    if (!spread) {
+      if (cp_k) dma_k(kdst, j + 2);
+      if (cp_v) dma_v(vdst, j + 1);
+    }
     if (j < nkt_w) {
       // [A] move the reference max when S(j) exceeds it by more than 2^8
       const bool need = (mx_cur - m_ref) * c2 > kRescaleLog2;
@@ -596,7 +621,8 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
       m_true = fmaxf(m_true, mx_cur);
       const float moff = -m_ref * c2;
       if (j + 2 < nkt_w) {
-        overlapped(kread, vread, cur, nxt, moff);
+        // (here j + 2 < nkt_w <= nkt: both K(j+2) and V(j+1) are due)
+        overlapped(kread, vread, cur, nxt, moff, [&](int c) { dma_one(c, kdst, j + 2, vdst, j + 1); });
       } else {
         // the wave's last two tiles: the next one (if any) is the masked diagonal tile
         uint32_t pk[2][8];
