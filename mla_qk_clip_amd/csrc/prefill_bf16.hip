@@ -657,41 +657,21 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
     if (j + 1 < nkt) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
-  // ---- epilogue: normalise, gate, store; log-sum-exp; per-head max logit ----
-  const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
-  const float inv = 1.0f / l_tot;
-  if (qvalid) {
-    const size_t t = static_cast<size_t>(a0 + qi);
-    const uint16_t* grow = gate ? gate + (t * heads + head) * kV : nullptr;
+  // ---- epilogue: block maxima of the raw row max and of |q_t|^2 for the
+  // max-logit refinement first (the barrier it needs then has no stores to
+  // wait for), then normalise, gate and store; the stores drain after the
+  // waves end. The gate values of the lane's 64 output columns are loaded
+  // first, all in flight together, behind the reduction ----
+  const size_t t_row = static_cast<size_t>(a0 + (qvalid ? qi : 0));
+  uint2 gates[kV / 32][4];
+  if (gate && qvalid) {
+    const uint16_t* gr = gate + (t_row * heads + head) * kV;
 #pragma unroll
     for (int db = 0; db < kV / 32; ++db)
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int d = 32 * db + 8 * grp + 4 * g;
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = oacc[db][4 * grp + e] * inv;
-        if (grow) {
-          const uint2 gv = *reinterpret_cast<const uint2*>(grow + d);
-          o[0] *= sigmoidf_(bf16lo(gv.x));
-          o[1] *= sigmoidf_(bf16hi(gv.x));
-          o[2] *= sigmoidf_(bf16lo(gv.y));
-          o[3] *= sigmoidf_(bf16hi(gv.y));
-        }
-        if (OUT_BF16) {
-          uint16_t* orow = static_cast<uint16_t*>(out) + (t * heads + head) * kV + d;
-          *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-        } else {
-          float* orow = static_cast<float*>(out) + (t * heads + head) * kV + d;
-          *reinterpret_cast<float4*>(orow) = make_float4(o[0], o[1], o[2], o[3]);
-        }
-      }
-    if (g == 0) {
-      if (lse) lse[static_cast<size_t>(head) * ntok + t] = m_ref * scale + __logf(l_tot);
-      rowmax[static_cast<size_t>(head) * ntok + t] = m_true;
-    }
+      for (int grp = 0; grp < 4; ++grp)
+        gates[db][grp] = *reinterpret_cast<const uint2*>(gr + 32 * db + 8 * grp + 4 * g);
   }
-  // block maxima of the raw row max and of |q_t|^2 for the max-logit refinement
   float qn2 = 0.0f;
 #pragma unroll
   for (int kk = 0; kk < kD / 16; ++kk)
@@ -719,6 +699,39 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
     }
     if (mm > -INFINITY) atomic_max_float(aux + head * kAuxStride, mm);
     atomic_max_float(aux + head * kAuxStride + 1, mq);
+  }
+  const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
+  const float inv = 1.0f / l_tot;
+  if (qvalid) {
+    const size_t t = static_cast<size_t>(a0 + qi);
+    const uint16_t* grow = gate ? gate + (t * heads + head) * kV : nullptr;
+#pragma unroll
+    for (int db = 0; db < kV / 32; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int d = 32 * db + 8 * grp + 4 * g;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = oacc[db][4 * grp + e] * inv;
+        if (grow) {
+          const uint2 gv = gates[db][grp];
+          o[0] *= sigmoidf_(bf16lo(gv.x));
+          o[1] *= sigmoidf_(bf16hi(gv.x));
+          o[2] *= sigmoidf_(bf16lo(gv.y));
+          o[3] *= sigmoidf_(bf16hi(gv.y));
+        }
+        if (OUT_BF16) {
+          uint16_t* orow = static_cast<uint16_t*>(out) + (t * heads + head) * kV + d;
+          *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        } else {
+          float* orow = static_cast<float*>(out) + (t * heads + head) * kV + d;
+          *reinterpret_cast<float4*>(orow) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+      }
+    if (g == 0) {
+      if (lse) lse[static_cast<size_t>(head) * ntok + t] = m_ref * scale + __logf(l_tot);
+      rowmax[static_cast<size_t>(head) * ntok + t] = m_true;
+    }
   }
 }
 
