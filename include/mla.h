@@ -125,7 +125,8 @@ mla_status mla_prefill(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_d
 /* Inference form (absorbed W_UK / W_UV over the latent cache)              */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of scratch memory mla_absorbed needs for these sizes. */
+/* Bytes of scratch memory mla_absorbed needs for these sizes (0 for invalid
+ * sizes). */
 size_t mla_absorbed_workspace_size(const mla_dims* dims, mla_dtype in_dtype,
                                    int32_t batch, int32_t tq);
 
@@ -152,7 +153,14 @@ size_t mla_absorbed_workspace_size(const mla_dims* dims, mla_dtype in_dtype,
  * max_logit [H] fp32, as for mla_prefill (over every visible (query, row) pair).
  *
  * bf16: q_abs is rounded to bf16 for the MFMA products; the softmax, the
- * split-K partials and their log-sum-exp merge stay in fp32.
+ * split-K partials and their log-sum-exp merge stay in fp32. max_logit is
+ * refined: with the rounding of q_abs bounded per 32-row tile (by the
+ * tile's largest row norm), every tile that could hold the head's exact
+ * maximum is re-scored in fp32 against q_abs carried to about 16 significant
+ * bits, so the result is the exact maximum up to fp32 rounding. Where more
+ * tiles than the refinement lists tie within that bound (q = 0, repeated
+ * rows), a head falls back to the streamed maximum, within the bound.
+ * cap is at most 2^31 - 1.
  */
 mla_status mla_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype,
                         const void* q, const void* cache, int64_t cap,

@@ -14,6 +14,11 @@
 // number of cache bytes whatever the length mix. For every (workgroup,
 // sequence) overlap it writes a partial (row max, denominator, unnormalised
 // o_lat) for all heads; the combine kernel merges them by log-sum-exp.
+//
+// The per-head max logit is refined to the exact value: the split kernel
+// bounds the bf16 rounding error of every 32-row tile's logits (from the
+// tile's largest row norm) and keeps the tiles that could hold the maximum;
+// the refine kernel re-scores those in fp32.
 #include "mla_common.h"
 #include "mla_internal.h"
 #include "timing.h"
@@ -82,8 +87,10 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
                                                        const uint16_t* __restrict__ w, int bt, int heads,
                                                        uint16_t* __restrict__ qabs, const int32_t* __restrict__ lens,
                                                        int tq, int64_t* __restrict__ P, int32_t* __restrict__ nflag,
-                                                       float* __restrict__ ml_init) {
+                                                       float* __restrict__ ml_init, float* __restrict__ qn2,
+                                                       float* __restrict__ hmax, uint16_t* __restrict__ qlo) {
   __shared__ __align__(16) uint16_t Wt[kN * kAqLd];
+  __shared__ float qsq[2][64];
   const int h = blockIdx.x, rc = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -106,11 +113,14 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
     absorbed_prefix_block(lens, tq, bt, P, nflag);
     // max-logit slots start at -inf unless the caller accumulates into them
     if (ml_init && tid < heads) ml_init[tid] = -INFINITY;
+    // state of the max-logit refinement (written by later kernels only)
+    for (int i = tid; i < heads; i += 256) hmax[i] = -INFINITY;
   }
   __syncthreads();
   const lds_u16* wl = (const lds_u16*)(Wt);
   const int vb = wave & 1;          // which 32 virtual sequences of the 64-chunk
   const int rb0 = 2 * (wave >> 1);  // two 32-column blocks
+  float qmax2 = 0.0f;
   for (int v0 = 0; v0 < bt; v0 += 64) {
     const int v = v0 + 32 * vb + l32;
     const bool vv = v < bt;
@@ -136,8 +146,14 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int vr = v0 + 32 * vb + acc_row(e, g);
-        if (vr < bt)
-          qabs[(static_cast<size_t>(vr) * heads + h) * kW + 128 * rc + 32 * (rb0 + j) + l32] = f32_to_bf16(acc[j][e]);
+        if (vr < bt) {
+          // q_abs in bf16 for the stream, and its rounding residual (in bf16)
+          // for the max-logit refinement
+          const uint16_t hi = f32_to_bf16(acc[j][e]);
+          const size_t col = (static_cast<size_t>(vr) * heads + h) * kR + 128 * rc + 32 * (rb0 + j) + l32;
+          qabs[(static_cast<size_t>(vr) * heads + h) * kW + 128 * rc + 32 * (rb0 + j) + l32] = hi;
+          qlo[col] = f32_to_bf16(acc[j][e] - bf16_to_f32(hi));
+        }
       }
     if (rc == 0) {
       for (int e = tid; e < 64 * kS; e += 256) {
@@ -145,6 +161,46 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
         if (vr < bt) qabs[(static_cast<size_t>(vr) * heads + h) * kW + kR + s] = q[(static_cast<size_t>(vr) * heads + h) * kD + kN + s];
       }
     }
+    // squared norm of this block's 128 rounded q_abs entries per virtual
+    // sequence: sum over the lane's two columns, then over the 32 lanes of
+    // each half-wave (which share their rows), then over the two waves that
+    // hold the same sequences
+    float sq[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float a = bf16_to_f32(f32_to_bf16(acc[0][e])), b = bf16_to_f32(f32_to_bf16(acc[1][e]));
+      sq[e] = fmaf(a, a, b * b);
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sq[e] += __shfl_xor(sq[e], o, 64);
+    if (l32 == 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) qsq[wave >> 1][32 * vb + acc_row(e, g)] = sq[e];
+    }
+    __syncthreads();
+    if (tid < 64 && v0 + tid < bt) {
+      float s2 = qsq[0][tid] + qsq[1][tid];
+      if (rc == 0) {
+        const uint16_t* qr = q + (static_cast<size_t>(v0 + tid) * heads + h) * kD + kN;
+#pragma unroll
+        for (int u = 0; u < kS / 8; ++u) {
+          const uint4 x = ldg16(qr + 8 * u);
+          const uint32_t* w4 = &x.x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s2 = fmaf(bf16lo(w4[i]), bf16lo(w4[i]), fmaf(bf16hi(w4[i]), bf16hi(w4[i]), s2));
+        }
+      }
+      qmax2 = fmaxf(qmax2, s2);
+    }
+    __syncthreads();
+  }
+  // max over the virtual sequences; the sum over the four column blocks of
+  // these maxima bounds every ||q_abs||^2 of the head
+  if (wave == 0) {
+    qmax2 = wave_max(qmax2);
+    if (lane == 0) qn2[h * 4 + rc] = qmax2;
   }
 }
 
@@ -171,6 +227,11 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
 //   part_o[slot][h][r] = sum_j p_j c_j[r] (relative to the reference max),
 //   part_ml[slot][h] = {reference max (raw), denominator, true raw max, flag}.
 // ---------------------------------------------------------------------------
+// Bound on |streamed - exact| logit per unit of ||q_abs|| * ||row||: bf16
+// rounding of q_abs (unit roundoff 2^-8, with 1% slack for the fp32
+// products that formed it) plus fp32 accumulation over 576 products.
+constexpr float kDecErrCoef = 1.01f / 256.0f + 4e-5f;
+
 constexpr int kChunks = kW / 8;                       // 72 data chunks of 16 bytes per row
 constexpr int kRowSlots = kChunks + 1;                // 73 slots per LDS row (one pad)
 constexpr int kTileSlots = kDecRows * kRowSlots;      // 2336
@@ -215,7 +276,8 @@ struct SplitState {
 };
 
 // Scores, softmax weights and the latent accumulation for one tile in `tile`.
-__device__ __forceinline__ void split_compute(const uint16_t* tile, int nrows, int lane, float c2, SplitState& S) {
+// Returns the tile's approximate max logit of the lane's head.
+__device__ __forceinline__ float split_compute(const uint16_t* tile, int nrows, int lane, float c2, SplitState& S) {
   const int g = lane >> 5, l32 = lane & 31;
   const int i16 = lane & 15;
   const int mhalf = 16 * ((lane >> 4) & 1);
@@ -293,19 +355,27 @@ __device__ __forceinline__ void split_compute(const uint16_t* tile, int nrows, i
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
   }
+  return mx;
 }
 
 // Wave 3 streams every tile of the workgroup into a ring of kStages LDS stages
 // with direct global->LDS copies (37 wave-wide 1 KB copies per tile), two
-// tiles ahead of the compute waves. It never reads LDS, and the compute waves
-// never copy, so neither code path has to wait on the other's memory ops
-// except through the explicit vmcnt wait and the barrier.
-__device__ __forceinline__ void split_issue(uint16_t* ring, int stage, TileCursor& lc, const int64_t* P,
-                                            const uint16_t* cache, int64_t cap, int tq, int lane) {
+// tiles ahead of the compute waves. It issues no other vector memory
+// operations (so its vmcnt waits count copies only), its LDS reads of the
+// ring are written in asm, and the compute waves never copy, so neither code
+// path has to wait on the other's memory ops except through the explicit
+// vmcnt wait and the barrier.
+struct TileRec {
+  int vs, row0, nrows;   // virtual sequence, first row within it, rows
+};
+
+__device__ __forceinline__ TileRec split_issue(uint16_t* ring, int stage, TileCursor& lc, const int64_t* P,
+                                               const uint16_t* cache, int64_t cap, int tq, int lane) {
   const int b = static_cast<int>(lc.vs / tq);
   const int64_t row0 = lc.pos - P[lc.vs];
   const int64_t left = lc.seg_end - lc.pos;
   const int nrows = left < kDecRows ? static_cast<int>(left) : kDecRows;
+  const TileRec rec{static_cast<int>(lc.vs), static_cast<int>(row0), nrows};
   const uint16_t* src = cache + (static_cast<size_t>(b) * cap + row0) * kW;
   char* dst = reinterpret_cast<char*>(ring) + stage * kTileBytes;
 #pragma unroll
@@ -323,13 +393,118 @@ __device__ __forceinline__ void split_issue(uint16_t* ring, int stage, TileCurso
                                      (__attribute__((address_space(3))) void*)(dst + 1024 * kc), 16, 0, 0);
   }
   cursor_next(lc, P);
+  return rec;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Nine 16-byte LDS reads at addr + 16 k, k < 9, with their wait in the same
+// asm block. Written this way because the compiler orders every LDS read of
+// the ring behind all of the wave's outstanding global->LDS copies; these
+// reads touch a stage whose copies have completed.
+__device__ __forceinline__ void lds_read9(uint32_t addr, u32x4 (&x)[9]) {
+  asm volatile(
+      "ds_read_b128 %0, %9\n"
+      "ds_read_b128 %1, %9 offset:16\n"
+      "ds_read_b128 %2, %9 offset:32\n"
+      "ds_read_b128 %3, %9 offset:48\n"
+      "ds_read_b128 %4, %9 offset:64\n"
+      "ds_read_b128 %5, %9 offset:80\n"
+      "ds_read_b128 %6, %9 offset:96\n"
+      "ds_read_b128 %7, %9 offset:112\n"
+      "ds_read_b128 %8, %9 offset:128\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]),
+        "=&v"(x[7]), "=&v"(x[8])
+      : "v"(addr)
+      : "memory");
+}
+
+// Largest row norm among the first nrows rows of an LDS tile. Lane l sums
+// the squares of half of row l % 32 (36 of its 72 chunks); the halves are
+// added, then the maximum is taken over the rows.
+__device__ __forceinline__ float tile_max_row_norm(const uint16_t* tile, int nrows, int lane) {
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u16*)tile)) +
+                        16 * ((lane & 31) * kRowSlots + (kChunks / 2) * (lane >> 5));
+  float s = 0.0f;
+#pragma unroll
+  for (int blk = 0; blk < kChunks / 2 / 9; ++blk) {
+    u32x4 x[9];
+    lds_read9(base + 16 * 9 * blk, x);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+      // (bit-casting single elements of a vector would read element 0 with this compiler)
+      const bf16x8 v = __builtin_bit_cast(bf16x8, x[k]);
+      const bf16x2 v0 = __builtin_shufflevector(v, v, 0, 1), v1 = __builtin_shufflevector(v, v, 2, 3);
+      const bf16x2 v2 = __builtin_shufflevector(v, v, 4, 5), v3 = __builtin_shufflevector(v, v, 6, 7);
+      s = __builtin_amdgcn_fdot2_f32_bf16(v0, v0, s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(v1, v1, s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(v3, v3, s, false);
+    }
+  }
+  s += __shfl_xor(s, 32, 64);
+  if ((lane & 31) >= nrows) s = 0.0f;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) s = fmaxf(s, __shfl_xor(s, o, 64));
+  return sqrtf(s);
+}
+
+// Workgroup barrier for the loader wave: the caller has already waited for
+// exactly the copies the other waves need. (__syncthreads would also wait for
+// the copies of the tile two ahead, which are not needed yet.) The compiler
+// keeps memory accesses on their side of the asm statements.
+__device__ __forceinline__ void loader_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Candidate list of one head in one split workgroup, kept by the lane that
+// owns the head. lb is a lower bound of the head's exact max logit (the
+// largest tile max minus its error bound so far); a tile can hold the exact
+// maximum only if its max plus its error bound reaches lb, so entries below
+// the current lb are dropped whenever the list fills up. cnt == kDecList + 1
+// marks a list that overflowed with live entries.
+struct CandEntry {
+  int vsn;    // virtual sequence | rows << 24
+  int row0;   // first row within the sequence
+  float u;    // upper bound of the tile's exact max logit (raw)
+};
+__device__ __forceinline__ void cand_compact(CandEntry* list, int& cnt, float lb) {
+  int j = 0;
+  for (int k = 0; k < cnt; ++k) {
+    const CandEntry e = list[k];
+    if (e.u >= lb) list[j++] = e;
+  }
+  cnt = j;
+}
+__device__ __forceinline__ void cand_record(CandEntry* list, int& cnt, float& lb, float mx, float d, int vsn,
+                                            int row0) {
+  lb = fmaxf(lb, mx - d);
+  const float u = mx + d;
+  if (cnt > kDecList || u < lb) return;
+  if (cnt == kDecList) {
+    cand_compact(list, cnt, lb);
+    if (cnt == kDecList) {
+      cnt = kDecList + 1;
+      return;
+    }
+  }
+  list[cnt++] = CandEntry{vsn, row0, u};
 }
 
 __global__ void __launch_bounds__(256) absorbed_split_kernel(
     const uint16_t* __restrict__ cache, int64_t cap, int tq, int heads, int64_t bt,
     const int64_t* __restrict__ P, const uint16_t* __restrict__ qabs, float scale,
-    float* __restrict__ part_o, float* __restrict__ part_ml, int32_t* __restrict__ nflag) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, int32_t* __restrict__ nflag,
+    const float* __restrict__ qn2, float* __restrict__ dlb, int32_t* __restrict__ dcnt, int4* __restrict__ dent) {
   __shared__ __align__(16) uint16_t ring[kStages * kTileBytes / 2];
+  // largest row norm of the tile being computed (double-buffered), from the
+  // loader to the compute waves
+  __shared__ float tnorm[2];
+  // per head of the block: candidate tiles for the max-logit refinement
+  __shared__ CandEntry clist[kDecHeadsPerWg][kDecList];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -337,7 +512,18 @@ __global__ void __launch_bounds__(256) absorbed_split_kernel(
   const int64_t total = P[bt];
   const int64_t lo = total * blockIdx.x / G;
   const int64_t hi = total * (blockIdx.x + 1) / G;
-  if (lo >= hi) return;
+  // the first head block writes the bounds of every head of an empty workgroup
+  const bool rec = blockIdx.y == 0;
+  if (lo >= hi) {
+    // no rows: no bound and no candidates for any head
+    if (rec) {
+      for (int h = tid; h < heads; h += 256) {
+        dlb[blockIdx.x * heads + h] = -INFINITY;
+        dcnt[blockIdx.x * heads + h] = 0;
+      }
+    }
+    return;
+  }
 
   int ntiles = 0;
   {
@@ -351,17 +537,28 @@ __global__ void __launch_bounds__(256) absorbed_split_kernel(
 
   if (wave == 3) {
     // ---------------- loader ----------------
+    // It also measures each tile the compute waves are working on (its
+    // largest row norm, from LDS, while the next copies are in flight) and
+    // leaves the result in tnorm for the compute waves.
     TileCursor lc;
     cursor_init(lc, P, bt, lo, hi);
-    split_issue(ring, 0, lc, P, cache, cap, tq, lane);
-    if (ntiles > 1) split_issue(ring, 1, lc, P, cache, cap, tq, lane);
+    TileRec r0 = split_issue(ring, 0, lc, P, cache, cap, tq, lane);
+    TileRec r1 = ntiles > 1 ? split_issue(ring, 1, lc, P, cache, cap, tq, lane) : TileRec{0, 0, 0};
     if (ntiles > 1) wait_vmcnt<kDmaCopies>(); else wait_vmcnt<0>();   // tile 0 landed
-    __syncthreads();
+    loader_barrier();
     for (int i = 0; i < ntiles; ++i) {
-      if (i + 2 < ntiles) split_issue(ring, (i + 2) % kStages, lc, P, cache, cap, tq, lane);
-      // tile i+1 must have landed before the barrier that ends tile i
+      TileRec r2{0, 0, 0};
+      if (i + 2 < ntiles) r2 = split_issue(ring, (i + 2) % kStages, lc, P, cache, cap, tq, lane);
+      {
+        const float kn = tile_max_row_norm(ring + (i % kStages) * (kTileBytes / 2), r0.nrows, lane);
+        if (lane == 0) tnorm[i & 1] = kn;
+      }
+      r0 = r1;
+      r1 = r2;
+      // tile i+1 must have landed (and tnorm been written) before the barrier that ends tile i
       if (i + 2 < ntiles) wait_vmcnt<kDmaCopies>(); else wait_vmcnt<0>();
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+      loader_barrier();
     }
     return;
   }
@@ -372,6 +569,13 @@ __global__ void __launch_bounds__(256) absorbed_split_kernel(
   const bool active = 32 * hb < heads;
   const bool hvalid = active && head < heads;
   const float c2 = scale * kLog2e;
+  // the head's logit error bound per unit row norm, and its candidate list
+  const int hq = hvalid ? head : 0;
+  const float qerr =
+      kDecErrCoef * sqrtf((qn2[4 * hq] + qn2[4 * hq + 1]) + (qn2[4 * hq + 2] + qn2[4 * hq + 3]));
+  CandEntry* clst = clist[32 * wave + l32];
+  float clb = -INFINITY;
+  int ccnt = 0;
   __syncthreads();   // tile 0
 
   TileCursor cur;
@@ -382,6 +586,7 @@ __global__ void __launch_bounds__(256) absorbed_split_kernel(
     // ---- one segment: the rows of virtual sequence cur.vs inside [lo, hi) ----
     const int64_t vs = cur.vs;
     const int64_t seg_end = cur.seg_end;
+    const int64_t seg_p = P[vs];   // global index of the sequence's first visible row
     {
       const uint16_t* qrow = qabs + (static_cast<size_t>(vs) * heads + (hvalid ? head : 0)) * kW + 8 * g;
 #pragma unroll
@@ -402,9 +607,15 @@ __global__ void __launch_bounds__(256) absorbed_split_kernel(
     do {
       const int64_t left = seg_end - cur.pos;
       const int nrows = left < kDecRows ? static_cast<int>(left) : kDecRows;
-      if (active) split_compute(ring + (i % kStages) * (kTileBytes / 2), nrows, lane, c2, S);
+      float mx = 0.0f;
+      if (active) mx = split_compute(ring + (i % kStages) * (kTileBytes / 2), nrows, lane, c2, S);
       S.first = false;
       __syncthreads();
+      // the finished tile into the head's candidate list for the max-logit
+      // refinement, with the loader's row norm for its error bound
+      if (hvalid && g == 0)
+        cand_record(clst, ccnt, clb, mx, qerr * tnorm[i & 1], static_cast<int>(vs) | (nrows << 24),
+                    static_cast<int>(cur.pos - seg_p));
       cursor_next(cur, P);
       ++i;
     } while (cur.pos < seg_end);
@@ -426,6 +637,17 @@ __global__ void __launch_bounds__(256) absorbed_split_kernel(
         *reinterpret_cast<float4*>(part_ml + (slot * heads + head) * 4) =
             make_float4(S.m_ref, l_tot, S.m_true, S.overflow ? 1.0f : 0.0f);
       if (__ballot(S.overflow) && lane == 0) atomicAdd(nflag, 1);
+    }
+  }
+  // the head's bound and live candidates of this workgroup
+  if (hvalid && g == 0) {
+    if (ccnt <= kDecList) cand_compact(clst, ccnt, clb);
+    const size_t o = static_cast<size_t>(blockIdx.x) * heads + head;
+    dlb[o] = clb;
+    dcnt[o] = ccnt;
+    for (int k = 0; k < ccnt && k < kDecList; ++k) {
+      const CandEntry e = clst[k];
+      dent[o * kDecList + k] = make_int4(e.vsn & 0xffffff, e.row0, e.vsn >> 24, __float_as_int(e.u));
     }
   }
 }
@@ -507,7 +729,7 @@ __global__ void __launch_bounds__(256) absorbed_fixup_kernel(
 
 // ---------------------------------------------------------------------------
 // Combine: merge the partials of each (virtual sequence, head) by log-sum-exp,
-// then O~ = o_lat W_UV_h^T, gate, store, and the per-head max logit.
+// then O~ = o_lat W_UV_h^T, gate, store, and the per-head approximate max logit.
 // Grid (heads, ceil(bt / 16)); 256 threads.
 // Phase 1: 16 threads per virtual sequence, thread `sub` owning the latent
 // columns 4 sub + 64 e + j (e < 8, j < 4), so that one load instruction reads
@@ -521,6 +743,7 @@ __global__ void __launch_bounds__(256) absorbed_fixup_kernel(
 // W_UV_h operands at kernel start, so they arrive during phase 1.
 // ---------------------------------------------------------------------------
 constexpr int kCmbV = 16;
+
 constexpr int kCmbLd = kR + 8;   // LDS row of the o_lat parts (16-byte pad)
 
 // First cache row of split workgroup w (the split kernel's partition).
@@ -546,7 +769,7 @@ template <bool OUT_BF16>
 __global__ void __launch_bounds__(256) absorbed_combine_kernel(
     const int64_t* __restrict__ P, int64_t bt, int heads, float scale, const float* __restrict__ part_o,
     const float* __restrict__ part_ml, const uint16_t* __restrict__ w, const uint16_t* __restrict__ gate,
-    void* __restrict__ out, float* __restrict__ max_logit) {
+    void* __restrict__ out, float* __restrict__ hmax) {
   __shared__ __align__(16) uint16_t ohi[kCmbV * kCmbLd];
   __shared__ __align__(16) uint16_t olo[kCmbV * kCmbLd];
   __shared__ float red[kCmbV];
@@ -657,7 +880,7 @@ __global__ void __launch_bounds__(256) absorbed_combine_kernel(
   if (tid == 0) {
     float mm = -INFINITY;
     for (int i = 0; i < kCmbV; ++i) mm = fmaxf(mm, red[i]);
-    if (mm > -INFINITY) atomic_max_float(max_logit + h, mm * scale);
+    if (mm > -INFINITY) atomic_max_float(hmax + h, mm);   // approximate, raw; refined below
   }
 
   // ---- phase 2: O~^T = W_UV_h o_lat^T ----
@@ -696,12 +919,141 @@ __global__ void __launch_bounds__(256) absorbed_combine_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Max-logit refinement. The stream's logits use q_abs rounded to bf16, so
+// the logit of row j carries an error of at most
+//   delta_j = kDecErrCoef * max ||q_abs|| * ||row_j||
+// (per tile, with the tile's largest row norm). The exact maximum E is then
+// at least L = max over tiles of (streamed tile max - delta), and only a tile
+// whose streamed max + delta reaches L can hold it. The split kernel keeps,
+// per workgroup and head, its part of L and the tiles that pass against it;
+// one workgroup per head here takes L over all split workgroups, keeps the
+// listed tiles that still pass, and re-scores their rows in fp32 against
+// q_abs carried to about 16 significant bits (its bf16 value plus the bf16
+// rounding residual). The head's max logit is the maximum of those scores.
+// If a list overflowed (near-ties: q = 0, repeated rows) the streamed maximum
+// M is folded in as well, which is within max_j delta_j of E.
+// ---------------------------------------------------------------------------
+constexpr int kRefTiles = 128;   // candidate tiles per refine workgroup
+constexpr int kRefSplit = 4;     // refine workgroups per head
+
+// Grid (heads, kRefSplit): workgroup (h, y) takes the lists of the split
+// workgroups w with w % kRefSplit == y. Scoring: one wave per listed tile;
+// lane l takes row l % 32, half l / 32 of its 72 16-byte chunks.
+__global__ void __launch_bounds__(256) absorbed_refine_kernel(
+    int heads, const float* __restrict__ dlb, const int32_t* __restrict__ dcnt, const int4* __restrict__ dent,
+    const float* __restrict__ hmax, const uint16_t* __restrict__ qabs, const uint16_t* __restrict__ qlo,
+    const uint16_t* __restrict__ cache, int64_t cap, int tq, float scale, float* __restrict__ max_logit) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  __shared__ i32x4 tl[kRefTiles + 1];
+  __shared__ float red[4];
+  __shared__ int ntile, overflow;
+  __shared__ __align__(16) float qe[4][kW];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float M = hmax[h];
+  if (tid == 0) {
+    ntile = 0;
+    overflow = 0;
+  }
+  // ---- L over all split workgroups (kDecSplits == 256 threads)
+  {
+    const float lbw = wave_max(dlb[static_cast<size_t>(tid) * heads + h]);
+    if (lane == 0) red[wave] = lbw;
+  }
+  // this thread's share of the lists: workgroup w, entries k = j (mod 4)
+  const int w = kRefSplit * (tid >> 2) + blockIdx.y, j = tid & 3;
+  const bool own = w < kDecSplits;
+  const size_t o = static_cast<size_t>(own ? w : 0) * heads + h;
+  const int c = own ? dcnt[o] : 0;
+  i32x4 e[kDecList / 4];
+  const i32x4* ent = reinterpret_cast<const i32x4*>(dent) + o * kDecList;
+  // all slots, in flight with the count (slots past the count are ignored)
+#pragma unroll
+  for (int u = 0; u < kDecList / 4; ++u) e[u] = ent[j + 4 * u];
+  __syncthreads();
+  const float L = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (c > kDecList && j == 0) overflow = 1;
+  // ---- the listed tiles that pass against L: slots reserved with one
+  // atomic per thread, entries written without branches (an entry that does
+  // not pass, or finds the list full, goes to the spare slot kRefTiles)
+  {
+    int npass = 0;
+#pragma unroll
+    for (int u = 0; u < kDecList / 4; ++u) {
+      const int k = j + 4 * u;
+      npass += (k < c && k < kDecList && __int_as_float(e[u][3]) >= L) ? 1 : 0;
+    }
+    int q = npass ? atomicAdd(&ntile, npass) : 0;
+#pragma unroll
+    for (int u = 0; u < kDecList / 4; ++u) {
+      const int k = j + 4 * u;
+      const bool p = k < c && k < kDecList && __int_as_float(e[u][3]) >= L;
+      tl[p && q < kRefTiles ? q : kRefTiles] = e[u];
+      q += p ? 1 : 0;
+    }
+    if (q > kRefTiles) overflow = 1;
+  }
+  __syncthreads();
+  if (tid == 0 && overflow) atomic_max_float(max_logit + h, M * scale);   // some list overflowed
+  // ---- rows of the listed tiles, one wave per tile
+  const int nt = min(ntile, kRefTiles);
+  float best = -INFINITY;
+  float* q = qe[wave];
+  const int rw = lane & 31, half = lane >> 5;
+  for (int k = wave; k < nt; k += 4) {
+    const i32x4 ti = tl[k];
+    const int vs = ti[0], row0 = ti[1], nrows = ti[2];
+    const uint16_t* qa = qabs + (static_cast<size_t>(vs) * heads + h) * kW;
+    const uint16_t* ql = qlo + (static_cast<size_t>(vs) * heads + h) * kR;
+    float qv[kW / 64];
+#pragma unroll
+    for (int u = 0; u < kW / 64; ++u) {
+      const int c = lane + 64 * u;
+      qv[u] = bf16_to_f32(qa[c]) + (c < kR ? bf16_to_f32(ql[c]) : 0.0f);
+    }
+    const bool rvalid = rw < nrows;
+    const uint4* row = reinterpret_cast<const uint4*>(
+        cache + (static_cast<size_t>(vs / tq) * cap + row0 + (rvalid ? rw : 0)) * kW) + (kChunks / 2) * half;
+    // the lane's 36 chunks, all in flight together with the query
+    uint4 rv[kChunks / 2];
+#pragma unroll
+    for (int u = 0; u < kChunks / 2; ++u) rv[u] = row[u];
+#pragma unroll
+    for (int u = 0; u < kW / 64; ++u) q[lane + 64 * u] = qv[u];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    float sc = 0.0f;
+    const float* qq = q + 8 * (kChunks / 2) * half;
+#pragma unroll
+    for (int u = 0; u < kChunks / 2; ++u) {
+      const uint32_t* w4 = &rv[u].x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sc = fmaf(qq[8 * u + 2 * e], bf16lo(w4[e]), fmaf(qq[8 * u + 2 * e + 1], bf16hi(w4[e]), sc));
+    }
+    sc += __shfl_xor(sc, 32, 64);
+    if (rvalid) best = fmaxf(best, sc);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+  best = wave_max(best);
+  if (lane == 0 && best > -INFINITY) atomic_max_float(max_logit + h, best * scale);
+}
+
 hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const void* q, const void* cache,
                                 int64_t cap, const int32_t* lens, int batch, int tq, const void* w_kv_b,
                                 const void* gate, void* out, float* max_logit, bool init_max_logit, void* ws,
                                 hipStream_t st) {
   const AbsorbedWs L = absorbed_ws_layout(heads, batch, tq);
   char* base = static_cast<char*>(ws);
+  float* dlb = reinterpret_cast<float*>(base + L.dlb);
+  int32_t* dcnt = reinterpret_cast<int32_t*>(base + L.dcnt);
+  int4* dent = reinterpret_cast<int4*>(base + L.dent);
+  float* qn2 = reinterpret_cast<float*>(base + L.qn2);
+  float* hmax = reinterpret_cast<float*>(base + L.hmax);
+  uint16_t* qlo = reinterpret_cast<uint16_t*>(base + L.qlo);
   uint16_t* qabs = reinterpret_cast<uint16_t*>(base + L.qabs);
   int64_t* P = reinterpret_cast<int64_t*>(base + L.prefix);
   float* part_o = reinterpret_cast<float*>(base + L.part_o);
@@ -714,7 +1066,7 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
     TimedScope ts_("absorb_q", st);
     hipLaunchKernelGGL(absorb_q_kernel, dim3(heads, kR / 128), dim3(256), 0, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(w_kv_b), static_cast<int>(bt), heads, qabs, lens, tq, P, nflag,
-                       init_max_logit ? max_logit : nullptr);
+                       init_max_logit ? max_logit : nullptr, qn2, hmax, qlo);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -722,7 +1074,7 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
     TimedScope ts_("absorbed_split", st);
     hipLaunchKernelGGL(absorbed_split_kernel, dim3(kDecSplits, (heads + kDecHeadsPerWg - 1) / kDecHeadsPerWg), dim3(256), 0, st,
                        static_cast<const uint16_t*>(cache), cap, tq, heads, bt, P, qabs, scale, part_o, part_ml,
-                       nflag);
+                       nflag, qn2, dlb, dcnt, dent);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -740,15 +1092,22 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
       TimedScope ts_("absorbed_combine", st);
       hipLaunchKernelGGL(absorbed_combine_kernel<true>, cg, dim3(256), 0, st, P, bt, heads, scale,
                          part_o, part_ml, static_cast<const uint16_t*>(w_kv_b),
-                         static_cast<const uint16_t*>(gate), out, max_logit);
+                         static_cast<const uint16_t*>(gate), out, hmax);
     }
   } else {
     {
       TimedScope ts_("absorbed_combine", st);
       hipLaunchKernelGGL(absorbed_combine_kernel<false>, cg, dim3(256), 0, st, P, bt, heads, scale,
                          part_o, part_ml, static_cast<const uint16_t*>(w_kv_b),
-                         static_cast<const uint16_t*>(gate), out, max_logit);
+                         static_cast<const uint16_t*>(gate), out, hmax);
     }
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    TimedScope ts_("absorbed_refine", st);
+    hipLaunchKernelGGL(absorbed_refine_kernel, dim3(heads, kRefSplit), dim3(256), 0, st, heads, dlb, dcnt, dent,
+                       hmax, qabs, qlo, static_cast<const uint16_t*>(cache), cap, tq, scale, max_logit);
   }
   return hipGetLastError();
 }

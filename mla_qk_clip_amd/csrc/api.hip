@@ -171,6 +171,7 @@ mla_status mla_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_
     return fail(MLA_ERR_UNSUPPORTED, "fp32 inputs produce fp32 outputs only");
   if (batch < 0 || tq < 1) return fail(MLA_ERR_INVALID, "batch must be >= 0 and tq >= 1");
   if (cap < tq) return fail(MLA_ERR_INVALID, "cap (%lld) must be >= tq (%d)", static_cast<long long>(cap), tq);
+  if (cap > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "cap above 2^31 - 1");
   if (accumulate != 0 && accumulate != 1) return fail(MLA_ERR_INVALID, "accumulate must be 0 or 1");
   if (in_dtype == MLA_BF16 && s.H > mla::kDecMaxHeads)
     return fail(MLA_ERR_UNSUPPORTED, "bf16 absorbed kernel supports up to %d heads", mla::kDecMaxHeads);

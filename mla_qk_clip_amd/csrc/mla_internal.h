@@ -75,8 +75,22 @@ inline size_t prefill_f32_ws(int heads, int64_t ntok, int N, int V) {
 }
 
 // Workspace layout of the bf16 absorbed path.
+// Workspace of the bf16 absorbed form. Besides q_abs, the prefix sums and
+// the split-K partials it holds what the max-logit refinement needs:
+//   qlo  [bt][H][R]  bf16 rounding residual of the first R entries of q_abs
+//   dlb  [G][H]      per split workgroup and head: a lower bound of the
+//                    head's exact max logit (raw) from the workgroup's tiles
+//   dcnt [G][H]      live entries in dent (kDecList + 1: the list overflowed)
+//   dent [G][H][kDecList]  {virtual sequence, first row in the sequence,
+//                    rows, bits of an upper bound of the tile's exact max
+//                    logit (raw)} for the 32-row tiles that can reach the bound
+//   qn2  [H][4]      per head and 128-column block of q_abs: max over the
+//                    virtual sequences of the block's squared norm (block 0
+//                    also holds the q^R part)
+//   hmax [H]         approximate max logit (raw) per head
+constexpr int kDecList = 32;   // candidate tiles a split workgroup keeps per head
 struct AbsorbedWs {
-  size_t qabs, prefix, nflag, part_o, part_ml, total;
+  size_t qabs, qlo, prefix, nflag, part_o, part_ml, dlb, dcnt, dent, qn2, hmax, total;
   int64_t slots;
 };
 inline AbsorbedWs absorbed_ws_layout(int heads, int batch, int tq) {
@@ -85,10 +99,16 @@ inline AbsorbedWs absorbed_ws_layout(int heads, int batch, int tq) {
   w.slots = kDecSplits + bt;
   size_t off = 0;
   w.qabs = off; off = align_up(off + static_cast<size_t>(bt) * heads * (kR + kS) * 2, 256);
+  w.qlo = off; off = align_up(off + static_cast<size_t>(bt) * heads * kR * 2, 256);
   w.prefix = off; off = align_up(off + static_cast<size_t>(bt + 1) * 8, 256);
   w.nflag = off; off = align_up(off + 4, 256);   // count of segments the fix-up kernel must redo
   w.part_o = off; off = align_up(off + static_cast<size_t>(w.slots) * heads * kR * 4, 256);
   w.part_ml = off; off = align_up(off + static_cast<size_t>(w.slots) * heads * 4 * 4, 256);
+  w.dlb = off; off = align_up(off + static_cast<size_t>(kDecSplits) * heads * 4, 256);
+  w.dcnt = off; off = align_up(off + static_cast<size_t>(kDecSplits) * heads * 4, 256);
+  w.dent = off; off = align_up(off + static_cast<size_t>(kDecSplits) * heads * kDecList * 16, 256);
+  w.qn2 = off; off = align_up(off + static_cast<size_t>(heads) * 4 * 4, 256);
+  w.hmax = off; off = align_up(off + static_cast<size_t>(heads) * 4, 256);
   w.total = off;
   return w;
 }
