@@ -361,17 +361,31 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
   __shared__ uint4 V0[kVTile];
   __shared__ uint4 V1[kVTile];
 
-  // ---- work item: blocks that share a head run on the same XCD ----
+  // ---- work item. Blocks are dealt to the 8 XCDs in turn. With 8 heads or
+  // more, XCD x owns the heads [x H / 8, (x + 1) H / 8) (so a head's K and V
+  // stay in one L2) and takes them two at a time, the two heads' query tiles
+  // interleaved in the tile order (longest first): the heaviest tiles of
+  // every pair start early, which evens out the end of the launch, while only
+  // two heads' K and V are being read at a time. With fewer heads the
+  // (head, tile) items are split evenly over the XCDs. ----
   const int ntiles = hdr[0];
-  const int total = ntiles * heads;
-  const int per_xcd = (total + 7) >> 3;
   const int b = blockIdx.x;
-  const int slot = b >> 3;
-  if (slot >= per_xcd) return;
-  const int item = (b & 7) * per_xcd + slot;
-  if (item >= total) return;
-  const int head = item / ntiles;
-  const int tile = item - head * ntiles;
+  const int x = b & 7, slot = b >> 3;
+  int head, tile;
+  if (heads >= 8) {
+    const int h0 = x * heads / 8, nh = (x + 1) * heads / 8 - h0;
+    if (slot >= nh * ntiles) return;
+    const int pair = slot / (2 * ntiles), rem = slot - pair * 2 * ntiles;
+    const int two = min(2, nh - 2 * pair);
+    tile = rem / two;
+    head = h0 + 2 * pair + (rem - tile * two);
+  } else {
+    const int total = ntiles * heads, per_xcd = (total + 7) >> 3;
+    const int item = x * per_xcd + slot;
+    if (slot >= per_xcd || item >= total) return;
+    head = item / ntiles;
+    tile = item - head * ntiles;
+  }
   int lo = 0, hi = nseq - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -960,10 +974,10 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // upper bound on query tiles: sum over sequences of ceil(L/128) <= ntok/128 + nseq
+  // upper bound on query tiles: sum over sequences of ceil(L/128) <= ntok/128 + nseq;
+  // 8 XCDs with up to ceil(heads / 8) heads (or items) each
   const int64_t tiles_max = (ntok + kPrefBM - 1) / kPrefBM + nseq;
-  const int64_t total_max = tiles_max * heads;
-  const int64_t grid = ((total_max + 7) / 8) * 8;
+  const int64_t grid = 8 * tiles_max * ((heads + 7) / 8);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (out_bf16) {
     {
