@@ -109,6 +109,24 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _expect(name: str, t, shape, dtype, optional: bool = False):
+    """The C ABI takes bare pointers and trusts the sizes it is given, so the
+    binding checks every tensor against them first: a wrong shape, dtype or
+    device raises here instead of letting a kernel read past a buffer."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
@@ -135,15 +153,29 @@ def mla_prefill(dims: Dims, q, ckv, ks, w_kv_b, gate, cu_seqlens, *, out_dtype=N
     """
     in_dt = _dt(q)
     out_dt = MLA_F32 if out_dtype is None else (MLA_BF16 if out_dtype == torch.bfloat16 else MLA_F32)
+    if out is not None and out_dtype is None:
+        out_dt = _dt(out)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [T, H, N+S], got shape {tuple(q.shape)}")
     T = q.shape[0]
+    H, R, S = dims.heads, dims.kv_rank, dims.shared_dim
     nseq = cu_seqlens.numel() - 1
     dev = q.device
+    _expect("q", q, (T, H, dims.qk_dim), q.dtype)
+    _expect("ckv", ckv, (T, R), q.dtype)
+    _expect("ks", ks, (T, S), q.dtype)
+    _expect("w_kv_b", w_kv_b, (H * (dims.nope_dim + dims.v_dim), R), q.dtype)
+    _expect("gate", gate, (T, H * dims.v_dim), q.dtype, optional=True)
+    _expect("cu_seqlens", cu_seqlens, (nseq + 1,), torch.int32)
     if out is None:
         out = torch.empty((T, dims.heads * dims.v_dim), dtype=_torch_dt(out_dt), device=dev)
     if lse is None and want_lse:
         lse = torch.empty((dims.heads, T), dtype=torch.float32, device=dev)
     if max_logit is None:
         max_logit = torch.empty(dims.heads, dtype=torch.float32, device=dev)
+    _expect("out", out, (T, H * dims.v_dim), _torch_dt(out_dt))
+    _expect("lse", lse, (H, T), torch.float32, optional=True)
+    _expect("max_logit", max_logit, (H,), torch.float32)
     need = mla_prefill_workspace_size(dims, in_dt, T, nseq)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -163,13 +195,26 @@ def mla_absorbed(dims: Dims, q, cache, lens, w_kv_b, gate, *, out_dtype=None, ou
     """
     in_dt = _dt(q)
     out_dt = in_dt if out_dtype is None else (MLA_BF16 if out_dtype == torch.bfloat16 else MLA_F32)
+    if out is not None and out_dtype is None:
+        out_dt = _dt(out)
+    if q.dim() != 4 or cache.dim() != 3:
+        raise ValueError(f"q must be [B, Tq, H, N+S] and cache [B, cap, R+S], got {tuple(q.shape)}, "
+                         f"{tuple(cache.shape)}")
     B, Tq = q.shape[0], q.shape[1]
     cap = cache.shape[1]
+    H, R = dims.heads, dims.kv_rank
     dev = q.device
+    _expect("q", q, (B, Tq, H, dims.qk_dim), q.dtype)
+    _expect("cache", cache, (B, cap, R + dims.shared_dim), q.dtype)
+    _expect("lens", lens, (B,), torch.int32)
+    _expect("w_kv_b", w_kv_b, (H * (dims.nope_dim + dims.v_dim), R), q.dtype)
+    _expect("gate", gate, (B, Tq, H * dims.v_dim), q.dtype, optional=True)
     if out is None:
         out = torch.empty((B, Tq, dims.heads * dims.v_dim), dtype=_torch_dt(out_dt), device=dev)
     if max_logit is None:
         max_logit = torch.empty(dims.heads, dtype=torch.float32, device=dev)
+    _expect("out", out, (B, Tq, H * dims.v_dim), _torch_dt(out_dt))
+    _expect("max_logit", max_logit, (H,), torch.float32)
     need = mla_absorbed_workspace_size(dims, in_dt, B, Tq)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -186,10 +231,18 @@ def mla_qk_clip(dims: Dims, w_q_b, w_kv_b, max_logit, tau: float, *, clipped=Non
     Returns (clipped uint8 [H], gamma fp32 [H]).
     """
     dev = w_q_b.device
+    H = dims.heads
+    if w_q_b.dim() != 2:
+        raise ValueError(f"w_q_b must be [H*(N+S), q_in], got shape {tuple(w_q_b.shape)}")
+    _expect("w_q_b", w_q_b, (H * dims.qk_dim, w_q_b.shape[1]), w_q_b.dtype)
+    _expect("w_kv_b", w_kv_b, (H * (dims.nope_dim + dims.v_dim), dims.kv_rank), w_q_b.dtype)
+    _expect("max_logit", max_logit, (H,), torch.float32)
     if clipped is None:
-        clipped = torch.empty(dims.heads, dtype=torch.uint8, device=dev)
+        clipped = torch.empty(H, dtype=torch.uint8, device=dev)
     if gamma is None:
-        gamma = torch.empty(dims.heads, dtype=torch.float32, device=dev)
+        gamma = torch.empty(H, dtype=torch.float32, device=dev)
+    _expect("clipped", clipped, (H,), torch.uint8)
+    _expect("gamma", gamma, (H,), torch.float32)
     st = lib.mla_qk_clip(ctypes.byref(dims.c()), _dt(w_q_b), _ptr(w_q_b), w_q_b.shape[1], _ptr(w_kv_b),
                          _ptr(max_logit), float(tau), _ptr(clipped), _ptr(gamma), _stream(stream))
     _check(st)

@@ -107,3 +107,19 @@ def test_workspace_sizes(m):
     assert a >= 96 * 256 * 2 * 4096 and b >= 96 * 256 * 2 * 59392
     assert m.mla_absorbed_workspace_size(K3, m.MLA_BF16, 64, 1) > 0
     assert m.mla_prefill_workspace_size(m.Dims(0), m.MLA_BF16, 10, 1) == 0
+
+
+def test_binding_rejects_host_tensors_before_any_launch(m):
+    """The binding checks every tensor against the sizes it passes to the C ABI
+    (which takes bare pointers): host tensors are refused before any call."""
+    import torch
+    d = m.Dims(heads=2, kv_rank=16, shared_dim=8, nope_dim=8, v_dim=8)
+    T = 5
+    q = torch.zeros((T, 2, 16), dtype=torch.float32)
+    ckv, ks = torch.zeros((T, 16)), torch.zeros((T, 8))
+    w = torch.zeros((2 * 16, 16))
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensor"):
+        m.mla_prefill(d, q, ckv, ks, w, None, cu)
+    with pytest.raises(ValueError, match="device tensor"):
+        m.mla_absorbed(d, q[None, :1], torch.zeros((1, 8, 24)), torch.tensor([8], dtype=torch.int32), w, None)

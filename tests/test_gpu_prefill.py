@@ -168,3 +168,22 @@ def test_bf16_bitwise_deterministic(lib):
     o1, l1, m1 = run_prefill(p)
     o2, l2, m2 = run_prefill(p)
     assert bool((o1 == o2).all()) and bool((l1 == l2).all()) and bool((m1 == m2).all())
+
+
+def test_binding_rejects_wrong_shapes(lib):
+    """Sizes the C ABI trusts are checked against the tensors first: a short
+    or missing operand raises instead of being read past its end."""
+    import torch
+    import mla_qk_clip_amd as m
+    d = m.Dims()
+    T = 64
+    z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device="cuda")  # noqa: E731
+    q, ckv, ks, w, g = z(T, 96, 192), z(T, 512), z(T, 64), z(96 * 256, 512), z(T, 96 * 128)
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError, match="ckv has shape"):
+        m.mla_prefill(d, q, ckv[:T - 1], ks, w, g, cu)
+    with pytest.raises(ValueError, match="q must be"):
+        m.mla_prefill(d, z(1)[0], ckv, ks, w, g, cu)
+    with pytest.raises(ValueError, match="gate has shape"):
+        m.mla_absorbed(d, q[None, :1], z(1, 128, 576), torch.tensor([128], dtype=torch.int32, device="cuda"), w,
+                       g[None, :1, :100])
