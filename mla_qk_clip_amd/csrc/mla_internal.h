@@ -37,20 +37,18 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 //                                        positions 8u..8u+7 of the tile
 //   ksp[tile][8 units][64 rows][8]       k^S (shared by all heads)
 struct PrefillWs {
-  size_t kc, vt, ksp, pcu, order, toff, hdr, rowmax, aux, cand, total;
+  size_t kc, vt, ksp, pcu, order, toff, hdr, rowmax, aux, cand, qx, qmeta, total;
   int64_t npad_max;
 };
 constexpr int kTileElems = kPrefBN * kN;  // elements of one K^C (or V^T) tile of one head
 // aux[h][0] = approximate (raw, unscaled) head max logit, aux[h][1] = max |q_t|^2,
 // aux[h][2] = max |K^C_s|^2 (bf16 values), aux[h][3] unused; aux[H][0] = max |k^S_s|^2.
 constexpr int kAuxStride = 4;
-// Max-logit refinement candidates per head: [0] pair count, [1] overflow flag,
-// [2] row count, then kRefRows (row, sequence start) and kRefKeys (row, key) pairs.
+// Max-logit refinement candidates per head: [0] unused, [1] overflow flag,
+// [2] row count, [3] unused, then kRefRows (row, sequence start) pairs.
 constexpr int kRefRows = 64;
-constexpr int kRefKeys = 256;
 constexpr int kCandRows = 4;
-constexpr int kCandPairs = kCandRows + 2 * kRefRows;
-constexpr int kCandStride = kCandPairs + 2 * kRefKeys;
+constexpr int kCandStride = kCandRows + 2 * kRefRows;
 inline PrefillWs prefill_ws_layout(int heads, int64_t ntok, int nseq) {
   PrefillWs w{};
   w.npad_max = static_cast<int64_t>(align_up(static_cast<size_t>(ntok + static_cast<int64_t>(kSeqPad) * nseq), 256));
@@ -65,6 +63,9 @@ inline PrefillWs prefill_ws_layout(int heads, int64_t ntok, int nseq) {
   w.rowmax = off; off = align_up(off + static_cast<size_t>(heads) * ntok * 4, 256);
   w.aux = off; off = align_up(off + static_cast<size_t>(heads + 1) * kAuxStride * 4, 256);
   w.cand = off; off = align_up(off + static_cast<size_t>(heads) * kCandStride * 4, 256);
+  // listed rows of all heads, numbered densely: q_abs as bf16 hi | lo parts, and {row, sequence start, head}
+  w.qx = off; off = align_up(off + static_cast<size_t>(heads) * kRefRows * (kR + kS) * 2 * 2, 256);
+  w.qmeta = off; off = align_up(off + static_cast<size_t>(heads) * kRefRows * 16, 256);
   w.total = off;
   return w;
 }

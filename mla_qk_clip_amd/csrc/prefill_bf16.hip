@@ -756,13 +756,16 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
 // Every logit satisfies |approx - exact| <= delta with
 //   delta = (2^-8 * 1.01 + 3e-5) * max_t |q_t| * max_s |K_s|
 // (bf16 rounding of K^C plus fp32 accumulation), hence the exact maximum E
-// lies in [M - delta, M + delta] for the approximate maximum M, and its pair
-// has an approximate logit >= M - 2 delta. Three small launches:
+// lies in [M - delta, M + delta] for the approximate maximum M, and its row
+// has an approximate row max >= M - 2 delta. Three small launches:
 //   rows : rows whose approximate row max reaches M - 2 delta (per head);
-//   pairs: every key (one thread each) re-scored against those rows with the
-//          stored bf16 K^C; pairs reaching M - 2 delta are listed;
-//   exact: one workgroup per listed pair recomputes its logit in fp32 from
-//          c^KV and kv_b_proj (K^C_s = c_s W_UK_h) and takes the maximum.
+//   qabs : for each listed row t of head h, q_abs = [W_UK_h^T q^C_t, q^R_t]
+//          in fp32 (K^C_s . q^C_t = c_s . q_abs by associativity), stored as
+//          bf16 hi and lo parts (about 16 significant bits together), in the
+//          order the score kernel's MFMA operands are loaded;
+//   score: every key of every listed row (its sequence, up to the row) is
+//          scored against hi and lo with MFMAs over the shared [c^KV | k^S]
+//          rows, fp32 accumulation, and the maximum taken.
 // Too many candidates (near-ties, e.g. q = 0) fall back to M, which is then
 // within delta of E.
 // ---------------------------------------------------------------------------
@@ -775,7 +778,6 @@ __device__ __forceinline__ float refine_threshold(const float* aux, int h, int h
 }
 
 constexpr int kRefRowSplit = 8;     // workgroups per head scanning row maxima
-constexpr int kRefExactSplit = 16;  // workgroups per head recomputing listed pairs
 
 __device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int t) {
   int lo = 0, hi = nseq - 1;
@@ -809,119 +811,179 @@ __global__ void __launch_bounds__(256) prefill_refine_rows_kernel(const int32_t*
   }
 }
 
-__global__ void __launch_bounds__(256) prefill_refine_pairs_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ks, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ pcu, int nseq, int heads, int64_t ntok, int64_t npad_max,
-    const uint16_t* __restrict__ kc, const float* __restrict__ aux, int32_t* __restrict__ cand) {
-  __shared__ float qs[kRefRows][kD];
-  __shared__ int rt[kRefRows], ra[kRefRows];
-  const int h = blockIdx.x;
-  float M;
-  const float thr = refine_threshold(aux, h, heads, &M);
-  if (!(M > -INFINITY)) return;
-  int32_t* c = cand + static_cast<size_t>(h) * kCandStride;
-  if (c[1] != 0) return;
-  const int nrows = min(c[2], kRefRows);
-  const int tid = threadIdx.x;
-  for (int i = tid; i < nrows * kD; i += 256) {
-    const int r = i / kD, e = i - r * kD;
-    qs[r][e] = bf16_to_f32(q[(static_cast<size_t>(c[kCandRows + 2 * r]) * heads + h) * kD + e]);
-  }
-  if (tid < nrows) {
-    rt[tid] = c[kCandRows + 2 * tid];
-    ra[tid] = c[kCandRows + 2 * tid + 1];
-  }
-  __syncthreads();
-  const int64_t s64 = static_cast<int64_t>(blockIdx.y) * 256 + tid;
-  if (s64 >= ntok) return;
-  const int s = static_cast<int>(s64);
-  bool any = false;
-  for (int r = 0; r < nrows; ++r) any |= (s >= ra[r] && s <= rt[r]);
-  if (!any) return;
-  // this key's stored [K^C | k^S] (tile-blocked K^C: unit u of row p at tile p/64, offset u*64*8 + (p%64)*8)
-  const int sq = seq_of(cu, nseq, s);
-  const int p = pcu[sq] + (s - cu[sq]);
-  const uint16_t* kr = kc + (static_cast<size_t>(h) * (npad_max / kPrefBN) + p / kPrefBN) * kTileElems + (p % kPrefBN) * 8;
-  uint4 x[kD / 8];
-#pragma unroll
-  for (int u = 0; u < kN / 8; ++u) x[u] = ldg16(kr + u * (kPrefBN * 8));
-#pragma unroll
-  for (int u = 0; u < kS / 8; ++u) x[kN / 8 + u] = ldg16(ks + static_cast<size_t>(s) * kS + 8 * u);
-  for (int r = 0; r < nrows; ++r) {
-    if (s < ra[r] || s > rt[r]) continue;
-    float acc = 0.0f;
-#pragma unroll
-    for (int u = 0; u < kD / 8; ++u) {
-      const uint32_t* w4 = &x[u].x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // K^C unit u holds features kperm(8u .. 8u+7); the k^S units are in natural order
-        const int f0 = u < kN / 8 ? kperm(8 * u + 2 * e) : 8 * u + 2 * e;
-        const int f1 = u < kN / 8 ? kperm(8 * u + 2 * e + 1) : 8 * u + 2 * e + 1;
-        acc = fmaf(qs[r][f0], bf16lo(w4[e]), fmaf(qs[r][f1], bf16hi(w4[e]), acc));
-      }
-    }
-    if (acc >= thr) {
-      const int k = atomicAdd(&c[0], 1);
-      if (k < kRefKeys) {
-        c[kCandPairs + 2 * k] = rt[r];
-        c[kCandPairs + 2 * k + 1] = s;
-      } else {
-        c[1] = 1;
-      }
-    }
-  }
+// Listed rows of head h (0 if the head's list overflowed: it falls back to M).
+__device__ __forceinline__ int listed_rows(const int32_t* cand, int h) {
+  const int32_t* c = cand + static_cast<size_t>(h) * kCandStride;
+  return c[1] != 0 ? 0 : min(c[2], kRefRows);
 }
 
-__global__ void __launch_bounds__(256) prefill_refine_exact_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ckv, const uint16_t* __restrict__ ks,
-    const uint16_t* __restrict__ w, int heads, const float* __restrict__ aux, const int32_t* __restrict__ cand,
-    float scale, float* __restrict__ max_logit) {
-  __shared__ float qrow[kD];
-  __shared__ float crow[kR];
-  __shared__ float red[4];
-  const int h = blockIdx.x, pi = blockIdx.y;
+// Grid (heads, kRefRows). Workgroup (h, r) forms q_abs of the r-th listed row
+// of head h: thread t takes columns 8 (t % 64) .. +7 over the W_UK_h rows
+// 32 (t / 64) .. +31 (all 32 loads in flight), the four partial sums of a
+// column are added in a fixed order. Rows of all heads are numbered densely
+// in head order. Workgroup (h, 0) of an overflowed head folds M in instead.
+__global__ void __launch_bounds__(256) prefill_refine_qabs_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ w, int heads, const float* __restrict__ aux,
+    const int32_t* __restrict__ cand, float scale, uint16_t* __restrict__ qx, int4* __restrict__ qmeta,
+    float* __restrict__ max_logit) {
+  __shared__ float qc[kN];
+  __shared__ __align__(16) float part[4][kR];
+  __shared__ int red[4];
+  const int h = blockIdx.x, r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float M;
-  refine_threshold(aux, h, heads, &M);
-  if (!(M > -INFINITY)) return;
   const int32_t* c = cand + static_cast<size_t>(h) * kCandStride;
-  const int nk = c[0];
-  const bool fallback = c[1] != 0 || nk == 0 || nk > kRefKeys;
-  if (fallback) {
-    if (pi == 0 && tid == 0) atomic_max_float(max_logit + h, M * scale);
+  const float M = aux[h * kAuxStride];
+  if (c[1] != 0 || c[2] > kRefRows) {
+    if (r == 0 && tid == 0 && M > -INFINITY) atomic_max_float(max_logit + h, M * scale);
     return;
   }
-  float best = -INFINITY;
-  for (int k = pi; k < nk; k += gridDim.y) {
-    const int t = c[kCandPairs + 2 * k], s = c[kCandPairs + 2 * k + 1];
-    __syncthreads();
-    if (tid < kD) qrow[tid] = bf16_to_f32(q[(static_cast<size_t>(t) * heads + h) * kD + tid]);
-    for (int e = tid; e < kR; e += 256) crow[e] = bf16_to_f32(ckv[static_cast<size_t>(s) * kR + e]);
-    __syncthreads();
-    // K^C_s[n] = sum_r c_s[r] * w[h*256 + n][r] in fp32; two threads per feature n
-    const int n = tid >> 1, part = tid & 1;
-    const uint16_t* wr = w + (static_cast<size_t>(h) * 256 + n) * kR + part * (kR / 2);
-    uint4 x[kR / 16];
+  if (r >= c[2]) return;
+  // dense index: listed rows of the heads before h (one thread per head), plus r
+  {
+    int v = 0;
+    for (int hh = tid; hh < h; hh += 256) v += listed_rows(cand, hh);
 #pragma unroll
-    for (int e = 0; e < kR / 16; ++e) x[e] = ldg16(wr + 8 * e);
-    float kcn = 0.0f;
-#pragma unroll
-    for (int e = 0; e < kR / 16; ++e) {
-      const uint32_t* w4 = &x[e].x;
-      const float* cr = crow + part * (kR / 2) + 8 * e;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) kcn = fmaf(cr[2 * u], bf16lo(w4[u]), fmaf(cr[2 * u + 1], bf16hi(w4[u]), kcn));
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) red[wave] = v;
   }
-    kcn += __shfl_xor(kcn, 1, 64);
-    float pr = part == 0 ? qrow[n] * kcn : 0.0f;
-    if (tid < kS) pr += qrow[kN + tid] * bf16_to_f32(ks[static_cast<size_t>(s) * kS + tid]);
-    pr = wave_sum(pr);
-    if (lane == 0) red[wave] = pr;
-    __syncthreads();
-    best = fmaxf(best, (red[0] + red[1]) + (red[2] + red[3]));
+  const int t = c[kCandRows + 2 * r], a0 = c[kCandRows + 2 * r + 1];
+  const uint16_t* qt = q + (static_cast<size_t>(t) * heads + h) * kD;
+  const int cg = tid & 63, kg = tid >> 6;
+  uint4 wv[32];
+  const uint16_t* wr = w + (static_cast<size_t>(h) * (kN + kV) + 32 * kg) * kR + 8 * cg;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) wv[u] = ldg16(wr + static_cast<size_t>(u) * kR);
+  if (tid < kN) qc[tid] = bf16_to_f32(qt[tid]);
+  __syncthreads();
+  const int n = r + (red[0] + red[1]) + (red[2] + red[3]);
+  {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const float x = qc[32 * kg + u];
+      const uint32_t* w4 = &wv[u].x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(x, bf16lo(w4[e]), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(x, bf16hi(w4[e]), acc[2 * e + 1]);
+      }
+    }
+    float4* dst = reinterpret_cast<float4*>(&part[kg][8 * cg]);
+    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
-  if (tid == 0 && best > -INFINITY) atomic_max_float(max_logit + h, best * scale);
+  __syncthreads();
+  // Operand order: group n / 32, k-step kk = col / 16, lane 32 (col / 8 % 2)
+  // + n % 32, element col % 8; hi and lo are separate planes.
+  auto at = [&](int col) {
+    return ((static_cast<size_t>(n >> 5) * ((kR + kS) / 16) + col / 16) * 64 + 32 * ((col >> 3) & 1) + (n & 31)) * 8 +
+           (col & 7);
+  };
+  uint16_t* lo = qx + static_cast<size_t>(heads) * kRefRows * (kR + kS);
+  for (int col = tid; col < kR; col += 256) {
+    const float v = (part[0][col] + part[1][col]) + (part[2][col] + part[3][col]);
+    const uint16_t vh = f32_to_bf16(v);
+    qx[at(col)] = vh;
+    lo[at(col)] = f32_to_bf16(v - bf16_to_f32(vh));
+  }
+  if (tid < kS) {   // q^R is bf16 already
+    qx[at(kR + tid)] = qt[kN + tid];
+    lo[at(kR + tid)] = 0;
+  }
+  if (tid == 0) qmeta[n] = make_int4(t, a0, h, 0);
+}
+
+constexpr int kScoreBlocks = 512;
+
+// Grid (kScoreBlocks), persistent over units (group of 32 listed rows, 128
+// consecutive keys). A unit's B operands (the group's q_abs hi and lo planes,
+// 72 KB) are copied into LDS once; wave w then scores keys 32 w .. +31 of the
+// unit: S = [c^KV | k^S]_keys (hi + lo)^T with 32x32x16 bf16 MFMAs (A: key
+// rows from memory, loaded in three batches of 12 k-steps ahead of their
+// MFMAs), and each listed row's maximum over its keys (same sequence, up to
+// the row) is folded into the head's max logit. Units whose keys no listed
+// row of the group reaches are skipped.
+__global__ void __launch_bounds__(256) prefill_refine_score_kernel(
+    const uint16_t* __restrict__ ckv, const uint16_t* __restrict__ ks, int64_t ntok, int heads,
+    const int32_t* __restrict__ cand, const uint16_t* __restrict__ qx, const int4* __restrict__ qmeta, float scale,
+    float* __restrict__ max_logit) {
+  constexpr int kSteps = (kR + kS) / 16;   // 36
+  __shared__ __align__(16) uint4 bl[2][kSteps * 64];   // [hi | lo][k-step][lane]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  int ntot = 0;
+  for (int hh = lane; hh < heads; hh += 64) ntot += listed_rows(cand, hh);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ntot += __shfl_xor(ntot, o, 64);
+  if (ntot == 0) return;
+  const int ncg = (ntot + 31) / 32;
+  const int64_t nkb = (ntok + 127) / 128;
+  const int64_t units = nkb * ncg;
+  const size_t plane = static_cast<size_t>(heads) * kRefRows * (kR + kS);
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int cgp = static_cast<int>(u / nkb);
+    const int64_t kb0 = 128 * (u - static_cast<int64_t>(cgp) * nkb);
+    const int n = 32 * cgp + l32;
+    const bool nvalid = n < ntot;
+    const int4 mt = qmeta[nvalid ? n : 0];
+    const int t = mt.x, a0 = mt.y, h = mt.z;
+    const int64_t k0 = kb0 + 32 * wave;
+    const bool hit = nvalid && a0 <= k0 + 31 && t >= k0 && k0 < ntok;
+    // block-uniform skip; the barrier also orders the previous unit's reads
+    // of bl before this unit's writes
+    if (!__syncthreads_or(hit ? 1 : 0)) continue;
+    {
+      const uint4* src = reinterpret_cast<const uint4*>(qx) + static_cast<size_t>(cgp) * kSteps * 64;
+      const uint4* srl = reinterpret_cast<const uint4*>(qx + plane) + static_cast<size_t>(cgp) * kSteps * 64;
+      uint4 x[2 * kSteps * 64 / 256];
+#pragma unroll
+      for (int i = 0; i < kSteps * 64 / 256; ++i) {
+        x[i] = src[tid + 256 * i];
+        x[kSteps * 64 / 256 + i] = srl[tid + 256 * i];
+      }
+#pragma unroll
+      for (int i = 0; i < kSteps * 64 / 256; ++i) {
+        bl[0][tid + 256 * i] = x[i];
+        bl[1][tid + 256 * i] = x[kSteps * 64 / 256 + i];
+      }
+    }
+    __syncthreads();
+    if (__ballot(hit) == 0) continue;
+    const int64_t s = min(k0 + l32, ntok - 1);   // this lane's key (A row)
+    const uint16_t* crow = ckv + s * kR + 8 * g;
+    const uint16_t* srow = ks + s * kS + 8 * g;
+    f32x16 acc = f32x16{};
+    static_for<0, 3>([&](auto bb) {
+      constexpr int k0b = 12 * decltype(bb)::value;
+      uint4 av[12];
+      static_for<0, 12>([&](auto uu) {
+        constexpr int kk = k0b + decltype(uu)::value;
+        av[uu] = kk < kR / 16 ? ldg16(crow + 16 * kk) : ldg16(srow + 16 * (kk - kR / 16));
+      });
+      static_for<0, 12>([&](auto uu) {
+        constexpr int kk = k0b + decltype(uu)::value;
+        acc = mfma32(as_bf16x8(av[uu]), as_bf16x8(bl[0][kk * 64 + lane]), acc);
+        acc = mfma32(as_bf16x8(av[uu]), as_bf16x8(bl[1][kk * 64 + lane]), acc);
+      });
+      __builtin_amdgcn_sched_group_barrier(0x020, 12, decltype(bb)::value);
+      __builtin_amdgcn_sched_group_barrier(0x100, 24, decltype(bb)::value);
+      __builtin_amdgcn_sched_group_barrier(0x008, 24, decltype(bb)::value);
+    });
+    float best = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t key = k0 + acc_row(e, g);
+      if (key >= a0 && key <= t && key < ntok) best = fmaxf(best, acc[e]);
+    }
+    best = fmaxf(best, __shfl_xor(best, 32, 64));
+    // Atomics only where they raise the slot: its value only grows, so a
+    // stale read can only cost an extra atomic. (One atomic per row and item
+    // on the few dozen head slots would serialise in the L2.)
+    if (g == 0 && nvalid && best > -INFINITY) {
+      const float v = best * scale;
+      if (v > *reinterpret_cast<volatile const float*>(max_logit + h)) atomic_max_float(max_logit + h, v);
+    }
+  }
 }
 
 __global__ void prefill_aux_init_kernel(float* aux, int32_t* cand, int heads) {
@@ -1005,20 +1067,21 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  uint16_t* qx = reinterpret_cast<uint16_t*>(base + L.qx);
+  int4* qmeta = reinterpret_cast<int4*>(base + L.qmeta);
   {
-    TimedScope ts_("prefill_refine_pairs", st);
-    hipLaunchKernelGGL(prefill_refine_pairs_kernel, dim3(heads, static_cast<unsigned>((ntok + 255) / 256)), dim3(256),
-                       0, st, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(ks), cu, pcu, nseq, heads,
-                       ntok, L.npad_max, kc, aux, cand);
+    TimedScope ts_("prefill_refine_qabs", st);
+    hipLaunchKernelGGL(prefill_refine_qabs_kernel, dim3(heads, kRefRows), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(w_kv_b), heads, aux, cand, scale,
+                       qx, qmeta, max_logit);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    TimedScope ts_("prefill_refine_exact", st);
-    hipLaunchKernelGGL(prefill_refine_exact_kernel, dim3(heads, kRefExactSplit), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(ckv),
-                       static_cast<const uint16_t*>(ks), static_cast<const uint16_t*>(w_kv_b), heads, aux, cand, scale,
-                       max_logit);
+    TimedScope ts_("prefill_refine_score", st);
+    hipLaunchKernelGGL(prefill_refine_score_kernel, dim3(kScoreBlocks), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(ckv), static_cast<const uint16_t*>(ks), ntok, heads, cand, qx,
+                       qmeta, scale, max_logit);
   }
   return hipGetLastError();
 }
