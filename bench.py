@@ -214,7 +214,7 @@ def main():
         step()
     torch.cuda.synchronize()
     kern = {}
-    for k in ("fill", "prefill_aux_init", "prefill_plan", "prefill_expand", "prefill_attn", "prefill_refine_rows", "prefill_refine_qabs",
+    for k in ("fill", "prefill_plan", "prefill_expand", "prefill_attn", "prefill_refine_rows",
               "prefill_refine_score", "qk_clip", "absorb_q", "absorbed_split",
               "absorbed_fixup", "absorbed_combine", "absorbed_refine"):
         tot, n = m.mla_timing_read(k)

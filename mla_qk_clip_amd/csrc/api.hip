@@ -133,14 +133,16 @@ mla_status mla_prefill(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_d
   }
 
   hipError_t e = hipSuccess;
-  if (!accumulate) {
+  // the bf16 path clears the max-logit slots in its first kernel
+  const bool fused_init = in_dtype == MLA_BF16 && total_tokens > 0;
+  if (!accumulate && !fused_init) {
     e = mla::launch_fill(max_logit, s.H, -INFINITY, stream);
     if (e != hipSuccess) return hip_fail(e, "max_logit init");
   }
   if (total_tokens == 0) return MLA_OK;
   if (in_dtype == MLA_BF16) {
     e = mla::launch_prefill_bf16(s.H, s.scale, out_dtype == MLA_BF16, q, ckv, ks, w_kv_b, gate, cu_seqlens, nseq,
-                                 total_tokens, out, lse, max_logit, workspace, stream);
+                                 total_tokens, out, lse, max_logit, !accumulate, workspace, stream);
   } else {
     e = mla::launch_prefill_f32(s.H, s.R, s.S, s.N, s.V, s.scale, static_cast<const float*>(q),
                                 static_cast<const float*>(ckv), static_cast<const float*>(ks),

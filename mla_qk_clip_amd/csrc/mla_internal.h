@@ -44,11 +44,12 @@ constexpr int kTileElems = kPrefBN * kN;  // elements of one K^C (or V^T) tile o
 // aux[h][0] = approximate (raw, unscaled) head max logit, aux[h][1] = max |q_t|^2,
 // aux[h][2] = max |K^C_s|^2 (bf16 values), aux[h][3] unused; aux[H][0] = max |k^S_s|^2.
 constexpr int kAuxStride = 4;
-// Max-logit refinement candidates per head: [0] unused, [1] overflow flag,
-// [2] row count, [3] unused, then kRefRows (row, sequence start) pairs.
+// Max-logit refinement state (int32): [0] listed rows of all heads (they are
+// numbered densely), [1..3] unused, then per head the number of its rows that
+// reached the threshold (kCandHeadCount + h); a head with more than kRefRows
+// falls back to the approximate maximum.
 constexpr int kRefRows = 64;
-constexpr int kCandRows = 4;
-constexpr int kCandStride = kCandRows + 2 * kRefRows;
+constexpr int kCandHeadCount = 4;
 inline PrefillWs prefill_ws_layout(int heads, int64_t ntok, int nseq) {
   PrefillWs w{};
   w.npad_max = static_cast<int64_t>(align_up(static_cast<size_t>(ntok + static_cast<int64_t>(kSeqPad) * nseq), 256));
@@ -62,7 +63,7 @@ inline PrefillWs prefill_ws_layout(int heads, int64_t ntok, int nseq) {
   w.hdr = off; off = align_up(off + 64, 256);
   w.rowmax = off; off = align_up(off + static_cast<size_t>(heads) * ntok * 4, 256);
   w.aux = off; off = align_up(off + static_cast<size_t>(heads + 1) * kAuxStride * 4, 256);
-  w.cand = off; off = align_up(off + static_cast<size_t>(heads) * kCandStride * 4, 256);
+  w.cand = off; off = align_up(off + static_cast<size_t>(kCandHeadCount + heads) * 4, 256);
   // listed rows of all heads, numbered densely: q_abs as bf16 hi | lo parts, and {row, sequence start, head}
   w.qx = off; off = align_up(off + static_cast<size_t>(heads) * kRefRows * (kR + kS) * 2 * 2, 256);
   w.qmeta = off; off = align_up(off + static_cast<size_t>(heads) * kRefRows * 16, 256);
@@ -121,7 +122,8 @@ hipError_t launch_fill(float* p, int n, float v, hipStream_t st);
 hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16,
                                const void* q, const void* ckv, const void* ks, const void* w_kv_b,
                                const void* gate, const int32_t* cu, int nseq, int64_t ntok,
-                               void* out, float* lse, float* max_logit, void* ws, hipStream_t st);
+                               void* out, float* lse, float* max_logit, bool init_max_logit, void* ws,
+                               hipStream_t st);
 
 hipError_t launch_prefill_f32(int heads, int R, int S, int N, int V, float scale,
                               const float* q, const float* ckv, const float* ks, const float* w_kv_b,

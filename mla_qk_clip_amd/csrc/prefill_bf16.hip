@@ -21,6 +21,8 @@ namespace mla {
 // Plan: pcu[s] = start of sequence s in the padded workspace (each sequence
 // rounded up to 64 rows), order[] = sequences by descending length, toff[r] =
 // first query tile of the r-th sequence in that order, hdr = {tiles, padded rows}.
+// The same single workgroup also clears the max-logit refinement state and,
+// unless the caller accumulates, sets the max-logit slots to -inf.
 // ---------------------------------------------------------------------------
 constexpr int kPlanSortMax = 4096;
 
@@ -28,8 +30,15 @@ __global__ void __launch_bounds__(256) prefill_plan_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ pcu,
                                                            int32_t* __restrict__ order,
                                                            int32_t* __restrict__ toff,
-                                                           int32_t* __restrict__ hdr) {
+                                                           int32_t* __restrict__ hdr, int heads,
+                                                           float* __restrict__ aux, int32_t* __restrict__ cand,
+                                                           float* __restrict__ ml_init) {
   __shared__ int s_order[kPlanSortMax];
+  for (int i = threadIdx.x; i < (heads + 1) * kAuxStride; i += blockDim.x)
+    aux[i] = ((i % kAuxStride) == 0 && i < heads * kAuxStride) ? -INFINITY : 0.0f;
+  for (int i = threadIdx.x; i < kCandHeadCount + heads; i += blockDim.x) cand[i] = 0;
+  if (ml_init)
+    for (int i = threadIdx.x; i < heads; i += blockDim.x) ml_init[i] = -INFINITY;
   const bool sort = nseq <= kPlanSortMax;
   if (sort) {
     for (int s = threadIdx.x; s < nseq; s += blockDim.x) {
@@ -757,12 +766,12 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
 //   delta = (2^-8 * 1.01 + 3e-5) * max_t |q_t| * max_s |K_s|
 // (bf16 rounding of K^C plus fp32 accumulation), hence the exact maximum E
 // lies in [M - delta, M + delta] for the approximate maximum M, and its row
-// has an approximate row max >= M - 2 delta. Three small launches:
-//   rows : rows whose approximate row max reaches M - 2 delta (per head);
-//   qabs : for each listed row t of head h, q_abs = [W_UK_h^T q^C_t, q^R_t]
-//          in fp32 (K^C_s . q^C_t = c_s . q_abs by associativity), stored as
-//          bf16 hi and lo parts (about 16 significant bits together), in the
-//          order the score kernel's MFMA operands are loaded;
+// has an approximate row max >= M - 2 delta. Two small launches:
+//   rows : rows whose approximate row max reaches M - 2 delta are listed,
+//          and for each, q_abs = [W_UK_h^T q^C_t, q^R_t] in fp32
+//          (K^C_s . q^C_t = c_s . q_abs by associativity), stored as bf16 hi
+//          and lo parts (about 16 significant bits together) in the order
+//          the score kernel's MFMA operands are loaded;
 //   score: every key of every listed row (its sequence, up to the row) is
 //          scored against hi and lo with MFMAs over the shared [c^KV | k^S]
 //          rows, fp32 accumulation, and the maximum taken.
@@ -788,109 +797,115 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int t) {
   return lo;
 }
 
-__global__ void __launch_bounds__(256) prefill_refine_rows_kernel(const int32_t* __restrict__ cu, int nseq,
-                                                                  int heads, int64_t ntok,
-                                                                  const float* __restrict__ rowmax,
-                                                                  const float* __restrict__ aux,
-                                                                  int32_t* __restrict__ cand) {
+constexpr int kRowList = 64;   // rows one rows workgroup lists before its head falls back
+
+// Grid (heads, kRefRowSplit). Workgroup (h, y) scans every kRefRowSplit-th
+// 256-row block of head h's row maxima and, for each row t that reaches the
+// threshold (fewer than kRefRows per head), forms q_abs: thread i takes
+// columns 8 (i % 64) .. +7 over the W_UK_h rows 32 (i / 64) .. +31 (its slab
+// is loaded once, all 32 loads in flight, and kept for every row), the four
+// partial sums of a column are added in a fixed order. The rows of all heads
+// take dense numbers from one counter. A head with too many rows folds the
+// approximate maximum M in instead (its listed rows are still scored).
+__global__ void __launch_bounds__(256) prefill_refine_rows_kernel(
+    const int32_t* __restrict__ cu, int nseq, int heads, int64_t ntok, const float* __restrict__ rowmax,
+    const float* __restrict__ aux, const uint16_t* __restrict__ q, const uint16_t* __restrict__ w, float scale,
+    int32_t* __restrict__ cand, uint16_t* __restrict__ qx, int4* __restrict__ qmeta, float* __restrict__ max_logit) {
+  __shared__ int lst[kRowList], lst_a0[kRowList];
+  __shared__ int nl, n_acc, n_base;
+  __shared__ float qcs[kRowList][kN];
+  __shared__ __align__(16) float part[4][kR];
   const int h = blockIdx.x;
+  const int tid = threadIdx.x;
   float M;
   const float thr = refine_threshold(aux, h, heads, &M);
   if (!(M > -INFINITY)) return;
-  int32_t* c = cand + static_cast<size_t>(h) * kCandStride;
-  for (int64_t t = threadIdx.x + 256 * static_cast<int64_t>(blockIdx.y); t < ntok; t += 256 * gridDim.y) {
-    if (rowmax[static_cast<size_t>(h) * ntok + t] >= thr) {
-      const int k = atomicAdd(&c[2], 1);
-      if (k < kRefRows) {
-        c[kCandRows + 2 * k] = static_cast<int>(t);
-        c[kCandRows + 2 * k + 1] = cu[seq_of(cu, nseq, static_cast<int>(t))];
-      } else {
-        c[1] = 1;
+  if (tid == 0) nl = 0;
+  __syncthreads();
+  // ---- scan: eight loads of a thread in flight at a time
+  const int64_t step = 256 * static_cast<int64_t>(gridDim.y);
+  for (int64_t t0 = tid + 256 * static_cast<int64_t>(blockIdx.y); t0 < ntok; t0 += 8 * step) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t t = t0 + u * step;
+      v[u] = t < ntok ? rowmax[static_cast<size_t>(h) * ntok + t] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (v[u] >= thr) {
+        const int k = atomicAdd(&nl, 1);
+        if (k < kRowList) lst[k] = static_cast<int>(t0 + u * step);
       }
     }
   }
-}
-
-// Listed rows of head h (0 if the head's list overflowed: it falls back to M).
-__device__ __forceinline__ int listed_rows(const int32_t* cand, int h) {
-  const int32_t* c = cand + static_cast<size_t>(h) * kCandStride;
-  return c[1] != 0 ? 0 : min(c[2], kRefRows);
-}
-
-// Grid (heads, kRefRows). Workgroup (h, r) forms q_abs of the r-th listed row
-// of head h: thread t takes columns 8 (t % 64) .. +7 over the W_UK_h rows
-// 32 (t / 64) .. +31 (all 32 loads in flight), the four partial sums of a
-// column are added in a fixed order. Rows of all heads are numbered densely
-// in head order. Workgroup (h, 0) of an overflowed head folds M in instead.
-__global__ void __launch_bounds__(256) prefill_refine_qabs_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ w, int heads, const float* __restrict__ aux,
-    const int32_t* __restrict__ cand, float scale, uint16_t* __restrict__ qx, int4* __restrict__ qmeta,
-    float* __restrict__ max_logit) {
-  __shared__ float qc[kN];
-  __shared__ __align__(16) float part[4][kR];
-  __shared__ int red[4];
-  const int h = blockIdx.x, r = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t* c = cand + static_cast<size_t>(h) * kCandStride;
-  const float M = aux[h * kAuxStride];
-  if (c[1] != 0 || c[2] > kRefRows) {
-    if (r == 0 && tid == 0 && M > -INFINITY) atomic_max_float(max_logit + h, M * scale);
-    return;
+  __syncthreads();
+  const int nfound = nl;
+  if (nfound == 0) return;
+  // ---- places among the head's kRefRows, and dense numbers, for all rows at once
+  if (tid == 0) {
+    const int c0 = atomicAdd(cand + kCandHeadCount + h, nfound);
+    const int acc = max(0, min(min(nfound, kRowList), kRefRows - c0));
+    n_acc = acc;
+    n_base = acc > 0 ? atomicAdd(cand, acc) : 0;
+    if (nfound > kRowList || c0 + nfound > kRefRows) atomic_max_float(max_logit + h, M * scale);   // fallback
   }
-  if (r >= c[2]) return;
-  // dense index: listed rows of the heads before h (one thread per head), plus r
-  {
-    int v = 0;
-    for (int hh = tid; hh < h; hh += 256) v += listed_rows(cand, hh);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    if (lane == 0) red[wave] = v;
-  }
-  const int t = c[kCandRows + 2 * r], a0 = c[kCandRows + 2 * r + 1];
-  const uint16_t* qt = q + (static_cast<size_t>(t) * heads + h) * kD;
+  __syncthreads();
+  const int acc = n_acc, base = n_base;
+  if (acc == 0) return;
+  // ---- the W_UK_h slab of this thread and the queries of every accepted row, all loads in flight
   const int cg = tid & 63, kg = tid >> 6;
   uint4 wv[32];
-  const uint16_t* wr = w + (static_cast<size_t>(h) * (kN + kV) + 32 * kg) * kR + 8 * cg;
-#pragma unroll
-  for (int u = 0; u < 32; ++u) wv[u] = ldg16(wr + static_cast<size_t>(u) * kR);
-  if (tid < kN) qc[tid] = bf16_to_f32(qt[tid]);
-  __syncthreads();
-  const int n = r + (red[0] + red[1]) + (red[2] + red[3]);
   {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const uint16_t* wr = w + (static_cast<size_t>(h) * (kN + kV) + 32 * kg) * kR + 8 * cg;
 #pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const float x = qc[32 * kg + u];
-      const uint32_t* w4 = &wv[u].x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = fmaf(x, bf16lo(w4[e]), acc[2 * e]);
-        acc[2 * e + 1] = fmaf(x, bf16hi(w4[e]), acc[2 * e + 1]);
-      }
-    }
-    float4* dst = reinterpret_cast<float4*>(&part[kg][8 * cg]);
-    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    for (int u = 0; u < 32; ++u) wv[u] = ldg16(wr + static_cast<size_t>(u) * kR);
   }
+  for (int i = tid; i < acc * kN; i += 256) {
+    const int k = i / kN, e = i - k * kN;
+    qcs[k][e] = bf16_to_f32(q[(static_cast<size_t>(lst[k]) * heads + h) * kD + e]);
+  }
+  if (tid < acc) lst_a0[tid] = cu[seq_of(cu, nseq, lst[tid])];
   __syncthreads();
-  // Operand order: group n / 32, k-step kk = col / 16, lane 32 (col / 8 % 2)
-  // + n % 32, element col % 8; hi and lo are separate planes.
-  auto at = [&](int col) {
-    return ((static_cast<size_t>(n >> 5) * ((kR + kS) / 16) + col / 16) * 64 + 32 * ((col >> 3) & 1) + (n & 31)) * 8 +
-           (col & 7);
-  };
-  uint16_t* lo = qx + static_cast<size_t>(heads) * kRefRows * (kR + kS);
-  for (int col = tid; col < kR; col += 256) {
-    const float v = (part[0][col] + part[1][col]) + (part[2][col] + part[3][col]);
-    const uint16_t vh = f32_to_bf16(v);
-    qx[at(col)] = vh;
-    lo[at(col)] = f32_to_bf16(v - bf16_to_f32(vh));
+  const size_t plane = static_cast<size_t>(heads) * kRefRows * (kR + kS);
+  for (int k = 0; k < acc; ++k) {
+    const int t = lst[k], n = base + k;
+    {
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const float x = qcs[k][32 * kg + u];
+        const uint32_t* w4 = &wv[u].x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[2 * e] = fmaf(x, bf16lo(w4[e]), a[2 * e]);
+          a[2 * e + 1] = fmaf(x, bf16hi(w4[e]), a[2 * e + 1]);
+        }
+      }
+      float4* dst = reinterpret_cast<float4*>(&part[kg][8 * cg]);
+      dst[0] = make_float4(a[0], a[1], a[2], a[3]);
+      dst[1] = make_float4(a[4], a[5], a[6], a[7]);
+    }
+    __syncthreads();
+    // Operand order: group n / 32, k-step kk = col / 16, lane 32 (col / 8 % 2)
+    // + n % 32, element col % 8; hi and lo are separate planes.
+    auto at = [&](int col) {
+      return ((static_cast<size_t>(n >> 5) * ((kR + kS) / 16) + col / 16) * 64 + 32 * ((col >> 3) & 1) + (n & 31)) *
+                 8 + (col & 7);
+    };
+    for (int col = tid; col < kR; col += 256) {
+      const float v = (part[0][col] + part[1][col]) + (part[2][col] + part[3][col]);
+      const uint16_t vh = f32_to_bf16(v);
+      qx[at(col)] = vh;
+      qx[plane + at(col)] = f32_to_bf16(v - bf16_to_f32(vh));
+    }
+    if (tid < kS) {   // q^R is bf16 already
+      qx[at(kR + tid)] = q[(static_cast<size_t>(t) * heads + h) * kD + kN + tid];
+      qx[plane + at(kR + tid)] = 0;
+    }
+    if (tid == 0) qmeta[n] = make_int4(t, lst_a0[k], h, 0);
+    __syncthreads();   // part is rewritten for the next row
   }
-  if (tid < kS) {   // q^R is bf16 already
-    qx[at(kR + tid)] = qt[kN + tid];
-    lo[at(kR + tid)] = 0;
-  }
-  if (tid == 0) qmeta[n] = make_int4(t, a0, h, 0);
 }
 
 constexpr int kScoreBlocks = 512;
@@ -911,10 +926,7 @@ __global__ void __launch_bounds__(256) prefill_refine_score_kernel(
   __shared__ __align__(16) uint4 bl[2][kSteps * 64];   // [hi | lo][k-step][lane]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  int ntot = 0;
-  for (int hh = lane; hh < heads; hh += 64) ntot += listed_rows(cand, hh);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ntot += __shfl_xor(ntot, o, 64);
+  const int ntot = min(cand[0], heads * kRefRows);
   if (ntot == 0) return;
   const int ncg = (ntot + 31) / 32;
   const int64_t nkb = (ntok + 127) / 128;
@@ -986,20 +998,10 @@ __global__ void __launch_bounds__(256) prefill_refine_score_kernel(
   }
 }
 
-__global__ void prefill_aux_init_kernel(float* aux, int32_t* cand, int heads) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < (heads + 1) * kAuxStride) aux[i] = ((i % kAuxStride) == 0 && i < heads * kAuxStride) ? -INFINITY : 0.0f;
-  if (i < heads) {
-    cand[static_cast<size_t>(i) * kCandStride] = 0;
-    cand[static_cast<size_t>(i) * kCandStride + 1] = 0;
-    cand[static_cast<size_t>(i) * kCandStride + 2] = 0;
-  }
-}
-
 hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void* q, const void* ckv,
                                const void* ks, const void* w_kv_b, const void* gate, const int32_t* cu,
-                               int nseq, int64_t ntok, void* out, float* lse, float* max_logit, void* ws,
-                               hipStream_t st) {
+                               int nseq, int64_t ntok, void* out, float* lse, float* max_logit,
+                               bool init_max_logit, void* ws, hipStream_t st) {
   const PrefillWs L = prefill_ws_layout(heads, ntok, nseq);
   char* base = static_cast<char*>(ws);
   uint16_t* kc = reinterpret_cast<uint16_t*>(base + L.kc);
@@ -1014,13 +1016,9 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
   int32_t* cand = reinterpret_cast<int32_t*>(base + L.cand);
 
   {
-    TimedScope ts_("prefill_aux_init", st);
-    hipLaunchKernelGGL(prefill_aux_init_kernel, dim3((heads + 1) * kAuxStride / 256 + 1), dim3(256), 0, st, aux,
-                       cand, heads);
-  }
-  {
     TimedScope ts_("prefill_plan", st);
-    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(256), 0, st, cu, nseq, pcu, order, toff, hdr);
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(256), 0, st, cu, nseq, pcu, order, toff, hdr, heads, aux,
+                       cand, init_max_logit ? max_logit : nullptr);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1060,20 +1058,13 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  {
-    TimedScope ts_("prefill_refine_rows", st);
-    hipLaunchKernelGGL(prefill_refine_rows_kernel, dim3(heads, kRefRowSplit), dim3(256), 0, st, cu, nseq, heads, ntok,
-                       rowmax, aux, cand);
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   uint16_t* qx = reinterpret_cast<uint16_t*>(base + L.qx);
   int4* qmeta = reinterpret_cast<int4*>(base + L.qmeta);
   {
-    TimedScope ts_("prefill_refine_qabs", st);
-    hipLaunchKernelGGL(prefill_refine_qabs_kernel, dim3(heads, kRefRows), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(w_kv_b), heads, aux, cand, scale,
-                       qx, qmeta, max_logit);
+    TimedScope ts_("prefill_refine_rows", st);
+    hipLaunchKernelGGL(prefill_refine_rows_kernel, dim3(heads, kRefRowSplit), dim3(256), 0, st, cu, nseq, heads, ntok,
+                       rowmax, aux, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(w_kv_b), scale,
+                       cand, qx, qmeta, max_logit);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
