@@ -7,8 +7,10 @@
 //   o = sigma(g) . reshape(O~); plus the per-head maximum of S that QK-Clip
 //   ("SOTA-131") needs.
 //
-// Three launches: a one-workgroup plan (per-sequence padded offsets and a
-// longest-first tile order), the expansion GEMM, and the attention kernel.
+// Five launches: a one-workgroup plan (per-sequence padded offsets, a
+// longest-first tile order, and the clearing of the max-logit state), the
+// expansion GEMM, the attention kernel, and the two max-logit refinement
+// kernels.
 #include <type_traits>
 
 #include "mla_common.h"
