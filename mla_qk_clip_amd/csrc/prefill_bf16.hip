@@ -822,6 +822,10 @@ __global__ void __launch_bounds__(256) prefill_refine_rows_kernel(
   float M;
   const float thr = refine_threshold(aux, h, heads, &M);
   if (!(M > -INFINITY)) return;
+  // Seed the head slot with M - delta, a lower bound of the exact maximum
+  // (which is among the scores formed below, so the result is unchanged):
+  // the score kernel then only raises it with atomics near the maximum.
+  if (blockIdx.y == 0 && tid == 0) atomic_max_float(max_logit + h, (M - 0.5f * (M - thr)) * scale);
   if (tid == 0) nl = 0;
   __syncthreads();
   // ---- scan: eight loads of a thread in flight at a time
@@ -990,9 +994,10 @@ __global__ void __launch_bounds__(256) prefill_refine_score_kernel(
       if (key >= a0 && key <= t && key < ntok) best = fmaxf(best, acc[e]);
     }
     best = fmaxf(best, __shfl_xor(best, 32, 64));
-    // Atomics only where they raise the slot: its value only grows, so a
-    // stale read can only cost an extra atomic. (One atomic per row and item
-    // on the few dozen head slots would serialise in the L2.)
+    // Atomics only where they raise the slot (seeded with a lower bound of
+    // the exact maximum by the rows kernel): its value only grows, so a stale
+    // read can only cost an extra atomic. (One atomic per row and item on
+    // the few dozen head slots would serialise in the L2.)
     if (g == 0 && nvalid && best > -INFINITY) {
       const float v = best * scale;
       if (v > *reinterpret_cast<volatile const float*>(max_logit + h)) atomic_max_float(max_logit + h, v);
