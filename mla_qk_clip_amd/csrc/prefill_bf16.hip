@@ -80,13 +80,15 @@ __global__ void __launch_bounds__(256) prefill_plan_kernel(const int32_t* __rest
 // Expansion: [K^C_h | V_h][p] = c^KV[src(p)] W_UKV[:, 256h : 256h+256] over
 // padded rows p. One workgroup = 256 padded rows (four key tiles) x the 256
 // columns of one head; 8 waves, wave w owns rows 64 (w & 3) .. +63 of the
-// K^C half (w < 4) or of the V half. K = 512 in 16 steps of 32 through a
-// double-buffered LDS tile staged through registers one step ahead.
+// K^C half (w < 4) or of the V half. K = 512 in 8 steps of 64: both operand
+// tiles of a step (256 rows x 128 bytes each) are copied straight into LDS
+// (buffer loads to LDS, no register staging) one step ahead, into two slots.
 //
-// LDS tile layout (one operand, 256 rows x four 16-byte k-units): unit (r, c)
-// at (r / 16) * 64 + c * 16 + r % 16: a wave's staging store of 64 units
-// covers 16 whole row segments, and a 16-lane group of a fragment read
-// touches 16 consecutive units.
+// Each copy instruction moves 8 whole 128-byte row segments (eight lanes per
+// row), so every request is a full cache line. LDS tile layout (one operand,
+// 256 rows x eight 16-byte k-units): unit (r, c) at 64 (r / 8) + 8 (r % 8) +
+// (c ^ ((r / 2) % 8)); a 16-lane group of a fragment read (16 consecutive
+// rows, one k-unit) then falls into 16 different bank groups.
 //
 // Both halves are stored straight from the accumulators with 16-byte stores:
 // V is formed as C = c^KV W_V (accumulator lane = feature d, its rows = keys)
@@ -99,8 +101,8 @@ __global__ void __launch_bounds__(256) prefill_plan_kernel(const int32_t* __rest
 // ---------------------------------------------------------------------------
 constexpr int kExRows = 256;      // padded rows per workgroup
 constexpr int kExThreads = 512;
-constexpr int kExSteps = kR / 32;  // k-steps of 32
-constexpr int kExUnits = kExRows * 4;  // 16-byte units per operand slot
+constexpr int kExSteps = kR / 64;  // k-steps of 64
+constexpr int kExUnits = kExRows * 8;  // 16-byte units per operand slot
 constexpr int kExGroupRows = 2, kExGroupHeads = 16, kExGroup = kExGroupRows * kExGroupHeads;
 
 __global__ void __launch_bounds__(kExThreads) prefill_expand_kernel(
@@ -108,8 +110,8 @@ __global__ void __launch_bounds__(kExThreads) prefill_expand_kernel(
     int nseq, const int32_t* __restrict__ pcu, const int32_t* __restrict__ hdr, int64_t npad_max, int64_t ntok,
     int heads, const uint16_t* __restrict__ ks, uint16_t* __restrict__ kc, uint16_t* __restrict__ vt,
     uint16_t* __restrict__ ksp, float* __restrict__ aux) {
-  __shared__ uint4 Cs[2][kExUnits];   // c^KV slots
-  __shared__ uint4 Ws[2][kExUnits];   // W_UKV slots
+  __shared__ uint4 Cs0[kExUnits], Cs1[kExUnits];   // c^KV slots
+  __shared__ uint4 Ws0[kExUnits], Ws1[kExUnits];   // W_UKV slots
   __shared__ int src_row[kExRows];
   __shared__ float red[8];
 
@@ -152,35 +154,41 @@ __global__ void __launch_bounds__(kExThreads) prefill_expand_kernel(
   }
   __syncthreads();
 
-  // ---- staging: thread (wave w, lane i) carries unit (row 16 b + i % 16,
-  // k-unit i / 16) of blocks b = 2w, 2w+1 of both operands ----
-  const uint16_t* csrc[2];
-  const uint16_t* wsrc[2];
+  // ---- staging: copy q of wave w covers rows 8 (4 w + q) .. +7; lane i
+  // takes row 8 (4 w + q) + i / 8 and k-unit (i % 8) ^ ((row / 2) % 8). The
+  // c^KV resource starts at the tile's first source row (its rows are
+  // consecutive source rows, with padding between sequences), so 32-bit
+  // offsets suffice; padding rows read past its end and get zeros.
+  int src0 = 0x7fffffff;
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) {
-    const int r = 16 * (2 * wave + bb) + (lane & 15), c = lane >> 4;
-    const int src = src_row[r];
-    csrc[bb] = src >= 0 ? ckv + static_cast<size_t>(src) * kR + 8 * c : nullptr;   // padding rows: zeros
-    wsrc[bb] = w + (static_cast<size_t>(head) * 256 + r) * kR + 8 * c;
+  for (int j = 0; j < kExRows / 64; ++j) {
+    const int v = src_row[64 * j + lane];
+    if (v >= 0) src0 = min(src0, v);
   }
-  uint4 rc[2], rw[2];
-  auto gload = [&](int st) {
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      rc[bb] = csrc[bb] ? ldg16(csrc[bb] + 32 * st) : make_uint4(0, 0, 0, 0);
-      rw[bb] = ldg16(wsrc[bb] + 32 * st);
-    }
-  };
-  auto sstore = [&](int sl) {
+  for (int o = 32; o >= 1; o >>= 1) src0 = min(src0, __shfl_xor(src0, o));
+  if (src0 == 0x7fffffff) src0 = 0;
+  src0 = __builtin_amdgcn_readfirstlane(src0);   // uniform after the reduction
+  const auto rs_c = make_rsrc(ckv + static_cast<size_t>(src0) * kR, kExRows * kR * 2);
+  const auto rs_w = make_rsrc(w + static_cast<size_t>(head) * 256 * kR, 256 * kR * 2);
+  uint32_t voff_c[4], voff_w[4];
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      Cs[sl][64 * (2 * wave + bb) + lane] = rc[bb];
-      Ws[sl][64 * (2 * wave + bb) + lane] = rw[bb];
+  for (int q = 0; q < 4; ++q) {
+    const int r = 8 * (4 * wave + q) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+    const int src = src_row[r];
+    voff_c[q] = src >= 0 ? static_cast<uint32_t>(src - src0) * (kR * 2) + 16 * c : 0x80000000u;   // padding rows: zeros
+    voff_w[q] = static_cast<uint32_t>(r) * (kR * 2) + 16 * c;
+  }
+  auto issue = [&](uint4* cd, uint4* wd, int st) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      dma16_buf(rs_c, voff_c[q], 128 * st, cd + 64 * (4 * wave + q));
+      dma16_buf(rs_w, voff_w[q], 128 * st, wd + 64 * (4 * wave + q));
     }
   };
   auto frag = [&](const uint4* t, int r0, int kh) {   // rows r0 .. r0+31, k-units 2 kh + g
-    const int r = r0 + l32;
-    return as_bf16x8(t[(r >> 4) * 64 + (2 * kh + g) * 16 + (r & 15)]);
+    const int r = r0 + l32, c = 2 * kh + g;
+    return as_bf16x8(t[64 * (r >> 3) + 8 * (r & 7) + (c ^ ((r >> 1) & 7))]);
   };
 
   // acc: K half (transposed C^T): acc[2 fb + kb], fb = feature block (4), kb = key block (2);
@@ -194,15 +202,9 @@ __global__ void __launch_bounds__(kExThreads) prefill_expand_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
 
-    gload(0);
-    sstore(0);
-    gload(1);
-    __syncthreads();
-    for (int st = 0; st < kExSteps; ++st) {
-      const uint4* cs = Cs[st & 1];
-      const uint4* ws = Ws[st & 1];
+    auto step = [&](const uint4* cs, const uint4* ws) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
+      for (int kh = 0; kh < 4; ++kh) {
         bf16x8 cf[2], wf[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) cf[kb] = frag(cs, 64 * wm + 32 * kb, kh);
@@ -220,8 +222,20 @@ __global__ void __launch_bounds__(kExThreads) prefill_expand_kernel(
             for (int fb = 0; fb < 4; ++fb) acc[4 * kb + fb] = mfma32(cf[kb], wf[fb], acc[4 * kb + fb]);
         }
       }
-      if (st + 1 < kExSteps) sstore((st + 1) & 1);   // slot last read by step st - 1
-      if (st + 2 < kExSteps) gload(st + 2);
+    };
+    issue(Cs0, Ws0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int st = 0; st < kExSteps; st += 2) {
+      issue(Cs1, Ws1, st + 1);   // slot 1 was last read by step st - 1
+      __builtin_amdgcn_sched_barrier(0);
+      step(Cs0, Ws0);
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (st + 2 < kExSteps) issue(Cs0, Ws0, st + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      step(Cs1, Ws1);
+      wait_vmcnt<0>();
       __syncthreads();
     }
 
