@@ -17,6 +17,8 @@ from .mla_oracle import (  # noqa: F401
     absorbed_rows_selected,
     dense_prefill,
     expand_latent,
+    expanded,
+    expanded_cache,
     max_logit_head,
     prefill,
     prefill_rows,

@@ -294,6 +294,72 @@ def absorbed_rows_selected(q, cache_rows, w_kv_b, gate, dims, batches):
 
 
 # ---------------------------------------------------------------------------
+# Expanded-cache decode: the materialised K_h = [K^C_h, k^S] and V_h of every
+# cached token kept per head, as the training form builds them ([MLA] steps
+# "[k^C v] = c^KV W_UKV" and "K_h = [K^C_h k^S]"), instead of the single latent
+# row of [FR]. Attention over it is the [MLA] equation list for the last Tq
+# query positions.
+# ---------------------------------------------------------------------------
+
+
+def expanded_cache(cache_rows, w_kv_b, dims):
+    """Per-head K and V of every cached token from latent rows [c^KV | k^S].
+
+    ``cache_rows[b]`` is [L_b, R+S]. Returns lists ``k_rows[b]`` [H, L_b, N+S]
+    and ``v_rows[b]`` [H, L_b, V] in float64.
+    """
+    d = _dims(dims)
+    R = d.kv_rank
+    k_rows, v_rows = [], []
+    for rows in cache_rows:
+        rows = np.asarray(rows, dtype=f64)
+        ks, vs = [], []
+        for h in range(d.heads):
+            kc, vv = expand_latent(rows[:, :R], w_kv_b, d, h)
+            ks.append(key_of_head(kc, rows[:, R:]))
+            vs.append(vv)
+        k_rows.append(np.stack(ks))
+        v_rows.append(np.stack(vs))
+    return k_rows, v_rows
+
+
+def expanded(q, k_rows, v_rows, gate, dims):
+    """Gated MLA decode over a per-head (expanded) cache.
+
+    q [B, Tq, H, D]; ``k_rows[b]`` [H, L_b, D] and ``v_rows[b]`` [H, L_b, V]
+    hold the valid rows of sequence b; gate [B, Tq, H*V] or None. Query i of Tq
+    sees rows j <= L_b - Tq + i, with the scale 1/sqrt(N+S):
+      s_j = scale * q[b, i, h] . K_h[j],  p = softmax(s),  O~_h = sum_j p_j V_h[j],
+      out = sigma(g) . O~.
+    Returns (out [B, Tq, H*V], max_logit [H]).
+    """
+    d = _dims(dims)
+    H, V = d.heads, d.v_dim
+    scale = scale_of(d)
+    q = np.asarray(q)
+    B, Tq = q.shape[0], q.shape[1]
+    out = np.zeros((B, Tq, H * V), dtype=f64)
+    smax = np.full(H, -np.inf, dtype=f64)
+    for b in range(B):
+        K = np.asarray(k_rows[b], dtype=f64)
+        Vv = np.asarray(v_rows[b], dtype=f64)
+        L = K.shape[1]
+        for i in range(Tq):
+            vis = L - Tq + i + 1
+            if vis <= 0:
+                continue
+            for h in range(H):
+                s = (K[h, :vis] @ np.asarray(q[b, i, h], dtype=f64)) * scale
+                smax[h] = max(smax[h], float(s.max()))
+                e = np.exp(s - s.max())
+                p = e / e.sum()
+                out[b, i, h * V:(h + 1) * V] = p @ Vv[h, :vis]
+    if gate is not None:
+        out = sigmoid(gate) * out
+    return out, smax
+
+
+# ---------------------------------------------------------------------------
 # Query projection ([MLA] "q = c^Q W_UQ") and QK-Clip ([CLIP])
 # ---------------------------------------------------------------------------
 

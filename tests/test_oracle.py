@@ -293,6 +293,77 @@ def test_absorbed_max_logit_matches_materialised_last_rows():
 
 
 # ---------------------------------------------------------------------------
+# Expanded-cache decode (per-head K and V rows)
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("tq", [1, 3])
+def test_expanded_equals_absorbed_on_latent_derived_cache(tq):
+    """Per-head K/V built from latent rows give the absorbed form's result
+    (associativity of the [MLA] equations), outputs and max logits."""
+    dims = synth.TINY
+    rng = np.random.default_rng(31)
+    lens = [7, 19, 12]
+    rows = [rng.standard_normal((L, dims.kv_rank + dims.shared_dim)) for L in lens]
+    w = rng.standard_normal((dims.heads * (dims.nope_dim + dims.v_dim), dims.kv_rank)) / math.sqrt(dims.kv_rank)
+    D = dims.nope_dim + dims.shared_dim
+    q = rng.standard_normal((len(lens), tq, dims.heads, D))
+    g = rng.standard_normal((len(lens), tq, dims.heads * dims.v_dim))
+    ref, sm_ref = oracle.absorbed(q, rows, w, g, dims)
+    k_rows, v_rows = oracle.expanded_cache(rows, w, dims)
+    assert k_rows[1].shape == (dims.heads, 19, D) and v_rows[1].shape == (dims.heads, 19, dims.v_dim)
+    out, sm = oracle.expanded(q, k_rows, v_rows, g, dims)
+    assert rel_err(out, ref) < 1e-10
+    assert np.allclose(sm, sm_ref, rtol=1e-12)
+
+
+def test_expanded_with_all_positions_queried_is_dense_causal_attention():
+    """Tq = L: every position of the sequence is a query, so the decode form is
+    the brute-force masked softmax of the training form."""
+    dims = synth.TINY
+    p = synth.prefill_inputs(dims, [23], seed=12, bf16=False)
+    ref, _, sm_ref = oracle.dense_prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, dims)
+    rows = [np.concatenate([p.ckv, p.ks], axis=1)]
+    k_rows, v_rows = oracle.expanded_cache(rows, p.w_kv_b, dims)
+    out, sm = oracle.expanded(p.q[None], k_rows, v_rows, p.gate[None], dims)
+    assert rel_err(out[0], ref) < 1e-10
+    assert np.allclose(sm, sm_ref, rtol=1e-12)
+
+
+def test_expanded_zero_query_gives_prefix_mean_of_values():
+    """q = 0: every visible score is 0, so query i returns the mean of the
+    first L - Tq + i + 1 value rows (times the gate)."""
+    dims = synth.TINY
+    rng = np.random.default_rng(5)
+    L, tq = 11, 4
+    D = dims.nope_dim + dims.shared_dim
+    K = rng.standard_normal((dims.heads, L, D))
+    Vv = rng.standard_normal((dims.heads, L, dims.v_dim))
+    g = rng.standard_normal((1, tq, dims.heads * dims.v_dim))
+    out, sm = oracle.expanded(np.zeros((1, tq, dims.heads, D)), [K], [Vv], g, dims)
+    sig = 1.0 / (1.0 + np.exp(-g))
+    for i in range(tq):
+        vis = L - tq + i + 1
+        want = Vv[:, :vis].mean(axis=1).reshape(-1)
+        assert np.allclose(out[0, i], sig[0, i] * want, rtol=0, atol=1e-13)
+    assert np.all(sm == 0.0)
+
+
+def test_expanded_single_visible_row_returns_gated_value_row():
+    dims = synth.TINY
+    rng = np.random.default_rng(6)
+    D = dims.nope_dim + dims.shared_dim
+    K = rng.standard_normal((dims.heads, 1, D))
+    Vv = rng.standard_normal((dims.heads, 1, dims.v_dim))
+    q = rng.standard_normal((1, 1, dims.heads, D))
+    g = rng.standard_normal((1, 1, dims.heads * dims.v_dim))
+    out, sm = oracle.expanded(q, [K], [Vv], g, dims)
+    assert np.allclose(out[0, 0], Vv[:, 0].reshape(-1) / (1.0 + np.exp(-g[0, 0])), rtol=1e-14, atol=0)
+    want = np.array([K[h, 0] @ q[0, 0, h] for h in range(dims.heads)]) / math.sqrt(D)
+    assert np.allclose(sm, want, rtol=1e-14, atol=0)
+
+
+# ---------------------------------------------------------------------------
 # QK-Clip
 # ---------------------------------------------------------------------------
 
