@@ -170,6 +170,43 @@ mla_status mla_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Expanded-cache decode (per-head K and V rows; bandwidth comparator)       */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of scratch memory mla_expanded needs for these sizes (0 for invalid
+ * sizes). */
+size_t mla_expanded_workspace_size(const mla_dims* dims, mla_dtype in_dtype,
+                                   int32_t batch, int32_t tq, int64_t cap);
+
+/*
+ * The result of mla_absorbed, read from a cache that keeps every token's
+ * materialised per-head key K_h = [K^C_h, k^S] and value V_h (the training
+ * form's "[k^C v] = c^KV W_UKV", "K_h = [K^C_h k^S]" of "Kimi K3 · Gated MLA"),
+ * instead of the single latent row of "Gated MLA et NoPE". Per token it reads
+ * H*(N+S+V)*2 bytes (61,440 for Kimi K3) against the latent row's (R+S)*2
+ * (1,152): it exists to measure that difference.
+ *   s_j = scale * q[b, i, h] . k_cache[b, h, j],  j <= lens[b] - tq + i,
+ *   O~_h = sum_j softmax(s)_j v_cache[b, h, j],  out = sigma(g) . O~.
+ *
+ * q         [batch, tq, H, N+S]     bf16
+ * k_cache   [batch, H, cap, N+S]    bf16, per head K^C_h then k^S
+ * v_cache   [batch, H, cap, V]      bf16
+ *           rows at or beyond lens[b] are never read (they may hold anything)
+ * lens      [batch] int32, device; tq <= lens[b] <= cap (not checked on the
+ *           device; a violation gives undefined results)
+ * gate      [batch, tq, H*V]        bf16, or NULL
+ * out       [batch, tq, H*V]        out_dtype
+ * max_logit [H] fp32, as for mla_prefill (over every visible (query, row)
+ *           pair; scores in fp32 from the bf16 inputs).
+ * bf16 only, Kimi K3 head shape; cap at most 2^27.
+ */
+mla_status mla_expanded(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype,
+                        const void* q, const void* k_cache, const void* v_cache, int64_t cap,
+                        const int32_t* lens, int32_t batch, int32_t tq,
+                        const void* gate, void* out, float* max_logit, int32_t accumulate,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* QK-Clip ("SOTA-131": rescale the query and key projection weights of every
  * head whose maximum logit exceeds tau)                                     */
 /* ------------------------------------------------------------------------ */
@@ -210,7 +247,7 @@ const char* mla_version(void);
  * mla_timing_enable(0) stops it. mla_timing_read waits for the recorded
  * events and returns the summed milliseconds and launch count of one kernel
  * ("prefill_expand", "prefill_attn", "absorb_q", "absorbed_split",
- * "absorbed_combine", "qk_clip", ...); it returns 0 if that kernel has not
+ * "absorbed_combine", "expanded_split", "qk_clip", ...); it returns 0 if that kernel has not
  * run. Intended for one thread at a time.
  */
 void mla_timing_enable(int32_t on);

@@ -23,7 +23,7 @@ MLA_F32, MLA_BF16 = 0, 1
 
 EXPORTED = (
     "mla_prefill_workspace_size", "mla_prefill", "mla_absorbed_workspace_size", "mla_absorbed",
-    "mla_qk_clip", "mla_status_string", "mla_last_error", "mla_version", "mla_timing_enable",
+    "mla_expanded_workspace_size", "mla_expanded", "mla_qk_clip", "mla_status_string", "mla_last_error", "mla_version", "mla_timing_enable",
     "mla_timing_read",
 )
 
@@ -70,6 +70,10 @@ def _load():
     lib.mla_absorbed_workspace_size.restype = SZ
     lib.mla_absorbed.argtypes = [D, I32, I32, P, P, I64, P, I32, I32, P, P, P, P, I32, P, SZ, P]
     lib.mla_absorbed.restype = I32
+    lib.mla_expanded_workspace_size.argtypes = [D, I32, I32, I32, I64]
+    lib.mla_expanded_workspace_size.restype = SZ
+    lib.mla_expanded.argtypes = [D, I32, I32, P, P, P, I64, P, I32, I32, P, P, P, I32, P, SZ, P]
+    lib.mla_expanded.restype = I32
     lib.mla_qk_clip.argtypes = [D, I32, P, I32, P, P, F, P, P, P]
     lib.mla_qk_clip.restype = I32
     lib.mla_status_string.argtypes = [I32]
@@ -220,6 +224,49 @@ def mla_absorbed(dims: Dims, q, cache, lens, w_kv_b, gate, *, out_dtype=None, ou
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = lib.mla_absorbed(ctypes.byref(dims.c()), in_dt, out_dt, _ptr(q), _ptr(cache), cap, _ptr(lens), B, Tq,
                           _ptr(w_kv_b), _ptr(gate), _ptr(out), _ptr(max_logit), 1 if accumulate else 0,
+                          _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st)
+    return out, max_logit
+
+
+def mla_expanded_workspace_size(dims: Dims, in_dtype: int, batch: int, tq: int, cap: int) -> int:
+    return int(lib.mla_expanded_workspace_size(ctypes.byref(dims.c()), in_dtype, batch, tq, cap))
+
+
+def mla_expanded(dims: Dims, q, k_cache, v_cache, lens, gate, *, out_dtype=None, out=None, max_logit=None,
+                 accumulate=False, workspace=None, stream=None):
+    """Gated MLA decode over a per-head (expanded) K/V cache (see ``mla_expanded`` in include/mla.h).
+
+    q [B, Tq, H, N+S], k_cache [B, H, cap, N+S], v_cache [B, H, cap, V], lens int32 [B] on the
+    device, gate [B, Tq, H*V] or None, all bf16. Returns (out [B, Tq, H*V], max_logit [H]).
+    """
+    in_dt = _dt(q)
+    out_dt = in_dt if out_dtype is None else (MLA_BF16 if out_dtype == torch.bfloat16 else MLA_F32)
+    if out is not None and out_dtype is None:
+        out_dt = _dt(out)
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError(f"q must be [B, Tq, H, N+S] and k_cache [B, H, cap, N+S], got {tuple(q.shape)}, "
+                         f"{tuple(k_cache.shape)}")
+    B, Tq = q.shape[0], q.shape[1]
+    H, V = dims.heads, dims.v_dim
+    cap = k_cache.shape[2]
+    dev = q.device
+    _expect("q", q, (B, Tq, H, dims.qk_dim), q.dtype)
+    _expect("k_cache", k_cache, (B, H, cap, dims.qk_dim), q.dtype)
+    _expect("v_cache", v_cache, (B, H, cap, V), q.dtype)
+    _expect("lens", lens, (B,), torch.int32)
+    _expect("gate", gate, (B, Tq, H * V), q.dtype, optional=True)
+    if out is None:
+        out = torch.empty((B, Tq, H * V), dtype=_torch_dt(out_dt), device=dev)
+    if max_logit is None:
+        max_logit = torch.empty(H, dtype=torch.float32, device=dev)
+    _expect("out", out, (B, Tq, H * V), _torch_dt(out_dt))
+    _expect("max_logit", max_logit, (H,), torch.float32)
+    need = mla_expanded_workspace_size(dims, in_dt, B, Tq, cap)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.mla_expanded(ctypes.byref(dims.c()), in_dt, out_dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), cap,
+                          _ptr(lens), B, Tq, _ptr(gate), _ptr(out), _ptr(max_logit), 1 if accumulate else 0,
                           _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st)
     return out, max_logit

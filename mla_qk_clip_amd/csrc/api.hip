@@ -215,6 +215,57 @@ mla_status mla_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_
   return MLA_OK;
 }
 
+size_t mla_expanded_workspace_size(const mla_dims* dims, mla_dtype in_dtype, int32_t batch, int32_t tq,
+                                   int64_t cap) {
+  Shape s;
+  if (in_dtype != MLA_BF16 || check_dims(dims, in_dtype, &s) != MLA_OK || batch < 0 || tq < 0 || cap < 0 ||
+      cap > (int64_t{1} << 27))
+    return 0;
+  return mla::expanded_ws_layout(s.H, batch, tq, cap).total;
+}
+
+mla_status mla_expanded(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype, const void* q,
+                        const void* k_cache, const void* v_cache, int64_t cap, const int32_t* lens, int32_t batch,
+                        int32_t tq, const void* gate, void* out, float* max_logit, int32_t accumulate,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (in_dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "the expanded-cache decode takes bf16 inputs only");
+  Shape s;
+  mla_status st = check_dims(dims, in_dtype, &s);
+  if (st != MLA_OK) return st;
+  if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return fail(MLA_ERR_INVALID, "unknown out_dtype");
+  if (batch < 0 || tq < 1) return fail(MLA_ERR_INVALID, "batch must be >= 0 and tq >= 1");
+  if (cap < tq) return fail(MLA_ERR_INVALID, "cap (%lld) must be >= tq (%d)", static_cast<long long>(cap), tq);
+  if (cap > (int64_t{1} << 27)) return fail(MLA_ERR_UNSUPPORTED, "cap above 2^27");
+  if (accumulate != 0 && accumulate != 1) return fail(MLA_ERR_INVALID, "accumulate must be 0 or 1");
+  if (static_cast<int64_t>(batch) * tq * ((s.H + 3) / 4) > INT32_MAX)
+    return fail(MLA_ERR_UNSUPPORTED, "batch * tq * heads too large");
+  REQUIRE_PTR(max_logit, 4);
+  if (batch > 0) {
+    REQUIRE_PTR(q, 16);
+    REQUIRE_PTR(k_cache, 16);
+    REQUIRE_PTR(v_cache, 16);
+    REQUIRE_PTR(lens, 4);
+    REQUIRE_PTR(out, 16);
+    OPTIONAL_PTR(gate, 16);
+    const size_t need = mla_expanded_workspace_size(dims, in_dtype, batch, tq, cap);
+    if (!workspace || workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    if (!aligned(workspace, 16)) return fail(MLA_ERR_INVALID, "workspace is not 16-byte aligned");
+  }
+  hipError_t e = hipSuccess;
+  if (!accumulate) {
+    e = mla::launch_fill(max_logit, s.H, -INFINITY, stream);
+    if (e != hipSuccess) return hip_fail(e, "max_logit init");
+  }
+  if (batch == 0) return MLA_OK;
+  e = mla::launch_expanded_bf16(s.H, s.scale, out_dtype == MLA_BF16, q, k_cache, v_cache, cap, lens, batch, tq, gate,
+                                out, max_logit, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "mla_expanded launch");
+  return MLA_OK;
+}
+
 mla_status mla_qk_clip(const mla_dims* dims, mla_dtype wdtype, void* w_q_b, int32_t q_in, void* w_kv_b,
                        const float* max_logit, float tau, uint8_t* clipped, float* gamma, hipStream_t stream) {
   g_last_error.clear();

@@ -115,6 +115,25 @@ inline AbsorbedWs absorbed_ws_layout(int heads, int batch, int tq) {
   return w;
 }
 
+// Workspace of the bf16 expanded-cache decode: per (query, head, split of
+// kExpSplitRows visible rows) the unnormalised output [V] and {max (log2
+// units), sum}.
+constexpr int kExpSplitRows = 2048;
+struct ExpandedWs {
+  size_t part_o, part_ml, total;
+  int smax;   // splits per (query, head): ceil(cap / kExpSplitRows)
+};
+inline ExpandedWs expanded_ws_layout(int heads, int batch, int tq, int64_t cap) {
+  ExpandedWs w{};
+  w.smax = static_cast<int>((cap + kExpSplitRows - 1) / kExpSplitRows);
+  const size_t items = static_cast<size_t>(batch) * tq * heads * w.smax;
+  size_t off = 0;
+  w.part_o = off; off = align_up(off + items * kV * 4, 256);
+  w.part_ml = off; off = align_up(off + items * 2 * 4, 256);
+  w.total = off;
+  return w;
+}
+
 // ---- launchers (defined next to their kernels) ----
 
 hipError_t launch_fill(float* p, int n, float v, hipStream_t st);
@@ -134,6 +153,10 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16,
                                 const void* q, const void* cache, int64_t cap, const int32_t* lens,
                                 int batch, int tq, const void* w_kv_b, const void* gate, void* out,
                                 float* max_logit, bool init_max_logit, void* ws, hipStream_t st);
+
+hipError_t launch_expanded_bf16(int heads, float scale, bool out_bf16, const void* q, const void* kcache,
+                                const void* vcache, int64_t cap, const int32_t* lens, int batch, int tq,
+                                const void* gate, void* out, float* max_logit, void* ws, hipStream_t st);
 
 hipError_t launch_absorbed_f32(int heads, int R, int S, int N, int V, float scale,
                                const float* q, const float* cache, int64_t cap, const int32_t* lens,

@@ -88,6 +88,36 @@ def test_absorbed_validation(m):
              None) == m.MLA_ERR_UNSUPPORTED
 
 
+def test_expanded_validation(m):
+    K3 = m.Dims()
+    d = K3.c()
+    f = m.lib.mla_expanded
+    good = dict(in_dt=m.MLA_BF16, q=16, k=16, v=16, cap=100, lens=16, B=2, tq=1, gate=None, out=16, ml=16, acc=0,
+                ws=16, wsb=1 << 40)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return f(ctypes.byref(d), a["in_dt"], m.MLA_BF16, a["q"], a["k"], a["v"], a["cap"], a["lens"], a["B"],
+                 a["tq"], a["gate"], a["out"], a["ml"], a["acc"], a["ws"], a["wsb"], None)
+    assert call(in_dt=m.MLA_F32) == m.MLA_ERR_UNSUPPORTED
+    assert call(tq=0) == m.MLA_ERR_INVALID
+    assert call(cap=0) == m.MLA_ERR_INVALID
+    assert call(cap=(1 << 27) + 1) == m.MLA_ERR_UNSUPPORTED
+    assert call(k=None) == m.MLA_ERR_INVALID
+    assert call(v=24) == m.MLA_ERR_INVALID
+    assert b"aligned" in m.lib.mla_last_error()
+    assert call(ml=None) == m.MLA_ERR_INVALID
+    assert call(wsb=5) == m.MLA_ERR_WORKSPACE
+    assert call(acc=3) == m.MLA_ERR_INVALID
+    small = m.Dims(4, 256, 64, 128, 128).c()
+    assert f(ctypes.byref(small), m.MLA_BF16, m.MLA_BF16, 16, 16, 16, 100, 16, 1, 1, None, 16, 16, 0, 16, 1 << 40,
+             None) == m.MLA_ERR_UNSUPPORTED
+    # per (query, head, split of 2048 rows): 128 outputs and {max, sum} in fp32
+    assert m.mla_expanded_workspace_size(K3, m.MLA_BF16, 64, 1, 32768) >= 64 * 96 * 16 * 130 * 4
+    assert m.mla_expanded_workspace_size(K3, m.MLA_F32, 64, 1, 32768) == 0
+
+
 def test_qk_clip_validation(m):
     K3 = m.Dims()
     d = K3.c()
@@ -123,3 +153,8 @@ def test_binding_rejects_host_tensors_before_any_launch(m):
         m.mla_prefill(d, q, ckv, ks, w, None, cu)
     with pytest.raises(ValueError, match="device tensor"):
         m.mla_absorbed(d, q[None, :1], torch.zeros((1, 8, 24)), torch.tensor([8], dtype=torch.int32), w, None)
+    K3 = m.Dims(heads=2)
+    with pytest.raises(ValueError, match="device tensor"):
+        m.mla_expanded(K3, torch.zeros((1, 1, 2, 192), dtype=torch.bfloat16),
+                       torch.zeros((1, 2, 8, 192), dtype=torch.bfloat16), torch.zeros((1, 2, 8, 128), dtype=torch.bfloat16),
+                       torch.tensor([8], dtype=torch.int32), None)
