@@ -108,6 +108,51 @@ def cpu_baseline(p, budget_s: float = 12.0):
             "sample": f"{heads} of {H} heads of the T={T} prefill (fp64 NumPy), {dt:.1f} s"}
 
 
+def expanded_comparator(m, dims, d, dq, dg, lens, absorbed_ms, absorbed_split_ms, steps: int = 3):
+    """The decode workload over a per-head cache (K 192 + V 128 values per head
+    and token, the materialised form) instead of the latent rows: the bytes the
+    latent cache saves, measured. Same q, gate and lengths; the cache rows are
+    seeded N(0,1) draws (the spread of K^C, k^S and V), NaN past each length."""
+    import torch
+    B, H, cap = d.batch, dims.heads, d.cap
+    log(f"expanded-cache comparator: allocating {B * H * cap * 320 * 2 / 1e9:.1f} GB of per-head cache")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    kc = torch.randn((B, H, cap, 192), generator=g, dtype=torch.bfloat16, device="cuda")
+    vc = torch.randn((B, H, cap, 128), generator=g, dtype=torch.bfloat16, device="cuda")
+    for b in range(B):
+        kc[b, :, int(d.lens[b]):] = float("nan")
+        vc[b, :, int(d.lens[b]):] = float("nan")
+    out = torch.empty((B, 1, H * 128), dtype=torch.bfloat16, device="cuda")
+    ml = torch.empty(H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.mla_expanded_workspace_size(dims, m.MLA_BF16, B, 1, cap), dtype=torch.uint8, device="cuda")
+    m.mla_expanded(dims, dq, kc, vc, lens, dg, out=out, max_logit=ml, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m.mla_timing_enable(True)
+    t0.record(stream)
+    for _ in range(steps):
+        m.mla_expanded(dims, dq, kc, vc, lens, dg, out=out, max_logit=ml, workspace=ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    split_tot, split_n = m.mla_timing_read("expanded_split")
+    comb_tot, comb_n = m.mla_timing_read("expanded_combine")
+    m.mla_timing_enable(False)
+    cache_bytes = float(d.lens.astype(np.int64).sum()) * H * (192 + 128) * 2
+    split_ms = split_tot / max(split_n, 1)
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 4), "cache_bytes": int(cache_bytes), "cache_gbps": round(cache_bytes / (ms * 1e-3) / 1e9, 1),
+            "kernels_ms": {"expanded_split": round(split_ms, 4), "expanded_combine": round(comb_tot / max(comb_n, 1), 4)},
+            "roofline": {"kernel": "expanded_split", "bound": "hbm",
+                         "achieved": round(cache_bytes / (split_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": round(cache_bytes / (split_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+            "bytes_vs_latent": round(H * 320 / 576, 2),
+            "time_vs_absorbed": round(ms / absorbed_ms, 2) if absorbed_ms else None}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +160,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-expanded", action="store_true",
+                    help="skip the expanded-cache decode comparator (needs 129 GB of device memory)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first copy 512 MiB device-to-device once (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
@@ -261,6 +308,8 @@ def main():
                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(split_gbps / PEAK_HBM_GBPS, 4),
                                   "traffic": recorded_traffic("absorbed_split", DECODE_SOURCES),
                                   "algorithmic": f"{cache_bytes / 1e9:.4f} GB of cache rows per launch"}
+    if decode and not args.no_expanded:
+        res["expanded_decode"] = expanded_comparator(m, dims, d, dq, dg, lens, dec_ms, kern.get("absorbed_split"))
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         res["cpu_baseline"] = cpu_baseline(p)

@@ -234,6 +234,20 @@ def decode_inputs(dims: Dims, lens, cap: int, tq: int, seed: int, bf16: bool,
     return DecodeInputs(dims, lens, int(cap), int(tq), q, w, g, bf16, seed)
 
 
+def expanded_rows(dims: Dims, L: int, seed: int, b: int = 0, bf16: bool = True):
+    """Per-head cache rows of one sequence for the expanded-cache decode:
+    K [H, L, N+S] and V [H, L, V], N(0,1) entries (the spread of K^C = c^KV W_UK,
+    k^S and V under the weight recipe), rounded to bf16; float32.
+
+    Sequence b draws from its own child stream of ``seed``.
+    """
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 13, b]))
+    H, D, V = dims.heads, dims.nope_dim + dims.shared_dim, dims.v_dim
+    k = _quant(_normal(rng, (H, L, D)), bf16)
+    v = _quant(_normal(rng, (H, L, V)), bf16)
+    return k, v
+
+
 def decode_lens(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
     """Per-sequence cache lengths, uniform integers in [lo, hi]."""
     rng = np.random.default_rng(np.random.SeedSequence([seed, 7]))
