@@ -15,8 +15,9 @@
 //    c, c+8, c+16 of the K row (192 bf16 = 24 units) and c, c+8 of the V row
 //    (16 units), so each 16-byte load instruction of the wave covers eight
 //    whole 128-byte lines. A pass covers 8 rows; four passes are loaded
-//    together. The score of a row is the sum over its eight lanes (three DPP
-//    steps). Every lane keeps an online softmax (max, sum, 16 output values)
+//    together, as nontemporal loads. The score of a row is the sum over its
+//    eight lanes (three DPP steps). Every lane keeps an online softmax (max,
+//    sum, 16 output values)
 //    over the rows of its row group; the eight groups are merged at the end
 //    and the partial (max, sum, 128 unnormalised outputs) is written.
 //  - Combine kernel: per (query, head), the log-sum-exp merge of the splits,
@@ -40,6 +41,13 @@ constexpr int kVU = kV / 8;   // 16-byte units per V row (16)
 constexpr int kKUL = kKU / 8;  // K units per lane (3)
 constexpr int kVUL = kVU / 8;  // V units per lane (2)
 constexpr int kPass = 4;       // 8-row passes loaded together
+
+// Cache rows are read once: nontemporal loads keep them from displacing
+// reusable lines in the caches.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16_stream(const uint16_t* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p)));
+}
 
 // Sum over the eight lanes of an aligned group (xor 1, xor 2 inside a quad,
 // then the other quad of the 8 through the half-row mirror).
@@ -105,9 +113,9 @@ __global__ void __launch_bounds__(256) expanded_split_kernel(
     for (int k = 0; k < kPass; ++k) {
       const int j = min(base + 8 * k + g, r1 - 1);   // rows past the split repeat its last row, then are masked
 #pragma unroll
-      for (int u = 0; u < kKUL; ++u) kr[k][u] = ldg16(kbase + static_cast<int64_t>(j) * kD + 64 * u);
+      for (int u = 0; u < kKUL; ++u) kr[k][u] = ldg16_stream(kbase + static_cast<int64_t>(j) * kD + 64 * u);
 #pragma unroll
-      for (int u = 0; u < kVUL; ++u) vr[k][u] = ldg16(vbase + static_cast<int64_t>(j) * kV + 64 * u);
+      for (int u = 0; u < kVUL; ++u) vr[k][u] = ldg16_stream(vbase + static_cast<int64_t>(j) * kV + 64 * u);
     }
     float s[kPass];
     float mb = -INFINITY;
