@@ -17,9 +17,9 @@
 //    whole 128-byte lines. A pass covers 8 rows; four passes are loaded
 //    together, as nontemporal loads. The score of a row is the sum over its
 //    eight lanes (three DPP steps). Every lane keeps an online softmax (max,
-//    sum, 16 output values)
-//    over the rows of its row group; the eight groups are merged at the end
-//    and the partial (max, sum, 128 unnormalised outputs) is written.
+//    sum, 16 output values) over the rows of its row group; the eight groups
+//    are merged at the end and the partial (max, sum, 128 unnormalised
+//    outputs) is written.
 //  - Combine kernel: per (query, head), the log-sum-exp merge of the splits,
 //    then the sigmoid gate.
 // The per-head maximum logit is the maximum of the fp32 scores, one atomic
