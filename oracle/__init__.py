@@ -19,10 +19,13 @@ from .mla_oracle import (  # noqa: F401
     expand_latent,
     expanded,
     expanded_cache,
+    layer_forward,
+    linear,
     max_logit_head,
     prefill,
     prefill_rows,
     q_projection,
     qk_clip,
+    rms_norm,
     round_to,
 )

@@ -360,6 +360,61 @@ def expanded(q, k_rows, v_rows, gate, dims):
 
 
 # ---------------------------------------------------------------------------
+# The whole gated MLA layer ([MLA] equation list, all 20 steps, and the
+# KimiMLAAttention constructor/forward excerpts): q_a_proj -> q_a_layernorm ->
+# q_b_proj; kv_a_proj_with_mqa -> [c^KV | k^S] -> kv_a_layernorm on c^KV;
+# g_proj; attention; o_proj. Every projection is nn.Linear without bias.
+# ---------------------------------------------------------------------------
+
+
+def linear(x, weight):
+    """nn.Linear without bias: y = x W^T, W = weight [out, in]."""
+    return np.asarray(x, dtype=f64) @ np.asarray(weight, dtype=f64).T
+
+
+def rms_norm(x, weight, eps: float):
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps), times the
+    learned per-feature weight. (The pages name KimiRMSNorm without printing
+    it; this is the standard definition, with eps a parameter.)"""
+    x = np.asarray(x, dtype=f64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x * r * np.asarray(weight, dtype=f64)
+
+
+def layer_forward(x, w_dq, g_q, w_uq, w_kv_a, g_kv, w_kv_b, w_g, w_o, cu_seqlens, dims, eps: float,
+                  round_bf16: bool = True):
+    """Delta_attn for packed sequences: the [MLA] equation list end to end.
+
+      c^Q = x W_DQ,  c^Q^ = RMSNorm(c^Q),  q = c^Q^ W_UQ  (q_b_proj),
+      [c^KV | k^S] = x W_DKV,  c^KV^ = RMSNorm(c^KV),
+      g = x W_g,  o = sigma(g) . attention(q, c^KV^, k^S)  (``prefill``),
+      Delta = o W_O.
+
+    x [Ntok, hidden]; weights in the nn.Linear layout [out, in]: w_dq
+    [q_rank, hidden], w_uq [H*D, q_rank], w_kv_a [R+S, hidden], w_kv_b
+    [H*(N+V), R], w_g [H*V, hidden], w_o [hidden, H*V]; g_q [q_rank] and g_kv
+    [R] are the RMSNorm weights. With ``round_bf16`` every activation that the
+    model keeps in its bf16 dtype (each projection's output and each norm's
+    output) is rounded to bf16 (nearest-even) where it is produced; the
+    arithmetic itself stays float64.
+
+    Returns (Delta [Ntok, hidden], max_logit [H]).
+    """
+    d = _dims(dims)
+    H, R, D = d.heads, d.kv_rank, d.nope_dim + d.shared_dim
+    rnd = (lambda a: round_to(a, "bf16")) if round_bf16 else (lambda a: np.asarray(a, dtype=f64))
+    n = np.asarray(x).shape[0]
+    cq = rnd(linear(x, w_dq))
+    q = rnd(linear(rnd(rms_norm(cq, g_q, eps)), w_uq)).reshape(n, H, D)
+    ckv_ks = rnd(linear(x, w_kv_a))
+    ckv = rnd(rms_norm(ckv_ks[:, :R], g_kv, eps))
+    ks = ckv_ks[:, R:]
+    g = rnd(linear(x, w_g))
+    o, _, smax = prefill(q, ckv, ks, w_kv_b, g, cu_seqlens, d)
+    return linear(rnd(o), w_o), smax
+
+
+# ---------------------------------------------------------------------------
 # Query projection ([MLA] "q = c^Q W_UQ") and QK-Clip ([CLIP])
 # ---------------------------------------------------------------------------
 

@@ -185,6 +185,58 @@ def clip_stress_inputs(dims: Dims, seqlen: int, seed: int, q_in: int = K3_Q_LORA
 
 
 # --------------------------------------------------------------------------
+# Whole-layer inputs (x and every projection of the attention layer)
+# --------------------------------------------------------------------------
+
+K3_HIDDEN = 7168
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    dims: Dims
+    hidden: int
+    q_rank: int
+    cu_seqlens: np.ndarray   # int32 [nseq+1]
+    x: np.ndarray            # [Ntok, hidden]
+    w_dq: np.ndarray         # q_a_proj.weight [q_rank, hidden]
+    g_q: np.ndarray          # q_a_layernorm.weight [q_rank]
+    w_uq: np.ndarray         # q_b_proj.weight [H*D, q_rank]
+    w_kv_a: np.ndarray       # kv_a_proj_with_mqa.weight [R+S, hidden]
+    g_kv: np.ndarray         # kv_a_layernorm.weight [R]
+    w_kv_b: np.ndarray       # kv_b_proj.weight [H*(N+V), R]
+    w_g: np.ndarray          # g_proj.weight [H*V, hidden]
+    w_o: np.ndarray          # o_proj.weight [hidden, H*V]
+    bf16: bool
+
+    @property
+    def ntok(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+
+def layer_inputs(dims: Dims, hidden: int, q_rank: int, seqlens, seed: int, bf16: bool = True) -> LayerInputs:
+    """Draw order: x, w_dq, g_q, w_uq, w_kv_a, g_kv, w_kv_b, w_g, w_o.
+
+    x ~ N(0,1); every projection N(0,1)/sqrt(fan_in); RMSNorm weights
+    1 + 0.1 N(0,1) (trained norms sit near their initial 1).
+    """
+    H, R, S, N, V = dims.heads, dims.kv_rank, dims.shared_dim, dims.nope_dim, dims.v_dim
+    D = N + S
+    rng = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    n = int(cu[-1])
+    x = _quant(_normal(rng, (n, hidden)), bf16)
+    w_dq = _quant(_normal(rng, (q_rank, hidden), 1.0 / math.sqrt(hidden)), bf16)
+    g_q = _quant(1.0 + _normal(rng, (q_rank,), 0.1), bf16)
+    w_uq = _quant(_normal(rng, (H * D, q_rank), 1.0 / math.sqrt(q_rank)), bf16)
+    w_kv_a = _quant(_normal(rng, (R + S, hidden), 1.0 / math.sqrt(hidden)), bf16)
+    g_kv = _quant(1.0 + _normal(rng, (R,), 0.1), bf16)
+    w_kv_b = _quant(_normal(rng, (H * (N + V), R), 1.0 / math.sqrt(R)), bf16)
+    w_g = _quant(_normal(rng, (H * V, hidden), 1.0 / math.sqrt(hidden)), bf16)
+    w_o = _quant(_normal(rng, (hidden, H * V), 1.0 / math.sqrt(H * V)), bf16)
+    return LayerInputs(dims, hidden, q_rank, cu, x, w_dq, g_q, w_uq, w_kv_a, g_kv, w_kv_b, w_g, w_o, bf16)
+
+
+# --------------------------------------------------------------------------
 # Absorbed-form (decode) inputs
 # --------------------------------------------------------------------------
 
@@ -296,6 +348,11 @@ def k3_clip_stress(seed: int = 3, seqlen: int = 2048) -> PrefillInputs:
 def k3_varlen(seed: int = 4, seqlens=VARLEN_SEQLENS) -> PrefillInputs:
     """Long-context packed varlen prefill: 32768 + 16384 + 8192 + 2048 tokens."""
     return prefill_inputs(K3, list(seqlens), seed, bf16=True)
+
+
+def k3_layer(seed: int = 5, seqlen: int = 4096) -> LayerInputs:
+    """The whole Kimi K3 attention layer (hidden 7168, q_lora_rank 1536) at T = seqlen."""
+    return layer_inputs(K3, K3_HIDDEN, K3_Q_LORA_RANK, [seqlen], seed, bf16=True)
 
 
 def k3_q_weight(seed: int = 11, q_in: int = K3_Q_LORA_RANK) -> np.ndarray:

@@ -364,6 +364,94 @@ def test_expanded_single_visible_row_returns_gated_value_row():
 
 
 # ---------------------------------------------------------------------------
+# The whole layer (projections, RMSNorms, attention, output projection)
+# ---------------------------------------------------------------------------
+
+
+def test_rms_norm_closed_forms():
+    w = np.array([1.0, 2.0, -0.5])
+    # a constant row c: mean(x^2) = c^2, so x / sqrt(c^2 + eps) = c / sqrt(c^2 + eps)
+    c, eps = 3.0, 1e-6
+    got = oracle.rms_norm(np.full((1, 3), c), w, eps)
+    assert np.allclose(got, w * c / math.sqrt(c * c + eps), rtol=1e-15, atol=0)
+    # [3, 4, 0]: mean of squares 25/3
+    got = oracle.rms_norm(np.array([[3.0, 4.0, 0.0]]), w, 0.0)
+    assert np.allclose(got, np.array([3.0, 8.0, 0.0]) / math.sqrt(25.0 / 3.0), rtol=1e-15, atol=0)
+    # scale invariance (eps = 0) and eps only matters near zero
+    x = np.random.default_rng(1).standard_normal((4, 3))
+    assert np.allclose(oracle.rms_norm(7.5 * x, w, 0.0), oracle.rms_norm(x, w, 0.0), rtol=1e-13, atol=0)
+
+
+def test_linear_matches_brute_force_sums():
+    rng = np.random.default_rng(2)
+    x, w = rng.standard_normal((3, 5)), rng.standard_normal((4, 5))
+    want = np.array([[sum(x[i, k] * w[j, k] for k in range(5)) for j in range(4)] for i in range(3)])
+    assert np.allclose(oracle.linear(x, w), want, rtol=1e-14, atol=1e-15)
+
+
+def _tiny_layer(seed=3, seqlens=(9, 14)):
+    return synth.layer_inputs(synth.TINY, 40, 24, list(seqlens), seed, bf16=False)
+
+
+def _layer(L, eps=1e-6, **over):
+    a = dict(x=L.x, w_dq=L.w_dq, g_q=L.g_q, w_uq=L.w_uq, w_kv_a=L.w_kv_a, g_kv=L.g_kv, w_kv_b=L.w_kv_b, w_g=L.w_g,
+             w_o=L.w_o)
+    a.update(over)
+    return oracle.layer_forward(a["x"], a["w_dq"], a["g_q"], a["w_uq"], a["w_kv_a"], a["g_kv"], a["w_kv_b"], a["w_g"],
+                                a["w_o"], L.cu_seqlens, L.dims, eps, round_bf16=False)
+
+
+def test_layer_norms_follow_the_down_projections():
+    """The RMSNorms sit on c^Q and on c^KV only: scaling W_DQ, or the c^KV rows
+    of W_DKV, leaves Delta unchanged (eps = 0); scaling the k^S rows does not."""
+    L = _tiny_layer()
+    R = L.dims.kv_rank
+    ref, sm = _layer(L, eps=0.0)
+    wkv = L.w_kv_a.copy()
+    wkv[:R] *= 8.0   # powers of two: the scaled weights are exact
+    got, sm2 = _layer(L, eps=0.0, w_dq=L.w_dq * 4.0, w_kv_a=wkv)
+    assert rel_err(got, ref) < 1e-10 and np.allclose(sm2, sm, rtol=1e-10)
+    wks = L.w_kv_a.copy()
+    wks[R:] *= 8.0
+    assert rel_err(_layer(L, eps=0.0, w_kv_a=wks)[0], ref) > 1e-3
+
+
+def test_layer_zero_query_projection_gives_gated_prefix_mean():
+    """W_UQ = 0 makes every visible score 0: token t of a sequence gets
+    sigma(g_t) times the mean of V over the sequence's first t+1 tokens, and
+    Delta_t is that times W_O^T."""
+    L = _tiny_layer()
+    d = L.dims
+    H, R, N, V = d.heads, d.kv_rank, d.nope_dim, d.v_dim
+    got, sm = _layer(L, w_uq=np.zeros_like(L.w_uq))
+    ckv = oracle.rms_norm(oracle.linear(L.x, L.w_kv_a)[:, :R], L.g_kv, 1e-6)
+    sig = 1.0 / (1.0 + np.exp(-oracle.linear(L.x, L.w_g)))
+    want = np.zeros((L.ntok, H * V))
+    for h in range(H):
+        vh = ckv @ L.w_kv_b[h * (N + V) + N:(h + 1) * (N + V)].T
+        for a, b in zip(L.cu_seqlens[:-1], L.cu_seqlens[1:]):
+            csum = np.cumsum(vh[a:b], axis=0) / np.arange(1, b - a + 1)[:, None]
+            want[a:b, h * V:(h + 1) * V] = csum
+    want = (sig * want) @ L.w_o.T
+    assert rel_err(got, want) < 1e-12
+    assert np.all(sm == 0.0)
+
+
+def test_layer_is_causal_within_each_sequence():
+    """Changing token t of the second sequence changes Delta only at that
+    sequence's rows from t on."""
+    L = _tiny_layer()
+    ref, _ = _layer(L)
+    x2 = L.x.copy()
+    t = 9 + 6
+    x2[t] += 1.0
+    got, _ = _layer(L, x=x2)
+    diff = np.abs(got - ref).max(axis=1)
+    assert np.all(diff[:t] == 0.0)
+    assert np.all(diff[t:] > 0.0)
+
+
+# ---------------------------------------------------------------------------
 # QK-Clip
 # ---------------------------------------------------------------------------
 
