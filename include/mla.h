@@ -207,6 +207,58 @@ mla_status mla_expanded(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* The whole attention layer ("Kimi K3 · Gated MLA", all 20 steps) and its    */
+/* building blocks                                                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * nn.Linear without bias, as every projection of the layer: y = x W^T.
+ * x [m, k], w [n, k] (weight [out, in]), y [m, n]; bf16, fp32 accumulation,
+ * one rounding to bf16. k a multiple of 128 (at most 65536), n a multiple of 8.
+ */
+mla_status mla_linear(mla_dtype dtype, const void* x, int64_t m, int32_t k, const void* w, int32_t n,
+                      void* y, hipStream_t stream);
+
+/*
+ * RMSNorm over rows of n features: y = x / sqrt(mean(x^2) + eps) * weight.
+ * The pages name KimiRMSNorm (q_a_layernorm, kv_a_layernorm) without printing
+ * it; this is the standard definition, with eps a parameter. x, y [rows, n],
+ * weight [n]; bf16 with fp32 arithmetic and one rounding. n a multiple of 8,
+ * at most 2048.
+ */
+mla_status mla_rms_norm(mla_dtype dtype, const void* x, int64_t rows, int32_t n, const void* weight, float eps,
+                        void* y, hipStream_t stream);
+
+/* Bytes of scratch memory mla_layer_forward needs (0 for invalid sizes). */
+size_t mla_layer_workspace_size(const mla_dims* dims, int32_t hidden, int32_t q_rank,
+                                int64_t total_tokens, int32_t nseq);
+
+/*
+ * Delta_attn of the gated MLA layer for packed sequences, the equation list of
+ * "Kimi K3 · Gated MLA" end to end with the KimiMLAAttention projections:
+ *   c^Q = x W_DQ (q_a_proj), c^Q^ = RMSNorm(c^Q) (q_a_layernorm),
+ *   q = c^Q^ W_UQ (q_b_proj), [c^KV | k^S] = x W_DKV (kv_a_proj_with_mqa),
+ *   c^KV^ = RMSNorm(c^KV) (kv_a_layernorm), g = x W_g (g_proj),
+ *   o = sigma(g) . causal attention (as mla_prefill), Delta = o W_O (o_proj).
+ * Every activation between the steps is kept in bf16 (the model's dtype);
+ * products accumulate in fp32.
+ *
+ * x       [total_tokens, hidden]        w_dq   [q_rank, hidden]   g_q  [q_rank]
+ * w_uq    [H*(N+S), q_rank]             w_kv_a [R+S, hidden]      g_kv [R]
+ * w_kv_b  [H*(N+V), R]                  w_g    [H*V, hidden]      w_o  [hidden, H*V]
+ * out     [total_tokens, hidden]        all bf16; cu_seqlens and max_logit as mla_prefill.
+ * Kimi K3 head shape; hidden a multiple of 128 (at most 65536), q_rank a
+ * multiple of 128 (at most 2048).
+ */
+mla_status mla_layer_forward(const mla_dims* dims, int32_t hidden, int32_t q_rank, float eps,
+                             const void* x, const void* w_dq, const void* g_q, const void* w_uq,
+                             const void* w_kv_a, const void* g_kv, const void* w_kv_b,
+                             const void* w_g, const void* w_o,
+                             const int32_t* cu_seqlens, int32_t nseq, int64_t total_tokens,
+                             void* out, float* max_logit, int32_t accumulate,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* QK-Clip ("SOTA-131": rescale the query and key projection weights of every
  * head whose maximum logit exceeds tau)                                     */
 /* ------------------------------------------------------------------------ */

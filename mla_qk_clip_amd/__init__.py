@@ -23,7 +23,8 @@ MLA_F32, MLA_BF16 = 0, 1
 
 EXPORTED = (
     "mla_prefill_workspace_size", "mla_prefill", "mla_absorbed_workspace_size", "mla_absorbed",
-    "mla_expanded_workspace_size", "mla_expanded", "mla_qk_clip", "mla_status_string", "mla_last_error", "mla_version", "mla_timing_enable",
+    "mla_expanded_workspace_size", "mla_expanded", "mla_linear", "mla_rms_norm", "mla_layer_workspace_size",
+    "mla_layer_forward", "mla_qk_clip", "mla_status_string", "mla_last_error", "mla_version", "mla_timing_enable",
     "mla_timing_read",
 )
 
@@ -74,6 +75,14 @@ def _load():
     lib.mla_expanded_workspace_size.restype = SZ
     lib.mla_expanded.argtypes = [D, I32, I32, P, P, P, I64, P, I32, I32, P, P, P, I32, P, SZ, P]
     lib.mla_expanded.restype = I32
+    lib.mla_linear.argtypes = [I32, P, I64, I32, P, I32, P, P]
+    lib.mla_linear.restype = I32
+    lib.mla_rms_norm.argtypes = [I32, P, I64, I32, P, F, P, P]
+    lib.mla_rms_norm.restype = I32
+    lib.mla_layer_workspace_size.argtypes = [D, I32, I32, I64, I32]
+    lib.mla_layer_workspace_size.restype = SZ
+    lib.mla_layer_forward.argtypes = [D, I32, I32, F, P, P, P, P, P, P, P, P, P, P, I32, I64, P, P, I32, P, SZ, P]
+    lib.mla_layer_forward.restype = I32
     lib.mla_qk_clip.argtypes = [D, I32, P, I32, P, P, F, P, P, P]
     lib.mla_qk_clip.restype = I32
     lib.mla_status_string.argtypes = [I32]
@@ -268,6 +277,80 @@ def mla_expanded(dims: Dims, q, k_cache, v_cache, lens, gate, *, out_dtype=None,
     st = lib.mla_expanded(ctypes.byref(dims.c()), in_dt, out_dt, _ptr(q), _ptr(k_cache), _ptr(v_cache), cap,
                           _ptr(lens), B, Tq, _ptr(gate), _ptr(out), _ptr(max_logit), 1 if accumulate else 0,
                           _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st)
+    return out, max_logit
+
+
+def mla_linear(x, w, *, out=None, stream=None):
+    """y = x W^T (nn.Linear without bias; see ``mla_linear`` in include/mla.h). x [m, k], w [n, k], bf16."""
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError(f"x must be [m, k] and w [n, k], got {tuple(x.shape)}, {tuple(w.shape)}")
+    m, k = x.shape
+    n = w.shape[0]
+    _expect("x", x, (m, k), torch.bfloat16)
+    _expect("w", w, (n, k), torch.bfloat16)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _expect("out", out, (m, n), torch.bfloat16)
+    _check(lib.mla_linear(MLA_BF16, _ptr(x), m, k, _ptr(w), n, _ptr(out), _stream(stream)))
+    return out
+
+
+def mla_rms_norm(x, weight, eps: float, *, out=None, stream=None):
+    """RMSNorm over the rows of x [rows, n] with weight [n] (see ``mla_rms_norm`` in include/mla.h), bf16."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [rows, n], got {tuple(x.shape)}")
+    rows, n = x.shape
+    _expect("x", x, (rows, n), torch.bfloat16)
+    _expect("weight", weight, (n,), torch.bfloat16)
+    if out is None:
+        out = torch.empty_like(x)
+    _expect("out", out, (rows, n), torch.bfloat16)
+    _check(lib.mla_rms_norm(MLA_BF16, _ptr(x), rows, n, _ptr(weight), float(eps), _ptr(out), _stream(stream)))
+    return out
+
+
+def mla_layer_workspace_size(dims: Dims, hidden: int, q_rank: int, total_tokens: int, nseq: int) -> int:
+    return int(lib.mla_layer_workspace_size(ctypes.byref(dims.c()), hidden, q_rank, total_tokens, nseq))
+
+
+def mla_layer_forward(dims: Dims, x, w_dq, g_q, w_uq, w_kv_a, g_kv, w_kv_b, w_g, w_o, cu_seqlens, *, eps=1e-6,
+                      out=None, max_logit=None, accumulate=False, workspace=None, stream=None):
+    """Delta_attn of the whole gated MLA layer (see ``mla_layer_forward`` in include/mla.h), bf16.
+
+    x [T, hidden]; weights in the nn.Linear layout [out, in]; cu_seqlens int32 [nseq+1] on the device.
+    Returns (out [T, hidden], max_logit [H]).
+    """
+    if x.dim() != 2:
+        raise ValueError(f"x must be [tokens, hidden], got {tuple(x.shape)}")
+    T, hidden = x.shape
+    q_rank = w_dq.shape[0]
+    H, R, S, N, V = dims.heads, dims.kv_rank, dims.shared_dim, dims.nope_dim, dims.v_dim
+    bf = torch.bfloat16
+    _expect("x", x, (T, hidden), bf)
+    _expect("w_dq", w_dq, (q_rank, hidden), bf)
+    _expect("g_q", g_q, (q_rank,), bf)
+    _expect("w_uq", w_uq, (H * (N + S), q_rank), bf)
+    _expect("w_kv_a", w_kv_a, (R + S, hidden), bf)
+    _expect("g_kv", g_kv, (R,), bf)
+    _expect("w_kv_b", w_kv_b, (H * (N + V), R), bf)
+    _expect("w_g", w_g, (H * V, hidden), bf)
+    _expect("w_o", w_o, (hidden, H * V), bf)
+    nseq = cu_seqlens.shape[0] - 1
+    _expect("cu_seqlens", cu_seqlens, (nseq + 1,), torch.int32)
+    if out is None:
+        out = torch.empty((T, hidden), dtype=bf, device=x.device)
+    if max_logit is None:
+        max_logit = torch.empty(H, dtype=torch.float32, device=x.device)
+    _expect("out", out, (T, hidden), bf)
+    _expect("max_logit", max_logit, (H,), torch.float32)
+    need = mla_layer_workspace_size(dims, hidden, q_rank, T, nseq)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib.mla_layer_forward(ctypes.byref(dims.c()), hidden, q_rank, float(eps), _ptr(x), _ptr(w_dq), _ptr(g_q),
+                               _ptr(w_uq), _ptr(w_kv_a), _ptr(g_kv), _ptr(w_kv_b), _ptr(w_g), _ptr(w_o),
+                               _ptr(cu_seqlens), nseq, T, _ptr(out), _ptr(max_logit), 1 if accumulate else 0,
+                               _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st)
     return out, max_logit
 

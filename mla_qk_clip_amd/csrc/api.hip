@@ -266,6 +266,99 @@ mla_status mla_expanded(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_
   return MLA_OK;
 }
 
+mla_status mla_linear(mla_dtype dtype, const void* x, int64_t m, int32_t k, const void* w, int32_t n, void* y,
+                      hipStream_t stream) {
+  g_last_error.clear();
+  if (dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "mla_linear takes bf16 only");
+  if (m < 0 || m > (int64_t{1} << 30)) return fail(MLA_ERR_INVALID, "m must be in [0, 2^30]");
+  if (k < 128 || k % 128 != 0 || k > 65536)
+    return fail(MLA_ERR_UNSUPPORTED, "k must be a multiple of 128 in [128, 65536]");
+  if (n < 8 || n % 8 != 0) return fail(MLA_ERR_UNSUPPORTED, "n must be a positive multiple of 8");
+  if (m == 0) return MLA_OK;
+  REQUIRE_PTR(x, 16);
+  REQUIRE_PTR(w, 16);
+  REQUIRE_PTR(y, 16);
+  const hipError_t e = mla::launch_linear_bf16(x, m, k, w, n, y, stream);
+  if (e != hipSuccess) return hip_fail(e, "mla_linear launch");
+  return MLA_OK;
+}
+
+mla_status mla_rms_norm(mla_dtype dtype, const void* x, int64_t rows, int32_t n, const void* weight, float eps,
+                        void* y, hipStream_t stream) {
+  g_last_error.clear();
+  if (dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "mla_rms_norm takes bf16 only");
+  if (rows < 0) return fail(MLA_ERR_INVALID, "rows must be >= 0");
+  if (n < 8 || n % 8 != 0 || n > 2048) return fail(MLA_ERR_UNSUPPORTED, "n must be a multiple of 8 in [8, 2048]");
+  if (!(eps >= 0.0f) || !isfinite(eps)) return fail(MLA_ERR_INVALID, "eps must be finite and >= 0");
+  if (rows == 0) return MLA_OK;
+  REQUIRE_PTR(x, 16);
+  REQUIRE_PTR(weight, 16);
+  REQUIRE_PTR(y, 16);
+  const hipError_t e = mla::launch_rms_norm_bf16(x, rows, n, weight, eps, y, stream);
+  if (e != hipSuccess) return hip_fail(e, "mla_rms_norm launch");
+  return MLA_OK;
+}
+
+size_t mla_layer_workspace_size(const mla_dims* dims, int32_t hidden, int32_t q_rank, int64_t total_tokens,
+                                int32_t nseq) {
+  Shape s;
+  if (check_dims(dims, MLA_BF16, &s) != MLA_OK || hidden < 128 || q_rank < 128 || total_tokens < 0 || nseq < 0)
+    return 0;
+  return mla::layer_ws_layout(s.H, hidden, q_rank, total_tokens, nseq).total;
+}
+
+mla_status mla_layer_forward(const mla_dims* dims, int32_t hidden, int32_t q_rank, float eps, const void* x,
+                             const void* w_dq, const void* g_q, const void* w_uq, const void* w_kv_a,
+                             const void* g_kv, const void* w_kv_b, const void* w_g, const void* w_o,
+                             const int32_t* cu_seqlens, int32_t nseq, int64_t total_tokens, void* out,
+                             float* max_logit, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  g_last_error.clear();
+  Shape s;
+  mla_status st = check_dims(dims, MLA_BF16, &s);
+  if (st != MLA_OK) return st;
+  if (hidden < 128 || hidden % 128 != 0 || hidden > 65536)
+    return fail(MLA_ERR_UNSUPPORTED, "hidden must be a multiple of 128 in [128, 65536]");
+  if (q_rank < 128 || q_rank % 128 != 0 || q_rank > 2048)
+    return fail(MLA_ERR_UNSUPPORTED, "q_rank must be a multiple of 128 in [128, 2048]");
+  if (!(eps >= 0.0f) || !isfinite(eps)) return fail(MLA_ERR_INVALID, "eps must be finite and >= 0");
+  if (nseq < 0 || total_tokens < 0) return fail(MLA_ERR_INVALID, "nseq and total_tokens must be >= 0");
+  if (nseq == 0 && total_tokens != 0) return fail(MLA_ERR_INVALID, "total_tokens > 0 needs nseq >= 1");
+  if (total_tokens > (int64_t{1} << 30)) return fail(MLA_ERR_UNSUPPORTED, "total_tokens above 2^30");
+  if (accumulate != 0 && accumulate != 1) return fail(MLA_ERR_INVALID, "accumulate must be 0 or 1");
+  REQUIRE_PTR(max_logit, 4);
+  if (total_tokens > 0) {
+    REQUIRE_PTR(x, 16);
+    REQUIRE_PTR(w_dq, 16);
+    REQUIRE_PTR(g_q, 16);
+    REQUIRE_PTR(w_uq, 16);
+    REQUIRE_PTR(w_kv_a, 16);
+    REQUIRE_PTR(g_kv, 16);
+    REQUIRE_PTR(w_kv_b, 16);
+    REQUIRE_PTR(w_g, 16);
+    REQUIRE_PTR(w_o, 16);
+    REQUIRE_PTR(cu_seqlens, 4);
+    REQUIRE_PTR(out, 16);
+    const size_t need = mla_layer_workspace_size(dims, hidden, q_rank, total_tokens, nseq);
+    if (!workspace || workspace_bytes < need)
+      return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    if (!aligned(workspace, 16)) return fail(MLA_ERR_INVALID, "workspace is not 16-byte aligned");
+  }
+  hipError_t e = hipSuccess;
+  if (total_tokens == 0) {
+    if (!accumulate) {
+      e = mla::launch_fill(max_logit, s.H, -INFINITY, stream);
+      if (e != hipSuccess) return hip_fail(e, "max_logit init");
+    }
+    return MLA_OK;
+  }
+  e = mla::launch_layer_bf16(s.H, s.scale, hidden, q_rank, eps, x, w_dq, g_q, w_uq, w_kv_a, g_kv, w_kv_b, w_g, w_o,
+                             cu_seqlens, nseq, total_tokens, out, max_logit, !accumulate, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "mla_layer_forward launch");
+  return MLA_OK;
+}
+
 mla_status mla_qk_clip(const mla_dims* dims, mla_dtype wdtype, void* w_q_b, int32_t q_in, void* w_kv_b,
                        const float* max_logit, float tau, uint8_t* clipped, float* gamma, hipStream_t stream) {
   g_last_error.clear();

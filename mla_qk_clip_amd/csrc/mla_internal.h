@@ -134,6 +134,30 @@ inline ExpandedWs expanded_ws_layout(int heads, int batch, int tq, int64_t cap) 
   return w;
 }
 
+// Workspace of the bf16 whole layer: the projections' outputs and the norms'
+// (bf16, row-major), then the prefill's own workspace.
+constexpr int kGemmMaxProblems = 3;
+struct LayerWs {
+  size_t cq, ckv_raw, g, cqn, ckvn, ks, q, o, prefill, total;
+};
+inline LayerWs layer_ws_layout(int heads, int hidden, int q_rank, int64_t ntok, int nseq) {
+  (void)hidden;
+  LayerWs w{};
+  const size_t T = static_cast<size_t>(ntok);
+  size_t off = 0;
+  w.cq = off; off = align_up(off + T * q_rank * 2, 256);
+  w.ckv_raw = off; off = align_up(off + T * (kR + kS) * 2, 256);
+  w.g = off; off = align_up(off + T * heads * kV * 2, 256);
+  w.cqn = off; off = align_up(off + T * q_rank * 2, 256);
+  w.ckvn = off; off = align_up(off + T * kR * 2, 256);
+  w.ks = off; off = align_up(off + T * kS * 2, 256);
+  w.q = off; off = align_up(off + T * heads * kD * 2, 256);
+  w.o = off; off = align_up(off + T * heads * kV * 2, 256);
+  w.prefill = off; off = align_up(off + prefill_ws_layout(heads, ntok, nseq).total, 256);
+  w.total = off;
+  return w;
+}
+
 // ---- launchers (defined next to their kernels) ----
 
 hipError_t launch_fill(float* p, int n, float v, hipStream_t st);
@@ -157,6 +181,15 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16,
 hipError_t launch_expanded_bf16(int heads, float scale, bool out_bf16, const void* q, const void* kcache,
                                 const void* vcache, int64_t cap, const int32_t* lens, int batch, int tq,
                                 const void* gate, void* out, float* max_logit, void* ws, hipStream_t st);
+
+hipError_t launch_linear_bf16(const void* x, int64_t m, int k, const void* w, int n, void* y, hipStream_t st);
+hipError_t launch_rms_norm_bf16(const void* x, int64_t rows, int n, const void* w, float eps, void* y,
+                                hipStream_t st);
+hipError_t launch_layer_bf16(int heads, float scale, int hidden, int q_rank, float eps, const void* x,
+                             const void* w_dq, const void* g_q, const void* w_uq, const void* w_kv_a,
+                             const void* g_kv, const void* w_kv_b, const void* w_g, const void* w_o,
+                             const int32_t* cu, int nseq, int64_t ntok, void* out, float* max_logit,
+                             bool init_max_logit, void* ws, hipStream_t st);
 
 hipError_t launch_absorbed_f32(int heads, int R, int S, int N, int V, float scale,
                                const float* q, const float* cache, int64_t cap, const int32_t* lens,

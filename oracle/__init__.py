@@ -20,6 +20,7 @@ from .mla_oracle import (  # noqa: F401
     expanded,
     expanded_cache,
     layer_forward,
+    layer_rows,
     linear,
     max_logit_head,
     prefill,

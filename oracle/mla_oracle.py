@@ -414,6 +414,32 @@ def layer_forward(x, w_dq, g_q, w_uq, w_kv_a, g_kv, w_kv_b, w_g, w_o, cu_seqlens
     return linear(rnd(o), w_o), smax
 
 
+def layer_rows(x, w_dq, g_q, w_uq, w_kv_a, g_kv, w_kv_b, w_g, w_o, cu_seqlens, dims, eps: float, rows,
+               round_bf16: bool = True):
+    """``layer_forward`` for the listed global token rows only (spot checks at
+    sizes the full oracle cannot finish): q, c^KV^ and k^S are formed for every
+    token (the rows attend to their whole prefix), the gate and the output only
+    for the listed rows.
+
+    Returns (Delta [len(rows), hidden], q [Ntok, H, D], c^KV^ [Ntok, R], k^S [Ntok, S]).
+    """
+    d = _dims(dims)
+    H, R, V, D = d.heads, d.kv_rank, d.v_dim, d.nope_dim + d.shared_dim
+    rnd = (lambda a: round_to(a, "bf16")) if round_bf16 else (lambda a: np.asarray(a, dtype=f64))
+    n = np.asarray(x).shape[0]
+    rows = [int(t) for t in rows]
+    q = rnd(linear(rnd(rms_norm(rnd(linear(x, w_dq)), g_q, eps)), w_uq)).reshape(n, H, D)
+    ckv_ks = rnd(linear(x, w_kv_a))
+    ckv = rnd(rms_norm(ckv_ks[:, :R], g_kv, eps))
+    ks = ckv_ks[:, R:]
+    g = np.zeros((n, H * V), dtype=f64)
+    g[rows] = rnd(linear(np.asarray(x)[rows], w_g))
+    o = np.zeros((len(rows), H * V), dtype=f64)
+    for h in range(H):
+        o[:, h * V:(h + 1) * V] = prefill_rows(q, ckv, ks, w_kv_b, g, cu_seqlens, d, h, rows)[0]
+    return linear(rnd(o), w_o), q, ckv, ks
+
+
 # ---------------------------------------------------------------------------
 # Query projection ([MLA] "q = c^Q W_UQ") and QK-Clip ([CLIP])
 # ---------------------------------------------------------------------------

@@ -451,6 +451,15 @@ def test_layer_is_causal_within_each_sequence():
     assert np.all(diff[t:] > 0.0)
 
 
+def test_layer_rows_equals_full_layer_on_listed_rows():
+    L = synth.layer_inputs(synth.TINY, 40, 24, [9, 14], 7, bf16=True)
+    args = (L.x, L.w_dq, L.g_q, L.w_uq, L.w_kv_a, L.g_kv, L.w_kv_b, L.w_g, L.w_o, L.cu_seqlens, L.dims, 1e-6)
+    full, _ = oracle.layer_forward(*args)
+    rows = [0, 8, 9, 15, 22]
+    part = oracle.layer_rows(*args, rows)[0]
+    assert np.array_equal(part, full[rows])
+
+
 # ---------------------------------------------------------------------------
 # QK-Clip
 # ---------------------------------------------------------------------------
