@@ -108,6 +108,63 @@ def cpu_baseline(p, budget_s: float = 12.0):
             "sample": f"{heads} of {H} heads of the T={T} prefill (fp64 NumPy), {dt:.1f} s"}
 
 
+def layer_leg(m, dims, steps: int = 5):
+    """The whole gated MLA layer (hidden 7168, q_lora_rank 1536, 96 heads) at
+    T = 4096: projections of x, RMSNorms, q up-projection, attention, output
+    projection. Seeded random-init weights of that architecture."""
+    import torch
+    import synth
+    L = synth.k3_layer()
+    T, hid, qr = L.ntok, L.hidden, L.q_rank
+    H, R, S, D, V = 96, 512, 64, 192, 128
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
+    log("whole-layer leg (T=4096, hidden 7168)")
+    t = [up(a) for a in (L.x, L.w_dq, L.g_q, L.w_uq, L.w_kv_a, L.g_kv, L.w_kv_b, L.w_g, L.w_o)]
+    cu = torch.from_numpy(L.cu_seqlens).cuda()
+    out = torch.empty((T, hid), dtype=torch.bfloat16, device="cuda")
+    ml = torch.empty(H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.mla_layer_workspace_size(dims, hid, qr, T, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        m.mla_layer_forward(dims, *t, cu, out=out, max_logit=ml, workspace=ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    m.mla_timing_enable(True)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    kern = {}
+    for k in ("layer_proj_x", "layer_norm", "layer_proj_q", "prefill_plan", "prefill_expand", "prefill_attn",
+              "prefill_refine_rows", "prefill_refine_score", "layer_proj_o"):
+        tot, n = m.mla_timing_read(k)
+        if n:
+            kern[k] = tot / n
+    m.mla_timing_enable(False)
+    gf = {"layer_proj_x": 2.0 * T * hid * (qr + R + S + H * V), "layer_proj_q": 2.0 * T * qr * H * D,
+          "layer_proj_o": 2.0 * T * H * V * hid}
+    qk, pv, ex = prefill_flops(T, H)
+    total = sum(gf.values()) + qk + pv + ex
+    gx = gf["layer_proj_x"] / (kern["layer_proj_x"] * 1e-3) / 1e12
+    return {"workload": "Kimi K3 gated MLA layer, T=4096, hidden 7168, q_lora_rank 1536, H=96, bf16",
+            "ms": round(ms, 4), "gflop": round(total / 1e9, 1), "tflops": round(total / (ms * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(total / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+            "roofline": {"kernel": "layer_proj_x", "bound": "mfma", "achieved": round(gx, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(gx / PEAK_BF16_TFLOPS, 4),
+                         "algorithmic": f"{gf['layer_proj_x'] / 1e9:.1f} GFLOP per launch (x W^T for q_a, kv_a, g)"}}
+
+
 def expanded_comparator(m, dims, d, dq, dg, lens, absorbed_ms, absorbed_split_ms, steps: int = 3):
     """The decode workload over a per-head cache (K 192 + V 128 values per head
     and token, the materialised form) instead of the latent rows: the bytes the
@@ -160,6 +217,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer leg")
     ap.add_argument("--no-expanded", action="store_true",
                     help="skip the expanded-cache decode comparator (needs 129 GB of device memory)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -308,6 +366,8 @@ def main():
                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(split_gbps / PEAK_HBM_GBPS, 4),
                                   "traffic": recorded_traffic("absorbed_split", DECODE_SOURCES),
                                   "algorithmic": f"{cache_bytes / 1e9:.4f} GB of cache rows per launch"}
+    if not args.no_layer:
+        res["layer"] = layer_leg(m, dims)
     if decode and not args.no_expanded:
         res["expanded_decode"] = expanded_comparator(m, dims, d, dq, dg, lens, dec_ms, kern.get("absorbed_split"))
     if not args.no_cpu_baseline:
