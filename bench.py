@@ -81,6 +81,10 @@ PREFILL_SOURCES = ("mla_qk_clip_amd/csrc/prefill_bf16.hip", "mla_qk_clip_amd/csr
                    "mla_qk_clip_amd/csrc/mla_internal.h")
 DECODE_SOURCES = ("mla_qk_clip_amd/csrc/absorbed_bf16.hip", "mla_qk_clip_amd/csrc/mla_common.h",
                   "mla_qk_clip_amd/csrc/mla_internal.h")
+EXPANDED_SOURCES = ("mla_qk_clip_amd/csrc/expanded_bf16.hip", "mla_qk_clip_amd/csrc/mla_common.h",
+                    "mla_qk_clip_amd/csrc/mla_internal.h")
+LAYER_SOURCES = ("mla_qk_clip_amd/csrc/layer_bf16.hip", "mla_qk_clip_amd/csrc/mla_common.h",
+                 "mla_qk_clip_amd/csrc/mla_internal.h")
 
 
 def cpu_baseline(p, budget_s: float = 12.0):
@@ -162,6 +166,7 @@ def layer_leg(m, dims, steps: int = 5):
             "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
             "roofline": {"kernel": "layer_proj_x", "bound": "mfma", "achieved": round(gx, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(gx / PEAK_BF16_TFLOPS, 4),
+                         "traffic": recorded_traffic("layer_proj_x", LAYER_SOURCES),
                          "algorithmic": f"{gf['layer_proj_x'] / 1e9:.1f} GFLOP per launch (x W^T for q_a, kv_a, g)"}}
 
 
@@ -205,7 +210,8 @@ def expanded_comparator(m, dims, d, dq, dg, lens, absorbed_ms, absorbed_split_ms
             "kernels_ms": {"expanded_split": round(split_ms, 4), "expanded_combine": round(comb_tot / max(comb_n, 1), 4)},
             "roofline": {"kernel": "expanded_split", "bound": "hbm",
                          "achieved": round(cache_bytes / (split_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
-                         "unit": "GB/s", "frac": round(cache_bytes / (split_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+                         "unit": "GB/s", "frac": round(cache_bytes / (split_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                         "traffic": recorded_traffic("expanded_split", EXPANDED_SOURCES)},
             "bytes_vs_latent": round(H * 320 / 576, 2),
             "time_vs_absorbed": round(ms / absorbed_ms, 2) if absorbed_ms else None}
 
