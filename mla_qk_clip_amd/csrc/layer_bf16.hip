@@ -56,13 +56,19 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
   __shared__ uint4 As0[kGmUnits], As1[kGmUnits];
   __shared__ uint4 Bs0[kGmUnits], Bs1[kGmUnits];
 
-  // item = (column tile, row tile), row tile fastest; consecutive items of an
-  // XCD share a B tile and walk the A tiles
+  // items are dealt to the XCDs in contiguous ranges (block b runs on XCD b % 8)
   const int total = args.mtiles * args.ntiles;
   const int per_xcd = (total + 7) >> 3;
   const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (item >= total) return;
-  const int nt = item / args.mtiles, mt = item - nt * args.mtiles;
+  // groups of 8 row tiles x all column tiles, row tile fastest inside a group:
+  // an XCD's 32 concurrent workgroups cover 8 row tiles x 4 column tiles
+  constexpr int kGroupM = 8;
+  const int group = item / (kGroupM * args.ntiles);
+  const int first_m = group * kGroupM;
+  const int gm = min(args.mtiles - first_m, kGroupM);
+  const int in_group = item - group * kGroupM * args.ntiles;
+  const int mt = first_m + in_group % gm, nt = in_group / gm;
   // this tile's problem (selected field by field: indexing the argument array
   // would copy it to private memory)
   const bool p1 = args.nprob > 1 && nt >= args.p[1].tile0;
