@@ -12,7 +12,13 @@ layers, inputs resident in HBM:
 causal pairs) from HIP events around the prefill calls; the decode's cache
 GB/s and the per-kernel roofline figures are reported beside it.
 
+Two legs are timed apart from the step and reported in their own objects:
+``layer`` (the whole attention layer at T=4096: projections, RMSNorms,
+attention, output projection) and ``expanded_decode`` (the decode workload over
+a per-head K/V cache, the comparator of the latent cache).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-decode] [--no-layer] [--no-expanded]
 """
 from __future__ import annotations
 
@@ -230,7 +236,7 @@ def main():
                     help="first copy 512 MiB device-to-device once (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
 
