@@ -107,3 +107,28 @@ def test_layer_k3_4096_sampled(lib):
     for h in (0, 41, 95):
         want = oracle.max_logit_head(q, ckv, ks, L.w_kv_b, L.cu_seqlens, L.dims, h)
         assert abs(sm[h] - want) <= SMAX_TOL * abs(want), (h, sm[h], want)
+
+
+def test_empty_inputs_only_reset_the_max_logit(lib):
+    """Zero tokens (layer), zero sequences (expanded decode) and zero rows
+    (linear) launch nothing but the max-logit reset."""
+    import torch
+    import mla_qk_clip_amd as m
+    from tests._gpu import host, log
+    log("empty inputs")
+    dims = m.Dims(4)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    ml = torch.full((4,), 7.0, dtype=torch.float32, device="cuda")
+    w = lambda *s: torch.zeros(s, **bf)
+    m.mla_layer_forward(dims, w(0, 256), w(128, 256), w(128), w(4 * 192, 128), w(576, 256), w(512), w(4 * 256, 512),
+                        w(4 * 128, 256), w(256, 4 * 128), torch.zeros(1, dtype=torch.int32, device="cuda"),
+                        max_logit=ml)
+    torch.cuda.synchronize()
+    assert np.all(host(ml) == -np.inf)
+    ml.fill_(7.0)
+    m.mla_expanded(dims, w(0, 1, 4, 192), w(0, 4, 8, 192), w(0, 4, 8, 128),
+                   torch.zeros(0, dtype=torch.int32, device="cuda"), None, max_logit=ml)
+    torch.cuda.synchronize()
+    assert np.all(host(ml) == -np.inf)
+    y = m.mla_linear(w(0, 128), w(8, 128))
+    assert tuple(y.shape) == (0, 8)
