@@ -24,6 +24,7 @@ from .mla_oracle import (  # noqa: F401
     linear,
     max_logit_head,
     prefill,
+    prefill_backward,
     prefill_rows,
     q_projection,
     qk_clip,

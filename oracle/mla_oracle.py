@@ -360,6 +360,73 @@ def expanded(q, k_rows, v_rows, gate, dims):
 
 
 # ---------------------------------------------------------------------------
+# Backward of the training-form prefill: the gradients of the [MLA] equation
+# list (expansion, key assembly, scaled causal softmax, value mix, gate) with
+# respect to q, c^KV, k^S, kv_b_proj.weight and the gate logits, for an
+# upstream gradient dO of the output o. Chain rule through
+#   o = sigma(g) . O~,  O~ = A V,  A = softmax(S) (causal),  S = scale Q K^T,
+#   K = [K^C, k^S],  [K^C V] = c^KV W_UKV.
+# ---------------------------------------------------------------------------
+
+
+def prefill_backward(q, ckv, ks, w_kv_b, gate, cu_seqlens, dims, dout):
+    """Returns (dq [Ntok, H, D], dckv [Ntok, R], dks [Ntok, S], dw_kv_b
+    [H*(N+V), R], dgate [Ntok, H*V] or None), all float64.
+
+    Per head and sequence, with P the causal softmax rows:
+      dO~ = dO . sigma(g),  dg = dO . O~ . sigma(g) (1 - sigma(g)),
+      dV = P^T dO~,  dP = dO~ V^T,  dS = P . (dP - rowsum(dP . P)),
+      dQ = scale dS K,  dK = scale dS^T Q;
+    then dK^C, dV flow back through W_UKV into c^KV and the weight, and the
+    k^S part of dK sums over the heads.
+    """
+    d = _dims(dims)
+    H, R, S_, N, V = d.heads, d.kv_rank, d.shared_dim, d.nope_dim, d.v_dim
+    scale = scale_of(d)
+    cu = [int(x) for x in cu_seqlens]
+    n = cu[-1]
+    q = np.asarray(q, dtype=f64)
+    c = np.asarray(ckv, dtype=f64)
+    w = np.asarray(w_kv_b, dtype=f64)
+    dout = np.asarray(dout, dtype=f64)
+    sig = sigmoid(gate) if gate is not None else np.ones((n, H * V))
+    dq = np.zeros((n, H, N + S_))
+    dckv = np.zeros((n, R))
+    dks = np.zeros((n, S_))
+    dw = np.zeros_like(w)
+    dgate = np.zeros((n, H * V)) if gate is not None else None
+    for h in range(H):
+        kc, vv = expand_latent(c, w, d, h)
+        K = key_of_head(kc, ks)
+        cols = slice(h * V, (h + 1) * V)
+        dKh = np.zeros((n, N + S_))
+        dVh = np.zeros((n, V))
+        for a, b in zip(cu[:-1], cu[1:]):
+            if b <= a:
+                continue
+            Q = q[a:b, h]
+            Sm = (Q @ K[a:b].T) * scale
+            Sm = np.where(np.tril(np.ones((b - a, b - a), dtype=bool)), Sm, -np.inf)
+            P = np.exp(Sm - Sm.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            Ot = P @ vv[a:b]                                    # O~ of this head
+            dOt = dout[a:b, cols] * sig[a:b, cols]
+            if dgate is not None:
+                dgate[a:b, cols] = dout[a:b, cols] * Ot * sig[a:b, cols] * (1.0 - sig[a:b, cols])
+            dVh[a:b] = P.T @ dOt
+            dP = dOt @ vv[a:b].T
+            dS = P * (dP - np.sum(dP * P, axis=1, keepdims=True))
+            dq[a:b, h] = scale * (dS @ K[a:b])
+            dKh[a:b] = scale * (dS.T @ Q)
+        blk = slice(h * (N + V), (h + 1) * (N + V))
+        dkv = np.concatenate([dKh[:, :N], dVh], axis=1)           # d[K^C_h V_h]
+        dckv += dkv @ w[blk]
+        dw[blk] += dkv.T @ c
+        dks += dKh[:, N:]
+    return dq, dckv, dks, dw, dgate
+
+
+# ---------------------------------------------------------------------------
 # The whole gated MLA layer ([MLA] equation list, all 20 steps, and the
 # KimiMLAAttention constructor/forward excerpts): q_a_proj -> q_a_layernorm ->
 # q_b_proj; kv_a_proj_with_mqa -> [c^KV | k^S] -> kv_a_layernorm on c^KV;

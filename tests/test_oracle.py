@@ -364,6 +364,60 @@ def test_expanded_single_visible_row_returns_gated_value_row():
 
 
 # ---------------------------------------------------------------------------
+# Backward of the prefill
+# ---------------------------------------------------------------------------
+
+
+def test_prefill_backward_matches_central_differences():
+    """Every gradient against central differences of the forward oracle along
+    random directions: d/de <dO, out(x + e v)> = <grad_x, v> for x = q, c^KV,
+    k^S, kv_b_proj.weight and the gate logits (two sequences, causal)."""
+    dims = synth.TINY
+    p = synth.prefill_inputs(dims, [6, 9], seed=61, bf16=False)
+    rng = np.random.default_rng(62)
+    dout = rng.standard_normal((p.ntok, dims.heads * dims.v_dim))
+    grads = oracle.prefill_backward(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, dims, dout)
+    base = dict(q=p.q.astype(np.float64), ckv=p.ckv.astype(np.float64), ks=p.ks.astype(np.float64),
+                w=p.w_kv_b.astype(np.float64), g=p.gate.astype(np.float64))
+
+    def loss(**over):
+        a = dict(base)
+        a.update(over)
+        out = oracle.prefill(a["q"], a["ckv"], a["ks"], a["w"], a["g"], p.cu_seqlens, dims)[0]
+        return float(np.sum(out * dout))
+    eps = 1e-5
+    for name, g in zip(["q", "ckv", "ks", "w", "g"], grads):
+        for _ in range(2):
+            v = rng.standard_normal(base[name].shape)
+            fd = (loss(**{name: base[name] + eps * v}) - loss(**{name: base[name] - eps * v})) / (2 * eps)
+            assert abs(fd - float(np.sum(g * v))) <= 1e-7 * max(1.0, abs(fd)), name
+
+
+def test_prefill_backward_value_gradient_closed_form_for_zero_query():
+    """q = 0: the softmax rows are uniform over the causal prefix, so the value
+    gradient at row s is sum over t >= s of dO~_t / (t + 1), dq's key part is
+    the only q gradient path, and without a gate dO~ = dO."""
+    dims = synth.TINY
+    p = synth.prefill_inputs(dims, [7], seed=63, bf16=False, gate=False)
+    rng = np.random.default_rng(64)
+    dout = rng.standard_normal((7, dims.heads * dims.v_dim))
+    q0 = np.zeros_like(p.q)
+    _, dckv, dks, dw, dg = oracle.prefill_backward(q0, p.ckv, p.ks, p.w_kv_b, None, p.cu_seqlens, dims, dout)
+    assert dg is None
+    N, V, R = dims.nope_dim, dims.v_dim, dims.kv_rank
+    # with q = 0 the keys get no gradient: dK = scale dS^T Q = 0, so dks = 0 and W_UK gets none
+    assert np.all(dks == 0.0)
+    for h in range(dims.heads):
+        assert np.all(dw[h * (N + V):h * (N + V) + N] == 0.0)
+        dV = np.zeros((7, V))
+        for s in range(7):
+            for t in range(s, 7):
+                dV[s] += dout[t, h * V:(h + 1) * V] / (t + 1)
+        want = dV.T @ p.ckv.astype(np.float64)      # d W_UV_h (rows)
+        assert np.allclose(dw[h * (N + V) + N:(h + 1) * (N + V)], want, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # The whole layer (projections, RMSNorms, attention, output projection)
 # ---------------------------------------------------------------------------
 
