@@ -121,6 +121,35 @@ mla_status mla_prefill(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_d
                        void* out, float* lse, float* max_logit, int32_t accumulate,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of scratch memory mla_prefill_backward needs (0 for invalid sizes). */
+size_t mla_prefill_backward_workspace_size(const mla_dims* dims, int64_t total_tokens, int32_t max_seqlen);
+
+/*
+ * Backward of mla_prefill (bf16, Kimi K3 head shape): the gradients of the
+ * "Kimi K3 · Gated MLA" equation list ([k^C v] = c^KV W_UKV, K_h = [K^C_h,
+ * k^S], S = Q K^T / sqrt(192), causal softmax, O~ = A V, o = sigma(g) . o~)
+ * for an upstream gradient dout of o:
+ *   dO~ = dout . sigma(g), dgate = dout . o . (1 - sigma(g)),
+ *   per head and sequence: dV = P^T dO~, dS = P . (dO~ V^T - rowsum(dout . o)),
+ *   dq = scale dS K, dK = scale dS^T Q;
+ *   dckv = sum_h [dK^C_h | dV_h] [W_UK_h; W_UV_h], dw_kv_b = [dK^C | dV]^T c^KV,
+ *   dks = sum_h of the k^S part of dK.
+ * P is recomputed from the forward's lse. Per sequence and chunk of heads the
+ * L x L score planes are materialised in the workspace.
+ *
+ * q, ckv, ks, w_kv_b, gate: the forward's bf16 inputs (gate may be NULL);
+ * cu_seqlens_host [nseq+1] int32 in HOST memory (the work is planned on the
+ * host); out [T, H*V] and lse [H, T] fp32 from mla_prefill; dout [T, H*V] fp32.
+ * Outputs (fp32, device): dq [T, H, N+S], dckv [T, R], dks [T, S],
+ * dw_kv_b [H*(N+V), R], dgate [T, H*V] (required when gate is given).
+ * total_tokens at most 2^20.
+ */
+mla_status mla_prefill_backward(const mla_dims* dims, const void* q, const void* ckv, const void* ks,
+                                const void* w_kv_b, const void* gate, const int32_t* cu_seqlens_host,
+                                int32_t nseq, int64_t total_tokens, const float* out, const float* lse,
+                                const float* dout, float* dq, float* dckv, float* dks, float* dw_kv_b,
+                                float* dgate, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Inference form (absorbed W_UK / W_UV over the latent cache)              */
 /* ------------------------------------------------------------------------ */

@@ -24,7 +24,7 @@ MLA_F32, MLA_BF16 = 0, 1
 EXPORTED = (
     "mla_prefill_workspace_size", "mla_prefill", "mla_absorbed_workspace_size", "mla_absorbed",
     "mla_expanded_workspace_size", "mla_expanded", "mla_linear", "mla_rms_norm", "mla_layer_workspace_size",
-    "mla_layer_forward", "mla_qk_clip", "mla_status_string", "mla_last_error", "mla_version", "mla_timing_enable",
+    "mla_layer_forward", "mla_prefill_backward_workspace_size", "mla_prefill_backward", "mla_qk_clip", "mla_status_string", "mla_last_error", "mla_version", "mla_timing_enable",
     "mla_timing_read",
 )
 
@@ -83,6 +83,10 @@ def _load():
     lib.mla_layer_workspace_size.restype = SZ
     lib.mla_layer_forward.argtypes = [D, I32, I32, F, P, P, P, P, P, P, P, P, P, P, I32, I64, P, P, I32, P, SZ, P]
     lib.mla_layer_forward.restype = I32
+    lib.mla_prefill_backward_workspace_size.argtypes = [D, I64, I32]
+    lib.mla_prefill_backward_workspace_size.restype = SZ
+    lib.mla_prefill_backward.argtypes = [D, P, P, P, P, P, P, I32, I64, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.mla_prefill_backward.restype = I32
     lib.mla_qk_clip.argtypes = [D, I32, P, I32, P, P, F, P, P, P]
     lib.mla_qk_clip.restype = I32
     lib.mla_status_string.argtypes = [I32]
@@ -353,6 +357,46 @@ def mla_layer_forward(dims: Dims, x, w_dq, g_q, w_uq, w_kv_a, g_kv, w_kv_b, w_g,
                                _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st)
     return out, max_logit
+
+
+def mla_prefill_backward(dims: Dims, q, ckv, ks, w_kv_b, gate, cu_seqlens_host, out, lse, dout, *, workspace=None,
+                         stream=None):
+    """Gradients of the training-form prefill (see ``mla_prefill_backward`` in include/mla.h).
+
+    q [T, H, N+S], ckv [T, R], ks [T, S], w_kv_b [H*(N+V), R], gate [T, H*V] or None (bf16); cu_seqlens_host
+    int32 [nseq+1] on the HOST; out [T, H*V] and lse [H, T] from the forward (fp32); dout [T, H*V] fp32.
+    Returns (dq, dckv, dks, dw_kv_b, dgate or None), fp32 device tensors.
+    """
+    import numpy as _np
+    cu = _np.ascontiguousarray(_np.asarray(cu_seqlens_host.cpu() if isinstance(cu_seqlens_host, torch.Tensor)
+                                           else cu_seqlens_host, dtype=_np.int32))
+    T = q.shape[0]
+    H, R, S, N, V = dims.heads, dims.kv_rank, dims.shared_dim, dims.nope_dim, dims.v_dim
+    bf, f32 = torch.bfloat16, torch.float32
+    _expect("q", q, (T, H, N + S), bf)
+    _expect("ckv", ckv, (T, R), bf)
+    _expect("ks", ks, (T, S), bf)
+    _expect("w_kv_b", w_kv_b, (H * (N + V), R), bf)
+    _expect("gate", gate, (T, H * V), bf, optional=True)
+    _expect("out", out, (T, H * V), f32)
+    _expect("lse", lse, (H, T), f32)
+    _expect("dout", dout, (T, H * V), f32)
+    nseq = cu.shape[0] - 1
+    dev = q.device
+    dq = torch.empty((T, H, N + S), dtype=f32, device=dev)
+    dckv = torch.empty((T, R), dtype=f32, device=dev)
+    dks = torch.empty((T, S), dtype=f32, device=dev)
+    dw = torch.empty((H * (N + V), R), dtype=f32, device=dev)
+    dg = torch.empty((T, H * V), dtype=f32, device=dev) if gate is not None else None
+    max_len = int(_np.max(_np.diff(cu))) if nseq > 0 else 0
+    need = int(lib.mla_prefill_backward_workspace_size(ctypes.byref(dims.c()), T, max_len))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.mla_prefill_backward(ctypes.byref(dims.c()), _ptr(q), _ptr(ckv), _ptr(ks), _ptr(w_kv_b), _ptr(gate),
+                                  cu.ctypes.data, nseq, T, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dckv),
+                                  _ptr(dks), _ptr(dw), _ptr(dg), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st)
+    return dq, dckv, dks, dw, dg
 
 
 def mla_qk_clip(dims: Dims, w_q_b, w_kv_b, max_logit, tau: float, *, clipped=None, gamma=None, stream=None):

@@ -359,6 +359,61 @@ mla_status mla_layer_forward(const mla_dims* dims, int32_t hidden, int32_t q_ran
   return MLA_OK;
 }
 
+size_t mla_prefill_backward_workspace_size(const mla_dims* dims, int64_t total_tokens, int32_t max_seqlen) {
+  Shape s;
+  if (check_dims(dims, MLA_BF16, &s) != MLA_OK || total_tokens < 0 || total_tokens > (int64_t{1} << 20) ||
+      max_seqlen < 0 || max_seqlen > total_tokens)
+    return 0;
+  return mla::backward_ws_layout(s.H, total_tokens, max_seqlen).total;
+}
+
+mla_status mla_prefill_backward(const mla_dims* dims, const void* q, const void* ckv, const void* ks,
+                                const void* w_kv_b, const void* gate, const int32_t* cu_seqlens_host, int32_t nseq,
+                                int64_t total_tokens, const float* out, const float* lse, const float* dout,
+                                float* dq, float* dckv, float* dks, float* dw_kv_b, float* dgate, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  Shape s;
+  mla_status st = check_dims(dims, MLA_BF16, &s);
+  if (st != MLA_OK) return st;
+  if (nseq < 0 || total_tokens < 0) return fail(MLA_ERR_INVALID, "nseq and total_tokens must be >= 0");
+  if (total_tokens > (int64_t{1} << 20)) return fail(MLA_ERR_UNSUPPORTED, "total_tokens above 2^20");
+  if (total_tokens == 0) return MLA_OK;
+  if (nseq < 1) return fail(MLA_ERR_INVALID, "total_tokens > 0 needs nseq >= 1");
+  if (!cu_seqlens_host) return fail(MLA_ERR_INVALID, "cu_seqlens_host is NULL");
+  if (cu_seqlens_host[0] != 0 || cu_seqlens_host[nseq] != total_tokens)
+    return fail(MLA_ERR_INVALID, "cu_seqlens_host must run from 0 to total_tokens");
+  int max_len = 0;
+  for (int i = 0; i < nseq; ++i) {
+    const int L = cu_seqlens_host[i + 1] - cu_seqlens_host[i];
+    if (L < 0) return fail(MLA_ERR_INVALID, "cu_seqlens_host must be non-decreasing");
+    max_len = L > max_len ? L : max_len;
+  }
+  REQUIRE_PTR(q, 16);
+  REQUIRE_PTR(ckv, 16);
+  REQUIRE_PTR(ks, 16);
+  REQUIRE_PTR(w_kv_b, 16);
+  OPTIONAL_PTR(gate, 16);
+  REQUIRE_PTR(out, 16);
+  REQUIRE_PTR(lse, 16);
+  REQUIRE_PTR(dout, 16);
+  REQUIRE_PTR(dq, 16);
+  REQUIRE_PTR(dckv, 16);
+  REQUIRE_PTR(dks, 16);
+  REQUIRE_PTR(dw_kv_b, 16);
+  if (gate) REQUIRE_PTR(dgate, 16);
+  const size_t need = mla_prefill_backward_workspace_size(dims, total_tokens, max_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : static_cast<size_t>(0));
+  if (!aligned(workspace, 16)) return fail(MLA_ERR_INVALID, "workspace is not 16-byte aligned");
+  const hipError_t e = mla::launch_prefill_backward_bf16(s.H, s.scale, q, ckv, ks, w_kv_b, gate, cu_seqlens_host,
+                                                         nseq, total_tokens, max_len, out, lse, dout, dq, dckv, dks,
+                                                         dw_kv_b, gate ? dgate : nullptr, workspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "mla_prefill_backward launch");
+  return MLA_OK;
+}
+
 mla_status mla_qk_clip(const mla_dims* dims, mla_dtype wdtype, void* w_q_b, int32_t q_in, void* w_kv_b,
                        const float* max_logit, float tau, uint8_t* clipped, float* gamma, hipStream_t stream) {
   g_last_error.clear();

@@ -39,19 +39,22 @@ constexpr int kGmUnits = kGmT * 8;   // 16-byte units of one operand slot (256 r
 
 struct GemmProblem {
   const uint16_t* b;
-  uint16_t* c;
+  void* c;          // bf16 or fp32, row-major
   int64_t ldb, ldc;
+  int64_t sb, sc;   // batch strides (elements) of B and C
   int n;       // columns of C (rows of B)
   int tile0;   // first column tile of this problem in the combined tile space
 };
 struct GemmArgs {
   const uint16_t* a;
-  int64_t lda;
+  int64_t lda, sa;   // row stride and batch stride (elements) of A
   int m, k;
   int nprob, mtiles, ntiles;
   GemmProblem p[kGemmMaxProblems];
 };
 
+// blockIdx.y is the batch index (a separate A, B and C per batch entry).
+template <bool kOutF32>
 __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
   __shared__ uint4 As0[kGmUnits], As1[kGmUnits];
   __shared__ uint4 Bs0[kGmUnits], Bs1[kGmUnits];
@@ -73,12 +76,17 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
   // would copy it to private memory)
   const bool p1 = args.nprob > 1 && nt >= args.p[1].tile0;
   const bool p2 = args.nprob > 2 && nt >= args.p[2].tile0;
-  const GemmProblem P{p2 ? args.p[2].b : p1 ? args.p[1].b : args.p[0].b,
+  const int64_t bz = blockIdx.y;
+  const GemmProblem P{(p2 ? args.p[2].b : p1 ? args.p[1].b : args.p[0].b) +
+                          bz * (p2 ? args.p[2].sb : p1 ? args.p[1].sb : args.p[0].sb),
                       p2 ? args.p[2].c : p1 ? args.p[1].c : args.p[0].c,
                       p2 ? args.p[2].ldb : p1 ? args.p[1].ldb : args.p[0].ldb,
                       p2 ? args.p[2].ldc : p1 ? args.p[1].ldc : args.p[0].ldc,
+                      0,
+                      bz * (p2 ? args.p[2].sc : p1 ? args.p[1].sc : args.p[0].sc),
                       p2 ? args.p[2].n : p1 ? args.p[1].n : args.p[0].n,
                       p2 ? args.p[2].tile0 : p1 ? args.p[1].tile0 : args.p[0].tile0};
+  const uint16_t* a_base = args.a + bz * args.sa;
   const int m0 = mt * kGmT, n0 = (nt - P.tile0) * kGmT;
   const int rows_a = min(kGmT, args.m - m0), rows_b = min(kGmT, P.n - n0);
 
@@ -89,7 +97,7 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
 
   // staging: copy q of wave w covers tile rows 8 (4 w + q) .. +7; lane i takes
   // row 8 (4 w + q) + i / 8 and k-unit (i % 8) ^ ((row / 2) % 8)
-  const auto rs_a = make_rsrc(args.a + static_cast<int64_t>(m0) * args.lda,
+  const auto rs_a = make_rsrc(a_base + static_cast<int64_t>(m0) * args.lda,
                               static_cast<uint32_t>(rows_a * args.lda * 2));
   const auto rs_b = make_rsrc(P.b + static_cast<int64_t>(n0) * P.ldb, static_cast<uint32_t>(rows_b * P.ldb * 2));
   uint32_t voff_a[4], voff_b[4];
@@ -172,18 +180,35 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
         const f32x16& a = acc[2 * fb + kb];
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {   // runs 2 pr (kept by g = 0) and 2 pr + 1 (kept by g = 1)
-          uint32_t x[2], y[2];
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const uint32_t lo = pack_bf16x2(a[8 * pr + 2 * w], a[8 * pr + 2 * w + 1]);
-            const uint32_t hi = pack_bf16x2(a[8 * pr + 4 + 2 * w], a[8 * pr + 4 + 2 * w + 1]);
-            const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
-            x[w] = sw[0];
-            y[w] = sw[1];
-          }
           const int n = n0 + 128 * wn + 32 * fb + 16 * pr + 8 * g;
-          if (m < args.m && n < P.n)
-            stg16(P.c + static_cast<int64_t>(m) * P.ldc + n, make_uint4(x[0], x[1], y[0], y[1]));
+          if constexpr (kOutF32) {
+            uint32_t x[4], y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[8 * pr + e]),
+                                                               __float_as_uint(a[8 * pr + 4 + e]), false, false);
+              x[e] = sw[0];
+              y[e] = sw[1];
+            }
+            if (m < args.m && n < P.n) {
+              float* dst = static_cast<float*>(P.c) + P.sc + static_cast<int64_t>(m) * P.ldc + n;
+              stg16(dst, make_uint4(x[0], x[1], x[2], x[3]));
+              stg16(dst + 4, make_uint4(y[0], y[1], y[2], y[3]));
+            }
+          } else {
+            uint32_t x[2], y[2];
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const uint32_t lo = pack_bf16x2(a[8 * pr + 2 * w], a[8 * pr + 2 * w + 1]);
+              const uint32_t hi = pack_bf16x2(a[8 * pr + 4 + 2 * w], a[8 * pr + 4 + 2 * w + 1]);
+              const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+              x[w] = sw[0];
+              y[w] = sw[1];
+            }
+            if (m < args.m && n < P.n)
+              stg16(static_cast<uint16_t*>(P.c) + P.sc + static_cast<int64_t>(m) * P.ldc + n,
+                    make_uint4(x[0], x[1], y[0], y[1]));
+          }
         }
       }
     }
@@ -240,38 +265,39 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(NormJob j0, NormJob j1, in
   if (J.ytail && lane < J.ntail / 8) stg16(J.ytail + row * J.ntail + 8 * lane, ldg16(xr + J.n + 8 * lane));
 }
 
-hipError_t gemm(const uint16_t* a, int64_t lda, int m, int k, int nprob, const uint16_t* const* b,
-                const int64_t* ldb, uint16_t* const* c, const int64_t* ldc, const int* n, const char* name,
-                hipStream_t st) {
+}  // namespace
+
+hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_t sa, int m, int k, int batch,
+                            int nprob, const GemmSpec* p, const char* name, hipStream_t st) {
   GemmArgs args{};
   args.a = a;
   args.lda = lda;
+  args.sa = sa;
   args.m = m;
   args.k = k;
   args.nprob = nprob;
   args.mtiles = (m + kGmT - 1) / kGmT;
   int tiles = 0;
   for (int i = 0; i < nprob; ++i) {
-    args.p[i] = GemmProblem{b[i], c[i], ldb[i], ldc[i], n[i], tiles};
-    tiles += (n[i] + kGmT - 1) / kGmT;
+    args.p[i] = GemmProblem{p[i].b, p[i].c, p[i].ldb, p[i].ldc, p[i].sb, p[i].sc, p[i].n, tiles};
+    tiles += (p[i].n + kGmT - 1) / kGmT;
   }
   args.ntiles = tiles;
   const int total = args.mtiles * tiles;
-  if (total == 0) return hipSuccess;
-  const int grid = ((total + 7) / 8) * 8;
+  if (total == 0 || batch == 0) return hipSuccess;
+  const dim3 grid(((total + 7) / 8) * 8, batch);
   TimedScope ts_(name, st);
-  hipLaunchKernelGGL(gemm_nt_kernel, dim3(grid), dim3(kGmThreads), 0, st, args);
+  if (out_f32) hipLaunchKernelGGL(gemm_nt_kernel<true>, grid, dim3(kGmThreads), 0, st, args);
+  else hipLaunchKernelGGL(gemm_nt_kernel<false>, grid, dim3(kGmThreads), 0, st, args);
   return hipGetLastError();
 }
 
+namespace {
 }  // namespace
 
 hipError_t launch_linear_bf16(const void* x, int64_t m, int k, const void* w, int n, void* y, hipStream_t st) {
-  const uint16_t* b[1] = {static_cast<const uint16_t*>(w)};
-  uint16_t* c[1] = {static_cast<uint16_t*>(y)};
-  const int64_t ldb[1] = {k}, ldc[1] = {n};
-  const int nn[1] = {n};
-  return gemm(static_cast<const uint16_t*>(x), k, static_cast<int>(m), k, 1, b, ldb, c, ldc, nn, "linear", st);
+  const GemmSpec p{static_cast<const uint16_t*>(w), y, k, n, 0, 0, n};
+  return launch_gemm_bf16(false, static_cast<const uint16_t*>(x), k, 0, static_cast<int>(m), k, 1, 1, &p, "linear", st);
 }
 
 hipError_t launch_rms_norm_bf16(const void* x, int64_t rows, int n, const void* w, float eps, void* y,
@@ -297,12 +323,10 @@ hipError_t launch_layer_bf16(int heads, float scale, int hidden, int q_rank, flo
   const int HV = heads * kV, HD = heads * kD, RS = kR + kS;
   hipError_t e;
   {  // c^Q, [c^KV | k^S] and g from x: one launch
-    const uint16_t* b[3] = {static_cast<const uint16_t*>(w_dq), static_cast<const uint16_t*>(w_kv_a),
-                            static_cast<const uint16_t*>(w_g)};
-    uint16_t* c[3] = {buf(L.cq), buf(L.ckv_raw), buf(L.g)};
-    const int64_t ldb[3] = {hidden, hidden, hidden}, ldc[3] = {q_rank, RS, HV};
-    const int n[3] = {q_rank, RS, HV};
-    e = gemm(static_cast<const uint16_t*>(x), hidden, m, hidden, 3, b, ldb, c, ldc, n, "layer_proj_x", st);
+    const GemmSpec p[3] = {{static_cast<const uint16_t*>(w_dq), buf(L.cq), hidden, q_rank, 0, 0, q_rank},
+                           {static_cast<const uint16_t*>(w_kv_a), buf(L.ckv_raw), hidden, RS, 0, 0, RS},
+                           {static_cast<const uint16_t*>(w_g), buf(L.g), hidden, HV, 0, 0, HV}};
+    e = launch_gemm_bf16(false, static_cast<const uint16_t*>(x), hidden, 0, m, hidden, 1, 3, p, "layer_proj_x", st);
     if (e != hipSuccess) return e;
   }
   {
@@ -315,22 +339,16 @@ hipError_t launch_layer_bf16(int heads, float scale, int hidden, int q_rank, flo
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    const uint16_t* b[1] = {static_cast<const uint16_t*>(w_uq)};
-    uint16_t* c[1] = {buf(L.q)};
-    const int64_t ldb[1] = {q_rank}, ldc[1] = {HD};
-    const int n[1] = {HD};
-    e = gemm(buf(L.cqn), q_rank, m, q_rank, 1, b, ldb, c, ldc, n, "layer_proj_q", st);
+    const GemmSpec p{static_cast<const uint16_t*>(w_uq), buf(L.q), q_rank, HD, 0, 0, HD};
+    e = launch_gemm_bf16(false, buf(L.cqn), q_rank, 0, m, q_rank, 1, 1, &p, "layer_proj_q", st);
     if (e != hipSuccess) return e;
   }
   e = launch_prefill_bf16(heads, scale, true, buf(L.q), buf(L.ckvn), buf(L.ks), w_kv_b, buf(L.g), cu, nseq, ntok,
                           buf(L.o), nullptr, max_logit, init_max_logit, base + L.prefill, st);
   if (e != hipSuccess) return e;
   {
-    const uint16_t* b[1] = {static_cast<const uint16_t*>(w_o)};
-    uint16_t* c[1] = {static_cast<uint16_t*>(out)};
-    const int64_t ldb[1] = {HV}, ldc[1] = {hidden};
-    const int n[1] = {hidden};
-    e = gemm(buf(L.o), HV, m, HV, 1, b, ldb, c, ldc, n, "layer_proj_o", st);
+    const GemmSpec p{static_cast<const uint16_t*>(w_o), out, HV, hidden, 0, 0, hidden};
+    e = launch_gemm_bf16(false, buf(L.o), HV, 0, m, HV, 1, 1, &p, "layer_proj_o", st);
   }
   return e;
 }

@@ -158,6 +158,16 @@ inline LayerWs layer_ws_layout(int heads, int hidden, int q_rank, int64_t ntok, 
   return w;
 }
 
+// Workspace of the bf16 prefill backward: [K^C | V] of every head, the
+// transposed weight and latent, the K^C / V gradients (and their transpose),
+// then one chunk of heads' per-sequence buffers (rows padded to a multiple of
+// 128, Q and K padded to 256 features; Lp x Lp score planes).
+struct BackwardWs {
+  size_t kv, wT, ckvT, dkv, dkvT, qp, qpT, kp, kpT, vh, dot, dotT, dv, s, dp, ds, dsT, pT, dqc, dkc, dvc, total;
+  int hc;   // heads per chunk
+};
+BackwardWs backward_ws_layout(int heads, int64_t ntok, int max_seqlen);
+
 // ---- launchers (defined next to their kernels) ----
 
 hipError_t launch_fill(float* p, int n, float v, hipStream_t st);
@@ -182,6 +192,17 @@ hipError_t launch_expanded_bf16(int heads, float scale, bool out_bf16, const voi
                                 const void* vcache, int64_t cap, const int32_t* lens, int batch, int tq,
                                 const void* gate, void* out, float* max_logit, void* ws, hipStream_t st);
 
+// C = A B^T (bf16 operands, K-contiguous rows; fp32 accumulation; bf16 or
+// fp32 C) for up to kGemmMaxProblems (B, C) pairs sharing A, batched over
+// blockIdx.y with element strides sa, sb, sc. K a multiple of 128.
+struct GemmSpec {
+  const uint16_t* b;
+  void* c;
+  int64_t ldb, ldc, sb, sc;
+  int n;
+};
+hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_t sa, int m, int k, int batch,
+                            int nprob, const GemmSpec* p, const char* name, hipStream_t st);
 hipError_t launch_linear_bf16(const void* x, int64_t m, int k, const void* w, int n, void* y, hipStream_t st);
 hipError_t launch_rms_norm_bf16(const void* x, int64_t rows, int n, const void* w, float eps, void* y,
                                 hipStream_t st);
@@ -190,6 +211,12 @@ hipError_t launch_layer_bf16(int heads, float scale, int hidden, int q_rank, flo
                              const void* g_kv, const void* w_kv_b, const void* w_g, const void* w_o,
                              const int32_t* cu, int nseq, int64_t ntok, void* out, float* max_logit,
                              bool init_max_logit, void* ws, hipStream_t st);
+
+hipError_t launch_prefill_backward_bf16(int heads, float scale, const void* q, const void* ckv, const void* ks,
+                                        const void* w_kv_b, const void* gate, const int32_t* cu_host, int nseq,
+                                        int64_t ntok, int max_seqlen, const float* out, const float* lse,
+                                        const float* dout, float* dq, float* dckv, float* dks, float* dw,
+                                        float* dgate, void* ws, hipStream_t st);
 
 hipError_t launch_absorbed_f32(int heads, int R, int S, int N, int V, float scale,
                                const float* q, const float* cache, int64_t cap, const int32_t* lens,
