@@ -12,17 +12,19 @@ layers, inputs resident in HBM:
 causal pairs) from HIP events around the prefill calls; the decode's cache
 GB/s and the per-kernel roofline figures are reported beside it.
 
-Two legs are timed apart from the step and reported in their own objects:
+Three legs are timed apart from the step and reported in their own objects:
 ``layer`` (the whole attention layer at T=4096: projections, RMSNorms,
-attention, output projection) and ``expanded_decode`` (the decode workload over
-a per-head K/V cache, the comparator of the latent cache).
+attention, output projection), ``backward`` (the gradients of the T=4096
+prefill) and ``expanded_decode`` (the decode workload over a per-head K/V
+cache, the comparator of the latent cache).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-decode] [--no-layer] [--no-expanded]
+                       [--no-decode] [--no-layer] [--no-backward] [--no-expanded]
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -116,6 +118,51 @@ def cpu_baseline(p, budget_s: float = 12.0):
     dt = time.perf_counter() - t0
     return {"value": per_head * heads / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{heads} of {H} heads of the T={T} prefill (fp64 NumPy), {dt:.1f} s"}
+
+
+def backward_leg(m, dims, p, q, ckv, ks, w_kv_b, gate, cu, steps: int = 3):
+    """Backward of the T=4096 prefill: gradients of q, c^KV, k^S, kv_b_proj
+    and the gate for a seeded upstream gradient, from the forward's lse."""
+    import torch
+    T, H = p.ntok, 96
+    log("prefill-backward leg (T=4096)")
+    out, lse, _ = m.mla_prefill(dims, q, ckv, ks, w_kv_b, gate, cu, out_dtype=torch.float32, want_lse=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    dout = torch.randn((T, H * 128), generator=g, dtype=torch.float32, device="cuda")
+    cu_host = p.cu_seqlens
+    need = int(m.lib.mla_prefill_backward_workspace_size(ctypes.byref(dims.c()), T, int(np.max(np.diff(cu_host)))))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    m.mla_prefill_backward(dims, q, ckv, ks, w_kv_b, gate, cu_host, out, lse, dout, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        m.mla_prefill_backward(dims, q, ckv, ks, w_kv_b, gate, cu_host, out, lse, dout, workspace=ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    m.mla_timing_enable(True)
+    m.mla_prefill_backward(dims, q, ckv, ks, w_kv_b, gate, cu_host, out, lse, dout, workspace=ws)
+    torch.cuda.synchronize()
+    kern = {}
+    for k in ("bw_expand", "bw_transpose", "bw_gather", "bw_scores", "bw_softmax", "bw_grads", "bw_scatter",
+              "bw_weights"):
+        tot, n = m.mla_timing_read(k)
+        if n:
+            kern[k] = tot
+    m.mla_timing_enable(False)
+    pairs = T * (T + 1) / 2
+    # causal pairs: QK^T recompute (192) + dP (128) + dQ (192) + dK (192) + dV (128); expansion recompute,
+    # dc^KV and dW (each 2 T H 256 R)
+    attn = 2.0 * H * pairs * (192 + 128 + 192 + 192 + 128)
+    lat = 3 * 2.0 * T * H * 256 * 512
+    return {"workload": "backward of the Kimi K3 prefill, B=1 T=4096 H=96 (bf16 operands, fp32 gradients)",
+            "ms": round(ms, 4), "gflop_algorithmic": round((attn + lat) / 1e9, 1),
+            "tflops": round((attn + lat) / (ms * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round((attn + lat) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels_ms_per_call": {k: round(v, 4) for k, v in kern.items()}}
 
 
 def layer_leg(m, dims, steps: int = 5):
@@ -230,6 +277,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the prefill-backward leg")
     ap.add_argument("--no-expanded", action="store_true",
                     help="skip the expanded-cache decode comparator (needs 129 GB of device memory)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -380,6 +428,8 @@ def main():
                                   "algorithmic": f"{cache_bytes / 1e9:.4f} GB of cache rows per launch"}
     if not args.no_layer:
         res["layer"] = layer_leg(m, dims)
+    if not args.no_backward:
+        res["backward"] = backward_leg(m, dims, p, q, ckv, ks, w_kv_b, gate, cu)
     if decode and not args.no_expanded:
         res["expanded_decode"] = expanded_comparator(m, dims, d, dq, dg, lens, dec_ms, kern.get("absorbed_split"))
     if not args.no_cpu_baseline:

@@ -10,6 +10,10 @@
 //   S = Q_h K_h^T, dP = dO~_h V_h^T                    (fp32, Lp x Lp)
 //   P = causal exp(scale S - lse), dS = scale P . (dP - D), D = rowsum(dO . o)
 //   dQ = dS K_h, dK = dS^T Q_h, dV = P^T dO~_h          (fp32)
+// Only the causal half is formed: the S and dP products skip the 256 x 256
+// tiles above the diagonal, the softmax kernel leaves them unwritten, and the
+// three gradient products sum only over k up to (dQ) or from (dK, dV) the
+// diagonal 256-block of their rows.
 // with dO~ = dO . sigma(g) and dg = dO . o . (1 - sigma(g)). Operands are bf16
 // (Q and K padded from 192 to 256 features with zeros); the GEMM kernel
 // needs K-contiguous rows on both sides, so the transposed operands (K_h^T,
@@ -122,6 +126,7 @@ __global__ void __launch_bounds__(256) bw_softmax_kernel(const float* __restrict
                                                          uint16_t* __restrict__ PT) {
   __shared__ uint16_t tp[64][64 + 2], ts[64][64 + 2];
   const int s0 = blockIdx.x * 64, t0 = blockIdx.y * 64, hh = blockIdx.z, h = h0 + hh;
+  if ((s0 >> 8) > (t0 >> 8)) return;   // above the diagonal 256-blocks: the causal products never read it
   const int64_t plane = static_cast<int64_t>(hh) * Lp * Lp;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const float sl2 = scale * kLog2e;
@@ -187,9 +192,11 @@ BackwardWs backward_ws_layout(int heads, int64_t ntok, int max_seqlen) {
   const size_t T = static_cast<size_t>(ntok), Tp = static_cast<size_t>(round128(ntok));
   const size_t HW = static_cast<size_t>(heads) * (kN + kV);
   const size_t Lp = static_cast<size_t>(round128(max_seqlen));
-  // heads per chunk: the Lp x Lp planes (S, dP fp32; dS, dS^T, P^T bf16) within about 16 GB
+  // heads per chunk: up to 32 (the gradient products have one or two 256-wide
+  // column tiles, so the chunk's heads are what fills the CUs), with the
+  // Lp x Lp planes (S, dP fp32; dS, dS^T, P^T bf16) within about 16 GB
   const size_t plane = Lp * Lp * (4 + 4 + 2 + 2 + 2);
-  w.hc = static_cast<int>(plane ? std::max<size_t>(1, std::min<size_t>(8, (size_t{16} << 30) / plane)) : 1);
+  w.hc = static_cast<int>(plane ? std::max<size_t>(1, std::min<size_t>(32, (size_t{16} << 30) / plane)) : 1);
   w.hc = std::min(w.hc, heads);
   const size_t hc = static_cast<size_t>(w.hc);
   size_t off = 0;
@@ -285,11 +292,11 @@ hipError_t launch_prefill_backward_bf16(int heads, float scale, const void* q, c
       {  // S = Q_h K_h^T and dP = dO~_h V_h^T (fp32)
         const GemmSpec ps{b16(W.kp), f32(W.s), kBwF, Lp, static_cast<int64_t>(Lp) * kBwF, LL, Lp};
         e = launch_gemm_bf16(true, b16(W.qp), kBwF, static_cast<int64_t>(Lp) * kBwF, Lp, kBwF, hc, 1, &ps,
-                             "bw_scores", st);
+                             "bw_scores", st, kGemmSkipUpper);
         if (e != hipSuccess) return e;
         const GemmSpec pd{b16(W.vh), f32(W.dp), kV, Lp, static_cast<int64_t>(Lp) * kV, LL, Lp};
         e = launch_gemm_bf16(true, b16(W.dot), kV, static_cast<int64_t>(Lp) * kV, Lp, kV, hc, 1, &pd, "bw_scores",
-                             st);
+                             st, kGemmSkipUpper);
         if (e != hipSuccess) return e;
       }
       {
@@ -301,15 +308,15 @@ hipError_t launch_prefill_backward_bf16(int heads, float scale, const void* q, c
       {  // dQ = dS K_h, dK = dS^T Q_h, dV = P^T dO~_h (fp32)
         const GemmSpec pq{b16(W.kpT), f32(W.dqc), Lp, kBwF, static_cast<int64_t>(kBwF) * Lp,
                           static_cast<int64_t>(Lp) * kBwF, kBwF};
-        e = launch_gemm_bf16(true, b16(W.ds), Lp, LL, Lp, Lp, hc, 1, &pq, "bw_grads", st);
+        e = launch_gemm_bf16(true, b16(W.ds), Lp, LL, Lp, Lp, hc, 1, &pq, "bw_grads", st, kGemmKToRow);
         if (e != hipSuccess) return e;
         const GemmSpec pk{b16(W.qpT), f32(W.dkc), Lp, kBwF, static_cast<int64_t>(kBwF) * Lp,
                           static_cast<int64_t>(Lp) * kBwF, kBwF};
-        e = launch_gemm_bf16(true, b16(W.dsT), Lp, LL, Lp, Lp, hc, 1, &pk, "bw_grads", st);
+        e = launch_gemm_bf16(true, b16(W.dsT), Lp, LL, Lp, Lp, hc, 1, &pk, "bw_grads", st, kGemmKFromRow);
         if (e != hipSuccess) return e;
         const GemmSpec pv{b16(W.dotT), f32(W.dvc), Lp, kV, static_cast<int64_t>(kV) * Lp,
                           static_cast<int64_t>(Lp) * kV, kV};
-        e = launch_gemm_bf16(true, b16(W.pT), Lp, LL, Lp, Lp, hc, 1, &pv, "bw_grads", st);
+        e = launch_gemm_bf16(true, b16(W.pT), Lp, LL, Lp, Lp, hc, 1, &pv, "bw_grads", st, kGemmKFromRow);
         if (e != hipSuccess) return e;
       }
       {

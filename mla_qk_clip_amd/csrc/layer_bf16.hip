@@ -50,6 +50,7 @@ struct GemmArgs {
   int64_t lda, sa;   // row stride and batch stride (elements) of A
   int m, k;
   int nprob, mtiles, ntiles;
+  int kmode;   // kGemmFull, or a causal mode (see mla_internal.h)
   GemmProblem p[kGemmMaxProblems];
 };
 
@@ -59,19 +60,39 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
   __shared__ uint4 As0[kGmUnits], As1[kGmUnits];
   __shared__ uint4 Bs0[kGmUnits], Bs1[kGmUnits];
 
-  // items are dealt to the XCDs in contiguous ranges (block b runs on XCD b % 8)
-  const int total = args.mtiles * args.ntiles;
-  const int per_xcd = (total + 7) >> 3;
-  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (item >= total) return;
-  // groups of 8 row tiles x all column tiles, row tile fastest inside a group:
-  // an XCD's 32 concurrent workgroups cover 8 row tiles x 4 column tiles
-  constexpr int kGroupM = 8;
-  const int group = item / (kGroupM * args.ntiles);
-  const int first_m = group * kGroupM;
-  const int gm = min(args.mtiles - first_m, kGroupM);
-  const int in_group = item - group * kGroupM * args.ntiles;
-  const int mt = first_m + in_group % gm, nt = in_group / gm;
+  int mt, nt;
+  if (args.kmode == kGemmFull) {
+    // items are dealt to the XCDs in contiguous ranges (block b runs on XCD b % 8)
+    const int total = args.mtiles * args.ntiles;
+    const int per_xcd = (total + 7) >> 3;
+    const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (item >= total) return;
+    // groups of 8 row tiles x all column tiles, row tile fastest inside a group:
+    // an XCD's 32 concurrent workgroups cover 8 row tiles x 4 column tiles
+    constexpr int kGroupM = 8;
+    const int group = item / (kGroupM * args.ntiles);
+    const int first_m = group * kGroupM;
+    const int gm = min(args.mtiles - first_m, kGroupM);
+    const int in_group = item - group * kGroupM * args.ntiles;
+    mt = first_m + in_group % gm;
+    nt = in_group / gm;
+  } else if (args.kmode == kGemmSkipUpper) {
+    // only the tiles on or below the diagonal (square tile grid), in turn over the XCDs
+    const int item = blockIdx.x;
+    if (item >= args.mtiles * (args.mtiles + 1) / 2) return;
+    mt = static_cast<int>((sqrtf(8.0f * item + 1.0f) - 1.0f) * 0.5f);
+    while ((mt + 1) * (mt + 2) / 2 <= item) ++mt;
+    while (mt * (mt + 1) / 2 > item) --mt;
+    nt = item - mt * (mt + 1) / 2;
+  } else {
+    // causal K ranges: longest tiles first (row tiles in order of decreasing K
+    // range), dealt in turn over the XCDs
+    const int item = blockIdx.x;
+    if (item >= args.mtiles * args.ntiles) return;
+    const int rank = item / args.ntiles;
+    nt = item - rank * args.ntiles;
+    mt = args.kmode == kGemmKToRow ? args.mtiles - 1 - rank : rank;
+  }
   // this tile's problem (selected field by field: indexing the argument array
   // would copy it to private memory)
   const bool p1 = args.nprob > 1 && nt >= args.p[1].tile0;
@@ -88,6 +109,10 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
                       p2 ? args.p[2].tile0 : p1 ? args.p[1].tile0 : args.p[0].tile0};
   const uint16_t* a_base = args.a + bz * args.sa;
   const int m0 = mt * kGmT, n0 = (nt - P.tile0) * kGmT;
+  // K range of this tile (a multiple of 128 long in every mode)
+  const int kbeg = args.kmode == kGemmKFromRow ? m0 : 0;
+  const int kend = args.kmode == kGemmKToRow ? min(args.k, m0 + kGmT) : args.k;
+  const uint32_t kbyte = static_cast<uint32_t>(kbeg) * 2;
   const int rows_a = min(kGmT, args.m - m0), rows_b = min(kGmT, P.n - n0);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -110,8 +135,8 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
   auto issue = [&](uint4* ad, uint4* bd, int st) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      dma16_buf(rs_a, voff_a[q], 128 * st, ad + 64 * (4 * wave + q));
-      dma16_buf(rs_b, voff_b[q], 128 * st, bd + 64 * (4 * wave + q));
+      dma16_buf(rs_a, voff_a[q], kbyte + 128 * st, ad + 64 * (4 * wave + q));
+      dma16_buf(rs_b, voff_b[q], kbyte + 128 * st, bd + 64 * (4 * wave + q));
     }
   };
   // Fragment reads: rows r0 .. r0+31 (r0 a multiple of 32), k-units 2 kh + g.
@@ -144,7 +169,7 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
           for (int kb = 0; kb < 2; ++kb) acc[2 * fb + kb] = mfma32(bf[fb], af[kb], acc[2 * fb + kb]);
       }
     };
-    const int nsteps = args.k / 64;
+    const int nsteps = (kend - kbeg) / 64;
     issue(As0, Bs0, 0);
     wait_vmcnt<0>();
     __syncthreads();
@@ -268,8 +293,9 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(NormJob j0, NormJob j1, in
 }  // namespace
 
 hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_t sa, int m, int k, int batch,
-                            int nprob, const GemmSpec* p, const char* name, hipStream_t st) {
+                            int nprob, const GemmSpec* p, const char* name, hipStream_t st, int kmode) {
   GemmArgs args{};
+  args.kmode = kmode;
   args.a = a;
   args.lda = lda;
   args.sa = sa;
@@ -283,8 +309,9 @@ hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_
     tiles += (p[i].n + kGmT - 1) / kGmT;
   }
   args.ntiles = tiles;
-  const int total = args.mtiles * tiles;
+  const int total = kmode == kGemmSkipUpper ? args.mtiles * (args.mtiles + 1) / 2 : args.mtiles * tiles;
   if (total == 0 || batch == 0) return hipSuccess;
+  if (kmode == kGemmSkipUpper && (tiles != args.mtiles || nprob != 1)) return hipErrorInvalidValue;
   const dim3 grid(((total + 7) / 8) * 8, batch);
   TimedScope ts_(name, st);
   if (out_f32) hipLaunchKernelGGL(gemm_nt_kernel<true>, grid, dim3(kGmThreads), 0, st, args);

@@ -201,8 +201,14 @@ struct GemmSpec {
   int64_t ldb, ldc, sb, sc;
   int n;
 };
+// K ranges for causal products over square row x K planes (m0 = first row of
+// a 256-row tile; K, M multiples of 128):
+//   kGemmSkipUpper  tiles whose columns all lie above the diagonal are skipped
+//   kGemmKToRow     each tile sums k < min(K, m0 + 256)   (C[t] = sum_{s <= t})
+//   kGemmKFromRow   each tile sums k >= m0                (C[s] = sum_{t >= s})
+constexpr int kGemmFull = 0, kGemmSkipUpper = 1, kGemmKToRow = 2, kGemmKFromRow = 3;
 hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_t sa, int m, int k, int batch,
-                            int nprob, const GemmSpec* p, const char* name, hipStream_t st);
+                            int nprob, const GemmSpec* p, const char* name, hipStream_t st, int kmode = kGemmFull);
 hipError_t launch_linear_bf16(const void* x, int64_t m, int k, const void* w, int n, void* y, hipStream_t st);
 hipError_t launch_rms_norm_bf16(const void* x, int64_t rows, int n, const void* w, float eps, void* y,
                                 hipStream_t st);
