@@ -55,3 +55,9 @@ def test_backward_96_heads_2048(lib):
     """96 heads, one sequence of 2048 tokens (12 chunks of 8 heads)."""
     p = synth.prefill_inputs(synth.K3, [2048], seed=73, bf16=True)
     _check(p, 74)
+
+
+def test_backward_k3_prefill_4096(lib):
+    """The configuration the benchmark times: the Kimi K3 prefill workload
+    (T = 4096, 96 heads, gate on), every gradient against the full oracle."""
+    _check(synth.k3_prefill(), 75)
