@@ -147,7 +147,7 @@ def backward_leg(m, dims, p, q, ckv, ks, w_kv_b, gate, cu, steps: int = 3):
     m.mla_prefill_backward(dims, q, ckv, ks, w_kv_b, gate, cu_host, out, lse, dout, workspace=ws)
     torch.cuda.synchronize()
     kern = {}
-    for k in ("bw_expand", "bw_transpose", "bw_gather", "bw_scores", "bw_softmax", "bw_grads", "bw_scatter",
+    for k in ("bw_expand", "bw_transpose", "bw_gather", "bw_scores", "bw_dp_softmax", "bw_grads", "bw_scatter",
               "bw_weights"):
         tot, n = m.mla_timing_read(k)
         if n:

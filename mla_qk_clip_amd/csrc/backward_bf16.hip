@@ -7,17 +7,19 @@
 // Per sequence (length L, padded to Lp = L rounded up to 128) and chunk of
 // heads, the score and probability matrices are materialised in HBM and every
 // product runs on the NT GEMM kernel (batched over the chunk's heads):
-//   S = Q_h K_h^T, dP = dO~_h V_h^T                    (fp32, Lp x Lp)
-//   P = causal exp(scale S - lse), dS = scale P . (dP - D), D = rowsum(dO . o)
+//   S = Q_h K_h^T (fp32, Lp x Lp), then dP = dO~_h V_h^T with, in the same
+//   kernel's epilogue, P = causal exp(scale S - lse) and
+//   dS = scale P . (dP - D), D = rowsum(dO . o) (dS, dS^T, P^T in bf16)
 //   dQ = dS K_h, dK = dS^T Q_h, dV = P^T dO~_h          (fp32)
 // Only the causal half is formed: the S and dP products skip the 256 x 256
-// tiles above the diagonal, the softmax kernel leaves them unwritten, and the
+// tiles above the diagonal (their dS, dS^T, P^T stay unwritten), and the
 // three gradient products sum only over k up to (dQ) or from (dK, dV) the
 // diagonal 256-block of their rows.
 // with dO~ = dO . sigma(g) and dg = dO . o . (1 - sigma(g)). Operands are bf16
 // (Q and K padded from 192 to 256 features with zeros); the GEMM kernel
 // needs K-contiguous rows on both sides, so the transposed operands (K_h^T,
-// Q_h^T, dO~^T, dS^T, P^T) are written by the kernels that produce them.
+// Q_h^T, dO~^T by a tiled transpose; dS^T, P^T by the dP product's epilogue)
+// are written out.
 // Then dK^C and dV flow back through W_UKV: dc^KV = dKV W_UKV^T-rows,
 // dW = dKV^T c^KV, and the k^S part of dK sums over the heads.
 #include <hip/hip_runtime.h>
@@ -116,44 +118,6 @@ __global__ void __launch_bounds__(256) bw_transpose_kernel(const uint16_t* __res
   }
 }
 
-// P and dS of one 64 x 64 tile (rows t, columns s) of one head of the chunk:
-// P = exp(scale S - lse) for s <= t < L (else 0), dS = scale P (dP - D).
-// Writes dS [t][s], and through LDS dS^T [s][t] and P^T [s][t] (bf16).
-__global__ void __launch_bounds__(256) bw_softmax_kernel(const float* __restrict__ S, const float* __restrict__ dP,
-                                                         const float* __restrict__ Dv, const float* __restrict__ lse,
-                                                         int64_t ntok, int64_t a, int L, int Lp, int h0, float scale,
-                                                         uint16_t* __restrict__ dS, uint16_t* __restrict__ dST,
-                                                         uint16_t* __restrict__ PT) {
-  __shared__ uint16_t tp[64][64 + 2], ts[64][64 + 2];
-  const int s0 = blockIdx.x * 64, t0 = blockIdx.y * 64, hh = blockIdx.z, h = h0 + hh;
-  if ((s0 >> 8) > (t0 >> 8)) return;   // above the diagonal 256-blocks: the causal products never read it
-  const int64_t plane = static_cast<int64_t>(hh) * Lp * Lp;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const float sl2 = scale * kLog2e;
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int lt = ty + 4 * i, t = t0 + lt, s = s0 + tx;
-    const int64_t idx = plane + static_cast<int64_t>(t) * Lp + s;
-    float p = 0.0f, g = 0.0f;
-    if (s <= t && t < L) {
-      const float m = lse[static_cast<int64_t>(h) * ntok + a + t] * kLog2e;
-      p = fast_exp2(S[idx] * sl2 - m);
-      g = scale * p * (dP[idx] - Dv[static_cast<int64_t>(hh) * Lp + t]);
-    }
-    dS[idx] = f32_to_bf16(g);
-    ts[lt][tx] = f32_to_bf16(g);
-    tp[lt][tx] = f32_to_bf16(p);
-  }
-  __syncthreads();
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int ls = ty + 4 * i;
-    const int64_t idx = plane + static_cast<int64_t>(s0 + ls) * Lp + t0 + tx;
-    dST[idx] = ts[tx][ls];
-    PT[idx] = tp[tx][ls];
-  }
-}
-
 // dq (fp32), the K^C / V gradients into dKV (bf16, head-major columns as in
 // kv_b_proj) for rows t < L of one chunk; grid (L, hc), 128 threads.
 __global__ void __launch_bounds__(128) bw_scatter_kernel(const float* __restrict__ dQc, const float* __restrict__ dKc,
@@ -194,8 +158,8 @@ BackwardWs backward_ws_layout(int heads, int64_t ntok, int max_seqlen) {
   const size_t Lp = static_cast<size_t>(round128(max_seqlen));
   // heads per chunk: up to 32 (the gradient products have one or two 256-wide
   // column tiles, so the chunk's heads are what fills the CUs), with the
-  // Lp x Lp planes (S, dP fp32; dS, dS^T, P^T bf16) within about 16 GB
-  const size_t plane = Lp * Lp * (4 + 4 + 2 + 2 + 2);
+  // Lp x Lp planes (S fp32; dS, dS^T, P^T bf16) within about 16 GB
+  const size_t plane = Lp * Lp * (4 + 2 + 2 + 2);
   w.hc = static_cast<int>(plane ? std::max<size_t>(1, std::min<size_t>(32, (size_t{16} << 30) / plane)) : 1);
   w.hc = std::min(w.hc, heads);
   const size_t hc = static_cast<size_t>(w.hc);
@@ -215,7 +179,6 @@ BackwardWs backward_ws_layout(int heads, int64_t ntok, int max_seqlen) {
   w.dotT = take(hc * Lp * kV * 2);
   w.dv = take(hc * Lp * 4);
   w.s = take(hc * Lp * Lp * 4);
-  w.dp = take(hc * Lp * Lp * 4);
   w.ds = take(hc * Lp * Lp * 2);
   w.dsT = take(hc * Lp * Lp * 2);
   w.pT = take(hc * Lp * Lp * 2);
@@ -294,17 +257,13 @@ hipError_t launch_prefill_backward_bf16(int heads, float scale, const void* q, c
         e = launch_gemm_bf16(true, b16(W.qp), kBwF, static_cast<int64_t>(Lp) * kBwF, Lp, kBwF, hc, 1, &ps,
                              "bw_scores", st, kGemmSkipUpper);
         if (e != hipSuccess) return e;
-        const GemmSpec pd{b16(W.vh), f32(W.dp), kV, Lp, static_cast<int64_t>(Lp) * kV, LL, Lp};
-        e = launch_gemm_bf16(true, b16(W.dot), kV, static_cast<int64_t>(Lp) * kV, Lp, kV, hc, 1, &pd, "bw_scores",
-                             st, kGemmSkipUpper);
+        // dP = dO~_h V_h^T with the softmax backward in its epilogue: dS, dS^T, P^T (bf16)
+        const GemmSpec pd{b16(W.vh), b16(W.ds), kV, Lp, static_cast<int64_t>(Lp) * kV, LL, Lp};
+        const GemmSoftmaxBwd sm{f32(W.s), lse, f32(W.dv), b16(W.dsT), b16(W.pT), LL, ntok, a, h0, L, scale};
+        e = launch_gemm_bf16(false, b16(W.dot), kV, static_cast<int64_t>(Lp) * kV, Lp, kV, hc, 1, &pd, "bw_dp_softmax",
+                             st, kGemmSkipUpper, &sm);
         if (e != hipSuccess) return e;
       }
-      {
-        TimedScope ts_("bw_softmax", st);
-        hipLaunchKernelGGL(bw_softmax_kernel, dim3(Lp / 64, Lp / 64, hc), dim3(256), 0, st, f32(W.s), f32(W.dp),
-                           f32(W.dv), lse, ntok, a, L, Lp, h0, scale, b16(W.ds), b16(W.dsT), b16(W.pT));
-      }
-      BW_CHECK();
       {  // dQ = dS K_h, dK = dS^T Q_h, dV = P^T dO~_h (fp32)
         const GemmSpec pq{b16(W.kpT), f32(W.dqc), Lp, kBwF, static_cast<int64_t>(kBwF) * Lp,
                           static_cast<int64_t>(Lp) * kBwF, kBwF};

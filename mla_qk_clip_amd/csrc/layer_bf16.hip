@@ -52,11 +52,15 @@ struct GemmArgs {
   int nprob, mtiles, ntiles;
   int kmode;   // kGemmFull, or a causal mode (see mla_internal.h)
   GemmProblem p[kGemmMaxProblems];
+  GemmSoftmaxBwd sm;   // softmax-backward epilogue (kEpi == 2)
 };
 
 // blockIdx.y is the batch index (a separate A, B and C per batch entry).
-template <bool kOutF32>
+// Epilogue kEpi: 0 bf16 C, 1 fp32 C, 2 the softmax backward of a causal
+// score plane (C = dP; see GemmSoftmaxBwd).
+template <int kEpi>
 __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
+  constexpr bool kOutF32 = kEpi == 1;
   __shared__ uint4 As0[kGmUnits], As1[kGmUnits];
   __shared__ uint4 Bs0[kGmUnits], Bs1[kGmUnits];
 
@@ -200,9 +204,42 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int m = m0 + 64 * wm + 32 * kb + l32;
+      float lse2 = 0.0f, dv = 0.0f;
+      if constexpr (kEpi == 2) {
+        if (m < args.sm.L) {
+          lse2 = args.sm.lse[(args.sm.h0 + bz) * args.sm.ntok + args.sm.a + m] * kLog2e;
+          dv = args.sm.D[bz * args.m + m];
+        }
+      }
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) {
-        const f32x16& a = acc[2 * fb + kb];
+        f32x16 a = acc[2 * fb + kb];
+        if constexpr (kEpi == 2) {
+          // P = exp(scale S - lse) on and below the diagonal of the first L
+          // rows, dS = scale P (dP - D); dS^T and P^T go out here, dS below
+          const int nb = n0 + 128 * wn + 32 * fb + 4 * g;
+          const float* srow = args.sm.S + bz * args.sm.plane + static_cast<int64_t>(m) * args.m;
+          const float sl2 = args.sm.scale * kLog2e;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float4 sv = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (m < args.sm.L && nb + 8 * r <= m) sv = *reinterpret_cast<const float4*>(srow + nb + 8 * r);
+            const float se[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int n = nb + 8 * r + e;
+              const bool on = m < args.sm.L && n <= m;
+              const float pv = on ? fast_exp2(se[e] * sl2 - lse2) : 0.0f;
+              const float gv = args.sm.scale * pv * (a[4 * r + e] - dv);
+              a[4 * r + e] = gv;
+              if (m < args.m && n < args.m) {
+                const int64_t tix = bz * args.sm.plane + static_cast<int64_t>(n) * args.m + m;
+                args.sm.dST[tix] = f32_to_bf16(gv);
+                args.sm.PT[tix] = f32_to_bf16(pv);
+              }
+            }
+          }
+        }
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {   // runs 2 pr (kept by g = 0) and 2 pr + 1 (kept by g = 1)
           const int n = n0 + 128 * wn + 32 * fb + 16 * pr + 8 * g;
@@ -293,7 +330,8 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(NormJob j0, NormJob j1, in
 }  // namespace
 
 hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_t sa, int m, int k, int batch,
-                            int nprob, const GemmSpec* p, const char* name, hipStream_t st, int kmode) {
+                            int nprob, const GemmSpec* p, const char* name, hipStream_t st, int kmode,
+                            const GemmSoftmaxBwd* sm) {
   GemmArgs args{};
   args.kmode = kmode;
   args.a = a;
@@ -314,8 +352,14 @@ hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_
   if (kmode == kGemmSkipUpper && (tiles != args.mtiles || nprob != 1)) return hipErrorInvalidValue;
   const dim3 grid(((total + 7) / 8) * 8, batch);
   TimedScope ts_(name, st);
-  if (out_f32) hipLaunchKernelGGL(gemm_nt_kernel<true>, grid, dim3(kGmThreads), 0, st, args);
-  else hipLaunchKernelGGL(gemm_nt_kernel<false>, grid, dim3(kGmThreads), 0, st, args);
+  if (sm) {
+    args.sm = *sm;
+    hipLaunchKernelGGL(gemm_nt_kernel<2>, grid, dim3(kGmThreads), 0, st, args);
+  } else if (out_f32) {
+    hipLaunchKernelGGL(gemm_nt_kernel<1>, grid, dim3(kGmThreads), 0, st, args);
+  } else {
+    hipLaunchKernelGGL(gemm_nt_kernel<0>, grid, dim3(kGmThreads), 0, st, args);
+  }
   return hipGetLastError();
 }
 

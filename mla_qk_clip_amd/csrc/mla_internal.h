@@ -163,7 +163,7 @@ inline LayerWs layer_ws_layout(int heads, int hidden, int q_rank, int64_t ntok, 
 // then one chunk of heads' per-sequence buffers (rows padded to a multiple of
 // 128, Q and K padded to 256 features; Lp x Lp score planes).
 struct BackwardWs {
-  size_t kv, wT, ckvT, dkv, dkvT, qp, qpT, kp, kpT, vh, dot, dotT, dv, s, dp, ds, dsT, pT, dqc, dkc, dvc, total;
+  size_t kv, wT, ckvT, dkv, dkvT, qp, qpT, kp, kpT, vh, dot, dotT, dv, s, ds, dsT, pT, dqc, dkc, dvc, total;
   int hc;   // heads per chunk
 };
 BackwardWs backward_ws_layout(int heads, int64_t ntok, int max_seqlen);
@@ -207,8 +207,23 @@ struct GemmSpec {
 //   kGemmKToRow     each tile sums k < min(K, m0 + 256)   (C[t] = sum_{s <= t})
 //   kGemmKFromRow   each tile sums k >= m0                (C[s] = sum_{t >= s})
 constexpr int kGemmFull = 0, kGemmSkipUpper = 1, kGemmKToRow = 2, kGemmKFromRow = 3;
+// Softmax-backward epilogue for C = dP = dO~ V^T over square planes (M = N =
+// the plane width): with S the plane of raw scores, for row t < L and column
+// s <= t, P = exp(scale S - lse[h][a + t]) and dS = scale P (dP - D[t]) (zero
+// elsewhere); C receives dS (bf16), dST and PT the transposes of dS and P.
+struct GemmSoftmaxBwd {
+  const float* S;        // [batch][M][M] fp32
+  const float* lse;      // [H][ntok] natural-log LSE of the scaled scores
+  const float* D;        // [batch][M] rowsum(dO . o)
+  uint16_t* dST;         // [batch][M][M]
+  uint16_t* PT;          // [batch][M][M]
+  int64_t plane, ntok, a, h0;   // plane stride, tokens, first token of the sequence, first head of the batch
+  int L;
+  float scale;
+};
 hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_t sa, int m, int k, int batch,
-                            int nprob, const GemmSpec* p, const char* name, hipStream_t st, int kmode = kGemmFull);
+                            int nprob, const GemmSpec* p, const char* name, hipStream_t st, int kmode = kGemmFull,
+                            const GemmSoftmaxBwd* sm = nullptr);
 hipError_t launch_linear_bf16(const void* x, int64_t m, int k, const void* w, int n, void* y, hipStream_t st);
 hipError_t launch_rms_norm_bf16(const void* x, int64_t rows, int n, const void* w, float eps, void* y,
                                 hipStream_t st);
