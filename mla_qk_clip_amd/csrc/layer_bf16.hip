@@ -201,6 +201,14 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
     // ---- store: lane = output row l32 of the row block; element i of a tile is
     // column 8 (i / 4) + 4 g + i % 4 of the column block. Lanes l and l + 32 swap
     // runs so that each holds 8 consecutive columns (two 16-byte stores per tile).
+    // softmax-backward epilogue: dS^T and P^T go through a wave-private 16 KB of
+    // LDS (the operand slots are free once every wave is past the k loop)
+    uint16_t* tst = nullptr;
+    if constexpr (kEpi == 2) {
+      __syncthreads();
+      uint4* slot = wave < 2 ? As0 : wave < 4 ? As1 : wave < 6 ? Bs0 : Bs1;
+      tst = reinterpret_cast<uint16_t*>(slot + (wave & 1) * 1024);   // [2][128 columns][32 rows] bf16
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int m = m0 + 64 * wm + 32 * kb + l32;
@@ -232,11 +240,9 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
               const float pv = on ? fast_exp2(se[e] * sl2 - lse2) : 0.0f;
               const float gv = args.sm.scale * pv * (a[4 * r + e] - dv);
               a[4 * r + e] = gv;
-              if (m < args.m && n < args.m) {
-                const int64_t tix = bz * args.sm.plane + static_cast<int64_t>(n) * args.m + m;
-                args.sm.dST[tix] = f32_to_bf16(gv);
-                args.sm.PT[tix] = f32_to_bf16(pv);
-              }
+              const int cl = 32 * fb + 8 * r + 4 * g + e;   // column within the wave's 128
+              tst[cl * 32 + l32] = f32_to_bf16(gv);
+              tst[4096 + cl * 32 + l32] = f32_to_bf16(pv);
             }
           }
         }
@@ -272,6 +278,26 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
                     make_uint4(x[0], x[1], y[0], y[1]));
           }
         }
+      }
+      if constexpr (kEpi == 2) {
+        // rows s of dS^T and P^T: 32 consecutive t (64 bytes) per column of this row block
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        const int t0 = m0 + 64 * wm + 32 * kb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = lane + 64 * j, cl = c >> 2, part = c & 3;
+          const int n = n0 + 128 * wn + cl, t = t0 + 8 * part;
+          const uint4 vd = *reinterpret_cast<const uint4*>(tst + cl * 32 + 8 * part);
+          const uint4 vp = *reinterpret_cast<const uint4*>(tst + 4096 + cl * 32 + 8 * part);
+          if (n < args.m && t < args.m) {
+            const int64_t tix = bz * args.sm.plane + static_cast<int64_t>(n) * args.m + t;
+            stg16(args.sm.dST + tix, vd);
+            stg16(args.sm.PT + tix, vp);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
       }
     }
   };
