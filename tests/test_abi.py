@@ -118,6 +118,53 @@ def test_expanded_validation(m):
     assert m.mla_expanded_workspace_size(K3, m.MLA_F32, 64, 1, 32768) == 0
 
 
+def test_linear_norm_layer_and_backward_validation(m):
+    """The whole-layer blocks and the backward refuse bad sizes, dtypes and
+    pointers on the host, before any launch."""
+    K3 = m.Dims()
+    d = K3.c()
+    lin = m.lib.mla_linear
+    assert lin(m.MLA_F32, 16, 4, 128, 16, 8, 16, None) == m.MLA_ERR_UNSUPPORTED
+    assert lin(m.MLA_BF16, 16, 4, 96, 16, 8, 16, None) == m.MLA_ERR_UNSUPPORTED      # k not a multiple of 128
+    assert lin(m.MLA_BF16, 16, 4, 128, 16, 12, 16, None) == m.MLA_ERR_UNSUPPORTED    # n not a multiple of 8
+    assert lin(m.MLA_BF16, None, 4, 128, 16, 8, 16, None) == m.MLA_ERR_INVALID
+    assert lin(m.MLA_BF16, 24, 4, 128, 16, 8, 16, None) == m.MLA_ERR_INVALID         # misaligned
+    assert lin(m.MLA_BF16, None, 0, 128, None, 8, None, None) == m.MLA_OK            # nothing to do
+    nrm = m.lib.mla_rms_norm
+    assert nrm(m.MLA_BF16, 16, 4, 4096, 16, 1e-6, 16, None) == m.MLA_ERR_UNSUPPORTED  # wider than 2048
+    assert nrm(m.MLA_BF16, 16, 4, 512, 16, -1.0, 16, None) == m.MLA_ERR_INVALID
+    assert nrm(m.MLA_BF16, 16, 4, 512, None, 1e-6, 16, None) == m.MLA_ERR_INVALID
+    lay = m.lib.mla_layer_forward
+
+    def layer(hidden=256, q_rank=128, eps=1e-6, x=16, out=16, ml=16, ws=16, wsb=1 << 40):
+        return lay(ctypes.byref(d), hidden, q_rank, eps, x, 16, 16, 16, 16, 16, 16, 16, 16, 16, 1, 10, out, ml, 0,
+                   ws, wsb, None)
+    assert layer(hidden=200) == m.MLA_ERR_UNSUPPORTED
+    assert layer(q_rank=4096) == m.MLA_ERR_UNSUPPORTED
+    assert layer(eps=float("nan")) == m.MLA_ERR_INVALID
+    assert layer(x=None) == m.MLA_ERR_INVALID
+    assert layer(ml=None) == m.MLA_ERR_INVALID
+    assert layer(wsb=16) == m.MLA_ERR_WORKSPACE
+    assert m.mla_layer_workspace_size(K3, 7168, 1536, 4096, 1) > 4096 * (1536 + 576 + 12288 + 18432) * 2
+    bwd = m.lib.mla_prefill_backward
+    cu = (ctypes.c_int32 * 3)(0, 5, 10)
+    bad = (ctypes.c_int32 * 3)(0, 7, 5)
+
+    def back(cu_=cu, T=10, dq=16, gate=None, dgate=None, wsb=1 << 40):
+        return bwd(ctypes.byref(d), 16, 16, 16, 16, gate, cu_, 2, T, 16, 16, 16, dq, 16, 16, 16, dgate, 16, wsb,
+                   None)
+    assert back(T=11) == m.MLA_ERR_INVALID          # cu_seqlens must end at total_tokens
+    assert back(cu_=bad) == m.MLA_ERR_INVALID       # decreasing
+    assert back(cu_=None) == m.MLA_ERR_INVALID
+    assert back(dq=None) == m.MLA_ERR_INVALID
+    assert back(gate=16, dgate=None) == m.MLA_ERR_INVALID   # a gate needs its gradient buffer
+    assert back(wsb=16) == m.MLA_ERR_WORKSPACE
+    assert back(T=0) == m.MLA_OK
+    assert bwd(ctypes.byref(d), 16, 16, 16, 16, None, cu, 2, (1 << 20) + 1, 16, 16, 16, 16, 16, 16, 16, None, 16,
+               1 << 40, None) == m.MLA_ERR_UNSUPPORTED
+    assert m.lib.mla_prefill_backward_workspace_size(ctypes.byref(d), 4096, 4096) > 4096 * 4096 * 10
+
+
 def test_qk_clip_validation(m):
     K3 = m.Dims()
     d = K3.c()
