@@ -12,14 +12,15 @@ layers, inputs resident in HBM:
 causal pairs) from HIP events around the prefill calls; the decode's cache
 GB/s and the per-kernel roofline figures are reported beside it.
 
-Three legs are timed apart from the step and reported in their own objects:
+Four legs are timed apart from the step and reported in their own objects:
 ``layer`` (the whole attention layer at T=4096: projections, RMSNorms,
 attention, output projection), ``backward`` (the gradients of the T=4096
-prefill) and ``expanded_decode`` (the decode workload over a per-head K/V
-cache, the comparator of the latent cache).
+prefill), ``varlen_prefill`` (the long packed prefill, 59,392 tokens) and
+``expanded_decode`` (the decode workload over a per-head K/V cache, the
+comparator of the latent cache).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-decode] [--no-layer] [--no-backward] [--no-expanded]
+                       [--no-decode] [--no-layer] [--no-backward] [--no-varlen] [--no-expanded]
 """
 from __future__ import annotations
 
@@ -118,6 +119,50 @@ def cpu_baseline(p, budget_s: float = 12.0):
     dt = time.perf_counter() - t0
     return {"value": per_head * heads / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{heads} of {H} heads of the T={T} prefill (fp64 NumPy), {dt:.1f} s"}
+
+
+def varlen_leg(m, dims, steps: int = 3):
+    """The long packed prefill: sequences of 32768, 16384, 8192 and 2048 tokens
+    (59,392 in all), 96 heads, gate on, fp32 out. Inputs are drawn on the device
+    (seeded torch generator) with the synthetic recipe's spreads: N(0,1)
+    activations, kv_b_proj N(0,1)/sqrt(512)."""
+    import torch
+    import synth
+    lens = list(synth.VARLEN_SEQLENS)
+    T, H = sum(lens), 96
+    log(f"long varlen prefill leg ({'+'.join(map(str, lens))} tokens)")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    bf = dict(generator=g, dtype=torch.bfloat16, device="cuda")
+    q = torch.randn((T, H, 192), **bf)
+    ckv = torch.randn((T, 512), **bf)
+    ks = torch.randn((T, 64), **bf)
+    w = (torch.randn((H * 256, 512), generator=g, dtype=torch.float32, device="cuda") / 512 ** 0.5).to(torch.bfloat16)
+    gate = torch.randn((T, H * 128), **bf)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H * 128), dtype=torch.float32, device="cuda")
+    ml = torch.empty(H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.mla_prefill_workspace_size(dims, m.MLA_BF16, T, len(lens)), dtype=torch.uint8, device="cuda")
+
+    def call():
+        m.mla_prefill(dims, q, ckv, ks, w, gate, cu, out=out, max_logit=ml, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    pairs = sum(L * (L + 1) // 2 for L in lens)
+    fl = 2.0 * H * pairs * (192 + 128) + 2.0 * T * H * 256 * 512
+    del q, ckv, ks, w, gate, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": "Kimi K3 gated MLA prefill, packed 32768+16384+8192+2048 tokens, H=96, bf16 in, fp32 out",
+            "ms": round(ms, 3), "gflop": round(fl / 1e9, 1), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def backward_leg(m, dims, p, q, ckv, ks, w_kv_b, gate, cu, steps: int = 3):
@@ -278,6 +323,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill-backward leg")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the long varlen prefill leg")
     ap.add_argument("--no-expanded", action="store_true",
                     help="skip the expanded-cache decode comparator (needs 129 GB of device memory)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -430,6 +476,8 @@ def main():
         res["layer"] = layer_leg(m, dims)
     if not args.no_backward:
         res["backward"] = backward_leg(m, dims, p, q, ckv, ks, w_kv_b, gate, cu)
+    if not args.no_varlen:
+        res["varlen_prefill"] = varlen_leg(m, dims)
     if decode and not args.no_expanded:
         res["expanded_decode"] = expanded_comparator(m, dims, d, dq, dg, lens, dec_ms, kern.get("absorbed_split"))
     if not args.no_cpu_baseline:
