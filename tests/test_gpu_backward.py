@@ -61,3 +61,10 @@ def test_backward_k3_prefill_4096(lib):
     """The configuration the benchmark times: the Kimi K3 prefill workload
     (T = 4096, 96 heads, gate on), every gradient against the full oracle."""
     _check(synth.k3_prefill(), 75)
+
+
+def test_backward_empty_and_single_token_sequences(lib):
+    """cu_seqlens with a zero-length sequence, a one-token sequence and a
+    sequence one row past a 128-row padding boundary."""
+    p = synth.prefill_inputs(synth.Dims(2, 512, 64, 128, 128), [0, 1, 129], seed=76, bf16=True)
+    _check(p, 77)
