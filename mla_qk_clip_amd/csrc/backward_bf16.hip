@@ -7,9 +7,9 @@
 // Per sequence (length L, padded to Lp = L rounded up to 128) and chunk of
 // heads, the score and probability matrices are materialised in HBM and every
 // product runs on the NT GEMM kernel (batched over the chunk's heads):
-//   S = Q_h K_h^T (fp32, Lp x Lp), then dP = dO~_h V_h^T with, in the same
-//   kernel's epilogue, P = causal exp(scale S - lse) and
-//   dS = scale P . (dP - D), D = rowsum(dO . o) (dS, dS^T, P^T in bf16)
+//   S = Q_h K_h^T with P = causal exp(scale S - lse) in its epilogue (P, P^T
+//   in bf16; S is never stored), then dP = dO~_h V_h^T with
+//   dS = scale P . (dP - D), D = rowsum(dO . o), in its epilogue (dS, dS^T)
 //   dQ = dS K_h, dK = dS^T Q_h, dV = P^T dO~_h          (fp32)
 // Only the causal half is formed: the S and dP products skip the 256 x 256
 // tiles above the diagonal (their dS, dS^T, P^T stay unwritten), and the
@@ -18,7 +18,7 @@
 // with dO~ = dO . sigma(g) and dg = dO . o . (1 - sigma(g)). Operands are bf16
 // (Q and K padded from 192 to 256 features with zeros); the GEMM kernel
 // needs K-contiguous rows on both sides, so the transposed operands (K_h^T,
-// Q_h^T, dO~^T by a tiled transpose; dS^T, P^T by the dP product's epilogue)
+// Q_h^T, dO~^T by a tiled transpose; P^T and dS^T by the products' epilogues)
 // are written out.
 // Then dK^C and dV flow back through W_UKV: dc^KV = dKV W_UKV^T-rows,
 // dW = dKV^T c^KV, and the k^S part of dK sums over the heads.
@@ -158,8 +158,8 @@ BackwardWs backward_ws_layout(int heads, int64_t ntok, int max_seqlen) {
   const size_t Lp = static_cast<size_t>(round128(max_seqlen));
   // heads per chunk: up to 32 (the gradient products have one or two 256-wide
   // column tiles, so the chunk's heads are what fills the CUs), with the
-  // Lp x Lp planes (S fp32; dS, dS^T, P^T bf16) within about 16 GB
-  const size_t plane = Lp * Lp * (4 + 2 + 2 + 2);
+  // Lp x Lp planes (P, P^T, dS, dS^T, bf16) within about 16 GB
+  const size_t plane = Lp * Lp * (2 + 2 + 2 + 2);
   w.hc = static_cast<int>(plane ? std::max<size_t>(1, std::min<size_t>(32, (size_t{16} << 30) / plane)) : 1);
   w.hc = std::min(w.hc, heads);
   const size_t hc = static_cast<size_t>(w.hc);
@@ -178,7 +178,7 @@ BackwardWs backward_ws_layout(int heads, int64_t ntok, int max_seqlen) {
   w.dot = take(hc * Lp * kV * 2);
   w.dotT = take(hc * Lp * kV * 2);
   w.dv = take(hc * Lp * 4);
-  w.s = take(hc * Lp * Lp * 4);
+  w.p = take(hc * Lp * Lp * 2);
   w.ds = take(hc * Lp * Lp * 2);
   w.dsT = take(hc * Lp * Lp * 2);
   w.pT = take(hc * Lp * Lp * 2);
@@ -252,14 +252,16 @@ hipError_t launch_prefill_backward_bf16(int heads, float scale, const void* q, c
                            s128, s128, b16(W.dotT));
       }
       BW_CHECK();
-      {  // S = Q_h K_h^T and dP = dO~_h V_h^T (fp32)
-        const GemmSpec ps{b16(W.kp), f32(W.s), kBwF, Lp, static_cast<int64_t>(Lp) * kBwF, LL, Lp};
-        e = launch_gemm_bf16(true, b16(W.qp), kBwF, static_cast<int64_t>(Lp) * kBwF, Lp, kBwF, hc, 1, &ps,
-                             "bw_scores", st, kGemmSkipUpper);
+      {  // S = Q_h K_h^T with P = causal exp(scale S - lse) in its epilogue: P, P^T (bf16)
+        const GemmSpec ps{b16(W.kp), b16(W.p), kBwF, Lp, static_cast<int64_t>(Lp) * kBwF, LL, Lp};
+        const GemmSoftmaxBwd smp{kGemmEpiP, nullptr, lse, nullptr, nullptr, b16(W.pT), LL, ntok, a, h0, L, scale};
+        e = launch_gemm_bf16(false, b16(W.qp), kBwF, static_cast<int64_t>(Lp) * kBwF, Lp, kBwF, hc, 1, &ps,
+                             "bw_scores", st, kGemmSkipUpper, &smp);
         if (e != hipSuccess) return e;
-        // dP = dO~_h V_h^T with the softmax backward in its epilogue: dS, dS^T, P^T (bf16)
+        // dP = dO~_h V_h^T with dS = scale P (dP - D) in its epilogue: dS, dS^T (bf16)
         const GemmSpec pd{b16(W.vh), b16(W.ds), kV, Lp, static_cast<int64_t>(Lp) * kV, LL, Lp};
-        const GemmSoftmaxBwd sm{f32(W.s), lse, f32(W.dv), b16(W.dsT), b16(W.pT), LL, ntok, a, h0, L, scale};
+        const GemmSoftmaxBwd sm{kGemmEpiDS, b16(W.p), nullptr, f32(W.dv), b16(W.dsT), nullptr, LL, ntok, a, h0, L,
+                                scale};
         e = launch_gemm_bf16(false, b16(W.dot), kV, static_cast<int64_t>(Lp) * kV, Lp, kV, hc, 1, &pd, "bw_dp_softmax",
                              st, kGemmSkipUpper, &sm);
         if (e != hipSuccess) return e;

@@ -52,12 +52,12 @@ struct GemmArgs {
   int nprob, mtiles, ntiles;
   int kmode;   // kGemmFull, or a causal mode (see mla_internal.h)
   GemmProblem p[kGemmMaxProblems];
-  GemmSoftmaxBwd sm;   // softmax-backward epilogue (kEpi == 2)
+  GemmSoftmaxBwd sm;   // softmax epilogues (kEpi 2 and 3)
 };
 
 // blockIdx.y is the batch index (a separate A, B and C per batch entry).
-// Epilogue kEpi: 0 bf16 C, 1 fp32 C, 2 the softmax backward of a causal
-// score plane (C = dP; see GemmSoftmaxBwd).
+// Epilogue kEpi: 0 bf16 C, 1 fp32 C, 2 and 3 the softmax epilogues of a
+// causal score plane (see GemmSoftmaxBwd).
 template <int kEpi>
 __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
   constexpr bool kOutF32 = kEpi == 1;
@@ -201,48 +201,51 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
     // ---- store: lane = output row l32 of the row block; element i of a tile is
     // column 8 (i / 4) + 4 g + i % 4 of the column block. Lanes l and l + 32 swap
     // runs so that each holds 8 consecutive columns (two 16-byte stores per tile).
-    // softmax-backward epilogue: dS^T and P^T go through a wave-private 16 KB of
-    // LDS (the operand slots are free once every wave is past the k loop)
+    // softmax epilogues of a causal score plane (kEpi 3: P from S; kEpi 2: dS
+    // from dP): the transposed plane goes through a wave-private 8 KB of LDS
+    // (the operand slots are free once every wave is past the k loop)
+    constexpr bool kSm = kEpi >= 2;
     uint16_t* tst = nullptr;
-    if constexpr (kEpi == 2) {
+    if constexpr (kSm) {
       __syncthreads();
       uint4* slot = wave < 2 ? As0 : wave < 4 ? As1 : wave < 6 ? Bs0 : Bs1;
-      tst = reinterpret_cast<uint16_t*>(slot + (wave & 1) * 1024);   // [2][128 columns][32 rows] bf16
+      tst = reinterpret_cast<uint16_t*>(slot + (wave & 1) * 1024);   // [128 columns][32 rows] bf16
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int m = m0 + 64 * wm + 32 * kb + l32;
       float lse2 = 0.0f, dv = 0.0f;
+      if constexpr (kEpi == 3) {
+        if (m < args.sm.L) lse2 = args.sm.lse[(args.sm.h0 + bz) * args.sm.ntok + args.sm.a + m] * kLog2e;
+      }
       if constexpr (kEpi == 2) {
-        if (m < args.sm.L) {
-          lse2 = args.sm.lse[(args.sm.h0 + bz) * args.sm.ntok + args.sm.a + m] * kLog2e;
-          dv = args.sm.D[bz * args.m + m];
-        }
+        if (m < args.sm.L) dv = args.sm.D[bz * args.m + m];
       }
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) {
         f32x16 a = acc[2 * fb + kb];
-        if constexpr (kEpi == 2) {
-          // P = exp(scale S - lse) on and below the diagonal of the first L
-          // rows, dS = scale P (dP - D); dS^T and P^T go out here, dS below
+        if constexpr (kSm) {
           const int nb = n0 + 128 * wn + 32 * fb + 4 * g;
-          const float* srow = args.sm.S + bz * args.sm.plane + static_cast<int64_t>(m) * args.m;
           const float sl2 = args.sm.scale * kLog2e;
+          const uint16_t* prow = args.sm.P + bz * args.sm.plane + static_cast<int64_t>(m) * args.m;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float4 sv = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (m < args.sm.L && nb + 8 * r <= m) sv = *reinterpret_cast<const float4*>(srow + nb + 8 * r);
-            const float se[4] = {sv.x, sv.y, sv.z, sv.w};
+            uint2 pw = make_uint2(0, 0);
+            if constexpr (kEpi == 2) {
+              if (m < args.m) pw = *reinterpret_cast<const uint2*>(prow + nb + 8 * r);
+            }
+            const float pe[4] = {bf16lo(pw.x), bf16hi(pw.x), bf16lo(pw.y), bf16hi(pw.y)};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int n = nb + 8 * r + e;
-              const bool on = m < args.sm.L && n <= m;
-              const float pv = on ? fast_exp2(se[e] * sl2 - lse2) : 0.0f;
-              const float gv = args.sm.scale * pv * (a[4 * r + e] - dv);
-              a[4 * r + e] = gv;
-              const int cl = 32 * fb + 8 * r + 4 * g + e;   // column within the wave's 128
-              tst[cl * 32 + l32] = f32_to_bf16(gv);
-              tst[4096 + cl * 32 + l32] = f32_to_bf16(pv);
+              float v;
+              if constexpr (kEpi == 3) {   // P = exp(scale S - lse) on and below the diagonal of the first L rows
+                v = (m < args.sm.L && n <= m) ? fast_exp2(a[4 * r + e] * sl2 - lse2) : 0.0f;
+              } else {                     // dS = scale P (dP - D)
+                v = args.sm.scale * pe[e] * (a[4 * r + e] - dv);
+              }
+              a[4 * r + e] = v;
+              tst[(32 * fb + 8 * r + 4 * g + e) * 32 + l32] = f32_to_bf16(v);
             }
           }
         }
@@ -279,22 +282,18 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
           }
         }
       }
-      if constexpr (kEpi == 2) {
-        // rows s of dS^T and P^T: 32 consecutive t (64 bytes) per column of this row block
+      if constexpr (kSm) {
+        // rows of the transposed plane: 32 consecutive t (64 bytes) per column of this row block
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
         const int t0 = m0 + 64 * wm + 32 * kb;
+        uint16_t* tout = kEpi == 2 ? args.sm.dST : args.sm.PT;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int c = lane + 64 * j, cl = c >> 2, part = c & 3;
           const int n = n0 + 128 * wn + cl, t = t0 + 8 * part;
-          const uint4 vd = *reinterpret_cast<const uint4*>(tst + cl * 32 + 8 * part);
-          const uint4 vp = *reinterpret_cast<const uint4*>(tst + 4096 + cl * 32 + 8 * part);
-          if (n < args.m && t < args.m) {
-            const int64_t tix = bz * args.sm.plane + static_cast<int64_t>(n) * args.m + t;
-            stg16(args.sm.dST + tix, vd);
-            stg16(args.sm.PT + tix, vp);
-          }
+          const uint4 vt = *reinterpret_cast<const uint4*>(tst + cl * 32 + 8 * part);
+          if (n < args.m && t < args.m) stg16(tout + bz * args.sm.plane + static_cast<int64_t>(n) * args.m + t, vt);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
@@ -380,7 +379,8 @@ hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_
   TimedScope ts_(name, st);
   if (sm) {
     args.sm = *sm;
-    hipLaunchKernelGGL(gemm_nt_kernel<2>, grid, dim3(kGmThreads), 0, st, args);
+    if (sm->mode == kGemmEpiP) hipLaunchKernelGGL(gemm_nt_kernel<3>, grid, dim3(kGmThreads), 0, st, args);
+    else hipLaunchKernelGGL(gemm_nt_kernel<2>, grid, dim3(kGmThreads), 0, st, args);
   } else if (out_f32) {
     hipLaunchKernelGGL(gemm_nt_kernel<1>, grid, dim3(kGmThreads), 0, st, args);
   } else {

@@ -163,7 +163,7 @@ inline LayerWs layer_ws_layout(int heads, int hidden, int q_rank, int64_t ntok, 
 // then one chunk of heads' per-sequence buffers (rows padded to a multiple of
 // 128, Q and K padded to 256 features; Lp x Lp score planes).
 struct BackwardWs {
-  size_t kv, wT, ckvT, dkv, dkvT, qp, qpT, kp, kpT, vh, dot, dotT, dv, s, ds, dsT, pT, dqc, dkc, dvc, total;
+  size_t kv, wT, ckvT, dkv, dkvT, qp, qpT, kp, kpT, vh, dot, dotT, dv, p, ds, dsT, pT, dqc, dkc, dvc, total;
   int hc;   // heads per chunk
 };
 BackwardWs backward_ws_layout(int heads, int64_t ntok, int max_seqlen);
@@ -207,16 +207,19 @@ struct GemmSpec {
 //   kGemmKToRow     each tile sums k < min(K, m0 + 256)   (C[t] = sum_{s <= t})
 //   kGemmKFromRow   each tile sums k >= m0                (C[s] = sum_{t >= s})
 constexpr int kGemmFull = 0, kGemmSkipUpper = 1, kGemmKToRow = 2, kGemmKFromRow = 3;
-// Softmax-backward epilogue for C = dP = dO~ V^T over square planes (M = N =
-// the plane width): with S the plane of raw scores, for row t < L and column
-// s <= t, P = exp(scale S - lse[h][a + t]) and dS = scale P (dP - D[t]) (zero
-// elsewhere); C receives dS (bf16), dST and PT the transposes of dS and P.
+// Softmax epilogues over square causal planes (M = N = the plane width; bf16 C):
+//   kGemmEpiP   on C = S (raw scores): P = exp(scale S - lse[h][a + t]) for row
+//               t < L and column s <= t, else 0; C receives P, PT its transpose
+//   kGemmEpiDS  on C = dP: dS = scale P (dP - D[t]) with P read from the plane
+//               written by kGemmEpiP; C receives dS, dST its transpose
+constexpr int kGemmEpiP = 3, kGemmEpiDS = 2;
 struct GemmSoftmaxBwd {
-  const float* S;        // [batch][M][M] fp32
-  const float* lse;      // [H][ntok] natural-log LSE of the scaled scores
-  const float* D;        // [batch][M] rowsum(dO . o)
-  uint16_t* dST;         // [batch][M][M]
-  uint16_t* PT;          // [batch][M][M]
+  int mode;              // kGemmEpiP or kGemmEpiDS
+  const uint16_t* P;     // [batch][M][M] bf16 (kGemmEpiDS)
+  const float* lse;      // [H][ntok] natural-log LSE of the scaled scores (kGemmEpiP)
+  const float* D;        // [batch][M] rowsum(dO . o) (kGemmEpiDS)
+  uint16_t* dST;         // [batch][M][M] (kGemmEpiDS)
+  uint16_t* PT;          // [batch][M][M] (kGemmEpiP)
   int64_t plane, ntok, a, h0;   // plane stride, tokens, first token of the sequence, first head of the batch
   int L;
   float scale;
