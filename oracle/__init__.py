@@ -14,6 +14,7 @@ passage each one follows.
 from .mla_oracle import (  # noqa: F401
     Dims,
     absorbed,
+    absorbed_max_logit,
     absorbed_rows_selected,
     dense_prefill,
     expand_latent,
@@ -28,6 +29,10 @@ from .mla_oracle import (  # noqa: F401
     prefill_rows,
     q_projection,
     qk_clip,
+    qk_norm_absorbed,
+    qk_norm_logit_bound,
+    qk_norm_prefill,
+    qk_norm_query,
     rms_norm,
     round_to,
 )

@@ -286,6 +286,36 @@ def absorbed(q, cache_rows, w_kv_b, gate, dims):
     return out, smax
 
 
+def absorbed_max_logit(q, cache_rows, w_kv_b, dims):
+    """Per-head maximum scaled logit of the absorbed form, without the softmax.
+
+    The same logits as ``absorbed``: s_j = scale * q_abs . [c^KV_j | k^S_j] with
+    q_abs = [W_UK_h q^C, q^R] (associativity of the [MLA] score step with the
+    key expansion), over the visible rows j <= L_b - Tq + i of every query i of
+    every sequence b. Sequences are taken one at a time, so a workload whose
+    cache is too large to hold whole can pass ``cache_rows`` as any indexable
+    whose item b returns sequence b's rows. Returns max_logit [H] (float64).
+    """
+    d = _dims(dims)
+    H = d.heads
+    scale = scale_of(d)
+    q = np.asarray(q)
+    B, Tq = q.shape[0], q.shape[1]
+    w = np.asarray(w_kv_b, dtype=f64)
+    smax = np.full(H, -np.inf, dtype=f64)
+    for b in range(B):
+        rows = np.asarray(cache_rows[b], dtype=f64)
+        L = rows.shape[0]
+        for i in range(Tq):
+            vis = L - Tq + i + 1
+            if vis <= 0:
+                continue
+            qa = np.stack([absorb_query(q[b, i, h], w, d, h) for h in range(H)])   # [H, R+S]
+            s = (rows[:vis] @ qa.T) * scale                                         # [vis, H]
+            smax = np.maximum(smax, s.max(axis=0))
+    return smax
+
+
 def absorbed_rows_selected(q, cache_rows, w_kv_b, gate, dims, batches):
     """``absorbed`` restricted to the listed sequences (spot checks)."""
     qs = np.asarray(q)[list(batches)]
@@ -508,6 +538,70 @@ def layer_rows(x, w_dq, g_q, w_uq, w_kv_a, g_kv, w_kv_b, w_g, w_o, cu_seqlens, d
 
 
 # ---------------------------------------------------------------------------
+# QK-norm variant ([CLIP] "Variations": the other route to bounded logits,
+# an RMSNorm on the attention queries and on the KV entries instead of a clip
+# of the weights; "Mechanism": the norm bounds the input of the logit). In
+# this MLA the compressed entry c^KV already leaves an RMSNorm
+# (kv_a_layernorm) and k^S is normalised where it is produced, so the
+# attention calls take them as given; the query is normalised per head.
+# ---------------------------------------------------------------------------
+
+
+def qk_norm_query(q, weight, eps: float, round_bf16: bool = True):
+    """Per-head RMSNorm of the queries: each head's D = N + S query features
+    (q^C and q^R together) divided by their root mean square, times the
+    per-feature weight [D] shared by the heads (None = ones). With
+    ``round_bf16`` the normalised query is rounded to bf16 where it is
+    produced, as every activation the model keeps in its dtype.
+
+    q [..., H, D] -> same shape, float64.
+    """
+    q = np.asarray(q, dtype=f64)
+    w = np.ones(q.shape[-1]) if weight is None else np.asarray(weight, dtype=f64)
+    y = rms_norm(q, w, eps)
+    return round_to(y, "bf16") if round_bf16 else y
+
+
+def qk_norm_prefill(q, ckv, ks, w_kv_b, gate, cu_seqlens, dims, q_norm_weight, eps: float,
+                    round_bf16: bool = True, heads=None):
+    """The training-form prefill on per-head normalised queries: first
+    ``qk_norm_query``, then ``prefill`` unchanged (c^KV and k^S as given)."""
+    qn = qk_norm_query(q, q_norm_weight, eps, round_bf16)
+    return prefill(qn, ckv, ks, w_kv_b, gate, cu_seqlens, dims, heads=heads)
+
+
+def qk_norm_absorbed(q, cache_rows, w_kv_b, gate, dims, q_norm_weight, eps: float, round_bf16: bool = True):
+    """The absorbed form on per-head normalised queries (``qk_norm_query``,
+    then ``absorbed``)."""
+    qn = qk_norm_query(q, q_norm_weight, eps, round_bf16)
+    return absorbed(qn, cache_rows, w_kv_b, gate, dims)
+
+
+def qk_norm_logit_bound(w_kv_b, dims, q_norm_weight, ckv_norm_max: float, ks_norm_max: float):
+    """Closed-form bound of every scaled logit of each head under the QK-norm
+    variant (with eps = 0):
+
+      |S| = |q_n^C . (c W_UK_h) + q_n^R . k^S| / sqrt(D)
+          <= ||q_n|| sqrt(||c W_UK_h||^2 + ||k^S||^2) / sqrt(D)          (Cauchy-Schwarz)
+          <= max|w| sqrt(sigma_h^2 ||c||^2 + ||k^S||^2),
+
+    since ||q_n|| <= sqrt(D) max|w|, with sigma_h the largest singular value
+    of W_UK_h and ||c||, ||k^S|| the largest entry norms. It grows with
+    sigma_h: the norm of the inputs does not bound the logit through the
+    key up-projection. Returns [H] (float64).
+    """
+    d = _dims(dims)
+    H, N, V = d.heads, d.nope_dim, d.v_dim
+    w = np.asarray(w_kv_b, dtype=f64)
+    wmax = 1.0 if q_norm_weight is None else float(np.max(np.abs(np.asarray(q_norm_weight, dtype=f64))))
+    out = np.zeros(H)
+    for h in range(H):
+        sigma = np.linalg.norm(w[h * (N + V):h * (N + V) + N, :], 2)   # largest singular value of W_UK_h
+        out[h] = wmax * math.sqrt(sigma ** 2 * ckv_norm_max ** 2 + ks_norm_max ** 2)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Query projection ([MLA] "q = c^Q W_UQ") and QK-Clip ([CLIP])
 # ---------------------------------------------------------------------------
 
@@ -549,13 +643,28 @@ def qk_clip(w_q_b, w_kv_b, max_logit, tau, dims):
     return wq, wk, mask, gamma
 
 
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127   # largest finite bf16 value
+BF16_MIN_NORMAL = 2.0 ** -126                # bf16 keeps fp32's exponent range
+BF16_SUBNORMAL_STEP = 2.0 ** -133            # spacing of bf16 values below the smallest normal
+
+
 def round_to(x, dtype: str):
-    """Round float64 values to the nearest 'f32' or 'bf16' value, ties to even."""
+    """Round float64 values to the nearest 'f32' or 'bf16' value, ties to even.
+
+    bf16 is fp32's sign and 8 exponent bits with 7 stored fraction bits: 8
+    significant bits for normal values, a fixed spacing of 2^-133 below the
+    smallest normal 2^-126 (subnormals), and values whose rounding would pass
+    the largest finite value (2 - 2^-7) 2^127 become infinite. NaN stays NaN.
+    """
     x = np.asarray(x, dtype=f64)
     if dtype == "f32":
         return x.astype(np.float32).astype(f64)
     if dtype != "bf16":
         raise ValueError(dtype)
-    m, e = np.frexp(x)                       # x = m * 2^e, 0.5 <= |m| < 1
-    r = np.rint(m * 256.0)                   # 8 significant bits, half to even
-    return np.ldexp(r, e - 8)
+    with np.errstate(invalid="ignore", over="ignore"):
+        m, e = np.frexp(x)                       # x = m * 2^e, 0.5 <= |m| < 1
+        r = np.ldexp(np.rint(m * 256.0), e - 8)  # 8 significant bits, half to even
+        sub = np.abs(x) < BF16_MIN_NORMAL
+        r = np.where(sub, np.rint(x / BF16_SUBNORMAL_STEP) * BF16_SUBNORMAL_STEP, r)
+        r = np.where(np.isfinite(r) & (np.abs(r) > BF16_MAX), np.copysign(np.inf, x), r)
+    return r

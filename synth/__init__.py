@@ -89,10 +89,6 @@ class Dims:
     def qk_dim(self) -> int:
         return self.nope_dim + self.shared_dim
 
-    @property
-    def scale(self) -> float:
-        return 1.0 / math.sqrt(self.qk_dim)
-
 
 K3 = Dims(heads=96, kv_rank=512, shared_dim=64, nope_dim=128, v_dim=128)
 TINY = Dims(heads=4, kv_rank=32, shared_dim=16, nope_dim=32, v_dim=32)

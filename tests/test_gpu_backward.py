@@ -52,7 +52,7 @@ def test_backward_ragged_varlen(lib, gate):
 
 
 def test_backward_96_heads_2048(lib):
-    """96 heads, one sequence of 2048 tokens (12 chunks of 8 heads)."""
+    """96 heads, one sequence of 2048 tokens (three chunks of 32 heads)."""
     p = synth.prefill_inputs(synth.K3, [2048], seed=73, bf16=True)
     _check(p, 74)
 

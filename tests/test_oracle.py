@@ -74,6 +74,33 @@ def test_bf16_rounding_two_implementations_agree():
     assert np.array_equal(synth.from_bf16_bits(bits), synth.round_bf16(x))
 
 
+def test_bf16_rounding_over_the_whole_float32_range():
+    """Both roundings over every binade of float32, its subnormals and the
+    overflow threshold: bf16 keeps fp32's exponent range, so values below
+    2^-126 round to multiples of 2^-133 and values at or past the midpoint
+    between the largest finite bf16 value and 2^128 become infinite."""
+    rng = np.random.default_rng(1)
+    # random bit patterns cover every exponent (normal and subnormal) and sign
+    u = rng.integers(0, 2 ** 32, size=400000, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    x = x[np.isfinite(x)]
+    a = synth.round_bf16(x).astype(np.float64)
+    b = oracle.round_to(x.astype(np.float64), "bf16")
+    assert np.array_equal(a, b)
+    bmax = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    edge = np.array([bmax, (2.0 - 2.0 ** -8) * 2.0 ** 127, np.nextafter(np.float32((2.0 - 2.0 ** -8) * 2.0 ** 127),
+                     np.float32(0)), 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -134, 2.0 ** -126 - 2.0 ** -140,
+                     np.float32(3.4e38)], dtype=np.float32)
+    assert np.array_equal(synth.round_bf16(edge).astype(np.float64), oracle.round_to(edge.astype(np.float64), "bf16"))
+    assert oracle.round_to(bmax, "bf16") == bmax
+    assert oracle.round_to((2.0 - 2.0 ** -8) * 2.0 ** 127, "bf16") == np.inf     # tie: to even (overflow)
+    assert oracle.round_to(-(2.0 - 2.0 ** -8) * 2.0 ** 127, "bf16") == -np.inf
+    assert oracle.round_to(2.0 ** -134, "bf16") == 0.0                             # half the smallest step: to even
+    assert oracle.round_to(3 * 2.0 ** -134, "bf16") == 2.0 ** -132                 # 1.5 steps: to even (2 steps)
+    assert oracle.round_to(2.0 ** -126 - 2.0 ** -140, "bf16") == 2.0 ** -126
+    assert np.isnan(oracle.round_to(np.nan, "bf16"))
+
+
 # ---------------------------------------------------------------------------
 # the pages' printed numbers
 # ---------------------------------------------------------------------------
@@ -290,6 +317,37 @@ def test_absorbed_max_logit_matches_materialised_last_rows():
         for t in range(33 - tq, 33):
             best = max(best, float((K[:t + 1] @ p.q[t, h].astype(np.float64)).max()) * oracle.mla_oracle.scale_of(dims))
         assert sm[h] == pytest.approx(best, rel=1e-12)
+
+
+@pytest.mark.parametrize("tq", [1, 4])
+def test_absorbed_max_logit_alone_matches_materialised_keys(tq):
+    """``absorbed_max_logit`` (no softmax) against the materialised side: the
+    key K_h = [c^KV W_UK_h, k^S] of every visible row scored with q directly,
+    on ragged sequences of several lengths; and against ``absorbed``'s own
+    maximum on the same inputs."""
+    dims = synth.TINY
+    d = synth.decode_inputs(dims, [9, 1 + tq, 30], cap=32, tq=tq, seed=12, bf16=True)
+    rows = [d.cache_rows(b) for b in range(d.batch)]
+    sm = oracle.absorbed_max_logit(d.q, rows, d.w_kv_b, dims)
+    _, sm_full = oracle.absorbed(d.q, rows, d.w_kv_b, d.gate, dims)
+    assert np.allclose(sm, sm_full, rtol=1e-12, atol=0)
+    R = dims.kv_rank
+    scale = 1.0 / math.sqrt(dims.nope_dim + dims.shared_dim)
+    for h in range(dims.heads):
+        best = -np.inf
+        for b, r in enumerate(rows):
+            kc, _ = oracle.expand_latent(r[:, :R], d.w_kv_b, dims, h)
+            K = np.concatenate([kc, r[:, R:].astype(np.float64)], axis=1)
+            L = r.shape[0]
+            for i in range(tq):
+                vis = L - tq + i + 1
+                best = max(best, float((K[:vis] @ d.q[b, i, h].astype(np.float64)).max()) * scale)
+        assert sm[h] == pytest.approx(best, rel=1e-12)
+    # a row planted late in one sequence and visible only to the last query
+    rows2 = [r.copy() for r in rows]
+    rows2[2][-1] = rows2[2][-1] * 50.0
+    sm2 = oracle.absorbed_max_logit(d.q, rows2, d.w_kv_b, dims)
+    assert np.all(sm2 >= sm - 1e-12) and np.any(sm2 > 10 * np.abs(sm))
 
 
 # ---------------------------------------------------------------------------
@@ -587,3 +645,125 @@ def test_clip_stress_recipe_clips_exactly_the_scaled_heads():
     assert list(np.nonzero(mask)[0]) == list(synth.CLIP_HEADS)
     assert sm[mask].min() > 1000.0
     assert sm[~mask].max() < 10.0
+
+
+# ---------------------------------------------------------------------------
+# QK-norm variant (per-head RMSNorm of the queries)
+# ---------------------------------------------------------------------------
+
+
+def test_qk_norm_query_closed_form_per_head():
+    """q_h = [a 1_N, b 1_S] has root mean square sqrt((N a^2 + S b^2) / D):
+    each head is divided by its own, then multiplied by the weight."""
+    dims = synth.TINY
+    H, N, S = dims.heads, dims.nope_dim, dims.shared_dim
+    D = N + S
+    ab = [(1.0, 2.0), (3.0, -0.5), (0.25, 0.0), (-7.0, 7.0)]
+    q = np.zeros((2, H, D))
+    for h, (a, b) in enumerate(ab):
+        q[:, h, :N], q[:, h, N:] = a, b
+    w = 1.0 + 0.1 * np.arange(D)
+    for eps in (0.0, 0.5):
+        got = oracle.qk_norm_query(q, w, eps, round_bf16=False)
+        for h, (a, b) in enumerate(ab):
+            r = math.sqrt((N * a * a + S * b * b) / D + eps)
+            want = np.concatenate([np.full(N, a), np.full(S, b)]) / r * w
+            assert np.allclose(got[0, h], want, rtol=1e-14, atol=0)
+    assert np.array_equal(oracle.qk_norm_query(q, w, 0.0), oracle.round_to(oracle.qk_norm_query(q, w, 0.0, False),
+                                                                             "bf16"))
+
+
+def test_qk_norm_is_blind_to_the_query_scale():
+    """Scaling any head's query by a positive factor leaves the output and the
+    max logit unchanged (eps = 0; exactly so with bf16 rounding for powers of 2)."""
+    dims = synth.TINY
+    p = synth.prefill_inputs(dims, [19, 30], seed=31, bf16=True)
+    w = 1.0 + 0.1 * np.random.default_rng(2).standard_normal(dims.nope_dim + dims.shared_dim)
+    c = np.array([7.3, 0.01, 1.0, 250.0])[None, :, None]
+    o1, l1, s1 = oracle.qk_norm_prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, dims, w, 0.0, False)
+    o2, l2, s2 = oracle.qk_norm_prefill(p.q * c, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, dims, w, 0.0, False)
+    assert rel_err(o2, o1) < 1e-12 and np.allclose(s2, s1, rtol=1e-12)
+    c2 = np.array([4.0, 0.125, 1.0, 1024.0])[None, :, None]
+    o3, _, s3 = oracle.qk_norm_prefill(p.q * c2, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, dims, w, 0.0)
+    o4, _, s4 = oracle.qk_norm_prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, dims, w, 0.0)
+    assert np.array_equal(o3, o4) and np.array_equal(s3, s4)
+    # without the norm the same scaling changes everything
+    o5, _, _ = oracle.prefill(p.q * c, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, dims)
+    assert rel_err(o5, oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, dims)[0]) > 1e-2
+
+
+def test_qk_norm_of_unit_rms_queries_is_the_plain_prefill():
+    dims = synth.TINY
+    p = synth.prefill_inputs(dims, [25], seed=32, bf16=False)
+    q = np.asarray(p.q, dtype=np.float64)
+    q = q / np.sqrt(np.mean(q * q, axis=-1, keepdims=True))
+    ref = oracle.prefill(q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, dims)
+    got = oracle.qk_norm_prefill(q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, dims, None, 0.0, False)
+    assert rel_err(got[0], ref[0]) < 1e-12 and np.allclose(got[2], ref[2], rtol=1e-12)
+    # decode with the norm equals the last rows of prefill with the norm
+    rows = [np.concatenate([p.ckv, p.ks], axis=1)]
+    out, sm = oracle.qk_norm_absorbed(p.q[None, -2:], rows, p.w_kv_b, p.gate[None, -2:], dims, None, 1e-6, False)
+    full = oracle.qk_norm_prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, dims, None, 1e-6, False)[0]
+    assert rel_err(out[0], full[-2:]) < 1e-10
+
+
+def test_qk_norm_logit_bound_holds_and_is_attained():
+    """Every logit stays within the closed-form bound; a constructed input
+    (latent along W_UK_h's top right singular vector, query along the key it
+    makes) reaches it exactly."""
+    dims = synth.TINY
+    H, R, S, N, V = dims.heads, dims.kv_rank, dims.shared_dim, dims.nope_dim, dims.v_dim
+    D = N + S
+    rng = np.random.default_rng(33)
+    p = synth.prefill_inputs(dims, [40], seed=33, bf16=False)
+    ckv = p.ckv / np.sqrt(np.mean(p.ckv.astype(np.float64) ** 2, axis=1, keepdims=True))   # unit-RMS entries
+    ks = p.ks / np.sqrt(np.mean(p.ks.astype(np.float64) ** 2, axis=1, keepdims=True))
+    w = 1.0 + 0.2 * rng.standard_normal(D)
+    bound = oracle.qk_norm_logit_bound(p.w_kv_b, dims, w, math.sqrt(R), math.sqrt(S))
+    qn = oracle.qk_norm_query(p.q, w, 0.0, False)
+    _, probs, sm = oracle.dense_prefill(qn, ckv, ks, p.w_kv_b, None, p.cu_seqlens, dims)
+    assert np.all(sm <= bound) and np.all(sm > 0.05 * bound)
+    # attainment: one token whose latent is sqrt(R) times the top right singular vector of W_UK_h
+    h = 2
+    wk = np.asarray(p.w_kv_b, dtype=np.float64)[h * (N + V):h * (N + V) + N]      # [N, R]
+    _, sv, vt = np.linalg.svd(wk)
+    c = math.sqrt(R) * vt[0]
+    k = np.ones(S)                                                               # unit RMS
+    key = np.concatenate([c @ wk.T, k])
+    q = np.ones((1, H, D))
+    q[0, h] = key
+    one = np.array([0, 1], dtype=np.int32)
+    sm1 = oracle.max_logit_head(oracle.qk_norm_query(q, None, 0.0, False), c[None], k[None], p.w_kv_b, one, dims, h)
+    b1 = oracle.qk_norm_logit_bound(p.w_kv_b, dims, None, math.sqrt(R), math.sqrt(S))[h]
+    assert sm1 == pytest.approx(b1, rel=1e-12)
+    assert b1 == pytest.approx(math.sqrt(sv[0] ** 2 * R + S), rel=1e-12)
+
+
+def test_qk_norm_ignores_a_scaled_query_weight_but_not_a_scaled_key_weight():
+    """The clip-stress mechanism under the norm: scaling a head's q_b_proj
+    rows x40 changes none of its logits, while scaling its W_UK rows x40 (with
+    k^S = 0, so every logit comes through W_UK) multiplies every logit of the
+    head by exactly 40. The norm on the inputs does not bound the logit
+    through the key up-projection."""
+    dims = synth.Dims(4, 32, 16, 32, 32)
+    H, N, V, S, D = 4, 32, 32, 16, 48
+    p = synth.clip_stress_inputs(dims, 24, seed=34, q_in=64, heads=(1,), factor=1.0)
+    ks0 = np.zeros_like(p.ks)
+    q = oracle.q_projection(p.cq, p.w_q_b, dims)
+    wq40 = np.array(p.w_q_b, dtype=np.float64)
+    wq40[1 * D:2 * D] *= 40.0
+    q40 = oracle.q_projection(p.cq, wq40, dims)
+    wk40 = np.array(p.w_kv_b, dtype=np.float64)
+    wk40[1 * (N + V):1 * (N + V) + N] *= 40.0
+
+    def smax(qq, wk, ks):
+        return oracle.qk_norm_prefill(qq, p.ckv, ks, wk, None, p.cu_seqlens, dims, None, 0.0, False)[2]
+    base = smax(q, p.w_kv_b, ks0)
+    assert np.allclose(smax(q40, p.w_kv_b, ks0), base, rtol=1e-12)
+    s40 = smax(q, wk40, ks0)
+    assert s40[1] == pytest.approx(40.0 * base[1], rel=1e-12)
+    assert np.array_equal(np.delete(s40, 1), np.delete(base, 1))
+    # without the norm the query weight's x40 multiplies the logits as well
+    plain = oracle.prefill(q40, p.ckv, ks0, p.w_kv_b, None, p.cu_seqlens, dims)[2]
+    assert plain[1] == pytest.approx(40.0 * oracle.prefill(q, p.ckv, ks0, p.w_kv_b, None, p.cu_seqlens, dims)[2][1],
+                                     rel=1e-12)
