@@ -12,15 +12,17 @@ layers, inputs resident in HBM:
 causal pairs) from HIP events around the prefill calls; the decode's cache
 GB/s and the per-kernel roofline figures are reported beside it.
 
-Four legs are timed apart from the step and reported in their own objects:
-``layer`` (the whole attention layer at T=4096: projections, RMSNorms,
-attention, output projection), ``backward`` (the gradients of the T=4096
-prefill), ``varlen_prefill`` (the long packed prefill, 59,392 tokens) and
+Five legs are timed apart from the step and reported in their own objects:
+``clip_stress`` (the QK-Clip stress workload at T=2048: the attention pass
+before and after a clip that rescales six heads, and the clip), ``layer``
+(the whole attention layer at T=4096: projections, RMSNorms, attention,
+output projection), ``backward`` (the gradients of the T=4096 prefill),
+``varlen_prefill`` (the long packed prefill, 59,392 tokens) and
 ``expanded_decode`` (the decode workload over a per-head K/V cache, the
 comparator of the latent cache).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-decode] [--no-layer] [--no-backward] [--no-varlen] [--no-expanded]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+                       [--no-clip-stress] [--no-layer] [--no-backward] [--no-varlen] [--no-expanded]
 """
 from __future__ import annotations
 
@@ -118,7 +120,20 @@ def cpu_baseline(p, budget_s: float = 12.0):
             break
     dt = time.perf_counter() - t0
     return {"value": per_head * heads / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{heads} of {H} heads of the T={T} prefill (fp64 NumPy), {dt:.1f} s"}
+            "sample": f"{heads} of {H} heads of the T={T} prefill (fp64 NumPy), {dt:.1f} s",
+            "cpu": cpu_model(), "cores_available": len(os.sched_getaffinity(0))}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def varlen_leg(m, dims, steps: int = 3):
@@ -268,6 +283,81 @@ def layer_leg(m, dims, steps: int = 5):
                          "algorithmic": f"{gf['layer_proj_x'] / 1e9:.1f} GFLOP per launch (x W^T for q_a, kv_a, g)"}}
 
 
+def clip_stress_leg(m, dims, steps: int = 5):
+    """The QK-Clip stress workload (T = 2048, heads 0, 19, 38, 57, 76, 95 with
+    their q_b_proj and W_UK blocks x40, tau = 100): the attention pass before
+    the clip, the clip itself, and the attention pass after it with the
+    queries re-projected through the clipped q_b_proj. The query projection
+    q = c^Q W_UQ^T runs on mla_linear and is not timed."""
+    import torch
+    import synth
+    log("QK-Clip stress leg (T=2048, six heads x40)")
+    p = synth.k3_clip_stress()
+    T, H = p.ntok, dims.heads
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16)
+    cq, ckv, ks, gate = up(p.cq), up(p.ckv), up(p.ks), up(p.gate)
+    wq0, wk0 = up(p.w_q_b), up(p.w_kv_b)
+    cu = torch.from_numpy(p.cu_seqlens).cuda()
+    out = torch.empty((T, H * 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.mla_prefill_workspace_size(dims, m.MLA_BF16, T, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def attention(wq, wk, q_norm=None):
+        q = m.mla_linear(cq, wq).view(T, H, 192)
+        ml = torch.empty(H, dtype=torch.float32, device="cuda")
+        m.mla_prefill(dims, q, ckv, ks, wk, gate, cu, out=out, max_logit=ml, workspace=ws, q_norm=q_norm)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            m.mla_prefill(dims, q, ckv, ks, wk, gate, cu, out=out, max_logit=ml, workspace=ws, q_norm=q_norm)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps, ml.cpu().numpy().astype(np.float64)
+
+    before_ms, sm0 = attention(wq0, wk0)
+    # the QK-norm variant on the same weights (per-head RMSNorm of the queries, unit weight)
+    norm_ms, smn = attention(wq0, wk0, q_norm=(None, 1e-6))
+    # the clip, timed on fresh copies of the weights (it rescales them in place)
+    clip_ms = []
+    wq, wk = wq0.clone(), wk0.clone()
+    ml0 = torch.from_numpy(sm0.astype(np.float32)).cuda()
+    for _ in range(steps):
+        wq.copy_(wq0)
+        wk.copy_(wk0)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        clipped, gamma = m.mla_qk_clip(dims, wq, wk, ml0, synth.TAU)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        clip_ms.append(ev[0].elapsed_time(ev[1]))
+    after_ms, sm1 = attention(wq, wk)
+    pairs = T * (T + 1) // 2
+    fl = 2.0 * H * pairs * (192 + 128) + 2.0 * T * H * 256 * 512
+    heads = [int(h) for h in np.nonzero(clipped.cpu().numpy())[0]]
+    res = {"workload": "QK-Clip stress: Kimi K3 gated MLA prefill T=2048 H=96 bf16, heads 0,19,38,57,76,95 "
+                       "with q_b_proj and W_UK blocks x40, tau=100",
+           "gflop_per_pass": round(fl / 1e9, 1),
+           "attn_ms_before_clip": round(before_ms, 4), "attn_ms_after_clip": round(after_ms, 4),
+           "tflops_before_clip": round(fl / (before_ms * 1e-3) / 1e12, 2),
+           "tflops_after_clip": round(fl / (after_ms * 1e-3) / 1e12, 2),
+           "frac_mfma_peak": round(fl / (min(before_ms, after_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "clip_ms": round(float(np.median(clip_ms)), 4),
+           "clipped_heads": heads,
+           "max_logit_before": {str(h): round(float(sm0[h]), 2) for h in heads},
+           "max_logit_after_max": round(float(sm1.max()), 4),
+           "max_logit_after_le_tau": bool(np.all(sm1 <= synth.TAU * (1 + 1e-3))),
+           "qk_norm": {"attn_ms": round(norm_ms, 4),
+                       "max_logit": {str(h): round(float(smn[h]), 2) for h in heads},
+                       "heads_above_tau": [int(h) for h in np.nonzero(smn > synth.TAU)[0]]}}
+    del cq, ckv, ks, gate, wq0, wk0, wq, wk, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def expanded_comparator(m, dims, d, dq, dg, lens, absorbed_ms, absorbed_split_ms, steps: int = 3):
     """The decode workload over a per-head cache (K 192 + V 128 values per head
     and token, the materialised form) instead of the latent rows: the bytes the
@@ -324,6 +414,7 @@ def main():
     ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill-backward leg")
     ap.add_argument("--no-varlen", action="store_true", help="skip the long varlen prefill leg")
+    ap.add_argument("--no-clip-stress", action="store_true", help="skip the QK-Clip stress leg (T=2048)")
     ap.add_argument("--no-expanded", action="store_true",
                     help="skip the expanded-cache decode comparator (needs 129 GB of device memory)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -472,6 +563,8 @@ def main():
                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(split_gbps / PEAK_HBM_GBPS, 4),
                                   "traffic": recorded_traffic("absorbed_split", DECODE_SOURCES),
                                   "algorithmic": f"{cache_bytes / 1e9:.4f} GB of cache rows per launch"}
+    if not args.no_clip_stress:
+        res["clip_stress"] = clip_stress_leg(m, dims)
     if not args.no_layer:
         res["layer"] = layer_leg(m, dims)
     if not args.no_backward:

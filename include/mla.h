@@ -33,8 +33,10 @@
  *    (never normalised, one row per token used by every head); gate logits
  *    [tokens, H*V]; outputs [tokens, H*V] head-major.
  *  - Every pointer argument is a DEVICE pointer, 16-byte aligned, owned by the
- *    caller. The library never allocates device memory and keeps no state
- *    between calls; all work is enqueued asynchronously on `stream`.
+ *    caller (mla_prefill_backward's cu_seqlens_host is the one host pointer).
+ *    The library never allocates device memory. Apart from the opt-in
+ *    per-kernel timing of mla_timing_* (host state), it keeps no state
+ *    between calls. All work is enqueued asynchronously on `stream`.
  *  - Arguments are validated before anything is launched. On error nothing is
  *    launched, the status is returned and mla_last_error() (thread-local)
  *    describes it. No C++ exception crosses this interface.
@@ -74,6 +76,29 @@ typedef struct {
   float scale;         /* score scale; 0 selects (N + S)^-1/2 = 1/sqrt(192)     */
 } mla_dims;
 
+/*
+ * Optional QK-norm variant of the attention calls ("SOTA-131", Variations:
+ * the other route to bounded logits, an RMSNorm on the attention queries and
+ * on the KV entries instead of clipping the weights; Mechanism: normalising
+ * the input of the logit). Passed as `q_norm` to mla_prefill and
+ * mla_absorbed; NULL leaves the query as given. When set, each head's query
+ * is first replaced by
+ *   q_h <- q_h / sqrt(mean over its N+S features of q_h^2 + eps) * weight
+ * (q^C and q^R together), rounded to the input dtype, and the call proceeds
+ * unchanged. The KV entries are the caller's: c^KV already leaves its own
+ * RMSNorm (kv_a_layernorm), and a normalised k^S is produced where k^S is
+ * (mla_rms_norm), as the cache rows are.
+ * The norm bounds every scaled logit of head h by
+ *   max|weight| * sqrt(sigma_h^2 max|c^KV|^2 + max|k^S|^2),
+ * sigma_h the largest singular value of W_UK_h: through the key
+ * up-projection the bound grows with the weights, which QK-Clip rescales.
+ */
+typedef struct {
+  const void* weight;  /* [N+S] per-feature weight, in_dtype, shared by the heads;
+                          NULL = ones                                            */
+  float eps;           /* added to the mean square; finite, >= 0                 */
+} mla_qk_norm;
+
 /* ------------------------------------------------------------------------ */
 /* Training form (materialised K and V)                                      */
 /* ------------------------------------------------------------------------ */
@@ -97,6 +122,7 @@ size_t mla_prefill_workspace_size(const mla_dims* dims, mla_dtype in_dtype,
  * ks        [total_tokens, S]       in_dtype
  * w_kv_b    [H*(N+V), R]            in_dtype
  * gate      [total_tokens, H*V]     in_dtype, or NULL
+ * q_norm    the QK-norm variant (see mla_qk_norm), or NULL
  * cu_seqlens[nseq+1] int32, device, non-decreasing, cu_seqlens[0] = 0 and
  *           cu_seqlens[nseq] = total_tokens (not checked on the device; a
  *           violation gives undefined results). Empty sequences are allowed.
@@ -116,7 +142,7 @@ size_t mla_prefill_workspace_size(const mla_dims* dims, mla_dtype in_dtype,
  */
 mla_status mla_prefill(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype,
                        const void* q, const void* ckv, const void* ks,
-                       const void* w_kv_b, const void* gate,
+                       const void* w_kv_b, const void* gate, const mla_qk_norm* q_norm,
                        const int32_t* cu_seqlens, int32_t nseq, int64_t total_tokens,
                        void* out, float* lse, float* max_logit, int32_t accumulate,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -178,6 +204,7 @@ size_t mla_absorbed_workspace_size(const mla_dims* dims, mla_dtype in_dtype,
  *           device; a violation gives undefined results)
  * w_kv_b    [H*(N+V), R]            in_dtype
  * gate      [batch, tq, H*V]        in_dtype, or NULL
+ * q_norm    the QK-norm variant (see mla_qk_norm), or NULL
  * out       [batch, tq, H*V]        out_dtype
  * max_logit [H] fp32, as for mla_prefill (over every visible (query, row) pair).
  *
@@ -194,8 +221,8 @@ size_t mla_absorbed_workspace_size(const mla_dims* dims, mla_dtype in_dtype,
 mla_status mla_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype,
                         const void* q, const void* cache, int64_t cap,
                         const int32_t* lens, int32_t batch, int32_t tq,
-                        const void* w_kv_b, const void* gate, void* out,
-                        float* max_logit, int32_t accumulate,
+                        const void* w_kv_b, const void* gate, const mla_qk_norm* q_norm,
+                        void* out, float* max_logit, int32_t accumulate,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
@@ -329,7 +356,10 @@ const char* mla_version(void);
  * events and returns the summed milliseconds and launch count of one kernel
  * ("prefill_expand", "prefill_attn", "absorb_q", "absorbed_split",
  * "absorbed_combine", "expanded_split", "qk_clip", ...); it returns 0 if that kernel has not
- * run. Intended for one thread at a time.
+ * run. This is the library's one piece of process-global host state (the
+ * pending events and the per-kernel totals, behind a mutex): it is off by
+ * default, changes no result, and while on, the events it creates are the
+ * only HIP objects the library creates. Intended for one thread at a time.
  */
 void mla_timing_enable(int32_t on);
 int32_t mla_timing_read(const char* kernel, double* total_ms, int64_t* launches);

@@ -9,7 +9,6 @@ Names match the C ABI in ``include/mla.h``. The library must have been built
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 
@@ -40,6 +39,10 @@ class mla_dims(ctypes.Structure):
                 ("nope_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
+class mla_qk_norm(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
 @dataclass(frozen=True)
 class Dims:
     heads: int = 96
@@ -65,11 +68,12 @@ def _load():
     D = ctypes.POINTER(mla_dims)
     lib.mla_prefill_workspace_size.argtypes = [D, I32, I64, I32]
     lib.mla_prefill_workspace_size.restype = SZ
-    lib.mla_prefill.argtypes = [D, I32, I32, P, P, P, P, P, P, I32, I64, P, P, P, I32, P, SZ, P]
+    QN = ctypes.POINTER(mla_qk_norm)
+    lib.mla_prefill.argtypes = [D, I32, I32, P, P, P, P, P, QN, P, I32, I64, P, P, P, I32, P, SZ, P]
     lib.mla_prefill.restype = I32
     lib.mla_absorbed_workspace_size.argtypes = [D, I32, I32, I32]
     lib.mla_absorbed_workspace_size.restype = SZ
-    lib.mla_absorbed.argtypes = [D, I32, I32, P, P, I64, P, I32, I32, P, P, P, P, I32, P, SZ, P]
+    lib.mla_absorbed.argtypes = [D, I32, I32, P, P, I64, P, I32, I32, P, P, QN, P, P, I32, P, SZ, P]
     lib.mla_absorbed.restype = I32
     lib.mla_expanded_workspace_size.argtypes = [D, I32, I32, I32, I64]
     lib.mla_expanded_workspace_size.restype = SZ
@@ -144,6 +148,15 @@ def _expect(name: str, t, shape, dtype, optional: bool = False):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
+def _qk_norm(q_norm, q, dim: int):
+    """(weight [dim] or None, eps) -> a pointer to an mla_qk_norm, or None when the variant is off."""
+    if q_norm is None:
+        return None
+    w, eps = q_norm
+    _expect("q_norm weight", w, (dim,), q.dtype, optional=True)
+    return ctypes.pointer(mla_qk_norm(_ptr(w), float(eps)))
+
+
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
@@ -162,11 +175,12 @@ def mla_absorbed_workspace_size(dims: Dims, in_dtype: int, batch: int, tq: int) 
 
 
 def mla_prefill(dims: Dims, q, ckv, ks, w_kv_b, gate, cu_seqlens, *, out_dtype=None, out=None, lse=None,
-                max_logit=None, accumulate=False, workspace=None, want_lse=False, stream=None):
+                max_logit=None, accumulate=False, workspace=None, want_lse=False, q_norm=None, stream=None):
     """Training-form gated MLA over packed sequences (see ``mla_prefill`` in include/mla.h).
 
     q [T, H, N+S], ckv [T, R], ks [T, S], w_kv_b [H*(N+V), R], gate [T, H*V] or None,
-    cu_seqlens int32 [nseq+1] on the device. Returns (out [T, H*V], lse or None, max_logit [H]).
+    cu_seqlens int32 [nseq+1] on the device; q_norm = (weight [N+S] or None, eps) selects the
+    QK-norm variant. Returns (out [T, H*V], lse or None, max_logit [H]).
     """
     in_dt = _dt(q)
     out_dt = MLA_F32 if out_dtype is None else (MLA_BF16 if out_dtype == torch.bfloat16 else MLA_F32)
@@ -197,18 +211,20 @@ def mla_prefill(dims: Dims, q, ckv, ks, w_kv_b, gate, cu_seqlens, *, out_dtype=N
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = lib.mla_prefill(ctypes.byref(dims.c()), in_dt, out_dt, _ptr(q), _ptr(ckv), _ptr(ks), _ptr(w_kv_b),
-                         _ptr(gate), _ptr(cu_seqlens), nseq, T, _ptr(out), _ptr(lse), _ptr(max_logit),
+                         _ptr(gate), _qk_norm(q_norm, q, dims.qk_dim), _ptr(cu_seqlens), nseq, T, _ptr(out),
+                         _ptr(lse), _ptr(max_logit),
                          1 if accumulate else 0, _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st)
     return out, lse, max_logit
 
 
 def mla_absorbed(dims: Dims, q, cache, lens, w_kv_b, gate, *, out_dtype=None, out=None, max_logit=None,
-                 accumulate=False, workspace=None, stream=None):
+                 accumulate=False, workspace=None, q_norm=None, stream=None):
     """Absorbed-form gated MLA over the latent cache (see ``mla_absorbed`` in include/mla.h).
 
     q [B, Tq, H, N+S], cache [B, cap, R+S], lens int32 [B] on the device, w_kv_b [H*(N+V), R],
-    gate [B, Tq, H*V] or None. Returns (out [B, Tq, H*V], max_logit [H]).
+    gate [B, Tq, H*V] or None; q_norm = (weight [N+S] or None, eps) selects the QK-norm variant.
+    Returns (out [B, Tq, H*V], max_logit [H]).
     """
     in_dt = _dt(q)
     out_dt = in_dt if out_dtype is None else (MLA_BF16 if out_dtype == torch.bfloat16 else MLA_F32)
@@ -236,7 +252,8 @@ def mla_absorbed(dims: Dims, q, cache, lens, w_kv_b, gate, *, out_dtype=None, ou
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = lib.mla_absorbed(ctypes.byref(dims.c()), in_dt, out_dt, _ptr(q), _ptr(cache), cap, _ptr(lens), B, Tq,
-                          _ptr(w_kv_b), _ptr(gate), _ptr(out), _ptr(max_logit), 1 if accumulate else 0,
+                          _ptr(w_kv_b), _ptr(gate), _qk_norm(q_norm, q, dims.qk_dim), _ptr(out), _ptr(max_logit),
+                          1 if accumulate else 0,
                           _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st)
     return out, max_logit
@@ -433,7 +450,3 @@ def mla_timing_read(kernel: str):
     n = ctypes.c_int64(0)
     lib.mla_timing_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(n))
     return ms.value, n.value
-
-
-def default_scale(dims: Dims) -> float:
-    return dims.scale if dims.scale > 0 else 1.0 / math.sqrt(dims.qk_dim)

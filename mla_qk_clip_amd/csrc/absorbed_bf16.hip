@@ -88,9 +88,11 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
                                                        uint16_t* __restrict__ qabs, const int32_t* __restrict__ lens,
                                                        int tq, int64_t* __restrict__ P, int32_t* __restrict__ nflag,
                                                        float* __restrict__ ml_init, float* __restrict__ qn2,
-                                                       float* __restrict__ hmax, uint16_t* __restrict__ qlo) {
+                                                       float* __restrict__ hmax, uint16_t* __restrict__ qlo,
+                                                       int qnorm, const uint16_t* __restrict__ qn_w, float qn_eps) {
   __shared__ __align__(16) uint16_t Wt[kN * kAqLd];
   __shared__ float qsq[2][64];
+  __shared__ float qrs[64];   // QK-norm factor of each virtual sequence of the chunk
   const int h = blockIdx.x, rc = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -129,6 +131,38 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
 #pragma unroll
     for (int kk = 0; kk < kN / 16; ++kk)
       qv[kk] = vv ? ldg16(q + (static_cast<size_t>(v) * heads + h) * kD + 16 * kk + 8 * g) : make_uint4(0, 0, 0, 0);
+    if (qnorm) {
+      // QK-norm variant: divide the head's query by the root mean square of
+      // its D features (this lane half's q^C and q^R units, plus the other
+      // half's sum), multiply by the weight, round to bf16
+      uint4 qr[kS / 16];
+#pragma unroll
+      for (int j = 0; j < kS / 16; ++j)
+        qr[j] = vv ? ldg16(q + (static_cast<size_t>(v) * heads + h) * kD + kN + 16 * j + 8 * g) : make_uint4(0, 0, 0, 0);
+      float ss = 0.0f;
+      auto acc_sq = [&](const uint4& u) {
+        const uint32_t* w4 = &u.x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss = fmaf(bf16hi(w4[i]), bf16hi(w4[i]), fmaf(bf16lo(w4[i]), bf16lo(w4[i]), ss));
+      };
+#pragma unroll
+      for (int kk = 0; kk < kN / 16; ++kk) acc_sq(qv[kk]);
+#pragma unroll
+      for (int j = 0; j < kS / 16; ++j) acc_sq(qr[j]);
+      const float r = vv ? 1.0f / sqrtf((ss + __shfl_xor(ss, 32, 64)) / static_cast<float>(kD) + qn_eps) : 0.0f;
+      auto norm_unit = [&](uint4& u, int f0) {
+        uint32_t* w4 = &u.x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float w0 = qn_w ? bf16_to_f32(qn_w[f0 + 2 * i]) : 1.0f;
+          const float w1 = qn_w ? bf16_to_f32(qn_w[f0 + 2 * i + 1]) : 1.0f;
+          w4[i] = pack_bf16x2(bf16lo(w4[i]) * r * w0, bf16hi(w4[i]) * r * w1);
+        }
+      };
+#pragma unroll
+      for (int kk = 0; kk < kN / 16; ++kk) norm_unit(qv[kk], 16 * kk + 8 * g);
+      if (wave < 2 && g == 0) qrs[32 * vb + l32] = r;   // waves 0 and 1 hold the chunk's 64 rows
+    }
 #pragma unroll
     for (int kk = 0; kk < kN / 16; ++kk) {
       const bf16x8 a = as_bf16x8(qv[kk]);
@@ -155,10 +189,17 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
           qlo[col] = f32_to_bf16(acc[j][e] - bf16_to_f32(hi));
         }
       }
+    if (qnorm) __syncthreads();   // qrs
+    // q^R (normalised and rounded to bf16 under the QK-norm variant)
+    auto qr_value = [&](int row, int s) {
+      const uint16_t x = q[(static_cast<size_t>(v0 + row) * heads + h) * kD + kN + s];
+      if (!qnorm) return x;
+      return f32_to_bf16(bf16_to_f32(x) * qrs[row] * (qn_w ? bf16_to_f32(qn_w[kN + s]) : 1.0f));
+    };
     if (rc == 0) {
       for (int e = tid; e < 64 * kS; e += 256) {
         const int vr = v0 + e / kS, s = e % kS;
-        if (vr < bt) qabs[(static_cast<size_t>(vr) * heads + h) * kW + kR + s] = q[(static_cast<size_t>(vr) * heads + h) * kD + kN + s];
+        if (vr < bt) qabs[(static_cast<size_t>(vr) * heads + h) * kW + kR + s] = qr_value(e / kS, s);
       }
     }
     // squared norm of this block's 128 rounded q_abs entries per virtual
@@ -183,13 +224,10 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
     if (tid < 64 && v0 + tid < bt) {
       float s2 = qsq[0][tid] + qsq[1][tid];
       if (rc == 0) {
-        const uint16_t* qr = q + (static_cast<size_t>(v0 + tid) * heads + h) * kD + kN;
-#pragma unroll
-        for (int u = 0; u < kS / 8; ++u) {
-          const uint4 x = ldg16(qr + 8 * u);
-          const uint32_t* w4 = &x.x;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) s2 = fmaf(bf16lo(w4[i]), bf16lo(w4[i]), fmaf(bf16hi(w4[i]), bf16hi(w4[i]), s2));
+#pragma unroll 8
+        for (int s = 0; s < kS; ++s) {
+          const float x = bf16_to_f32(qr_value(tid, s));
+          s2 = fmaf(x, x, s2);
         }
       }
       qmax2 = fmaxf(qmax2, s2);
@@ -1045,7 +1083,7 @@ __global__ void __launch_bounds__(256) absorbed_refine_kernel(
 hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const void* q, const void* cache,
                                 int64_t cap, const int32_t* lens, int batch, int tq, const void* w_kv_b,
                                 const void* gate, void* out, float* max_logit, bool init_max_logit, void* ws,
-                                hipStream_t st) {
+                                hipStream_t st, const QNorm& qn) {
   const AbsorbedWs L = absorbed_ws_layout(heads, batch, tq);
   char* base = static_cast<char*>(ws);
   float* dlb = reinterpret_cast<float*>(base + L.dlb);
@@ -1066,7 +1104,8 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
     TimedScope ts_("absorb_q", st);
     hipLaunchKernelGGL(absorb_q_kernel, dim3(heads, kR / 128), dim3(256), 0, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(w_kv_b), static_cast<int>(bt), heads, qabs, lens, tq, P, nflag,
-                       init_max_logit ? max_logit : nullptr, qn2, hmax, qlo);
+                       init_max_logit ? max_logit : nullptr, qn2, hmax, qlo, qn.on ? 1 : 0,
+                       static_cast<const uint16_t*>(qn.w), qn.eps);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

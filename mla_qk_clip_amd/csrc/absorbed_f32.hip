@@ -16,7 +16,8 @@ constexpr int kAbsF32MaxS = 256;
 __global__ void __launch_bounds__(256) absorbed_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ cache, int64_t cap, const int32_t* __restrict__ lens,
     int batch, int tq, int heads, int R, int S, int N, int V, const float* __restrict__ w,
-    const float* __restrict__ gate, float scale, float* __restrict__ out, float* __restrict__ max_logit) {
+    const float* __restrict__ gate, float scale, float* __restrict__ out, float* __restrict__ max_logit,
+    int qnorm, const float* __restrict__ qn_w, float qn_eps) {
   const int lane = threadIdx.x & 63;
   const int64_t wid = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   if (wid >= static_cast<int64_t>(batch) * tq * heads) return;
@@ -29,11 +30,20 @@ __global__ void __launch_bounds__(256) absorbed_f32_kernel(
   const float* wk = w + static_cast<int64_t>(h) * NV * R;      // rows of W_UK_h^T
   const float* wv = wk + static_cast<int64_t>(N) * R;           // rows of W_UV_h^T
 
+  // QK-norm variant: the query's features are multiplied by r w_k, with r the
+  // inverse root mean square over the head's D features
+  float r = 1.0f;
+  if (qnorm) {
+    float ss = 0.0f;
+    for (int d = lane; d < D; d += 64) ss = fmaf(qh[d], qh[d], ss);
+    r = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(D) + qn_eps);
+  }
+  auto qval = [&](int k) { return qnorm ? qh[k] * r * (qn_w ? qn_w[k] : 1.0f) : qh[k]; };
   float qa[kAbsF32MaxR / 64];
 #pragma unroll
   for (int j = 0; j < kAbsF32MaxR / 64; ++j) qa[j] = 0.0f;
   for (int k = 0; k < N; ++k) {
-    const float qk = qh[k];
+    const float qk = qval(k);
 #pragma unroll
     for (int j = 0; j < kAbsF32MaxR / 64; ++j) {
       const int r = lane + 64 * j;
@@ -44,7 +54,7 @@ __global__ void __launch_bounds__(256) absorbed_f32_kernel(
 #pragma unroll
   for (int j = 0; j < kAbsF32MaxS / 64; ++j) {
     const int s = lane + 64 * j;
-    qr[j] = s < S ? qh[N + s] : 0.0f;
+    qr[j] = s < S ? qval(N + s) : 0.0f;
   }
 
   const int vis = lens[b] - tq + i + 1;
@@ -99,12 +109,13 @@ __global__ void __launch_bounds__(256) absorbed_f32_kernel(
 hipError_t launch_absorbed_f32(int heads, int R, int S, int N, int V, float scale, const float* q,
                                const float* cache, int64_t cap, const int32_t* lens, int batch, int tq,
                                const float* w_kv_b, const float* gate, float* out, float* max_logit,
-                               hipStream_t st) {
+                               hipStream_t st, const QNorm& qn) {
   const int64_t waves = static_cast<int64_t>(batch) * tq * heads;
   {
     TimedScope ts_("absorbed_f32", st);
     hipLaunchKernelGGL(absorbed_f32_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, st, q,
-                       cache, cap, lens, batch, tq, heads, R, S, N, V, w_kv_b, gate, scale, out, max_logit);
+                       cache, cap, lens, batch, tq, heads, R, S, N, V, w_kv_b, gate, scale, out, max_logit,
+                       qn.on ? 1 : 0, static_cast<const float*>(qn.w), qn.eps);
   }
   return hipGetLastError();
 }

@@ -73,6 +73,74 @@ mla_status check_dims(const mla_dims* d, mla_dtype in, Shape* out) {
     if ((p) && !aligned((p), (align))) return fail(MLA_ERR_INVALID, "%s is not %d-byte aligned", #p, (align)); \
   } while (0)
 
+// The optional QK-norm argument: eps finite and >= 0, the weight (if any) aligned.
+mla_status check_qk_norm(const mla_qk_norm* qn, mla::QNorm* out) {
+  *out = mla::QNorm{};
+  if (!qn) return MLA_OK;
+  if (!(qn->eps >= 0.0f) || !isfinite(qn->eps)) return fail(MLA_ERR_INVALID, "q_norm eps must be finite and >= 0");
+  if (qn->weight && !aligned(qn->weight, 16)) return fail(MLA_ERR_INVALID, "q_norm weight is not 16-byte aligned");
+  out->w = qn->weight;
+  out->eps = qn->eps;
+  out->on = true;
+  return MLA_OK;
+}
+
+// Checks of an absorbed-form call other than its workspace.
+mla_status check_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype, const void* q,
+                          const void* cache, int64_t cap, const int32_t* lens, int32_t batch, int32_t tq,
+                          const void* w_kv_b, const void* gate, const mla_qk_norm* q_norm, void* out,
+                          float* max_logit, int32_t accumulate, Shape* s, mla::QNorm* qn) {
+  mla_status st = check_dims(dims, in_dtype, s);
+  if (st != MLA_OK) return st;
+  st = check_qk_norm(q_norm, qn);
+  if (st != MLA_OK) return st;
+  if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return fail(MLA_ERR_INVALID, "unknown out_dtype");
+  if (in_dtype == MLA_F32 && out_dtype != MLA_F32)
+    return fail(MLA_ERR_UNSUPPORTED, "fp32 inputs produce fp32 outputs only");
+  if (batch < 0 || tq < 1) return fail(MLA_ERR_INVALID, "batch must be >= 0 and tq >= 1");
+  if (cap < tq) return fail(MLA_ERR_INVALID, "cap (%lld) must be >= tq (%d)", static_cast<long long>(cap), tq);
+  if (cap > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "cap above 2^31 - 1");
+  if (accumulate != 0 && accumulate != 1) return fail(MLA_ERR_INVALID, "accumulate must be 0 or 1");
+  if (in_dtype == MLA_BF16 && s->H > mla::kDecMaxHeads)
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 absorbed kernel supports up to %d heads", mla::kDecMaxHeads);
+  if (static_cast<int64_t>(batch) * tq > (int64_t{1} << 24)) return fail(MLA_ERR_UNSUPPORTED, "batch * tq above 2^24");
+  REQUIRE_PTR(max_logit, 4);
+  if (batch > 0) {
+    REQUIRE_PTR(q, 16);
+    REQUIRE_PTR(cache, 16);
+    REQUIRE_PTR(lens, 4);
+    REQUIRE_PTR(w_kv_b, 16);
+    REQUIRE_PTR(out, 16);
+    OPTIONAL_PTR(gate, 16);
+  }
+  return MLA_OK;
+}
+
+mla_status run_absorbed(const Shape& s, mla_dtype in_dtype, mla_dtype out_dtype, const void* q, const void* cache,
+                        int64_t cap, const int32_t* lens, int32_t batch, int32_t tq, const void* w_kv_b,
+                        const void* gate, const mla::QNorm& qn, void* out, float* max_logit, int32_t accumulate,
+                        void* workspace, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  // the bf16 path clears the max-logit slots in its first kernel
+  const bool fused_init = in_dtype == MLA_BF16 && batch > 0;
+  if (!accumulate && !fused_init) {
+    e = mla::launch_fill(max_logit, s.H, -INFINITY, stream);
+    if (e != hipSuccess) return hip_fail(e, "max_logit init");
+  }
+  if (batch == 0) return MLA_OK;
+  if (in_dtype == MLA_BF16) {
+    e = mla::launch_absorbed_bf16(s.H, s.scale, out_dtype == MLA_BF16, q, cache, cap, lens, batch, tq, w_kv_b,
+                                  gate, out, max_logit, !accumulate, workspace, stream, qn);
+  } else {
+    e = mla::launch_absorbed_f32(s.H, s.R, s.S, s.N, s.V, s.scale, static_cast<const float*>(q),
+                                 static_cast<const float*>(cache), cap, lens, batch, tq,
+                                 static_cast<const float*>(w_kv_b), static_cast<const float*>(gate),
+                                 static_cast<float*>(out), max_logit, stream, qn);
+  }
+  if (e != hipSuccess) return hip_fail(e, "mla_absorbed launch");
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,12 +169,15 @@ size_t mla_prefill_workspace_size(const mla_dims* dims, mla_dtype in_dtype, int6
 
 mla_status mla_prefill(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype, const void* q,
                        const void* ckv, const void* ks, const void* w_kv_b, const void* gate,
-                       const int32_t* cu_seqlens, int32_t nseq, int64_t total_tokens, void* out, float* lse,
-                       float* max_logit, int32_t accumulate, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+                       const mla_qk_norm* q_norm, const int32_t* cu_seqlens, int32_t nseq, int64_t total_tokens,
+                       void* out, float* lse, float* max_logit, int32_t accumulate, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
   Shape s;
   mla_status st = check_dims(dims, in_dtype, &s);
+  if (st != MLA_OK) return st;
+  mla::QNorm qn;
+  st = check_qk_norm(q_norm, &qn);
   if (st != MLA_OK) return st;
   if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return fail(MLA_ERR_INVALID, "unknown out_dtype");
   if (in_dtype == MLA_F32 && out_dtype != MLA_F32)
@@ -142,12 +213,13 @@ mla_status mla_prefill(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_d
   if (total_tokens == 0) return MLA_OK;
   if (in_dtype == MLA_BF16) {
     e = mla::launch_prefill_bf16(s.H, s.scale, out_dtype == MLA_BF16, q, ckv, ks, w_kv_b, gate, cu_seqlens, nseq,
-                                 total_tokens, out, lse, max_logit, !accumulate, workspace, stream);
+                                 total_tokens, out, lse, max_logit, !accumulate, workspace, stream, qn);
   } else {
     e = mla::launch_prefill_f32(s.H, s.R, s.S, s.N, s.V, s.scale, static_cast<const float*>(q),
                                 static_cast<const float*>(ckv), static_cast<const float*>(ks),
                                 static_cast<const float*>(w_kv_b), static_cast<const float*>(gate), cu_seqlens,
-                                nseq, total_tokens, static_cast<float*>(out), lse, max_logit, workspace, stream);
+                                nseq, total_tokens, static_cast<float*>(out), lse, max_logit, workspace, stream,
+                                qn);
   }
   if (e != hipSuccess) return hip_fail(e, "mla_prefill launch");
   return MLA_OK;
@@ -162,30 +234,16 @@ size_t mla_absorbed_workspace_size(const mla_dims* dims, mla_dtype in_dtype, int
 
 mla_status mla_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype, const void* q,
                         const void* cache, int64_t cap, const int32_t* lens, int32_t batch, int32_t tq,
-                        const void* w_kv_b, const void* gate, void* out, float* max_logit, int32_t accumulate,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        const void* w_kv_b, const void* gate, const mla_qk_norm* q_norm, void* out,
+                        float* max_logit, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   g_last_error.clear();
   Shape s;
-  mla_status st = check_dims(dims, in_dtype, &s);
+  mla::QNorm qn;
+  mla_status st = check_absorbed(dims, in_dtype, out_dtype, q, cache, cap, lens, batch, tq, w_kv_b, gate, q_norm,
+                                 out, max_logit, accumulate, &s, &qn);
   if (st != MLA_OK) return st;
-  if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return fail(MLA_ERR_INVALID, "unknown out_dtype");
-  if (in_dtype == MLA_F32 && out_dtype != MLA_F32)
-    return fail(MLA_ERR_UNSUPPORTED, "fp32 inputs produce fp32 outputs only");
-  if (batch < 0 || tq < 1) return fail(MLA_ERR_INVALID, "batch must be >= 0 and tq >= 1");
-  if (cap < tq) return fail(MLA_ERR_INVALID, "cap (%lld) must be >= tq (%d)", static_cast<long long>(cap), tq);
-  if (cap > INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "cap above 2^31 - 1");
-  if (accumulate != 0 && accumulate != 1) return fail(MLA_ERR_INVALID, "accumulate must be 0 or 1");
-  if (in_dtype == MLA_BF16 && s.H > mla::kDecMaxHeads)
-    return fail(MLA_ERR_UNSUPPORTED, "bf16 absorbed kernel supports up to %d heads", mla::kDecMaxHeads);
-  if (static_cast<int64_t>(batch) * tq > (int64_t{1} << 24)) return fail(MLA_ERR_UNSUPPORTED, "batch * tq above 2^24");
-  REQUIRE_PTR(max_logit, 4);
   if (batch > 0) {
-    REQUIRE_PTR(q, 16);
-    REQUIRE_PTR(cache, 16);
-    REQUIRE_PTR(lens, 4);
-    REQUIRE_PTR(w_kv_b, 16);
-    REQUIRE_PTR(out, 16);
-    OPTIONAL_PTR(gate, 16);
     const size_t need = mla_absorbed_workspace_size(dims, in_dtype, batch, tq);
     if (need > 0) {
       if (!workspace || workspace_bytes < need)
@@ -194,25 +252,8 @@ mla_status mla_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_
       if (!aligned(workspace, 16)) return fail(MLA_ERR_INVALID, "workspace is not 16-byte aligned");
     }
   }
-  hipError_t e = hipSuccess;
-  // the bf16 path clears the max-logit slots in its first kernel
-  const bool fused_init = in_dtype == MLA_BF16 && batch > 0;
-  if (!accumulate && !fused_init) {
-    e = mla::launch_fill(max_logit, s.H, -INFINITY, stream);
-    if (e != hipSuccess) return hip_fail(e, "max_logit init");
-  }
-  if (batch == 0) return MLA_OK;
-  if (in_dtype == MLA_BF16) {
-    e = mla::launch_absorbed_bf16(s.H, s.scale, out_dtype == MLA_BF16, q, cache, cap, lens, batch, tq, w_kv_b,
-                                  gate, out, max_logit, !accumulate, workspace, stream);
-  } else {
-    e = mla::launch_absorbed_f32(s.H, s.R, s.S, s.N, s.V, s.scale, static_cast<const float*>(q),
-                                 static_cast<const float*>(cache), cap, lens, batch, tq,
-                                 static_cast<const float*>(w_kv_b), static_cast<const float*>(gate),
-                                 static_cast<float*>(out), max_logit, stream);
-  }
-  if (e != hipSuccess) return hip_fail(e, "mla_absorbed launch");
-  return MLA_OK;
+  return run_absorbed(s, in_dtype, out_dtype, q, cache, cap, lens, batch, tq, w_kv_b, gate, qn, out, max_logit,
+                      accumulate, workspace, stream);
 }
 
 size_t mla_expanded_workspace_size(const mla_dims* dims, mla_dtype in_dtype, int32_t batch, int32_t tq,

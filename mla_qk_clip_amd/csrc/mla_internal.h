@@ -168,6 +168,15 @@ struct BackwardWs {
 };
 BackwardWs backward_ws_layout(int heads, int64_t ntok, int max_seqlen);
 
+// QK-norm variant: per-head RMSNorm of the queries over their N + S features,
+// times a per-feature weight shared by the heads (w NULL: ones), the result
+// rounded to the input dtype where it is formed. Off when `on` is false.
+struct QNorm {
+  const void* w = nullptr;
+  float eps = 0.0f;
+  bool on = false;
+};
+
 // ---- launchers (defined next to their kernels) ----
 
 hipError_t launch_fill(float* p, int n, float v, hipStream_t st);
@@ -176,17 +185,19 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16,
                                const void* q, const void* ckv, const void* ks, const void* w_kv_b,
                                const void* gate, const int32_t* cu, int nseq, int64_t ntok,
                                void* out, float* lse, float* max_logit, bool init_max_logit, void* ws,
-                               hipStream_t st);
+                               hipStream_t st, const QNorm& qn = QNorm{});
 
 hipError_t launch_prefill_f32(int heads, int R, int S, int N, int V, float scale,
                               const float* q, const float* ckv, const float* ks, const float* w_kv_b,
                               const float* gate, const int32_t* cu, int nseq, int64_t ntok,
-                              float* out, float* lse, float* max_logit, void* ws, hipStream_t st);
+                              float* out, float* lse, float* max_logit, void* ws, hipStream_t st,
+                              const QNorm& qn = QNorm{});
 
 hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16,
                                 const void* q, const void* cache, int64_t cap, const int32_t* lens,
                                 int batch, int tq, const void* w_kv_b, const void* gate, void* out,
-                                float* max_logit, bool init_max_logit, void* ws, hipStream_t st);
+                                float* max_logit, bool init_max_logit, void* ws, hipStream_t st,
+                                const QNorm& qn = QNorm{});
 
 hipError_t launch_expanded_bf16(int heads, float scale, bool out_bf16, const void* q, const void* kcache,
                                 const void* vcache, int64_t cap, const int32_t* lens, int batch, int tq,
@@ -245,7 +256,7 @@ hipError_t launch_prefill_backward_bf16(int heads, float scale, const void* q, c
 hipError_t launch_absorbed_f32(int heads, int R, int S, int N, int V, float scale,
                                const float* q, const float* cache, int64_t cap, const int32_t* lens,
                                int batch, int tq, const float* w_kv_b, const float* gate, float* out,
-                               float* max_logit, hipStream_t st);
+                               float* max_logit, hipStream_t st, const QNorm& qn = QNorm{});
 
 hipError_t launch_qk_clip(int heads, int S, int N, int V, bool bf16, void* w_q_b, int q_in, int R,
                           void* w_kv_b, const float* max_logit, float tau, uint8_t* clipped,

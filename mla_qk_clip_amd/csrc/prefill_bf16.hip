@@ -317,6 +317,43 @@ __global__ void __launch_bounds__(kExThreads) prefill_expand_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// QK-norm variant ("SOTA-131", Variations and Mechanism): each head's query is
+// divided by the root mean square of its D = 192 features and multiplied by a
+// per-feature weight, then rounded to bf16 (the attention's operand). The
+// attention kernel and the max-logit refinement both form it, with the same
+// arithmetic in the same order, so they use bit-identical queries: the sum of
+// squares is two fp32 fma chains, one per lane half of the attention's query
+// layout (half g holds features 16 kk + 4 g .. +3 and 16 kk + 8 + 4 g .. +3 for
+// kk < 8, then 16 kk + 8 g .. +7 for kk = 8 .. 11), added at the end.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int qslot_feature(int g, int kk, int e) {
+  return kk < kN / 16 ? 16 * kk + 8 * (e >> 2) + 4 * g + (e & 3) : 16 * kk + 8 * g + e;
+}
+__device__ __forceinline__ float qnorm_scale(float sumsq, float eps) {
+  return 1.0f / sqrtf(sumsq / static_cast<float>(kD) + eps);
+}
+__device__ __forceinline__ float qnorm_value(float x, float r, const uint16_t* w, int f) {
+  return bf16_to_f32(f32_to_bf16(x * r * (w ? bf16_to_f32(w[f]) : 1.0f)));
+}
+// Sum of squares of one bf16 query row in the attention kernel's order.
+__device__ __forceinline__ float qnorm_sumsq_row(const uint16_t* qrow) {
+  float half[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < kD / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = bf16_to_f32(qrow[qslot_feature(g, kk, e)]);
+        ss = fmaf(x, x, ss);
+      }
+    half[g] = ss;
+  }
+  return half[0] + half[1];
+}
+
+// ---------------------------------------------------------------------------
 // Attention. One workgroup = one head x 128 queries of one sequence; 4 waves
 // of 32 queries, two workgroups per CU (80 KB of LDS and at most 256 VGPRs
 // each), so that one workgroup's prologue (query and first tile loads) and
@@ -380,7 +417,7 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
     const int32_t* __restrict__ toff, const int32_t* __restrict__ hdr, int nseq, int heads,
     int64_t ntok, int64_t npad_max, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vt,
     float scale, void* __restrict__ out, float* __restrict__ lse, float* __restrict__ rowmax,
-    float* __restrict__ aux) {
+    float* __restrict__ aux, int qnorm, const uint16_t* __restrict__ qn_w, float qn_eps) {
   __shared__ uint4 K0[kKTile];
   __shared__ uint4 K1[kKTile];
   __shared__ uint4 V0[kVTile];
@@ -450,6 +487,27 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int kk = kN / 16; kk < kD / 16; ++kk)
       qf[kk] = as_bf16x8(qvalid ? ldg16(qrow + 16 * kk + 8 * g) : make_uint4(0, 0, 0, 0));
+  }
+  if (qnorm) {
+    // QK-norm: this lane half's fma chain, the other half's added, then
+    // x r w rounded to bf16 (invalid lanes keep zeros)
+    float ss = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < kD / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = static_cast<float>(qf[kk][e]);
+        ss = fmaf(x, x, ss);
+      }
+    const float r = qvalid ? qnorm_scale(ss + __shfl_xor(ss, 32, 64), qn_eps) : 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < kD / 16; ++kk) {
+      bf16x8 v = qf[kk];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = static_cast<__bf16>(qnorm_value(static_cast<float>(qf[kk][e]), r, qn_w, qslot_feature(g, kk, e)));
+      qf[kk] = v;
+    }
   }
 
   // tile-blocked operands of this head and sequence (tile index = padded row / 64)
@@ -826,8 +884,10 @@ constexpr int kRowList = 64;   // rows one rows workgroup lists before its head 
 __global__ void __launch_bounds__(256) prefill_refine_rows_kernel(
     const int32_t* __restrict__ cu, int nseq, int heads, int64_t ntok, const float* __restrict__ rowmax,
     const float* __restrict__ aux, const uint16_t* __restrict__ q, const uint16_t* __restrict__ w, float scale,
-    int32_t* __restrict__ cand, uint16_t* __restrict__ qx, int4* __restrict__ qmeta, float* __restrict__ max_logit) {
+    int32_t* __restrict__ cand, uint16_t* __restrict__ qx, int4* __restrict__ qmeta, float* __restrict__ max_logit,
+    int qnorm, const uint16_t* __restrict__ qn_w, float qn_eps) {
   __shared__ int lst[kRowList], lst_a0[kRowList];
+  __shared__ float lst_r[kRowList];   // QK-norm factor of each listed row
   __shared__ int nl, n_acc, n_base;
   __shared__ float qcs[kRowList][kN];
   __shared__ __align__(16) float part[4][kR];
@@ -881,11 +941,17 @@ __global__ void __launch_bounds__(256) prefill_refine_rows_kernel(
 #pragma unroll
     for (int u = 0; u < 32; ++u) wv[u] = ldg16(wr + static_cast<size_t>(u) * kR);
   }
+  if (tid < acc) {
+    lst_a0[tid] = cu[seq_of(cu, nseq, lst[tid])];
+    lst_r[tid] = qnorm ? qnorm_scale(qnorm_sumsq_row(q + (static_cast<size_t>(lst[tid]) * heads + h) * kD), qn_eps)
+                       : 1.0f;
+  }
+  __syncthreads();
   for (int i = tid; i < acc * kN; i += 256) {
     const int k = i / kN, e = i - k * kN;
-    qcs[k][e] = bf16_to_f32(q[(static_cast<size_t>(lst[k]) * heads + h) * kD + e]);
+    const float x = bf16_to_f32(q[(static_cast<size_t>(lst[k]) * heads + h) * kD + e]);
+    qcs[k][e] = qnorm ? qnorm_value(x, lst_r[k], qn_w, e) : x;
   }
-  if (tid < acc) lst_a0[tid] = cu[seq_of(cu, nseq, lst[tid])];
   __syncthreads();
   const size_t plane = static_cast<size_t>(heads) * kRefRows * (kR + kS);
   for (int k = 0; k < acc; ++k) {
@@ -919,8 +985,9 @@ __global__ void __launch_bounds__(256) prefill_refine_rows_kernel(
       qx[at(col)] = vh;
       qx[plane + at(col)] = f32_to_bf16(v - bf16_to_f32(vh));
     }
-    if (tid < kS) {   // q^R is bf16 already
-      qx[at(kR + tid)] = q[(static_cast<size_t>(t) * heads + h) * kD + kN + tid];
+    if (tid < kS) {   // q^R is bf16 already (normalised: rounded to bf16 as in the attention kernel)
+      const uint16_t xr = q[(static_cast<size_t>(t) * heads + h) * kD + kN + tid];
+      qx[at(kR + tid)] = qnorm ? f32_to_bf16(qnorm_value(bf16_to_f32(xr), lst_r[k], qn_w, kN + tid)) : xr;
       qx[plane + at(kR + tid)] = 0;
     }
     if (tid == 0) qmeta[n] = make_int4(t, lst_a0[k], h, 0);
@@ -1022,8 +1089,10 @@ __global__ void __launch_bounds__(256) prefill_refine_score_kernel(
 hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void* q, const void* ckv,
                                const void* ks, const void* w_kv_b, const void* gate, const int32_t* cu,
                                int nseq, int64_t ntok, void* out, float* lse, float* max_logit,
-                               bool init_max_logit, void* ws, hipStream_t st) {
+                               bool init_max_logit, void* ws, hipStream_t st, const QNorm& qn) {
   const PrefillWs L = prefill_ws_layout(heads, ntok, nseq);
+  const int qnorm = qn.on ? 1 : 0;
+  const uint16_t* qn_w = static_cast<const uint16_t*>(qn.w);
   char* base = static_cast<char*>(ws);
   uint16_t* kc = reinterpret_cast<uint16_t*>(base + L.kc);
   uint16_t* vt = reinterpret_cast<uint16_t*>(base + L.vt);
@@ -1066,7 +1135,7 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
       hipLaunchKernelGGL(prefill_attn_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0, st,
                          static_cast<const uint16_t*>(q), ksp,
                          static_cast<const uint16_t*>(gate), cu, pcu, order, toff, hdr, nseq, heads, ntok,
-                         L.npad_max, kc, vt, scale, out, lse, rowmax, aux);
+                         L.npad_max, kc, vt, scale, out, lse, rowmax, aux, qnorm, qn_w, qn.eps);
     }
   } else {
     {
@@ -1074,7 +1143,7 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
       hipLaunchKernelGGL(prefill_attn_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0, st,
                          static_cast<const uint16_t*>(q), ksp,
                          static_cast<const uint16_t*>(gate), cu, pcu, order, toff, hdr, nseq, heads, ntok,
-                         L.npad_max, kc, vt, scale, out, lse, rowmax, aux);
+                         L.npad_max, kc, vt, scale, out, lse, rowmax, aux, qnorm, qn_w, qn.eps);
     }
   }
   e = hipGetLastError();
@@ -1085,7 +1154,7 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
     TimedScope ts_("prefill_refine_rows", st);
     hipLaunchKernelGGL(prefill_refine_rows_kernel, dim3(heads, kRefRowSplit), dim3(256), 0, st, cu, nseq, heads, ntok,
                        rowmax, aux, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(w_kv_b), scale,
-                       cand, qx, qmeta, max_logit);
+                       cand, qx, qmeta, max_logit, qnorm, qn_w, qn.eps);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

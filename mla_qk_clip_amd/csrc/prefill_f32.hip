@@ -37,7 +37,7 @@ __global__ void __launch_bounds__(256) prefill_attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ ks, const float* __restrict__ gate,
     const int32_t* __restrict__ cu, int nseq, int64_t ntok, int heads, int S, int N, int V,
     const float* __restrict__ kcv, float scale, float* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ max_logit) {
+    float* __restrict__ max_logit, int qnorm, const float* __restrict__ qn_w, float qn_eps) {
   const int lane = threadIdx.x & 63;
   const int64_t wid = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
   if (wid >= ntok * heads) return;
@@ -55,6 +55,19 @@ __global__ void __launch_bounds__(256) prefill_attn_f32_kernel(
   for (int j = 0; j < kF32MaxD / 64; ++j) {
     const int d = lane + 64 * j;
     qv[j] = d < D ? q[(t * heads + h) * D + d] : 0.0f;
+  }
+  if (qnorm) {
+    // QK-norm variant: the head's query over its D features divided by their
+    // root mean square, times the per-feature weight
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kF32MaxD / 64; ++j) ss = fmaf(qv[j], qv[j], ss);
+    const float r = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(D) + qn_eps);
+#pragma unroll
+    for (int j = 0; j < kF32MaxD / 64; ++j) {
+      const int d = lane + 64 * j;
+      if (d < D) qv[j] = qv[j] * r * (qn_w ? qn_w[d] : 1.0f);
+    }
   }
   float o[kF32MaxV / 64];
 #pragma unroll
@@ -100,7 +113,7 @@ __global__ void __launch_bounds__(256) prefill_attn_f32_kernel(
 hipError_t launch_prefill_f32(int heads, int R, int S, int N, int V, float scale, const float* q,
                               const float* ckv, const float* ks, const float* w_kv_b, const float* gate,
                               const int32_t* cu, int nseq, int64_t ntok, float* out, float* lse,
-                              float* max_logit, void* ws, hipStream_t st) {
+                              float* max_logit, void* ws, hipStream_t st, const QNorm& qn) {
   float* kcv = static_cast<float*>(ws);
   const int NV = N + V;
   const int64_t n1 = ntok * heads * NV;
@@ -115,7 +128,8 @@ hipError_t launch_prefill_f32(int heads, int R, int S, int N, int V, float scale
   {
     TimedScope ts_("prefill_attn_f32", st);
     hipLaunchKernelGGL(prefill_attn_f32_kernel, dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, st,
-                       q, ks, gate, cu, nseq, ntok, heads, S, N, V, kcv, scale, out, lse, max_logit);
+                       q, ks, gate, cu, nseq, ntok, heads, S, N, V, kcv, scale, out, lse, max_logit, qn.on ? 1 : 0,
+                       static_cast<const float*>(qn.w), qn.eps);
   }
   return hipGetLastError();
 }

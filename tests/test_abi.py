@@ -37,12 +37,12 @@ def test_version_and_status_strings(m):
 
 
 def _prefill(m, dims, **kw):
-    args = dict(in_dt=m.MLA_BF16, out_dt=m.MLA_F32, q=16, ckv=16, ks=16, w=16, gate=None, cu=16, nseq=1, ntok=10,
-                out=16, lse=None, ml=16, acc=0, ws=16, wsb=1 << 40)
+    args = dict(in_dt=m.MLA_BF16, out_dt=m.MLA_F32, q=16, ckv=16, ks=16, w=16, gate=None, qn=None, cu=16, nseq=1,
+                ntok=10, out=16, lse=None, ml=16, acc=0, ws=16, wsb=1 << 40)
     args.update(kw)
     d = dims.c()
     return m.lib.mla_prefill(ctypes.byref(d), args["in_dt"], args["out_dt"], args["q"], args["ckv"], args["ks"],
-                             args["w"], args["gate"], args["cu"], args["nseq"], args["ntok"], args["out"],
+                             args["w"], args["gate"], args["qn"], args["cu"], args["nseq"], args["ntok"], args["out"],
                              args["lse"], args["ml"], args["acc"], args["ws"], args["wsb"], None)
 
 
@@ -62,8 +62,16 @@ def test_prefill_validation(m):
     assert _prefill(m, m.Dims(96, 256, 64, 128, 128)) == m.MLA_ERR_UNSUPPORTED   # bf16 shape not compiled
     assert _prefill(m, m.Dims(0, 512, 64, 128, 128)) == m.MLA_ERR_INVALID
     assert _prefill(m, m.Dims(4, 2048, 16, 32, 32), in_dt=m.MLA_F32) == m.MLA_ERR_UNSUPPORTED
-    assert m.lib.mla_prefill(None, 1, 0, None, None, None, None, None, None, 1, 1, None, None, None, 0, None, 0,
-                             None) == m.MLA_ERR_INVALID
+    assert m.lib.mla_prefill(None, 1, 0, None, None, None, None, None, None, None, 1, 1, None, None, None, 0, None,
+                             0, None) == m.MLA_ERR_INVALID
+    # the QK-norm argument: eps finite and >= 0, weight aligned
+    qn = lambda w, eps: ctypes.pointer(m.mla_qk_norm(w, eps))  # noqa: E731
+    assert _prefill(m, K3, qn=qn(None, -1.0)) == m.MLA_ERR_INVALID
+    assert b"eps" in m.lib.mla_last_error()
+    assert _prefill(m, K3, qn=qn(None, float("inf"))) == m.MLA_ERR_INVALID
+    assert _prefill(m, K3, qn=qn(8, 1e-6)) == m.MLA_ERR_INVALID
+    assert b"q_norm weight" in m.lib.mla_last_error()
+    assert _prefill(m, K3, qn=qn(16, 1e-6), ws=16, wsb=10) == m.MLA_ERR_WORKSPACE   # a valid norm passes on
 
 
 def test_absorbed_validation(m):
@@ -77,15 +85,16 @@ def test_absorbed_validation(m):
         a = dict(good)
         a.update(kw)
         return f(ctypes.byref(d), m.MLA_BF16, m.MLA_BF16, a["q"], a["cache"], a["cap"], a["lens"], a["B"], a["tq"],
-                 a["w"], a["gate"], a["out"], a["ml"], a["acc"], a["ws"], a["wsb"], None)
+                 a["w"], a["gate"], a.get("qn"), a["out"], a["ml"], a["acc"], a["ws"], a["wsb"], None)
     assert call(tq=0) == m.MLA_ERR_INVALID
     assert call(cap=0) == m.MLA_ERR_INVALID
     assert call(lens=None) == m.MLA_ERR_INVALID
     assert call(wsb=5) == m.MLA_ERR_WORKSPACE
     assert call(gate=8) == m.MLA_ERR_INVALID
     big = m.Dims(200).c()
-    assert f(ctypes.byref(big), m.MLA_BF16, m.MLA_BF16, 16, 16, 100, 16, 1, 1, 16, None, 16, 16, 0, 16, 1 << 40,
-             None) == m.MLA_ERR_UNSUPPORTED
+    assert f(ctypes.byref(big), m.MLA_BF16, m.MLA_BF16, 16, 16, 100, 16, 1, 1, 16, None, None, 16, 16, 0, 16,
+             1 << 40, None) == m.MLA_ERR_UNSUPPORTED
+    assert call(qn=ctypes.pointer(m.mla_qk_norm(None, -0.5))) == m.MLA_ERR_INVALID
 
 
 def test_expanded_validation(m):
