@@ -34,9 +34,10 @@
  *    [tokens, H*V]; outputs [tokens, H*V] head-major.
  *  - Every pointer argument is a DEVICE pointer, 16-byte aligned, owned by the
  *    caller (mla_prefill_backward's cu_seqlens_host is the one host pointer).
- *    The library never allocates device memory. Apart from the opt-in
- *    per-kernel timing of mla_timing_* (host state), it keeps no state
- *    between calls. All work is enqueued asynchronously on `stream`.
+ *    The library never allocates device memory. Apart from two opt-in
+ *    exceptions (the per-kernel timing of mla_timing_*, host state, and the
+ *    static scratch array of mla_absorbed_noalloc, device state), it keeps no
+ *    state between calls. All work is enqueued asynchronously on `stream`.
  *  - Arguments are validated before anything is launched. On error nothing is
  *    launched, the status is returned and mla_last_error() (thread-local)
  *    describes it. No C++ exception crosses this interface.
@@ -80,9 +81,9 @@ typedef struct {
  * Optional QK-norm variant of the attention calls ("SOTA-131", Variations:
  * the other route to bounded logits, an RMSNorm on the attention queries and
  * on the KV entries instead of clipping the weights; Mechanism: normalising
- * the input of the logit). Passed as `q_norm` to mla_prefill and
- * mla_absorbed; NULL leaves the query as given. When set, each head's query
- * is first replaced by
+ * the input of the logit). Passed as `q_norm` to mla_prefill, mla_absorbed and
+ * mla_absorbed_noalloc; NULL leaves the query as given. When set, each head's
+ * query is first replaced by
  *   q_h <- q_h / sqrt(mean over its N+S features of q_h^2 + eps) * weight
  * (q^C and q^R together), rounded to the input dtype, and the call proceeds
  * unchanged. The KV entries are the caller's: c^KV already leaves its own
@@ -224,6 +225,32 @@ mla_status mla_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_
                         const void* w_kv_b, const void* gate, const mla_qk_norm* q_norm,
                         void* out, float* max_logit, int32_t accumulate,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mla_absorbed for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * arguments and the result are those of mla_absorbed without the workspace;
+ * its kernels (the same ones) take their scratch memory from a static device
+ * array of 128 MiB built into the library instead. Each GPU the library runs
+ * on holds its own copy of that array until the process ends. The call makes
+ * no device allocation and no allocating library call.
+ *
+ * Limit: the call succeeds only when mla_absorbed_workspace_size(dims,
+ * in_dtype, batch, tq) <= 128 MiB (for Kimi K3's 96 heads, batch * tq up to
+ * about 170; 64 single-token sequences need about 90 MB); larger sizes return
+ * MLA_ERR_UNSUPPORTED before anything is launched.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (the kernels set up everything they read in each call, so no state
+ * carries over). Calls that overlap on one GPU (on different streams, or from
+ * several host threads without ordering) race on the array and give
+ * undefined results; calls ordered on one stream are safe.
+ */
+mla_status mla_absorbed_noalloc(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype,
+                                const void* q, const void* cache, int64_t cap,
+                                const int32_t* lens, int32_t batch, int32_t tq,
+                                const void* w_kv_b, const void* gate, const mla_qk_norm* q_norm,
+                                void* out, float* max_logit, int32_t accumulate, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Expanded-cache decode (per-head K and V rows; bandwidth comparator)       */

@@ -22,6 +22,7 @@ MLA_F32, MLA_BF16 = 0, 1
 
 EXPORTED = (
     "mla_prefill_workspace_size", "mla_prefill", "mla_absorbed_workspace_size", "mla_absorbed",
+    "mla_absorbed_noalloc",
     "mla_expanded_workspace_size", "mla_expanded", "mla_linear", "mla_rms_norm", "mla_layer_workspace_size",
     "mla_layer_forward", "mla_prefill_backward_workspace_size", "mla_prefill_backward", "mla_qk_clip", "mla_status_string", "mla_last_error", "mla_version", "mla_timing_enable",
     "mla_timing_read",
@@ -75,6 +76,8 @@ def _load():
     lib.mla_absorbed_workspace_size.restype = SZ
     lib.mla_absorbed.argtypes = [D, I32, I32, P, P, I64, P, I32, I32, P, P, QN, P, P, I32, P, SZ, P]
     lib.mla_absorbed.restype = I32
+    lib.mla_absorbed_noalloc.argtypes = [D, I32, I32, P, P, I64, P, I32, I32, P, P, QN, P, P, I32, P]
+    lib.mla_absorbed_noalloc.restype = I32
     lib.mla_expanded_workspace_size.argtypes = [D, I32, I32, I32, I64]
     lib.mla_expanded_workspace_size.restype = SZ
     lib.mla_expanded.argtypes = [D, I32, I32, P, P, P, I64, P, I32, I32, P, P, P, I32, P, SZ, P]
@@ -255,6 +258,36 @@ def mla_absorbed(dims: Dims, q, cache, lens, w_kv_b, gate, *, out_dtype=None, ou
                           _ptr(w_kv_b), _ptr(gate), _qk_norm(q_norm, q, dims.qk_dim), _ptr(out), _ptr(max_logit),
                           1 if accumulate else 0,
                           _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st)
+    return out, max_logit
+
+
+def mla_absorbed_noalloc(dims: Dims, q, cache, lens, w_kv_b, gate, *, out, max_logit, accumulate=False,
+                         q_norm=None, stream=None):
+    """``mla_absorbed`` with the library's built-in scratch memory (see ``mla_absorbed_noalloc`` in
+    include/mla.h): nothing is allocated, so ``out`` and ``max_logit`` must be given.
+
+    q [B, Tq, H, N+S], cache [B, cap, R+S], lens int32 [B] on the device, w_kv_b [H*(N+V), R],
+    gate [B, Tq, H*V] or None, out [B, Tq, H*V] (its dtype selects the output dtype), max_logit [H].
+    """
+    in_dt = _dt(q)
+    out_dt = _dt(out)
+    if q.dim() != 4 or cache.dim() != 3:
+        raise ValueError(f"q must be [B, Tq, H, N+S] and cache [B, cap, R+S], got {tuple(q.shape)}, "
+                         f"{tuple(cache.shape)}")
+    B, Tq = q.shape[0], q.shape[1]
+    cap = cache.shape[1]
+    H, R = dims.heads, dims.kv_rank
+    _expect("q", q, (B, Tq, H, dims.qk_dim), q.dtype)
+    _expect("cache", cache, (B, cap, R + dims.shared_dim), q.dtype)
+    _expect("lens", lens, (B,), torch.int32)
+    _expect("w_kv_b", w_kv_b, (H * (dims.nope_dim + dims.v_dim), R), q.dtype)
+    _expect("gate", gate, (B, Tq, H * dims.v_dim), q.dtype, optional=True)
+    _expect("out", out, (B, Tq, H * dims.v_dim), out.dtype)
+    _expect("max_logit", max_logit, (H,), torch.float32)
+    st = lib.mla_absorbed_noalloc(ctypes.byref(dims.c()), in_dt, out_dt, _ptr(q), _ptr(cache), cap, _ptr(lens), B,
+                                  Tq, _ptr(w_kv_b), _ptr(gate), _qk_norm(q_norm, q, dims.qk_dim), _ptr(out),
+                                  _ptr(max_logit), 1 if accumulate else 0, _stream(stream))
     _check(st)
     return out, max_logit
 

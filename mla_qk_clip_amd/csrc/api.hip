@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "mla.h"
@@ -85,7 +86,8 @@ mla_status check_qk_norm(const mla_qk_norm* qn, mla::QNorm* out) {
   return MLA_OK;
 }
 
-// Checks of an absorbed-form call other than its workspace.
+// Checks of an absorbed-form call other than its workspace (shared by the
+// caller-workspace and the built-in-scratch entry points).
 mla_status check_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype, const void* q,
                           const void* cache, int64_t cap, const int32_t* lens, int32_t batch, int32_t tq,
                           const void* w_kv_b, const void* gate, const mla_qk_norm* q_norm, void* out,
@@ -139,6 +141,33 @@ mla_status run_absorbed(const Shape& s, mla_dtype in_dtype, mla_dtype out_dtype,
   }
   if (e != hipSuccess) return hip_fail(e, "mla_absorbed launch");
   return MLA_OK;
+}
+
+// Scratch memory of mla_absorbed_noalloc: one static device array, which every
+// GPU the library runs on holds (its own copy, at its own address) until the
+// process ends. In host code `scratch` names a host-side stand-in, not device
+// memory: its device address is looked up once per device with
+// hipGetSymbolAddress (that device current) and only that address is used.
+constexpr size_t kScratchBytes = size_t{128} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+hipError_t scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -254,6 +283,31 @@ mla_status mla_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_
   }
   return run_absorbed(s, in_dtype, out_dtype, q, cache, cap, lens, batch, tq, w_kv_b, gate, qn, out, max_logit,
                       accumulate, workspace, stream);
+}
+
+mla_status mla_absorbed_noalloc(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype, const void* q,
+                                const void* cache, int64_t cap, const int32_t* lens, int32_t batch, int32_t tq,
+                                const void* w_kv_b, const void* gate, const mla_qk_norm* q_norm, void* out,
+                                float* max_logit, int32_t accumulate, hipStream_t stream) {
+  g_last_error.clear();
+  Shape s;
+  mla::QNorm qn;
+  mla_status st = check_absorbed(dims, in_dtype, out_dtype, q, cache, cap, lens, batch, tq, w_kv_b, gate, q_norm,
+                                 out, max_logit, accumulate, &s, &qn);
+  if (st != MLA_OK) return st;
+  const size_t need = batch > 0 ? mla_absorbed_workspace_size(dims, in_dtype, batch, tq) : 0;
+  if (need > kScratchBytes)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "mla_absorbed_noalloc: these sizes need %zu bytes of scratch, the built-in scratch holds %zu "
+                "(use mla_absorbed with a caller workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = scratch_of_current_device(&ws);
+    if (e != hipSuccess) return hip_fail(e, "mla_absorbed_noalloc: scratch address");
+  }
+  return run_absorbed(s, in_dtype, out_dtype, q, cache, cap, lens, batch, tq, w_kv_b, gate, qn, out, max_logit,
+                      accumulate, ws, stream);
 }
 
 size_t mla_expanded_workspace_size(const mla_dims* dims, mla_dtype in_dtype, int32_t batch, int32_t tq,

@@ -97,6 +97,31 @@ def test_absorbed_validation(m):
     assert call(qn=ctypes.pointer(m.mla_qk_norm(None, -0.5))) == m.MLA_ERR_INVALID
 
 
+def test_absorbed_noalloc_validation(m):
+    """The no-allocation variant runs the same checks, then refuses sizes whose
+    scratch would not fit its built-in 128 MiB, all before any HIP call."""
+    d = m.Dims().c()
+    f = m.lib.mla_absorbed_noalloc
+    good = dict(q=16, cache=16, cap=100, lens=16, B=2, tq=1, w=16, gate=None, out=16, ml=16, acc=0)
+
+    def call(**kw):
+        a = dict(good)
+        a.update(kw)
+        return f(ctypes.byref(d), m.MLA_BF16, m.MLA_BF16, a["q"], a["cache"], a["cap"], a["lens"], a["B"], a["tq"],
+                 a["w"], a["gate"], None, a["out"], a["ml"], a["acc"], None)
+    assert call(tq=0) == m.MLA_ERR_INVALID
+    assert call(lens=None) == m.MLA_ERR_INVALID
+    assert call(ml=2) == m.MLA_ERR_INVALID
+    assert call(acc=2) == m.MLA_ERR_INVALID
+    limit = 128 << 20
+    K3 = m.Dims()
+    fits = max(b for b in range(1, 400) if m.mla_absorbed_workspace_size(K3, m.MLA_BF16, b, 1) <= limit)
+    assert 160 <= fits <= 180
+    assert call(B=fits + 1) == m.MLA_ERR_UNSUPPORTED
+    assert b"built-in scratch" in m.lib.mla_last_error()
+    assert call(B=fits // 2, tq=3) == m.MLA_ERR_UNSUPPORTED
+
+
 def test_expanded_validation(m):
     K3 = m.Dims()
     d = K3.c()
