@@ -66,12 +66,11 @@ def source_digest(files) -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(kernel: str, files):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    table (profiles/traffic_<kernel>.md: FETCH_SIZE + WRITE_SIZE per dispatch,
-    scaled by the copy-kernel calibration), or None when the table is missing
-    or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.md")
+def recorded(table: str, field: str, files):
+    """One figure of a committed rocprofv3 summary (profiles/<table>.md, lines
+    "- field: `value`"), or None when the table is missing or the kernel
+    sources changed since its counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{table}.md")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -83,9 +82,23 @@ def recorded_traffic(kernel: str, files):
     if rec.get("source_sha256") != source_digest(files):
         return None
     try:
-        return int(float(rec["bytes_per_launch"]))
+        return float(rec[field])
     except (KeyError, ValueError):
         return None
+
+
+def recorded_traffic(kernel: str, files):
+    """HBM bytes per launch of `kernel` (profiles/traffic_<kernel>.md: FETCH_SIZE +
+    WRITE_SIZE per dispatch, scaled by the copy-kernel calibration), or None."""
+    v = recorded(f"traffic_{kernel}", "bytes_per_launch", files)
+    return None if v is None else int(v)
+
+
+def recorded_mfma_busy(kernel: str, files):
+    """Fraction of SIMD cycles the matrix cores were busy during `kernel`
+    (profiles/mfma_<kernel>.md: SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE
+    per XCD x 1024 SIMDs), or None."""
+    return recorded(f"mfma_{kernel}", "mfma_busy", files)
 
 
 PREFILL_SOURCES = ("mla_qk_clip_amd/csrc/prefill_bf16.hip", "mla_qk_clip_amd/csrc/mla_common.h",
@@ -551,6 +564,7 @@ def main():
         "roofline": {"kernel": "prefill_attn", "bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic("prefill_attn", PREFILL_SOURCES),
+                     "mfma_busy": recorded_mfma_busy("prefill_attn", PREFILL_SOURCES),
                      "algorithmic": f"{(qk + pv) / 1e9:.1f} GFLOP per launch (QK^T + PV)"},
     }
     if decode:
@@ -562,6 +576,7 @@ def main():
         res["decode_roofline"] = {"kernel": "absorbed_split", "bound": "hbm", "achieved": round(split_gbps, 1),
                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(split_gbps / PEAK_HBM_GBPS, 4),
                                   "traffic": recorded_traffic("absorbed_split", DECODE_SOURCES),
+                                  "mfma_busy": recorded_mfma_busy("absorbed_split", DECODE_SOURCES),
                                   "algorithmic": f"{cache_bytes / 1e9:.4f} GB of cache rows per launch"}
     if not args.no_clip_stress:
         res["clip_stress"] = clip_stress_leg(m, dims)
