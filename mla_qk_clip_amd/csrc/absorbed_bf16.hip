@@ -243,19 +243,34 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Split kernel. Workgroup = 4 waves; waves 0-2 each own 32 heads (head block
-// 3*blockIdx.y + wave), wave 3 is the loader. The workgroup's rows are visited
-// in tiles of 32 rows, segment (virtual sequence) by segment. The loader
-// streams every tile straight from HBM into a ring of kStages LDS stages
-// (global_load_lds, 16 bytes per lane, no registers), two tiles ahead of the
-// compute; one barrier per tile.
-// LDS tile layout: [32 rows][73 chunks of 8 bf16] (72 data chunks and one pad
-// chunk per row, so rows are 36 banks apart and both read patterns below are
-// free of bank conflicts). A wave-wide copy fills 64 consecutive chunk slots;
-// lanes that land on a pad slot fetch a harmless valid chunk.
-// A compute wave keeps its heads' q_abs as MFMA operands in registers, forms
-// S^T = C Q^T (each lane owns one head column; rows of C read as b128) and
-// accumulates O_lat^T = C^T P^T with C^T read through the LDS transpose read.
+// Split kernel. One workgroup of 8 waves per CU, two waves per SIMD (waves w
+// and w + 4 share a SIMD). The workgroup's rows are visited in tiles of 32
+// rows, segment (virtual sequence) by segment, as a software pipeline with
+// one phase per tile and one barrier per phase:
+//  - S waves 0-2, one per block of 32 heads, keep their heads' q_abs as MFMA
+//    operands in registers. In phase i each forms S^T = C Q^T of tile i (36
+//    MFMAs, each lane owns one head column, rows of C read as b128), the
+//    tile's softmax weights against the segment's reference max, and writes
+//    them to LDS in the MFMA B-operand order.
+//  - PV waves 3-7 hold the latent accumulators O_lat^T = C^T P^T for a share
+//    of the 48 (head block, 32 latent columns) blocks: waves 3 and 7 (which
+//    share SIMD 3) 12 blocks each, waves 4-6 (beside an S wave) 8 each, so
+//    every SIMD issues 48 or 52 MFMAs per tile. In phase i they accumulate
+//    tile i-1 with the weights written in phase i-1, C^T read through the
+//    LDS transpose read.
+//  - The PV waves also stream the tiles into a ring of kStages LDS stages:
+//    in phase i each issues 8 of the 37 wave-wide 1 KB copies of tile i+2
+//    (buffer loads straight into LDS; the buffer ends at the tile's last row,
+//    so reads past it return zeros) and before the barrier waits for its
+//    copies of tile i+1. A stage is refilled two phases after its tile's S
+//    phase, once the PV phase of that tile has ended.
+// LDS tile layout: [32 rows][73 chunks of 8 bf16] (72 data chunks and one
+// pad chunk per row, so rows are 36 banks apart and both read patterns are
+// free of bank conflicts). A wave-wide copy fills 64 consecutive chunk
+// slots. The pad slots of a stage's rows carry the S waves' partial squared
+// row norms of that tile (the error bound of the max-logit refinement): S
+// wave j sums the chunks 2 kk + g with kk = j (mod 3) it reads anyway, so
+// the three partials cover each row once.
 // The softmax takes every probability against a fixed reference, the first
 // tile's max of the segment, so the accumulators are never rescaled; a head
 // whose later logits exceed the reference by more than 64 in exp2 units is
@@ -275,73 +290,203 @@ constexpr int kRowSlots = kChunks + 1;                // 73 slots per LDS row (o
 constexpr int kTileSlots = kDecRows * kRowSlots;      // 2336
 constexpr int kDmaCopies = (kTileSlots + 63) / 64;    // 37 wave-wide 1 KB copies per tile
 constexpr int kTileBytes = kDmaCopies * 1024;         // 37888 bytes per stage
-constexpr int kStages = 3;
+constexpr int kStages = 4;
+constexpr int kSplitThreads = 512;
+// Copies kc of a tile issued by each wave (first, count), weighted against
+// the wave's other work: none for the S waves, 10, 9, 6, 9 and 3 for the PV
+// waves 3-7.
+constexpr int kCopyFirst[8] = {0, 0, 0, 9, 0, 19, 25, 34};
+constexpr int kCopyCount[8] = {0, 0, 0, 10, 9, 6, 9, 3};
+constexpr int kPBytes = 2 * 3 * 2 * 64 * 16;          // weights: 2 buffers x 3 head blocks x 2 halves x 64 lanes
+static_assert(kCopyFirst[4] == 0 && kCopyFirst[3] == kCopyCount[4] && kCopyFirst[5] == kCopyFirst[3] + kCopyCount[3] &&
+                  kCopyFirst[6] == kCopyFirst[5] + kCopyCount[5] && kCopyFirst[7] == kCopyFirst[6] + kCopyCount[6] &&
+                  kCopyFirst[7] + kCopyCount[7] == kDmaCopies,
+              "the waves' copies cover the tile once");
+// Past the tile's slots a stage has room for the S waves' tile maxima (one
+// float per head of the workgroup).
+constexpr int kMaxOff = 16 * kTileSlots;
+static_assert(kMaxOff + 4 * kDecHeadsPerWg <= kTileBytes, "tile maxima in the stage");
+static_assert(kStages * kTileBytes + kPBytes <= 160 * 1024, "LDS of one workgroup");
+static_assert(kDecHeadsPerWg == 96 && kDecRows == 32, "three head blocks of 32, tiles of 32 rows");
 
+// Walk over a workgroup's row range [lo, lo + n), tile by tile and segment
+// (virtual sequence) by segment. Positions are row offsets from lo, 32-bit (a
+// range holds total / G rows); the 64-bit prefix P is turned into offsets
+// with 32-bit compares only. (This compiler has been seen to drop the
+// VCC-to-SCC step of a 64-bit scalar select in this kernel, which made a
+// cursor skip to its segment end; 32-bit scalar compares set SCC directly.)
 struct TileCursor {
-  int64_t vs;       // virtual sequence of the current tile
-  int64_t pos;      // global start row of the current tile
-  int64_t seg_end;  // global end of the current segment (within the workgroup range)
-  int64_t hi;
+  int64_t lo;   // global index of the workgroup's first row
+  int64_t vs;   // virtual sequence of the current tile
+  int pos;      // offset of the current tile
+  int seg_end;  // offset of the end of the current segment (at most n)
+  int n;        // rows of the workgroup
 };
 
+// p - lo, for p > lo, as an offset clamped to n.
+__device__ __forceinline__ int row_offset(int64_t p, int64_t lo, int n) {
+  const uint64_t d = static_cast<uint64_t>(p - lo);
+  uint32_t dh = static_cast<uint32_t>(d >> 32), dl = static_cast<uint32_t>(d);
+  asm volatile("" : "+s"(dh), "+s"(dl));   // keeps the compares below 32-bit
+  return (dh != 0u || dl > static_cast<uint32_t>(n)) ? n : static_cast<int>(dl);
+}
+// p <= lo (both row indices), with a 32-bit compare of the difference's high word.
+__device__ __forceinline__ bool row_le(int64_t p, int64_t lo) {
+  int h = static_cast<int>((lo - p) >> 32);
+  asm volatile("" : "+s"(h));
+  return h >= 0;
+}
+
 __device__ __forceinline__ void cursor_init(TileCursor& c, const int64_t* P, int64_t bt, int64_t lo, int64_t hi) {
-  int64_t vlo = 0, vhi = bt - 1;
+  int vlo = 0, vhi = static_cast<int>(bt) - 1;
   while (vlo < vhi) {
-    const int64_t mid = (vlo + vhi + 1) >> 1;
-    if (P[mid] <= lo) vlo = mid; else vhi = mid - 1;
+    const int mid = (vlo + vhi + 1) >> 1;
+    if (row_le(P[mid], lo)) vlo = mid; else vhi = mid - 1;
   }
-  while (P[vlo + 1] <= lo) ++vlo;
+  while (row_le(P[vlo + 1], lo)) ++vlo;
+  c.lo = lo;
   c.vs = vlo;
-  c.pos = lo;
-  c.hi = hi;
-  c.seg_end = min(hi, P[vlo + 1]);
+  c.pos = 0;
+  c.n = static_cast<int>(hi - lo);
+  c.seg_end = row_offset(P[vlo + 1], lo, c.n);
 }
 __device__ __forceinline__ void cursor_next(TileCursor& c, const int64_t* P) {
   c.pos = min(c.pos + kDecRows, c.seg_end);
-  if (c.pos >= c.seg_end && c.pos < c.hi) {
-    while (P[c.vs + 1] <= c.pos) ++c.vs;
-    c.seg_end = min(c.hi, P[c.vs + 1]);
+  if (c.pos >= c.seg_end && c.pos < c.n) {
+    while (row_offset(P[c.vs + 1], c.lo, c.n) <= c.pos) ++c.vs;
+    c.seg_end = row_offset(P[c.vs + 1], c.lo, c.n);
   }
 }
+__device__ __forceinline__ int cursor_rows(const TileCursor& c) { return min(kDecRows, c.seg_end - c.pos); }
+// First row of the current tile within its virtual sequence.
+__device__ __forceinline__ int64_t cursor_row0(const TileCursor& c, const int64_t* P) {
+  return c.lo + c.pos - P[c.vs];
+}
 
-// vmcnt-only wait (expcnt and lgkmcnt left at their maxima), gfx9 encoding
+// Barrier without the fence __syncthreads carries (which would also wait for
+// copies that are not needed yet); each wave waits for exactly what the
+// others need first. The compiler keeps memory accesses on their side of it.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
+// The ring's stages and the softmax-weight buffers are LDS arrays of their own.
+__shared__ __align__(16) char g_split_st0[kTileBytes];
+__shared__ __align__(16) char g_split_st1[kTileBytes];
+__shared__ __align__(16) char g_split_st2[kTileBytes];
+__shared__ __align__(16) char g_split_st3[kTileBytes];
+__shared__ __align__(16) uint4 g_split_p[kPBytes / 16];
+template <int S>
+__device__ __forceinline__ char* split_stage() {
+  static_assert(S >= 0 && S < kStages, "stage");
+  if constexpr (S == 0) return g_split_st0;
+  else if constexpr (S == 1) return g_split_st1;
+  else if constexpr (S == 2) return g_split_st2;
+  else return g_split_st3;
+}
+__device__ __forceinline__ char* split_stage(int s) {
+  return s == 0 ? g_split_st0 : s == 1 ? g_split_st1 : s == 2 ? g_split_st2 : g_split_st3;
+}
+
+// Buffer resource of the rows of one tile (4 dwords; reads past the last
+// row return zeros).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 rows_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+// 16 bytes per lane from the buffer at byte offset voff straight into LDS at
+// lds + 16 lane (lds: an LDS address, the same for the whole wave). Written
+// in asm: the compiler, which cannot tell the ring's stages apart behind a
+// copy in flight, would otherwise wait for every copy before each LDS read;
+// the callers order the copies against the reads with their own waits and
+// barriers. M0 holds no compiler value in the code that issues them; the
+// s_nop is the wait state an LDS-DMA load needs after a scalar write of M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is declared clobbered on purpose
+__device__ __forceinline__ void dma16_rows(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+
+// Issue this wave's copies of a tile (W: wave index): copy kc fills chunk
+// slots 64 kc .. +63 of the stage (lane i: slot 64 kc + i = row r, chunk k of
+// the tile).
+template <int W>
+__device__ __forceinline__ void split_copy(u32x4 rs, char* stage, int lane) {
+  const uint32_t base = lds_addr(stage);
+#pragma unroll
+  for (int c = 0; c < kCopyCount[W]; ++c) {
+    const int kc = kCopyFirst[W] + c;
+    const int slot = 64 * kc + lane;
+    const int r = slot / kRowSlots, k = slot - r * kRowSlots;
+    dma16_rows(rs, static_cast<uint32_t>(r * (kW * 2) + 16 * k), base + 1024 * kc);
+  }
+}
+__device__ __forceinline__ u32x4 tile_rsrc(const uint16_t* cache, int64_t cap, int tq, const int64_t* P,
+                                          const TileCursor& c) {
+  const int64_t b = c.vs / tq;
+  const int64_t row0 = cursor_row0(c, P);
+  return rows_rsrc(cache + (b * cap + row0) * kW, static_cast<uint32_t>(cursor_rows(c) * (kW * 2)));
+}
+
+// ---- S waves ----
 struct SplitState {
   bf16x8 qf[kW / 16];
-  f32x16 oacc[kR / 32];
   float m_ref, m_true, l_part;
   bool overflow, first;
 };
 
-// Scores, softmax weights and the latent accumulation for one tile in `tile`.
-// Returns the tile's approximate max logit of the lane's head.
-__device__ __forceinline__ float split_compute(const uint16_t* tile, int nrows, int lane, float c2, SplitState& S) {
-  const int g = lane >> 5, l32 = lane & 31;
-  const int i16 = lane & 15;
-  const int mhalf = 16 * ((lane >> 4) & 1);
-  const char* tb = reinterpret_cast<const char*>(tile);
-  const lds_u16* tl = (const lds_u16*)(tile);
-  // S^T = C Q^T with the LDS operand reads issued kPf k-steps ahead of their MFMA
+// Scores and softmax weights (pk: the B operands of the value product) for
+// the tile at tb, and this wave's partial squared norm of the lane's row (the
+// chunks 2 kk + g with kk = HB (mod 3), which it reads anyway; the three S
+// waves' partials cover each row once). Returns the tile's approximate max
+// logit of the lane's head.
+template <int HB>
+__device__ __forceinline__ float split_scores(const char* tb, int nrows, int lane, float c2, SplitState& S,
+                                              uint32_t (&pk)[8], float& nsq) {
+  const int g = lane >> 5;
   constexpr int kPf = 6;
-  const uint4* arow = reinterpret_cast<const uint4*>(tb + 16 * (l32 * kRowSlots + g));
+  const uint4* arow = reinterpret_cast<const uint4*>(tb + 16 * ((lane & 31) * kRowSlots + g));
   uint4 af[kPf];
 #pragma unroll
   for (int kk = 0; kk < kPf; ++kk) af[kk] = arow[2 * kk];
-  f32x16 sacc = f32x16{};
+  // two accumulator chains (even and odd k-steps), added at the end
+  f32x16 sacc = f32x16{}, sodd = f32x16{};
+  float n = 0.0f;
 #pragma unroll
   for (int kk = 0; kk < kW / 16; ++kk) {
-    const bf16x8 a = as_bf16x8(af[kk % kPf]);
+    const uint4 u = af[kk % kPf];
     if (kk + kPf < kW / 16) af[kk % kPf] = arow[2 * (kk + kPf)];
-    sacc = mfma32(a, S.qf[kk], sacc);
+    if (kk & 1) sodd = mfma32(as_bf16x8(u), S.qf[kk], sodd);
+    else sacc = mfma32(as_bf16x8(u), S.qf[kk], sacc);
+    if (kk % 3 == HB) {
+      const bf16x8 v = as_bf16x8(u);
+      n = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), __builtin_shufflevector(v, v, 0, 1), n, false);
+      n = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), __builtin_shufflevector(v, v, 2, 3), n, false);
+      n = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), __builtin_shufflevector(v, v, 4, 5), n, false);
+      n = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), __builtin_shufflevector(v, v, 6, 7), n, false);
+      asm volatile("" : "+v"(n));   // here, not sunk to the end of the loop (the chunk's registers are then free)
+    }
   }
+  nsq = n;
   // keep the reads kPf MFMAs ahead (the scheduler would otherwise sink them
   // next to their uses and expose the LDS latency on every MFMA)
   __builtin_amdgcn_sched_group_barrier(0x100, kPf, 0);
 #pragma unroll
   for (int kk = 0; kk < kW / 16; ++kk) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (kk + kPf < kW / 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
+  sacc += sodd;
   if (nrows < kDecRows) {
 #pragma unroll
     for (int e = 0; e < 16; ++e)
@@ -349,13 +494,12 @@ __device__ __forceinline__ float split_compute(const uint16_t* tile, int nrows, 
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  for (int e = 0; e < 16; e += 2) mx = fmax3_(mx, sacc[e], sacc[e + 1]);
+  mx = xor32_max(mx);
   if (S.first) S.m_ref = mx;
   S.m_true = fmaxf(S.m_true, mx);
   S.overflow = S.overflow || (mx - S.m_ref) * c2 > 64.0f;
   const float moff = -S.m_ref * c2;
-  uint32_t pk[8];
   float psum = 0.0f;
 #pragma unroll
   for (int e = 0; e < 16; e += 2) {
@@ -365,160 +509,44 @@ __device__ __forceinline__ float split_compute(const uint16_t* tile, int nrows, 
     pk[e >> 1] = pack_bf16x2(p0, p1);
   }
   S.l_part += psum;
-  // O_lat^T += C^T P^T: 32 MFMAs (2 row halves x 16 latent blocks); the two
-  // transpose reads of each operand are issued kPv MFMAs ahead
-  constexpr int kPv = 4;
-  const bf16x8 bp0 = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-  const bf16x8 bp1 = as_bf16x8(make_uint4(pk[4], pk[5], pk[6], pk[7]));
-  const lds_u16* rowp = tl + (4 * g + (i16 >> 2)) * (8 * kRowSlots) + mhalf + 4 * (i16 & 3);
-  auto pv_ptr = [&](int m) { return rowp + (m >> 4) * 16 * (8 * kRowSlots) + 32 * (m & 15); };
-  v4s t0[kPv], t1[kPv];
-#pragma unroll
-  for (int m = 0; m < kPv; ++m) {
-    t0[m] = lds_tr4(pv_ptr(m));
-    t1[m] = lds_tr4(pv_ptr(m) + 8 * (8 * kRowSlots));
-  }
-#pragma unroll
-  for (int m = 0; m < 2 * (kR / 32); ++m) {
-    const bf16x8 a = cat_bf16(t0[m % kPv], t1[m % kPv]);
-    if (m + kPv < 2 * (kR / 32)) {
-      t0[m % kPv] = lds_tr4(pv_ptr(m + kPv));
-      t1[m % kPv] = lds_tr4(pv_ptr(m + kPv) + 8 * (8 * kRowSlots));
-    }
-    S.oacc[m & 15] = mfma32(a, (m >> 4) ? bp1 : bp0, S.oacc[m & 15]);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPv, 1);
-#pragma unroll
-  for (int m = 0; m < 2 * (kR / 32); ++m) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-  }
+  S.first = false;
   return mx;
 }
 
-// Wave 3 streams every tile of the workgroup into a ring of kStages LDS stages
-// with direct global->LDS copies (37 wave-wide 1 KB copies per tile), two
-// tiles ahead of the compute waves. It issues no other vector memory
-// operations (so its vmcnt waits count copies only), its LDS reads of the
-// ring are written in asm, and the compute waves never copy, so neither code
-// path has to wait on the other's memory ops except through the explicit
-// vmcnt wait and the barrier.
-struct TileRec {
-  int vs, row0, nrows;   // virtual sequence, first row within it, rows
-};
-
-__device__ __forceinline__ TileRec split_issue(uint16_t* ring, int stage, TileCursor& lc, const int64_t* P,
-                                               const uint16_t* cache, int64_t cap, int tq, int lane) {
-  const int b = static_cast<int>(lc.vs / tq);
-  const int64_t row0 = lc.pos - P[lc.vs];
-  const int64_t left = lc.seg_end - lc.pos;
-  const int nrows = left < kDecRows ? static_cast<int>(left) : kDecRows;
-  const TileRec rec{static_cast<int>(lc.vs), static_cast<int>(row0), nrows};
-  const uint16_t* src = cache + (static_cast<size_t>(b) * cap + row0) * kW;
-  char* dst = reinterpret_cast<char*>(ring) + stage * kTileBytes;
-#pragma unroll
-  for (int kc = 0; kc < kDmaCopies; ++kc) {
-    const int slot = 64 * kc + lane;
-    int r = slot / kRowSlots;
-    int c = slot - r * kRowSlots;
-    // pad slots, slots past the tile and rows past the segment fetch a valid
-    // chunk of the tile's first row (finite; never used or masked)
-    if (r >= nrows || c >= kChunks) {
-      r = 0;
-      c = 0;
-    }
-    __builtin_amdgcn_global_load_lds(src + r * kW + 8 * c,
-                                     (__attribute__((address_space(3))) void*)(dst + 1024 * kc), 16, 0, 0);
-  }
-  cursor_next(lc, P);
-  return rec;
+// Maximum over the 32 lanes of each half of the wave (quad swaps, the 8- and
+// 16-lane mirrors, then one exchange of 16-lane rows; no LDS traffic).
+__device__ __forceinline__ float half_max32(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Nine 16-byte LDS reads at addr + 16 k, k < 9, with their wait in the same
-// asm block. Written this way because the compiler orders every LDS read of
-// the ring behind all of the wave's outstanding global->LDS copies; these
-// reads touch a stage whose copies have completed.
-__device__ __forceinline__ void lds_read9(uint32_t addr, u32x4 (&x)[9]) {
-  asm volatile(
-      "ds_read_b128 %0, %9\n"
-      "ds_read_b128 %1, %9 offset:16\n"
-      "ds_read_b128 %2, %9 offset:32\n"
-      "ds_read_b128 %3, %9 offset:48\n"
-      "ds_read_b128 %4, %9 offset:64\n"
-      "ds_read_b128 %5, %9 offset:80\n"
-      "ds_read_b128 %6, %9 offset:96\n"
-      "ds_read_b128 %7, %9 offset:112\n"
-      "ds_read_b128 %8, %9 offset:128\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]),
-        "=&v"(x[7]), "=&v"(x[8])
-      : "v"(addr)
-      : "memory");
-}
-
-// Largest row norm among the first nrows rows of an LDS tile. Lane l sums
-// the squares of half of row l % 32 (36 of its 72 chunks); the halves are
-// added, then the maximum is taken over the rows.
-__device__ __forceinline__ float tile_max_row_norm(const uint16_t* tile, int nrows, int lane) {
-  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u16*)tile)) +
-                        16 * ((lane & 31) * kRowSlots + (kChunks / 2) * (lane >> 5));
-  float s = 0.0f;
-#pragma unroll
-  for (int blk = 0; blk < kChunks / 2 / 9; ++blk) {
-    u32x4 x[9];
-    lds_read9(base + 16 * 9 * blk, x);
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      // (bit-casting single elements of a vector would read element 0 with this compiler)
-      const bf16x8 v = __builtin_bit_cast(bf16x8, x[k]);
-      const bf16x2 v0 = __builtin_shufflevector(v, v, 0, 1), v1 = __builtin_shufflevector(v, v, 2, 3);
-      const bf16x2 v2 = __builtin_shufflevector(v, v, 4, 5), v3 = __builtin_shufflevector(v, v, 6, 7);
-      s = __builtin_amdgcn_fdot2_f32_bf16(v0, v0, s, false);
-      s = __builtin_amdgcn_fdot2_f32_bf16(v1, v1, s, false);
-      s = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, s, false);
-      s = __builtin_amdgcn_fdot2_f32_bf16(v3, v3, s, false);
-    }
-  }
-  s += __shfl_xor(s, 32, 64);
-  if ((lane & 31) >= nrows) s = 0.0f;
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) s = fmaxf(s, __shfl_xor(s, o, 64));
-  return sqrtf(s);
-}
-
-// Workgroup barrier for the loader wave: the caller has already waited for
-// exactly the copies the other waves need. (__syncthreads would also wait for
-// the copies of the tile two ahead, which are not needed yet.) The compiler
-// keeps memory accesses on their side of the asm statements.
-__device__ __forceinline__ void loader_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Candidate list of one head in one split workgroup, kept by the lane that
-// owns the head. lb is a lower bound of the head's exact max logit (the
-// largest tile max minus its error bound so far); a tile can hold the exact
-// maximum only if its max plus its error bound reaches lb, so entries below
-// the current lb are dropped whenever the list fills up. cnt == kDecList + 1
-// marks a list that overflowed with live entries.
-struct CandEntry {
-  int vsn;    // virtual sequence | rows << 24
-  int row0;   // first row within the sequence
-  float u;    // upper bound of the tile's exact max logit (raw)
-};
-__device__ __forceinline__ void cand_compact(CandEntry* list, int& cnt, float lb) {
+// Candidate list of one head in one split workgroup: the slots dent[o][.] of
+// the workgroup, kept by the lane that owns the head (count and bound in its
+// registers). lb is a lower bound of the head's exact max logit (the largest
+// tile max minus its error bound so far); a tile can hold the exact maximum
+// only if its max plus its error bound reaches lb, so entries below the
+// current lb are dropped whenever the list fills up. cnt == kDecList + 1
+// marks a list that overflowed with live entries. Entries: {virtual
+// sequence, first row, rows, bits of the upper bound}.
+__device__ __forceinline__ void cand_compact(int4* list, int& cnt, float lb) {
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): the lane's earlier stores to the list are done
   int j = 0;
   for (int k = 0; k < cnt; ++k) {
-    const CandEntry e = list[k];
-    if (e.u >= lb) list[j++] = e;
+    int4 e;
+    e.x = __hip_atomic_load(&list[k].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    e.y = __hip_atomic_load(&list[k].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    e.z = __hip_atomic_load(&list[k].z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    e.w = __hip_atomic_load(&list[k].w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__int_as_float(e.w) >= lb) list[j++] = e;
   }
   cnt = j;
 }
-__device__ __forceinline__ void cand_record(CandEntry* list, int& cnt, float& lb, float mx, float d, int vsn,
-                                            int row0) {
+__device__ __forceinline__ void cand_record(int4* list, int& cnt, float& lb, float mx, float d, int vs, int row0,
+                                            int nrows) {
   lb = fmaxf(lb, mx - d);
   const float u = mx + d;
   if (cnt > kDecList || u < lb) return;
@@ -529,164 +557,295 @@ __device__ __forceinline__ void cand_record(CandEntry* list, int& cnt, float& lb
       return;
     }
   }
-  list[cnt++] = CandEntry{vsn, row0, u};
+  list[cnt++] = make_int4(vs, row0, nrows, __float_as_int(u));
 }
 
-__global__ void __launch_bounds__(256) absorbed_split_kernel(
+template <int HB>
+__device__ __forceinline__ void split_s_wave(int ntiles, int lane, int64_t lo, int64_t hi, int heads, int64_t bt,
+                                             const int64_t* P, const uint16_t* cache, int64_t cap, int tq,
+                                             const uint16_t* qabs, float c2, float* part_ml, int32_t* nflag) {
+  const int g = lane >> 5, l32 = lane & 31;
+  const int head = 32 * (3 * static_cast<int>(blockIdx.y) + HB) + l32;
+  const bool hvalid = head < heads;
+  const int hq = hvalid ? head : 0;
+  static_assert(kCopyCount[HB] == 0, "the S waves issue no copies");
+  TileCursor cur;   // the tile being scored
+  cursor_init(cur, P, bt, lo, hi);
+  phase_barrier();   // tile 0 has landed
+  SplitState S;
+  bool seg_new = true;
+  for (int i = 0; i <= ntiles; ++i) {
+    if (i < ntiles) {
+      const int64_t vs = cur.vs;
+      if (seg_new) {
+        const uint16_t* qrow = qabs + (static_cast<size_t>(vs) * heads + hq) * kW + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < kW / 16; ++kk)
+          S.qf[kk] = as_bf16x8(hvalid ? ldg16(qrow + 16 * kk) : make_uint4(0, 0, 0, 0));
+        // Fixed reference max per segment (the first tile's): probabilities
+        // relative to it may exceed 1 but stay far inside the bf16 / fp32
+        // range unless a later logit exceeds it by more than 64 / c2 (p >
+        // 2^64; flagged, and such segments are recomputed by the fix-up
+        // kernel).
+        S.m_ref = 0.0f;
+        S.m_true = -INFINITY;
+        S.l_part = 0.0f;
+        S.overflow = false;
+        S.first = true;
+        seg_new = false;
+      }
+      char* tb = split_stage(i % kStages);
+      uint32_t pk[8];
+      float nsq;
+      const float mx = split_scores<HB>(tb, cursor_rows(cur), lane, c2, S, pk, nsq);
+      // weights in the value product's B-operand order; for the candidate
+      // record made in the next phase, the norm partial of row l32 in its
+      // pad slot (float HB) and the tile max of each head past the tile
+      uint4* pw = g_split_p + ((i & 1) * 3 + HB) * 128;
+      pw[lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      pw[64 + lane] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+      nsq = xor32_sum(nsq);
+      if (g == 0) {
+        *reinterpret_cast<float*>(tb + 16 * (l32 * kRowSlots + kChunks) + 4 * HB) = nsq;
+        *reinterpret_cast<float*>(tb + kMaxOff + 4 * (32 * HB + l32)) = mx;
+      }
+      cursor_next(cur, P);
+      if (cur.pos >= cur.seg_end || cur.vs != vs) {
+        // the segment ends with this tile: its softmax statistics
+        if (hvalid) {
+          const size_t slot = static_cast<size_t>(blockIdx.x) + static_cast<size_t>(vs);
+          const float l_tot = xor32_sum(S.l_part);
+          if (g == 0)
+            *reinterpret_cast<float4*>(part_ml + (slot * heads + head) * 4) =
+                make_float4(S.m_ref, l_tot, S.m_true, S.overflow ? 1.0f : 0.0f);
+        }
+        if (__ballot(hvalid && S.overflow) && lane == 0) atomicAdd(nflag, 1);
+        seg_new = true;
+      }
+    }
+    wait_lgkm0();
+    phase_barrier();
+  }
+}
+
+// ---- PV waves ----
+// Blocks B0 .. B0+NB-1 of the 48 (block b: head block b / 16, latent columns
+// 32 (b % 16) .. +31), at most two head blocks.
+template <int B0, int NB>
+__device__ __forceinline__ void split_pv(const char* tb, const uint4* pb, int lane, f32x16 (&o)[12]) {
+  constexpr int H0 = B0 / 16;
+  constexpr int N0 = (NB < 16 - B0 % 16) ? NB : 16 - B0 % 16;   // blocks in head block H0
+  const int i16 = lane & 15;
+  const int mhalf = 16 * ((lane >> 4) & 1);
+  const int g = lane >> 5;
+  bf16x8 p0[2], p1[2];
+  p0[0] = as_bf16x8(pb[H0 * 128 + lane]);
+  p0[1] = as_bf16x8(pb[H0 * 128 + 64 + lane]);
+  if constexpr (N0 < NB) {
+    p1[0] = as_bf16x8(pb[(H0 + 1) * 128 + lane]);
+    p1[1] = as_bf16x8(pb[(H0 + 1) * 128 + 64 + lane]);
+  }
+  const lds_u16* tl = (const lds_u16*)(tb);
+  const lds_u16* rowp = tl + (4 * g + (i16 >> 2)) * (8 * kRowSlots) + mhalf + 4 * (i16 & 3);
+  // MFMA m = NB ks + j: k-step ks (rows 16 ks .. +15) of block j
+  auto ptr = [&](int m) {
+    const int ks = m / NB, cb = (B0 + m % NB) % 16;
+    return rowp + ks * 16 * (8 * kRowSlots) + 32 * cb;
+  };
+  constexpr int kPv = NB > 8 ? 3 : 4;   // operand reads in flight (registers are tight at 12 blocks)
+  v4s t0[kPv], t1[kPv];
+#pragma unroll
+  for (int m = 0; m < kPv; ++m) {
+    t0[m] = lds_tr4(ptr(m));
+    t1[m] = lds_tr4(ptr(m) + 8 * (8 * kRowSlots));
+  }
+#pragma unroll
+  for (int m = 0; m < 2 * NB; ++m) {
+    const bf16x8 a = cat_bf16(t0[m % kPv], t1[m % kPv]);
+    if (m + kPv < 2 * NB) {
+      t0[m % kPv] = lds_tr4(ptr(m + kPv));
+      t1[m % kPv] = lds_tr4(ptr(m + kPv) + 8 * (8 * kRowSlots));
+    }
+    const int ks = m / NB, j = m % NB;
+    o[j] = mfma32(a, j < N0 ? (ks ? p0[1] : p0[0]) : (ks ? p1[1] : p1[0]), o[j]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPv, 0);
+#pragma unroll
+  for (int m = 0; m < 2 * NB; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+}
+
+// PV wave with blocks B0 .. B0+NB-1 of the value product. The wave with CAND
+// also keeps the max-logit candidate lists of the workgroup's 96 heads (lane
+// l < 32 owns head l of each head block): for the tile accumulated in a
+// phase, the tile's largest row norm (from the S waves' partials in the
+// stage's pad slots) and the tile max of each head (past the tile's slots)
+// give the tile's error bound and its entry.
+template <int W, int B0, int NB, bool CAND>
+__device__ __forceinline__ void split_pv_wave(int ntiles, int lane, int64_t lo, int64_t hi, int heads, int64_t bt,
+                                              const int64_t* P, const uint16_t* cache, int64_t cap, int tq,
+                                              float* part_o, const float* qn2, float* dlb, int32_t* dcnt,
+                                              int4* dent) {
+  constexpr int NC = kCopyCount[W];
+  const int g = lane >> 5, l32 = lane & 31;
+  float qerr[3], clb[3];
+  int ccnt[3];
+  int4* clst[3];
+  bool cvalid[3];
+  size_t co[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int chead = 32 * (3 * static_cast<int>(blockIdx.y) + k) + l32;
+    cvalid[k] = CAND && chead < heads;
+    const int cq = cvalid[k] ? chead : 0;
+    qerr[k] = CAND ? kDecErrCoef * sqrtf((qn2[4 * cq] + qn2[4 * cq + 1]) + (qn2[4 * cq + 2] + qn2[4 * cq + 3]))
+                   : 0.0f;
+    co[k] = static_cast<size_t>(blockIdx.x) * heads + cq;
+    clst[k] = dent + co[k] * kDecList;
+    clb[k] = -INFINITY;
+    ccnt[k] = 0;
+  }
+  TileCursor pc, lc;   // the tile being accumulated, the tile being loaded
+  cursor_init(pc, P, bt, lo, hi);
+  cursor_init(lc, P, bt, lo, hi);
+  if constexpr (NC > 0) {
+    // this wave's copies of tiles 0 and 1
+    split_copy<W>(tile_rsrc(cache, cap, tq, P, lc), split_stage(0), lane);
+    cursor_next(lc, P);
+    if (ntiles > 1) {
+      split_copy<W>(tile_rsrc(cache, cap, tq, P, lc), split_stage(1), lane);
+      cursor_next(lc, P);
+      wait_vmcnt<NC>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  }
+  phase_barrier();   // tile 0 has landed
+  f32x16 o[12];
+#pragma unroll
+  for (int j = 0; j < 12; ++j) o[j] = f32x16{};
+  for (int i = 0; i <= ntiles; ++i) {
+    const bool load = NC > 0 && i + 2 < ntiles;
+    if (load) {
+      split_copy<W>(tile_rsrc(cache, cap, tq, P, lc), split_stage((i + 2) % kStages), lane);
+      cursor_next(lc, P);
+    }
+    if (i >= 1) {
+      // tile i-1, with the weights the S waves wrote in the previous phase
+      const int t = i - 1;
+      const char* tb = split_stage(t % kStages);
+      split_pv<B0, NB>(tb, g_split_p + (t & 1) * 3 * 128, lane, o);
+      const int64_t vs = pc.vs;
+      if constexpr (CAND) {
+        // the tile's largest row norm from the S waves' partials
+        const int nrows = cursor_rows(pc);
+        const float* pad = reinterpret_cast<const float*>(tb + 16 * (l32 * kRowSlots + kChunks));
+        const float tn = sqrtf(half_max32(l32 < nrows ? (pad[0] + pad[1]) + pad[2] : 0.0f));
+        const float* tmax = reinterpret_cast<const float*>(tb + kMaxOff);
+        const int row0 = static_cast<int>(cursor_row0(pc, P));
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+          if (cvalid[k] && g == 0)
+            cand_record(clst[k], ccnt[k], clb[k], tmax[32 * k + l32], qerr[k] * tn, static_cast<int>(vs), row0, nrows);
+      }
+      cursor_next(pc, P);
+      if (pc.pos >= pc.seg_end || pc.vs != vs) {
+        // the segment ends with this tile: this wave's blocks of its partial
+        const size_t slot = static_cast<size_t>(blockIdx.x) + static_cast<size_t>(vs);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int b = B0 + j;
+          const int head = 32 * (3 * static_cast<int>(blockIdx.y) + b / 16) + l32;
+          if (head < heads) {
+            float* po = part_o + (slot * heads + head) * kR + 32 * (b % 16);
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp)
+              *reinterpret_cast<float4*>(po + 8 * grp + 4 * g) =
+                  make_float4(o[j][4 * grp], o[j][4 * grp + 1], o[j][4 * grp + 2], o[j][4 * grp + 3]);
+          }
+          o[j] = f32x16{};
+        }
+      }
+    }
+    if constexpr (NC > 0) {
+      if (load) wait_vmcnt<NC>(); else wait_vmcnt<0>();
+    }
+    wait_lgkm0();
+    phase_barrier();
+  }
+  // the heads' bounds and live candidates of this workgroup
+  if constexpr (CAND) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      if (cvalid[k] && g == 0) {
+        if (ccnt[k] <= kDecList) cand_compact(clst[k], ccnt[k], clb[k]);
+        dlb[co[k]] = clb[k];
+        dcnt[co[k]] = ccnt[k];
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kSplitThreads) absorbed_split_kernel(
     const uint16_t* __restrict__ cache, int64_t cap, int tq, int heads, int64_t bt,
     const int64_t* __restrict__ P, const uint16_t* __restrict__ qabs, float scale,
     float* __restrict__ part_o, float* __restrict__ part_ml, int32_t* __restrict__ nflag,
     const float* __restrict__ qn2, float* __restrict__ dlb, int32_t* __restrict__ dcnt, int4* __restrict__ dent) {
-  __shared__ __align__(16) uint16_t ring[kStages * kTileBytes / 2];
-  // largest row norm of the tile being computed (double-buffered), from the
-  // loader to the compute waves
-  __shared__ float tnorm[2];
-  // per head of the block: candidate tiles for the max-logit refinement
-  __shared__ CandEntry clist[kDecHeadsPerWg][kDecList];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = gridDim.x;
   const int64_t total = P[bt];
   const int64_t lo = total * blockIdx.x / G;
   const int64_t hi = total * (blockIdx.x + 1) / G;
-  // the first head block writes the bounds of every head of an empty workgroup
-  const bool rec = blockIdx.y == 0;
   if (lo >= hi) {
-    // no rows: no bound and no candidates for any head
-    if (rec) {
-      for (int h = tid; h < heads; h += 256) {
-        dlb[blockIdx.x * heads + h] = -INFINITY;
-        dcnt[blockIdx.x * heads + h] = 0;
-      }
+    // no rows: no bound and no candidates for this workgroup's heads
+    for (int h = 96 * static_cast<int>(blockIdx.y) + tid; h < min(heads, 96 * (static_cast<int>(blockIdx.y) + 1));
+         h += kSplitThreads) {
+      dlb[blockIdx.x * heads + h] = -INFINITY;
+      dcnt[blockIdx.x * heads + h] = 0;
     }
     return;
   }
-
   int ntiles = 0;
   {
     TileCursor c;
     cursor_init(c, P, bt, lo, hi);
-    while (c.pos < hi) {
+    while (c.pos < c.n) {
       ++ntiles;
       cursor_next(c, P);
     }
   }
-
-  if (wave == 3) {
-    // ---------------- loader ----------------
-    // It also measures each tile the compute waves are working on (its
-    // largest row norm, from LDS, while the next copies are in flight) and
-    // leaves the result in tnorm for the compute waves.
-    TileCursor lc;
-    cursor_init(lc, P, bt, lo, hi);
-    TileRec r0 = split_issue(ring, 0, lc, P, cache, cap, tq, lane);
-    TileRec r1 = ntiles > 1 ? split_issue(ring, 1, lc, P, cache, cap, tq, lane) : TileRec{0, 0, 0};
-    if (ntiles > 1) wait_vmcnt<kDmaCopies>(); else wait_vmcnt<0>();   // tile 0 landed
-    loader_barrier();
-    for (int i = 0; i < ntiles; ++i) {
-      TileRec r2{0, 0, 0};
-      if (i + 2 < ntiles) r2 = split_issue(ring, (i + 2) % kStages, lc, P, cache, cap, tq, lane);
-      {
-        const float kn = tile_max_row_norm(ring + (i % kStages) * (kTileBytes / 2), r0.nrows, lane);
-        if (lane == 0) tnorm[i & 1] = kn;
-      }
-      r0 = r1;
-      r1 = r2;
-      // tile i+1 must have landed (and tnorm been written) before the barrier that ends tile i
-      if (i + 2 < ntiles) wait_vmcnt<kDmaCopies>(); else wait_vmcnt<0>();
-      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-      loader_barrier();
-    }
-    return;
-  }
-
-  // ---------------- compute waves ----------------
-  const int hb = 3 * blockIdx.y + wave;
-  const int head = 32 * hb + l32;
-  const bool active = 32 * hb < heads;
-  const bool hvalid = active && head < heads;
   const float c2 = scale * kLog2e;
-  // the head's logit error bound per unit row norm, and its candidate list
-  const int hq = hvalid ? head : 0;
-  const float qerr =
-      kDecErrCoef * sqrtf((qn2[4 * hq] + qn2[4 * hq + 1]) + (qn2[4 * hq + 2] + qn2[4 * hq + 3]));
-  CandEntry* clst = clist[32 * wave + l32];
-  float clb = -INFINITY;
-  int ccnt = 0;
-  __syncthreads();   // tile 0
-
-  TileCursor cur;
-  cursor_init(cur, P, bt, lo, hi);
-  int i = 0;   // global tile index of this workgroup
-  SplitState S;
-  while (cur.pos < hi) {
-    // ---- one segment: the rows of virtual sequence cur.vs inside [lo, hi) ----
-    const int64_t vs = cur.vs;
-    const int64_t seg_end = cur.seg_end;
-    const int64_t seg_p = P[vs];   // global index of the sequence's first visible row
-    {
-      const uint16_t* qrow = qabs + (static_cast<size_t>(vs) * heads + (hvalid ? head : 0)) * kW + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < kW / 16; ++kk)
-        S.qf[kk] = as_bf16x8(hvalid ? ldg16(qrow + 16 * kk) : make_uint4(0, 0, 0, 0));
-#pragma unroll
-      for (int j = 0; j < kR / 32; ++j) S.oacc[j] = f32x16{};
-    }
-    // Fixed reference max per segment (the first tile's): probabilities
-    // relative to it may exceed 1 but stay far inside the bf16 / fp32 range
-    // unless a later logit exceeds it by more than 64 / c2 (p > 2^64; flagged,
-    // and such segments are recomputed by the fix-up kernel).
-    S.m_ref = 0.0f;
-    S.m_true = -INFINITY;
-    S.l_part = 0.0f;
-    S.overflow = false;
-    S.first = true;
-    do {
-      const int64_t left = seg_end - cur.pos;
-      const int nrows = left < kDecRows ? static_cast<int>(left) : kDecRows;
-      float mx = 0.0f;
-      if (active) mx = split_compute(ring + (i % kStages) * (kTileBytes / 2), nrows, lane, c2, S);
-      S.first = false;
-      __syncthreads();
-      // the finished tile into the head's candidate list for the max-logit
-      // refinement, with the loader's row norm for its error bound
-      if (hvalid && g == 0)
-        cand_record(clst, ccnt, clb, mx, qerr * tnorm[i & 1], static_cast<int>(vs) | (nrows << 24),
-                    static_cast<int>(cur.pos - seg_p));
-      cursor_next(cur, P);
-      ++i;
-    } while (cur.pos < seg_end);
-
-    // ---- the segment's partial ----
-    if (hvalid) {
-      const size_t slot = static_cast<size_t>(blockIdx.x) + static_cast<size_t>(vs);
-      float* po = part_o + (slot * heads + head) * kR;
-#pragma unroll
-      for (int cbk = 0; cbk < kR / 32; ++cbk)
-#pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const int r = 32 * cbk + 8 * grp + 4 * g;
-          *reinterpret_cast<float4*>(po + r) = make_float4(S.oacc[cbk][4 * grp], S.oacc[cbk][4 * grp + 1],
-                                                           S.oacc[cbk][4 * grp + 2], S.oacc[cbk][4 * grp + 3]);
-        }
-      const float l_tot = S.l_part + __shfl_xor(S.l_part, 32, 64);
-      if (g == 0)
-        *reinterpret_cast<float4*>(part_ml + (slot * heads + head) * 4) =
-            make_float4(S.m_ref, l_tot, S.m_true, S.overflow ? 1.0f : 0.0f);
-      if (__ballot(S.overflow) && lane == 0) atomicAdd(nflag, 1);
-    }
-  }
-  // the head's bound and live candidates of this workgroup
-  if (hvalid && g == 0) {
-    if (ccnt <= kDecList) cand_compact(clst, ccnt, clb);
-    const size_t o = static_cast<size_t>(blockIdx.x) * heads + head;
-    dlb[o] = clb;
-    dcnt[o] = ccnt;
-    for (int k = 0; k < ccnt && k < kDecList; ++k) {
-      const CandEntry e = clst[k];
-      dent[o * kDecList + k] = make_int4(e.vsn & 0xffffff, e.row0, e.vsn >> 24, __float_as_int(e.u));
-    }
+  switch (wave) {
+    case 0:
+      split_s_wave<0>(ntiles, lane, lo, hi, heads, bt, P, cache, cap, tq, qabs, c2, part_ml, nflag);
+      break;
+    case 1:
+      split_s_wave<1>(ntiles, lane, lo, hi, heads, bt, P, cache, cap, tq, qabs, c2, part_ml, nflag);
+      break;
+    case 2:
+      split_s_wave<2>(ntiles, lane, lo, hi, heads, bt, P, cache, cap, tq, qabs, c2, part_ml, nflag);
+      break;
+    // value-product blocks: 12 + 12 for the two waves of SIMD 3, 2 + 11 + 11
+    // for the partners of the S waves (wave 4 also keeps the candidate lists)
+    case 3:
+      split_pv_wave<3, 0, 12, false>(ntiles, lane, lo, hi, heads, bt, P, cache, cap, tq, part_o, qn2, dlb, dcnt, dent);
+      break;
+    case 4:
+      split_pv_wave<4, 24, 2, true>(ntiles, lane, lo, hi, heads, bt, P, cache, cap, tq, part_o, qn2, dlb, dcnt, dent);
+      break;
+    case 5:
+      split_pv_wave<5, 26, 11, false>(ntiles, lane, lo, hi, heads, bt, P, cache, cap, tq, part_o, qn2, dlb, dcnt, dent);
+      break;
+    case 6:
+      split_pv_wave<6, 37, 11, false>(ntiles, lane, lo, hi, heads, bt, P, cache, cap, tq, part_o, qn2, dlb, dcnt, dent);
+      break;
+    default:
+      split_pv_wave<7, 12, 12, false>(ntiles, lane, lo, hi, heads, bt, P, cache, cap, tq, part_o, qn2, dlb, dcnt, dent);
+      break;
   }
 }
 
@@ -710,9 +869,10 @@ __global__ void __launch_bounds__(256) absorbed_fixup_kernel(
   const float c2 = scale * kLog2e;
   TileCursor cur;
   cursor_init(cur, P, bt, lo, hi);
-  while (cur.pos < hi) {
+  while (cur.pos < cur.n) {
     const int64_t vs = cur.vs;
-    const int64_t seg_beg = cur.pos, seg_end = cur.seg_end;
+    // the segment's rows within the sequence
+    const int64_t seg_beg = cursor_row0(cur, P), seg_len = cur.seg_end - cur.pos;
     const size_t slot = static_cast<size_t>(blockIdx.x) + static_cast<size_t>(vs);
     const int b = static_cast<int>(vs / tq);
     const uint16_t* cb = cache + static_cast<size_t>(b) * cap * kW;
@@ -728,7 +888,7 @@ __global__ void __launch_bounds__(256) absorbed_fixup_kernel(
 #pragma unroll
       for (int j = 0; j < kR / 64; ++j) o[j] = 0.0f;
       float m = -INFINITY, l = 0.0f;
-      for (int64_t r = seg_beg - P[vs]; r < seg_end - P[vs]; ++r) {
+      for (int64_t r = seg_beg; r < seg_beg + seg_len; ++r) {
         const uint16_t* row = cb + static_cast<size_t>(r) * kW;
         float part = 0.0f;
         float cv[kR / 64];
@@ -757,10 +917,10 @@ __global__ void __launch_bounds__(256) absorbed_fixup_kernel(
         ml[3] = 0.0f;
       }
     }
-    cur.pos = seg_end;
-    if (cur.pos < hi) {
-      while (P[cur.vs + 1] <= cur.pos) ++cur.vs;
-      cur.seg_end = min(hi, P[cur.vs + 1]);
+    cur.pos = cur.seg_end;
+    if (cur.pos < cur.n) {
+      while (row_offset(P[cur.vs + 1], cur.lo, cur.n) <= cur.pos) ++cur.vs;
+      cur.seg_end = row_offset(P[cur.vs + 1], cur.lo, cur.n);
     }
   }
 }
@@ -1111,7 +1271,7 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
   if (e != hipSuccess) return e;
   {
     TimedScope ts_("absorbed_split", st);
-    hipLaunchKernelGGL(absorbed_split_kernel, dim3(kDecSplits, (heads + kDecHeadsPerWg - 1) / kDecHeadsPerWg), dim3(256), 0, st,
+    hipLaunchKernelGGL(absorbed_split_kernel, dim3(kDecSplits, (heads + kDecHeadsPerWg - 1) / kDecHeadsPerWg), dim3(kSplitThreads), 0, st,
                        static_cast<const uint16_t*>(cache), cap, tq, heads, bt, P, qabs, scale, part_o, part_ml,
                        nflag, qn2, dlb, dcnt, dent);
   }
