@@ -720,16 +720,18 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
       if (j + 2 < nkt_w) {
         // (here j + 2 < nkt_w <= nkt: both K(j+2) and V(j+1) are due)
         overlapped(kread, vread, cur, nxt, moff, [&](int c) { dma_one(c, kdst, j + 2, vdst, j + 1); });
+      } else if (j + 1 < nkt_w) {
+        // the next tile is the wave's masked diagonal tile: the same
+        // interleaved body (its copies went out above), then the mask and
+        // the max of the masked scores
+        overlapped(kread, vread, cur, nxt, moff, [](int) {});
+        mask_tile(j + 1, nxt);
+        mx_cur = tile_max(nxt);
       } else {
-        // the wave's last two tiles: the next one (if any) is the masked diagonal tile
+        // the wave's last tile
         uint32_t pk[2][8];
         probs(cur, pk, moff);
         pv(vread, pk);
-        if (j + 1 < nkt_w) {
-          qk(kread, nxt);
-          mask_tile(j + 1, nxt);
-          mx_cur = tile_max(nxt);
-        }
       }
     }
     wait_vmcnt<0>();
