@@ -203,25 +203,23 @@ def backward_leg(m, dims, p, q, ckv, ks, w_kv_b, gate, cu, steps: int = 3):
     g = torch.Generator(device="cuda")
     g.manual_seed(9)
     dout = torch.randn((T, H * 128), generator=g, dtype=torch.float32, device="cuda")
-    cu_host = p.cu_seqlens
-    need = int(m.lib.mla_prefill_backward_workspace_size(ctypes.byref(dims.c()), T, int(np.max(np.diff(cu_host)))))
+    need = int(m.lib.mla_prefill_backward_workspace_size(ctypes.byref(dims.c()), T, cu.shape[0] - 1))
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    m.mla_prefill_backward(dims, q, ckv, ks, w_kv_b, gate, cu_host, out, lse, dout, workspace=ws)
+    m.mla_prefill_backward(dims, q, ckv, ks, w_kv_b, gate, cu, out, lse, dout, workspace=ws)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(steps):
-        m.mla_prefill_backward(dims, q, ckv, ks, w_kv_b, gate, cu_host, out, lse, dout, workspace=ws)
+        m.mla_prefill_backward(dims, q, ckv, ks, w_kv_b, gate, cu, out, lse, dout, workspace=ws)
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     m.mla_timing_enable(True)
-    m.mla_prefill_backward(dims, q, ckv, ks, w_kv_b, gate, cu_host, out, lse, dout, workspace=ws)
+    m.mla_prefill_backward(dims, q, ckv, ks, w_kv_b, gate, cu, out, lse, dout, workspace=ws)
     torch.cuda.synchronize()
     kern = {}
-    for k in ("bw_expand", "bw_transpose", "bw_gather", "bw_scores", "bw_dp_softmax", "bw_grads", "bw_scatter",
-              "bw_weights"):
+    for k in ("bw_plan", "bw_expand", "bw_prep", "bw_dkv", "bw_dq", "bw_dks", "bw_transpose", "bw_weights"):
         tot, n = m.mla_timing_read(k)
         if n:
             kern[k] = tot

@@ -32,8 +32,8 @@
  *    is the latent after its RMSNorm; k^S [tokens, S] is the shared key part
  *    (never normalised, one row per token used by every head); gate logits
  *    [tokens, H*V]; outputs [tokens, H*V] head-major.
- *  - Every pointer argument is a DEVICE pointer, 16-byte aligned, owned by the
- *    caller (mla_prefill_backward's cu_seqlens_host is the one host pointer).
+ *  - Every pointer argument is a DEVICE pointer, 16-byte aligned (cu_seqlens
+ *    and lens: 4-byte), owned by the caller.
  *    The library never allocates device memory. Apart from two opt-in
  *    exceptions (the per-kernel timing of mla_timing_*, host state, and the
  *    static scratch array of mla_absorbed_noalloc, device state), it keeps no
@@ -148,8 +148,9 @@ mla_status mla_prefill(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_d
                        void* out, float* lse, float* max_logit, int32_t accumulate,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of scratch memory mla_prefill_backward needs (0 for invalid sizes). */
-size_t mla_prefill_backward_workspace_size(const mla_dims* dims, int64_t total_tokens, int32_t max_seqlen);
+/* Bytes of scratch memory mla_prefill_backward needs (0 for invalid sizes):
+ * O(total_tokens * heads), independent of the sequence lengths. */
+size_t mla_prefill_backward_workspace_size(const mla_dims* dims, int64_t total_tokens, int32_t nseq);
 
 /*
  * Backward of mla_prefill (bf16, Kimi K3 head shape): the gradients of the
@@ -161,18 +162,19 @@ size_t mla_prefill_backward_workspace_size(const mla_dims* dims, int64_t total_t
  *   dq = scale dS K, dK = scale dS^T Q;
  *   dckv = sum_h [dK^C_h | dV_h] [W_UK_h; W_UV_h], dw_kv_b = [dK^C | dV]^T c^KV,
  *   dks = sum_h of the k^S part of dK.
- * P is recomputed from the forward's lse. Per sequence and chunk of heads the
- * L x L score planes are materialised in the workspace.
+ * P is recomputed tile by tile from the forward's lse (no L x L buffer); the
+ * call only enqueues work on the stream (nothing is read back to the host).
  *
  * q, ckv, ks, w_kv_b, gate: the forward's bf16 inputs (gate may be NULL);
- * cu_seqlens_host [nseq+1] int32 in HOST memory (the work is planned on the
- * host); out [T, H*V] and lse [H, T] fp32 from mla_prefill; dout [T, H*V] fp32.
- * Outputs (fp32, device): dq [T, H, N+S], dckv [T, R], dks [T, S],
- * dw_kv_b [H*(N+V), R], dgate [T, H*V] (required when gate is given).
- * total_tokens at most 2^20.
+ * cu_seqlens [nseq+1] int32 in DEVICE memory: non-decreasing from 0 to
+ * total_tokens (as for mla_prefill; every token belongs to one sequence);
+ * out [T, H*V] and lse [H, T] fp32 from mla_prefill; dout [T, H*V] fp32.
+ * Outputs (fp32, device, fully overwritten): dq [T, H, N+S], dckv [T, R],
+ * dks [T, S], dw_kv_b [H*(N+V), R], dgate [T, H*V] (required when gate is
+ * given). total_tokens at most 2^20.
  */
 mla_status mla_prefill_backward(const mla_dims* dims, const void* q, const void* ckv, const void* ks,
-                                const void* w_kv_b, const void* gate, const int32_t* cu_seqlens_host,
+                                const void* w_kv_b, const void* gate, const int32_t* cu_seqlens,
                                 int32_t nseq, int64_t total_tokens, const float* out, const float* lse,
                                 const float* dout, float* dq, float* dckv, float* dks, float* dw_kv_b,
                                 float* dgate, void* workspace, size_t workspace_bytes, hipStream_t stream);

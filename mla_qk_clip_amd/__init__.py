@@ -409,17 +409,14 @@ def mla_layer_forward(dims: Dims, x, w_dq, g_q, w_uq, w_kv_a, g_kv, w_kv_b, w_g,
     return out, max_logit
 
 
-def mla_prefill_backward(dims: Dims, q, ckv, ks, w_kv_b, gate, cu_seqlens_host, out, lse, dout, *, workspace=None,
+def mla_prefill_backward(dims: Dims, q, ckv, ks, w_kv_b, gate, cu_seqlens, out, lse, dout, *, workspace=None,
                          stream=None):
     """Gradients of the training-form prefill (see ``mla_prefill_backward`` in include/mla.h).
 
-    q [T, H, N+S], ckv [T, R], ks [T, S], w_kv_b [H*(N+V), R], gate [T, H*V] or None (bf16); cu_seqlens_host
-    int32 [nseq+1] on the HOST; out [T, H*V] and lse [H, T] from the forward (fp32); dout [T, H*V] fp32.
-    Returns (dq, dckv, dks, dw_kv_b, dgate or None), fp32 device tensors.
+    q [T, H, N+S], ckv [T, R], ks [T, S], w_kv_b [H*(N+V), R], gate [T, H*V] or None (bf16); cu_seqlens
+    int32 [nseq+1] on the device; out [T, H*V] and lse [H, T] from the forward (fp32); dout [T, H*V] fp32.
+    Returns (dq, dckv, dks, dw_kv_b, dgate or None), fp32 device tensors. Nothing is read back to the host.
     """
-    import numpy as _np
-    cu = _np.ascontiguousarray(_np.asarray(cu_seqlens_host.cpu() if isinstance(cu_seqlens_host, torch.Tensor)
-                                           else cu_seqlens_host, dtype=_np.int32))
     T = q.shape[0]
     H, R, S, N, V = dims.heads, dims.kv_rank, dims.shared_dim, dims.nope_dim, dims.v_dim
     bf, f32 = torch.bfloat16, torch.float32
@@ -431,19 +428,20 @@ def mla_prefill_backward(dims: Dims, q, ckv, ks, w_kv_b, gate, cu_seqlens_host, 
     _expect("out", out, (T, H * V), f32)
     _expect("lse", lse, (H, T), f32)
     _expect("dout", dout, (T, H * V), f32)
-    nseq = cu.shape[0] - 1
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda:
+        raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
+    nseq = cu_seqlens.shape[0] - 1
     dev = q.device
     dq = torch.empty((T, H, N + S), dtype=f32, device=dev)
     dckv = torch.empty((T, R), dtype=f32, device=dev)
     dks = torch.empty((T, S), dtype=f32, device=dev)
     dw = torch.empty((H * (N + V), R), dtype=f32, device=dev)
     dg = torch.empty((T, H * V), dtype=f32, device=dev) if gate is not None else None
-    max_len = int(_np.max(_np.diff(cu))) if nseq > 0 else 0
-    need = int(lib.mla_prefill_backward_workspace_size(ctypes.byref(dims.c()), T, max_len))
+    need = int(lib.mla_prefill_backward_workspace_size(ctypes.byref(dims.c()), T, nseq))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = lib.mla_prefill_backward(ctypes.byref(dims.c()), _ptr(q), _ptr(ckv), _ptr(ks), _ptr(w_kv_b), _ptr(gate),
-                                  cu.ctypes.data, nseq, T, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dckv),
+                                  _ptr(cu_seqlens), nseq, T, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dckv),
                                   _ptr(dks), _ptr(dw), _ptr(dg), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st)
     return dq, dckv, dks, dw, dg

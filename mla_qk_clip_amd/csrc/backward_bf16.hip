@@ -2,26 +2,33 @@
 // equation list of "Kimi K3 · Gated MLA · OpenModelAtlas" (expansion
 // [k^C v] = c^KV W_UKV, K_h = [K^C_h, k^S], S = Q K^T / sqrt(192), causal
 // softmax, O~ = A V, o = sigma(g) . o~) with respect to q, c^KV, k^S,
-// kv_b_proj.weight and the gate logits, for an upstream gradient dO of o.
+// kv_b_proj.weight and the gate logits, for an upstream gradient dO of o:
+//   dO~ = dO . sigma(g),  dg = dO . o . (1 - sigma(g)),  D = rowsum(dO . o),
+//   P = exp(scale S - lse) (recomputed from the forward's LSE),
+//   dV = P^T dO~,  dS' = P . (dO~ V^T - D),  dQ = scale dS' K,  dK = scale dS'^T Q,
+// then [dK^C | dV] flows back through W_UKV into c^KV and the weight, and the
+// k^S part of dK sums over the heads.
 //
-// Per sequence (length L, padded to Lp = L rounded up to 128) and chunk of
-// heads, the score and probability matrices are materialised in HBM and every
-// product runs on the NT GEMM kernel (batched over the chunk's heads):
-//   S = Q_h K_h^T with P = causal exp(scale S - lse) in its epilogue (P, P^T
-//   in bf16; S is never stored), then dP = dO~_h V_h^T with
-//   dS = scale P . (dP - D), D = rowsum(dO . o), in its epilogue (dS, dS^T)
-//   dQ = dS K_h, dK = dS^T Q_h, dV = P^T dO~_h          (fp32)
-// Only the causal half is formed: the S and dP products skip the 256 x 256
-// tiles above the diagonal (their dS, dS^T, P^T stay unwritten), and the
-// three gradient products sum only over k up to (dQ) or from (dK, dV) the
-// diagonal 256-block of their rows.
-// with dO~ = dO . sigma(g) and dg = dO . o . (1 - sigma(g)). Operands are bf16
-// (Q and K padded from 192 to 256 features with zeros); the GEMM kernel
-// needs K-contiguous rows on both sides, so the transposed operands (K_h^T,
-// Q_h^T, dO~^T by a tiled transpose; P^T and dS^T by the products' epilogues)
-// are written out.
-// Then dK^C and dV flow back through W_UKV: dc^KV = dKV W_UKV^T-rows,
-// dW = dKV^T c^KV, and the k^S part of dK sums over the heads.
+// No L x L plane is formed: the causal half of each head's score matrix is
+// recomputed tile by tile on the matrix cores, twice.
+//   dK/dV pass: one workgroup = one head x 128 keys of one sequence, 4 waves
+//     of 32 keys; a wave keeps its keys' K and V fragments and its dK, dV
+//     accumulators in registers and visits the query tiles (64 queries) from
+//     the end of the sequence down to its diagonal:
+//       S = Q K^T, dP = dO~ V^T (accumulator lane = key), P, dS';
+//       dV += P^T dO~, dK += dS'^T Q: P and dS' leave the accumulators as the
+//       key-major operand directly; dO~ and Q are read with the LDS transpose read.
+//   dQ pass: one workgroup = one head x 128 queries, 4 waves of 32 queries
+//     holding Q and dO~ fragments and the dQ accumulator; key tiles (64 keys)
+//     from the start of the sequence up to the diagonal:
+//       S^T = K Q^T, dP^T = V dO~^T (accumulator lane = query), dS';
+//       dQ += dS' K (K by the transpose read).
+// Both passes stream their tiles into two LDS stages with buffer loads
+// straight to LDS, one tile ahead. Work items (sequence, 128-row block) are
+// ordered longest first by a one-workgroup plan kernel that reads cu_seqlens
+// on the device, so the whole backward is asynchronous on the stream.
+// The expansion [K^C | V] = c^KV W_UKV^T-rows and the products
+// dc^KV = [dK^C | dV] W_UKV, dW = [dK^C | dV]^T c^KV run on the NT GEMM kernel.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -32,52 +39,616 @@
 #include "mla_internal.h"
 #include "timing.h"
 
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace mla {
 
 namespace {
 
-constexpr int kBwF = 256;   // padded feature width of Q_h and K_h (192 -> 256)
+constexpr int kBwThreads = 256;   // 4 waves
+constexpr int kBwBlock = 128;     // keys (dK/dV pass) or queries (dQ pass) per workgroup
+constexpr int kBwTile = 64;       // queries (dK/dV pass) or keys (dQ pass) per inner tile
 
-// Q_h, K_h (padded to 256 features), V_h and dO~_h of one sequence and head
-// chunk, rows t < Lp (zeros past L); D = rowsum(dO . o); dg for t < L.
-// Grid (Lp, hc), 128 threads: thread d covers features d and 128 + d.
-__global__ void __launch_bounds__(128) bw_gather_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ ks,
-    const uint16_t* __restrict__ gate, const float* __restrict__ out, const float* __restrict__ dout, int heads,
-    int64_t a, int L, int Lp, int h0, uint16_t* __restrict__ Qp, uint16_t* __restrict__ Kp, uint16_t* __restrict__ Vh,
-    uint16_t* __restrict__ dOt, float* __restrict__ Dv, float* __restrict__ dgate) {
-  __shared__ float red[2];
-  const int t = blockIdx.x, hh = blockIdx.y, h = h0 + hh, d = threadIdx.x;
-  const int64_t row = static_cast<int64_t>(hh) * Lp + t;
-  const bool live = t < L;
-  const int64_t tok = a + t;
-  uint16_t q0 = 0, q1 = 0, k0 = 0, k1 = 0, v = 0, go = 0;
-  float pr = 0.0f;
-  if (live) {
-    const uint16_t* qr = q + (tok * heads + h) * kD;
-    const uint16_t* kr = kv + tok * heads * (kN + kV) + static_cast<int64_t>(h) * (kN + kV);
-    q0 = qr[d];
-    if (d < kD - kN) q1 = qr[kN + d];
-    k0 = kr[d];
-    if (d < kS) k1 = ks[tok * kS + d];
-    v = kr[kN + d];
-    const int64_t col = tok * heads * kV + static_cast<int64_t>(h) * kV + d;
-    const float dov = dout[col], ov = out[col];
-    const float sg = gate ? sigmoidf_(bf16_to_f32(gate[col])) : 1.0f;
-    go = f32_to_bf16(dov * sg);
-    pr = dov * ov;
-    if (gate) dgate[col] = dov * ov * (1.0f - sg);
+// LDS tiles of 64 rows in 16-byte units. A 128-feature region holds 16 units
+// per row, unit u of row r at slot 16 r + (u ^ sw16(r)); a 64-feature region
+// holds 8, unit u at slot 8 r + (u ^ sw8(r)). Both swizzles keep the two read
+// patterns free of bank conflicts: 16 consecutive rows at one unit (operand
+// rows, 16 lanes of a 16-byte read) and 4 consecutive rows from a multiple of
+// 4 times an aligned quad of units (the transpose read).
+__host__ __device__ constexpr int sw16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__host__ __device__ constexpr int sw8(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+constexpr int kReg16 = kBwTile * 16 * 16;   // 16 KB
+constexpr int kReg8 = kBwTile * 8 * 16;     // 8 KB
+// dK/dV pass stage: Q^C | Q^R | dO~ | {lse log2(e), D} of the 64 query rows (1 KB slot)
+constexpr int kKvStage = 2 * kReg16 + kReg8 + 1024;
+// dQ pass stage: K^C | k^S | V
+constexpr int kQStage = 2 * kReg16 + kReg8;
+static_assert(kKvStage % 1024 == 0 && kQStage % 1024 == 0, "stage offsets keep the swizzle bits clear");
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char*)(p)));
+}
+
+// Buffer resource over [base, base + bytes): loads past the end read zeros.
+__device__ __forceinline__ u32x4 bw_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : static_cast<uint32_t>(bytes));
+  return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, n, 0x00020000u};
+}
+
+// 16 bytes per lane from buffer offset voff straight into LDS at lds + 16 lane.
+// Issued as inline assembly so that the compiler does not order its own LDS
+// reads of the other stage behind these copies; the caller waits for them
+// (vmcnt) before the barrier that publishes the stage. M0 is written here,
+// and one wait state separates that write from the load that reads it.
+__device__ __forceinline__ void bw_dma16(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void bw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Copies of one wave's share of a 64-row tile region (the region is split
+// over the 4 waves in whole 1 KB copies: rows 16 w .. 16 w + 15).
+//   16-unit region: copy i (0..3) holds rows 16 w + 4 i + lane / 16
+//   8-unit region:  copy i (0..1) holds rows 16 w + 8 i + lane / 8
+// rs: buffer over the region's rows (row stride rstride bytes), col: byte
+// offset of the region's first feature within a row.
+__device__ __forceinline__ void copy16(u32x4 rs, int64_t rstride, int col, uint32_t lds, int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * i + (lane >> 4);
+    const int u = (lane & 15) ^ sw16(r);
+    bw_dma16(rs, static_cast<uint32_t>(r * rstride + col + 16 * u), lds + (16 * 16) * (16 * w + 4 * i));
   }
-  Qp[row * kBwF + d] = q0;
-  Qp[row * kBwF + 128 + d] = q1;
-  Kp[row * kBwF + d] = k0;
-  Kp[row * kBwF + 128 + d] = k1;
-  Vh[row * kV + d] = v;
-  dOt[row * kV + d] = go;
-  pr = wave_sum(pr);
-  if ((d & 63) == 0) red[d >> 6] = pr;
+}
+__device__ __forceinline__ void copy8(u32x4 rs, int64_t rstride, int col, uint32_t lds, int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * w + 8 * i + (lane >> 3);
+    const int u = (lane & 7) ^ sw8(r);
+    bw_dma16(rs, static_cast<uint32_t>(r * rstride + col + 16 * u), lds + (8 * 16) * (16 * w + 8 * i));
+  }
+}
+
+// Per-lane LDS byte offsets of the two read patterns (lane l, half g = l / 32).
+//   row16 / row8: operand row R0 + l % 32 (R0 a multiple of 32), k-step ks:
+//     features 16 ks + 8 g .. +7 = unit 2 ks + g; byte offset
+//     256 R0 + (r16 ^ 32 ks)  or  128 R0 + (r8 ^ 32 ks).
+//   tr16 / tr8: the transpose read of rows R0 + 16 kk + {4 g + i / 4, +8}
+//     (i = l % 16) at columns 32 cb + 16 ((l / 16) % 2) + 4 (i % 4): lane l
+//     receives column 32 cb + l % 32 at rows R0 + 16 kk + acc_row(0..7, g),
+//     the k-slot order of a 32x32 accumulator; byte offset
+//     256 (R0 + 16 kk) + (t16[sec] ^ 64 cb)  (8-unit: 128 (..) + (t8[sec] ^ 64 cb)).
+struct LaneOff {
+  uint32_t r16, r8, t16[2], t8[2];
+};
+__device__ __forceinline__ LaneOff lane_offsets(int lane) {
+  const int g = lane >> 5, l32 = lane & 31, i16 = lane & 15, mh = (lane >> 4) & 1;
+  LaneOff o;
+  o.r16 = 256 * l32 + 16 * (g ^ sw16(l32 & 15));
+  o.r8 = 128 * l32 + 16 * (g ^ sw8(l32 & 15));
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec) {
+    const int rr = 4 * g + 8 * sec + (i16 >> 2);   // row within the 16-row k-block
+    const int lo = (2 * mh + ((i16 >> 1) & 1)) ^ (g + 2 * sec);
+    o.t16[sec] = 256 * rr + 16 * (i16 & 12) + 16 * lo + 8 * (i16 & 1);
+    o.t8[sec] = 128 * rr + 64 * ((i16 >> 3) & 1) + 16 * lo + 8 * (i16 & 1);
+  }
+  return o;
+}
+
+__device__ __forceinline__ bf16x8 ld_row16(const char* reg, const LaneOff& o, int R0, int ks) {
+  return *reinterpret_cast<const bf16x8*>(reg + (256 * R0 + (o.r16 ^ (32 * ks))));
+}
+__device__ __forceinline__ bf16x8 ld_row8(const char* reg, const LaneOff& o, int R0, int ks) {
+  return *reinterpret_cast<const bf16x8*>(reg + (128 * R0 + (o.r8 ^ (32 * ks))));
+}
+__device__ __forceinline__ v4s tr4(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)((const lds_char*)p));
+}
+__device__ __forceinline__ bf16x8 cat8(v4s lo, v4s hi) {
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  const v8s x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, x);
+}
+__device__ __forceinline__ bf16x8 ld_tr16(const char* reg, const LaneOff& o, int R0, int cb) {
+  const char* b = reg + 256 * R0;
+  return cat8(tr4(b + (o.t16[0] ^ (64 * cb))), tr4(b + (o.t16[1] ^ (64 * cb))));
+}
+__device__ __forceinline__ bf16x8 ld_tr8(const char* reg, const LaneOff& o, int R0, int cb) {
+  const char* b = reg + 128 * R0;
+  return cat8(tr4(b + (o.t8[0] ^ (64 * cb))), tr4(b + (o.t8[1] ^ (64 * cb))));
+}
+
+// Row of accumulator element i within a 32x32 block, lane half 0 (half g adds 4 g).
+__host__ __device__ constexpr int arow0(int i) { return ((i >> 2) << 3) + (i & 3); }
+
+// bf16 pack of accumulator elements 8 kk .. 8 kk + 7 (the k-slots of one
+// 16-row k-step when the accumulator is reused as an operand).
+__device__ __forceinline__ bf16x8 pack8(const float (&v)[16], int kk) {
+  uint4 u;
+  u.x = pack_bf16x2(v[8 * kk + 0], v[8 * kk + 1]);
+  u.y = pack_bf16x2(v[8 * kk + 2], v[8 * kk + 3]);
+  u.z = pack_bf16x2(v[8 * kk + 4], v[8 * kk + 5]);
+  u.w = pack_bf16x2(v[8 * kk + 6], v[8 * kk + 7]);
+  return as_bf16x8(u);
+}
+
+// ---------------------------------------------------------------------------
+// Plan: work items {sequence, block of 128 rows} for both passes, longest
+// first (counting sort on the item's tile count; ties in any order):
+//   dK/dV item (s, b): query tiles 2 b .. ceil(L / 64) - 1
+//   dQ item (s, b):    key tiles 0 .. min(2 b + 1, ceil(L / 64) - 1)
+// count[0] = number of items (the same for both lists).
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 4096;   // tile counts past this share the top bucket
+constexpr int kPlanPer = kPlanBuckets / kPlanThreads;
+
+__device__ __forceinline__ int bw_seq_len(const int32_t* cu, int s, int64_t ntok, int64_t* a_out) {
+  int64_t a = cu[s], b = cu[s + 1];
+  a = a < 0 ? 0 : (a > ntok ? ntok : a);
+  b = b < a ? a : (b > ntok ? ntok : b);
+  *a_out = a;
+  return static_cast<int>(b - a);
+}
+
+__global__ void __launch_bounds__(kPlanThreads) bwd_plan_kernel(const int32_t* __restrict__ cu, int nseq,
+                                                                int64_t ntok, int2* __restrict__ items_kv,
+                                                                int2* __restrict__ items_q,
+                                                                int32_t* __restrict__ count) {
+  __shared__ int hist[2][kPlanBuckets];
+  __shared__ int part[2][kPlanThreads];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 2 * kPlanBuckets; i += kPlanThreads) hist[i / kPlanBuckets][i % kPlanBuckets] = 0;
   __syncthreads();
-  if (d == 0) Dv[row] = red[0] + red[1];
+  auto bucket = [](int w) { return w < kPlanBuckets - 1 ? w : kPlanBuckets - 1; };
+  for (int s = tid; s < nseq; s += kPlanThreads) {
+    int64_t a;
+    const int L = bw_seq_len(cu, s, ntok, &a);
+    const int nt = (L + kBwTile - 1) / kBwTile, nb = (L + kBwBlock - 1) / kBwBlock;
+    for (int b = 0; b < nb; ++b) {
+      atomicAdd(&hist[0][bucket(nt - 2 * b)], 1);
+      atomicAdd(&hist[1][bucket(min(2 * b + 2, nt))], 1);
+    }
+  }
+  __syncthreads();
+  // Thread t owns the kPlanPer buckets ranked kPlanPer t .. from the top;
+  // inclusive scan of the per-thread sums, then each bucket's first slot.
+  for (int k = 0; k < 2; ++k) {
+    int sum = 0;
+    for (int j = 0; j < kPlanPer; ++j) sum += hist[k][kPlanBuckets - 1 - (kPlanPer * tid + j)];
+    part[k][tid] = sum;
+  }
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const int v0 = tid >= off ? part[0][tid - off] : 0, v1 = tid >= off ? part[1][tid - off] : 0;
+    __syncthreads();
+    part[0][tid] += v0;
+    part[1][tid] += v1;
+    __syncthreads();
+  }
+  for (int k = 0; k < 2; ++k) {
+    int run = tid ? part[k][tid - 1] : 0;
+    for (int j = 0; j < kPlanPer; ++j) {
+      const int idx = kPlanBuckets - 1 - (kPlanPer * tid + j);
+      const int c = hist[k][idx];
+      hist[k][idx] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) count[0] = part[0][kPlanThreads - 1];
+  for (int s = tid; s < nseq; s += kPlanThreads) {
+    int64_t a;
+    const int L = bw_seq_len(cu, s, ntok, &a);
+    const int nt = (L + kBwTile - 1) / kBwTile, nb = (L + kBwBlock - 1) / kBwBlock;
+    for (int b = 0; b < nb; ++b) {
+      items_kv[atomicAdd(&hist[0][bucket(nt - 2 * b)], 1)] = make_int2(s, b);
+      items_q[atomicAdd(&hist[1][bucket(min(2 * b + 2, nt))], 1)] = make_int2(s, b);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Preparation, per (token, head) row of 128: dO~ = dO . sigma(g) (bf16),
+// dg = dO . o . (1 - sigma(g)), and {lse log2(e), D = rowsum(dO . o)} into
+// lsed [H][T]. 32 threads per row, 8 rows per 256-thread block.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bwd_prep_kernel(const float* __restrict__ dout, const float* __restrict__ out,
+                                                       const uint16_t* __restrict__ gate,
+                                                       const float* __restrict__ lse, int heads, int64_t ntok,
+                                                       uint16_t* __restrict__ dot, float2* __restrict__ lsed,
+                                                       float* __restrict__ dgate) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int j = threadIdx.x & 31;
+  if (row >= ntok * heads) return;   // whole 32-lane groups leave together
+  const int64_t t = row / heads;
+  const int h = static_cast<int>(row - t * heads);
+  const int64_t col = row * kV + 4 * j;
+  const float4 dv = *reinterpret_cast<const float4*>(dout + col);
+  const float4 ov = *reinterpret_cast<const float4*>(out + col);
+  float sg0 = 1.0f, sg1 = 1.0f, sg2 = 1.0f, sg3 = 1.0f;
+  if (gate) {
+    const uint2 gb = *reinterpret_cast<const uint2*>(gate + col);
+    sg0 = sigmoidf_(bf16lo(gb.x));
+    sg1 = sigmoidf_(bf16hi(gb.x));
+    sg2 = sigmoidf_(bf16lo(gb.y));
+    sg3 = sigmoidf_(bf16hi(gb.y));
+    *reinterpret_cast<float4*>(dgate + col) = make_float4(dv.x * ov.x * (1.0f - sg0), dv.y * ov.y * (1.0f - sg1),
+                                                          dv.z * ov.z * (1.0f - sg2), dv.w * ov.w * (1.0f - sg3));
+  }
+  *reinterpret_cast<uint2*>(dot + col) =
+      make_uint2(pack_bf16x2(dv.x * sg0, dv.y * sg1), pack_bf16x2(dv.z * sg2, dv.w * sg3));
+  float pr = dv.x * ov.x + dv.y * ov.y + dv.z * ov.z + dv.w * ov.w;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) pr += __shfl_xor(pr, o, 64);
+  if (j == 0) lsed[static_cast<int64_t>(h) * ntok + t] = make_float2(lse[static_cast<int64_t>(h) * ntok + t] * kLog2e, pr);
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV pass. Block x = item * heads + head.
+// ---------------------------------------------------------------------------
+__shared__ __align__(1024) char g_bw_lds[2 * kKvStage];
+
+// Score-side products of one tile, shared by both passes: four accumulators
+// (block 0 and 1 of the wide product X = A F^T over 192 features, block 0
+// and 1 of the narrow one Y = B G^T over 128), A and B read as operand rows
+// from LDS (A: the 128-feature region a16 then the 64-feature region a8),
+// F and G held in registers. Issue order: X0, X1, Y0 round-robin over
+// k-steps 0..7, then X0, X1 k-steps 8..11 with Y1 k-steps 0..3, then Y1
+// 4..7, so that block 0 completes first; operand reads run kSW ahead.
+struct ScoreStep {
+  int t, blk, ks;   // t: 0 wide, 1 narrow
+};
+__host__ __device__ constexpr ScoreStep score_step(int e) {
+  return e < 24   ? ((e % 3) == 2 ? ScoreStep{1, 0, e / 3} : ScoreStep{0, e % 3, e / 3})
+         : e < 36 ? (((e - 24) % 3) == 2 ? ScoreStep{1, 1, (e - 24) / 3} : ScoreStep{0, (e - 24) % 3, 8 + (e - 24) / 3})
+                  : ScoreStep{1, 1, e - 32};
+}
+constexpr int kScoreSteps = 40;
+constexpr int kSW = 6;   // operand reads in flight
+
+__device__ __forceinline__ void score_products(const char* a16, const char* a8, const char* b16, const LaneOff& o,
+                                               const bf16x8 (&f)[12], const bf16x8 (&gv)[8], f32x16 (&x)[2],
+                                               f32x16 (&y)[2]) {
+  auto rd = [&](auto E) -> bf16x8 {
+    constexpr ScoreStep st = score_step(E);
+    if constexpr (st.t == 1) return ld_row16(b16, o, 32 * st.blk, st.ks);
+    else if constexpr (st.ks < 8) return ld_row16(a16, o, 32 * st.blk, st.ks);
+    else return ld_row8(a8, o, 32 * st.blk, st.ks - 8);
+  };
+  static_for<0, 2>([&](auto B) {
+    x[B] = f32x16{};
+    y[B] = f32x16{};
+  });
+  bf16x8 buf[kSW];
+  static_for<0, kSW>([&](auto E) { buf[E] = rd(E); });
+  static_for<0, kScoreSteps>([&](auto E) {
+    constexpr ScoreStep st = score_step(E);
+    const bf16x8 av = buf[E % kSW];
+    if constexpr (E + kSW < kScoreSteps) buf[E % kSW] = rd(std::integral_constant<int, E + kSW>{});
+    if constexpr (st.t == 0) x[st.blk] = mfma32(av, f[st.ks], x[st.blk]);
+    else y[st.blk] = mfma32(av, gv[st.ks], y[st.blk]);
+  });
+}
+
+// Instruction interleave of one tile body (sched groups over the whole
+// block): the score products with their operand reads, then the second
+// half of the softmax VALU work overlapping the last products, then two
+// rounds of gradient products (NG each, operand reads kGW ahead, two
+// transpose reads per product) with the remaining VALU work folded into
+// the first round.
+constexpr int kGW = 3;
+template <int NG, int PRE_READS, int VALU_A, int VALU_B>
+__device__ __forceinline__ void tile_schedule() {
+  __builtin_amdgcn_sched_group_barrier(0x100, kSW, 0);
+  static_for<0, kScoreSteps>([&](auto E) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (E + kSW < kScoreSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if constexpr (E == 30 && PRE_READS > 0) __builtin_amdgcn_sched_group_barrier(0x100, PRE_READS, 0);
+    if constexpr (E >= 34) __builtin_amdgcn_sched_group_barrier(0x002, VALU_A, 0);
+  });
+  static_for<0, 2>([&](auto R) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kGW + (R == 0 ? PRE_READS : 0), 0);
+    static_for<0, NG>([&](auto M) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (M + kGW < NG) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if constexpr (R == 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU_B, 0);
+    });
+  });
+}
+
+// One query tile for the wave's 32 keys. P is kept where
+// (unsigned)(kd + row) < span for the element's row in the tile: with
+// kd = q0 + 4 g - key and span = max(L - key, 0) that is key <= query < L;
+// tiles with no masked element pass kd = 0, span = 2^31 - 1 (one code path,
+// so the compiler has no common code to hoist out of two variants).
+__device__ __forceinline__ void dkv_tile(const char* st, const LaneOff& o, int lane, const bf16x8 (&kf)[12],
+                                         const bf16x8 (&vf)[8], f32x16 (&dk)[6], f32x16 (&dv)[4], float c, int kd,
+                                         int span) {
+  const char* qc = st;
+  const char* qr = st + kReg16;
+  const char* od = st + kReg16 + kReg8;
+  const char* info = st + 2 * kReg16 + kReg8;
+  const int g = lane >> 5;
+  f32x16 s[2], dp[2];
+  score_products(qc, qr, od, o, kf, vf, s, dp);
+  // P and dS' = P (dP - D) of both query blocks, as bf16 operands (k-step kk:
+  // elements 8 kk .. 8 kk + 7); {lse log2(e), D} of the rows the lane holds
+  bf16x8 pa[2][2], da[2][2];
+  static_for<0, 2>([&](auto QB) {
+    float p[16], d[16];
+    static_for<0, 4>([&](auto J) {
+      const float4* ip = reinterpret_cast<const float4*>(info + 8 * (32 * QB + 8 * J + 4 * g));
+      const float4 xv = ip[0], yv = ip[1];
+      const float l2[4] = {xv.x, xv.z, yv.x, yv.z}, dd[4] = {xv.y, xv.w, yv.y, yv.w};
+      static_for<0, 4>([&](auto E) {
+        constexpr int i = 4 * J + E;
+        constexpr int ci = 32 * QB + arow0(i);
+        float pv = fast_exp2(fmaf(s[QB][i], c, -l2[E]));
+        pv = static_cast<unsigned>(kd + ci) < static_cast<unsigned>(span) ? pv : 0.0f;
+        p[i] = pv;
+        d[i] = pv * (dp[QB][i] - dd[E]);
+      });
+    });
+    pa[QB][0] = pack8(p, 0);
+    pa[QB][1] = pack8(p, 1);
+    da[QB][0] = pack8(d, 0);
+    da[QB][1] = pack8(d, 1);
+  });
+  // dV += P^T dO~ and dK += dS'^T Q, query block by query block
+  static_for<0, 2>([&](auto QB) {
+    auto rd = [&](auto M) -> bf16x8 {
+      constexpr int KK = M / 10, j = M % 10, R0 = 32 * QB + 16 * KK;
+      if constexpr (j < 4) return ld_tr16(od, o, R0, j);
+      else if constexpr (j < 8) return ld_tr16(qc, o, R0, j - 4);
+      else return ld_tr8(qr, o, R0, j - 8);
+    };
+    bf16x8 buf[kGW];
+    static_for<0, kGW>([&](auto M) { buf[M] = rd(M); });
+    static_for<0, 20>([&](auto M) {
+      constexpr int KK = M / 10, j = M % 10;
+      const bf16x8 bv = buf[M % kGW];
+      if constexpr (M + kGW < 20) buf[M % kGW] = rd(std::integral_constant<int, M + kGW>{});
+      if constexpr (j < 4) dv[j] = mfma32(pa[QB][KK], bv, dv[j]);
+      else dk[j - 4] = mfma32(da[QB][KK], bv, dk[j - 4]);
+    });
+  });
+  tile_schedule<20, 8, 16, 6>();
+}
+
+__global__ void __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ ksh,
+    const uint16_t* __restrict__ dot, const float2* __restrict__ lsed, const int32_t* __restrict__ cu,
+    const int2* __restrict__ items, const int32_t* __restrict__ count, int heads, int64_t ntok, float scale,
+    uint16_t* __restrict__ dkv, float* __restrict__ dksp) {
+  const int h = static_cast<int>(blockIdx.x % heads);
+  const int item = static_cast<int>(blockIdx.x / heads);
+  if (item >= count[0]) return;
+  const int2 it = items[item];
+  int64_t a;
+  const int L = bw_seq_len(cu, it.x, ntok, &a);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int kb0 = kBwBlock * it.y, kw0 = kb0 + 32 * w;
+  const int key = kw0 + l32;   // this lane's key (sequence-relative)
+  const int span = max(L - key, 0);
+  const LaneOff o = lane_offsets(lane);
+  const int64_t HQ = static_cast<int64_t>(heads) * kD * 2, HO = static_cast<int64_t>(heads) * kV * 2;
+
+  const int nq = (L + kBwTile - 1) / kBwTile;
+  const int qt_lo = kb0 / kBwTile;
+  const int ntiles = nq - qt_lo;
+  const uint32_t lds0 = lds_off(g_bw_lds);
+  auto issue = [&](int j, int stage) {   // copies of query tile nq - 1 - j into a stage
+    const int64_t t0 = a + static_cast<int64_t>(kBwTile) * (nq - 1 - j);
+    const uint32_t base = lds0 + stage * kKvStage;
+    const int64_t rows_left = ntok - t0;
+    const u32x4 rq = bw_rsrc(q + (t0 * heads + h) * kD, rows_left * HQ - h * (kD * 2));
+    copy16(rq, HQ, 0, base, w, lane);
+    copy8(rq, HQ, kN * 2, base + kReg16, w, lane);
+    const u32x4 ro = bw_rsrc(dot + (t0 * heads + h) * kV, rows_left * HO - h * (kV * 2));
+    copy16(ro, HO, 0, base + kReg16 + kReg8, w, lane);
+    if (w == 0) {
+      const u32x4 ri = bw_rsrc(lsed + static_cast<int64_t>(h) * ntok + t0, rows_left * 8);
+      bw_dma16(ri, 16 * lane, base + 2 * kReg16 + kReg8);
+    }
+  };
+  if (ntiles > 0) issue(0, 0);
+
+  // the wave's K (K^C then k^S) and V fragments: key row, features 16 ks + 8 g ..
+  bf16x8 kf[12], vf[8];
+  {
+    const bool ok = key < L;
+    const int64_t t = a + key;
+    const uint16_t* kr = kv + (t * heads + h) * (kN + kV) + 8 * g;
+    const uint16_t* sr = ksh + t * kS + 8 * g;
+    static_for<0, 8>([&](auto KS) {
+      kf[KS] = ok ? as_bf16x8(ldg16(kr + 16 * KS)) : bf16x8{};
+      vf[KS] = ok ? as_bf16x8(ldg16(kr + kN + 16 * KS)) : bf16x8{};
+    });
+    static_for<0, 4>([&](auto KS) { kf[8 + KS] = ok ? as_bf16x8(ldg16(sr + 16 * KS)) : bf16x8{}; });
+  }
+  f32x16 dk[6], dv[4];
+  static_for<0, 6>([&](auto I) { dk[I] = f32x16{}; });
+  static_for<0, 4>([&](auto I) { dv[I] = f32x16{}; });
+  const float c = scale * kLog2e;
+  wait_vmcnt<0>();
+  bw_barrier();
+  for (int j = 0; j < ntiles; ++j) {
+    const int stage = j & 1;
+    if (j + 1 < ntiles) issue(j + 1, stage ^ 1);
+    const int q0 = kBwTile * (nq - 1 - j);
+    const char* st = g_bw_lds + stage * kKvStage;
+    if (q0 + kBwTile - 1 >= kw0) {   // else every query of the tile precedes the wave's keys
+      const bool masked = q0 < kw0 + 31 || q0 + kBwTile > L;
+      dkv_tile(st, o, lane, kf, vf, dk, dv, c, masked ? q0 + 4 * g - key : 0, masked ? span : 0x7fffffff);
+    }
+    wait_vmcnt<0>();
+    bw_barrier();
+  }
+  // dV rows (bf16), dK^C rows scaled (bf16), k^S part scaled into the per-head partials (fp32):
+  // accumulator block b: lane = column 32 b + l32, element i = key kw0 + acc_row(i, g)
+  static_for<0, 16>([&](auto II) {
+    constexpr int I = II;
+    const int kr = kw0 + acc_row(I, g);
+    if (kr < L) {
+      const int64_t t = a + kr;
+      uint16_t* dr = dkv + (t * heads + h) * (kN + kV) + l32;
+      static_for<0, 4>([&](auto B) {
+        dr[32 * B] = f32_to_bf16(scale * dk[B][I]);
+        dr[kN + 32 * B] = f32_to_bf16(dv[B][I]);
+      });
+      float* sp = dksp + (static_cast<int64_t>(h) * ntok + t) * kS + l32;
+      sp[0] = scale * dk[4][I];
+      sp[32] = scale * dk[5][I];
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// dQ pass. Block x = item * heads + head.
+// ---------------------------------------------------------------------------
+// One key tile for the wave's 32 queries (this lane's lse log2(e) l2 and
+// D dd). P is kept where the element's row (key) in the tile is <= m: with
+// m = query - k0 - 4 g that is key <= query; tiles with no masked element
+// pass a large m.
+__device__ __forceinline__ void dq_tile(const char* st, const LaneOff& o, const bf16x8 (&qf)[12],
+                                        const bf16x8 (&of)[8], f32x16 (&dq)[6], float c, float l2, float dd, int m) {
+  const char* kc = st;
+  const char* kr = st + kReg16;
+  const char* vt = st + kReg16 + kReg8;
+  f32x16 s[2], dp[2];
+  score_products(kc, kr, vt, o, qf, of, s, dp);
+  bf16x8 da[2][2];
+  static_for<0, 2>([&](auto KB) {
+    float d[16];
+    static_for<0, 16>([&](auto II) {
+      constexpr int I = II;
+      constexpr int ci = 32 * KB + arow0(I);
+      float pv = fast_exp2(fmaf(s[KB][I], c, -l2));
+      pv = ci <= m ? pv : 0.0f;
+      d[I] = pv * (dp[KB][I] - dd);
+    });
+    da[KB][0] = pack8(d, 0);
+    da[KB][1] = pack8(d, 1);
+  });
+  // dQ += dS' K, key block by key block
+  static_for<0, 2>([&](auto KB) {
+    auto rd = [&](auto M) -> bf16x8 {
+      constexpr int KK = M / 6, j = M % 6, R0 = 32 * KB + 16 * KK;
+      if constexpr (j < 4) return ld_tr16(kc, o, R0, j);
+      else return ld_tr8(kr, o, R0, j - 4);
+    };
+    bf16x8 buf[kGW];
+    static_for<0, kGW>([&](auto M) { buf[M] = rd(M); });
+    static_for<0, 12>([&](auto M) {
+      constexpr int KK = M / 6, j = M % 6;
+      const bf16x8 bv = buf[M % kGW];
+      if constexpr (M + kGW < 12) buf[M % kGW] = rd(std::integral_constant<int, M + kGW>{});
+      dq[j] = mfma32(da[KB][KK], bv, dq[j]);
+    });
+  });
+  tile_schedule<12, 0, 14, 7>();
+}
+
+__global__ void __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const uint16_t* __restrict__ ksh,
+    const uint16_t* __restrict__ dot, const float2* __restrict__ lsed, const int32_t* __restrict__ cu,
+    const int2* __restrict__ items, const int32_t* __restrict__ count, int heads, int64_t ntok, float scale,
+    float* __restrict__ dq) {
+  const int h = static_cast<int>(blockIdx.x % heads);
+  const int item = static_cast<int>(blockIdx.x / heads);
+  if (item >= count[0]) return;
+  const int2 it = items[item];
+  int64_t a;
+  const int L = bw_seq_len(cu, it.x, ntok, &a);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int qb0 = kBwBlock * it.y, qw0 = qb0 + 32 * w;
+  const int qrow = qw0 + l32;   // this lane's query (sequence-relative)
+  const LaneOff o = lane_offsets(lane);
+  const int64_t HK = static_cast<int64_t>(heads) * (kN + kV) * 2;
+
+  const int nq = (L + kBwTile - 1) / kBwTile;
+  const int ntiles = min(nq, (qb0 + kBwBlock - 1) / kBwTile + 1);
+  const uint32_t lds0 = lds_off(g_bw_lds);
+  auto issue = [&](int j, int stage) {   // copies of key tile j into a stage
+    const int64_t t0 = a + static_cast<int64_t>(kBwTile) * j;
+    const uint32_t base = lds0 + stage * kQStage;
+    const int64_t rows_left = ntok - t0;
+    const u32x4 rk = bw_rsrc(kv + (t0 * heads + h) * (kN + kV), rows_left * HK - h * ((kN + kV) * 2));
+    copy16(rk, HK, 0, base, w, lane);
+    copy16(rk, HK, kN * 2, base + kReg16 + kReg8, w, lane);
+    const u32x4 rs = bw_rsrc(ksh + t0 * kS, rows_left * (kS * 2));
+    copy8(rs, kS * 2, 0, base + kReg16, w, lane);
+  };
+  if (ntiles > 0) issue(0, 0);
+
+  bf16x8 qf[12], of[8];
+  float l2 = 0.0f, dd = 0.0f;
+  {
+    const bool ok = qrow < L;
+    const int64_t t = a + qrow;
+    const uint16_t* qp = q + (t * heads + h) * kD + 8 * g;
+    const uint16_t* op = dot + (t * heads + h) * kV + 8 * g;
+    static_for<0, 12>([&](auto KS) { qf[KS] = ok ? as_bf16x8(ldg16(qp + 16 * KS)) : bf16x8{}; });
+    static_for<0, 8>([&](auto KS) { of[KS] = ok ? as_bf16x8(ldg16(op + 16 * KS)) : bf16x8{}; });
+    if (ok) {
+      const float2 x = lsed[static_cast<int64_t>(h) * ntok + t];
+      l2 = x.x;
+      dd = x.y;
+    }
+  }
+  f32x16 acc[6];
+  static_for<0, 6>([&](auto I) { acc[I] = f32x16{}; });
+  const float c = scale * kLog2e;
+  wait_vmcnt<0>();
+  bw_barrier();
+  for (int j = 0; j < ntiles; ++j) {
+    const int stage = j & 1;
+    if (j + 1 < ntiles) issue(j + 1, stage ^ 1);
+    const int k0 = kBwTile * j;
+    const char* st = g_bw_lds + stage * kQStage;
+    if (k0 <= qw0 + 31) {   // else every key of the tile follows the wave's queries
+      const bool masked = k0 + kBwTile - 1 > qw0;
+      dq_tile(st, o, qf, of, acc, c, l2, dd, masked ? qrow - k0 - 4 * g : 0x3fffffff);
+    }
+    wait_vmcnt<0>();
+    bw_barrier();
+  }
+  // accumulator block b: lane = feature 32 b + l32, element i = query qw0 + acc_row(i, g)
+  static_for<0, 16>([&](auto II) {
+    constexpr int I = II;
+    const int qr = qw0 + acc_row(I, g);
+    if (qr < L) {
+      float* dr = dq + ((a + qr) * heads + h) * kD + l32;
+      static_for<0, 6>([&](auto B) { dr[32 * B] = scale * acc[B][I]; });
+    }
+  });
+}
+
+// dk^S[t][j] = sum over heads of the per-head partials.
+__global__ void __launch_bounds__(256) bwd_dks_kernel(const float* __restrict__ dksp, int heads, int64_t ntok,
+                                                      float* __restrict__ dks) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= ntok * kS) return;
+  float s = 0.0f;
+  for (int h = 0; h < heads; ++h) s += dksp[static_cast<int64_t>(h) * ntok * kS + i];
+  dks[i] = s;
 }
 
 // dst[b][c][r] = r < rvalid ? src[b][r][c] : 0 for r < rp, c < cols (bf16).
@@ -118,95 +689,59 @@ __global__ void __launch_bounds__(256) bw_transpose_kernel(const uint16_t* __res
   }
 }
 
-// dq (fp32), the K^C / V gradients into dKV (bf16, head-major columns as in
-// kv_b_proj) for rows t < L of one chunk; grid (L, hc), 128 threads.
-__global__ void __launch_bounds__(128) bw_scatter_kernel(const float* __restrict__ dQc, const float* __restrict__ dKc,
-                                                         const float* __restrict__ dVc, int heads, int64_t a, int Lp,
-                                                         int h0, float* __restrict__ dq, uint16_t* __restrict__ dKV) {
-  const int t = blockIdx.x, hh = blockIdx.y, h = h0 + hh, d = threadIdx.x;
-  const int64_t row = static_cast<int64_t>(hh) * Lp + t, tok = a + t;
-  float* dqr = dq + (tok * heads + h) * kD;
-  dqr[d] = dQc[row * kBwF + d];
-  if (d < kD - kN) dqr[kN + d] = dQc[row * kBwF + kN + d];
-  uint16_t* o = dKV + tok * heads * (kN + kV) + static_cast<int64_t>(h) * (kN + kV);
-  o[d] = f32_to_bf16(dKc[row * kBwF + d]);
-  o[kN + d] = f32_to_bf16(dVc[row * kV + d]);
-}
-
-// dk^S[t] += sum over the chunk's heads of dK_h[t][128 .. 191]; grid L, 64 threads.
-__global__ void __launch_bounds__(64) bw_dks_kernel(const float* __restrict__ dKc, int hc, int64_t a, int Lp,
-                                                    float* __restrict__ dks) {
-  const int t = blockIdx.x, j = threadIdx.x;
-  float s = 0.0f;
-  for (int hh = 0; hh < hc; ++hh) s += dKc[(static_cast<int64_t>(hh) * Lp + t) * kBwF + kN + j];
-  dks[(a + t) * kS + j] += s;
-}
-
-__global__ void bw_zero_kernel(float* __restrict__ p, int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.0f;
-}
-
 inline int64_t round128(int64_t x) { return (x + 127) / 128 * 128; }
 
 }  // namespace
 
-BackwardWs backward_ws_layout(int heads, int64_t ntok, int max_seqlen) {
+BackwardWs backward_ws_layout(int heads, int64_t ntok, int nseq) {
   BackwardWs w{};
   const size_t T = static_cast<size_t>(ntok), Tp = static_cast<size_t>(round128(ntok));
-  const size_t HW = static_cast<size_t>(heads) * (kN + kV);
-  const size_t Lp = static_cast<size_t>(round128(max_seqlen));
-  // heads per chunk: up to 32 (the gradient products have one or two 256-wide
-  // column tiles, so the chunk's heads are what fills the CUs), with the
-  // Lp x Lp planes (P, P^T, dS, dS^T, bf16) within about 16 GB
-  const size_t plane = Lp * Lp * (2 + 2 + 2 + 2);
-  w.hc = static_cast<int>(plane ? std::max<size_t>(1, std::min<size_t>(32, (size_t{16} << 30) / plane)) : 1);
-  w.hc = std::min(w.hc, heads);
-  const size_t hc = static_cast<size_t>(w.hc);
+  const size_t H = static_cast<size_t>(heads), HW = H * (kN + kV);
+  w.items = (ntok + kBwBlock - 1) / kBwBlock + nseq;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes, 256); return o; };
   w.kv = take(T * HW * 2);
-  w.wT = take(HW * kR * 2);
-  w.ckvT = take(static_cast<size_t>(kR) * Tp * 2);
+  w.dot = take(T * H * kV * 2);
+  w.lsed = take(H * T * 8);
   w.dkv = take(T * HW * 2);
   w.dkvT = take(HW * Tp * 2);
-  w.qp = take(hc * Lp * kBwF * 2);
-  w.qpT = take(hc * Lp * kBwF * 2);
-  w.kp = take(hc * Lp * kBwF * 2);
-  w.kpT = take(hc * Lp * kBwF * 2);
-  w.vh = take(hc * Lp * kV * 2);
-  w.dot = take(hc * Lp * kV * 2);
-  w.dotT = take(hc * Lp * kV * 2);
-  w.dv = take(hc * Lp * 4);
-  w.p = take(hc * Lp * Lp * 2);
-  w.ds = take(hc * Lp * Lp * 2);
-  w.dsT = take(hc * Lp * Lp * 2);
-  w.pT = take(hc * Lp * Lp * 2);
-  w.dqc = take(hc * Lp * kBwF * 4);
-  w.dkc = take(hc * Lp * kBwF * 4);
-  w.dvc = take(hc * Lp * kV * 4);
+  w.wT = take(HW * kR * 2);
+  w.ckvT = take(static_cast<size_t>(kR) * Tp * 2);
+  w.dksp = take(H * T * kS * 4);
+  w.items_kv = take(static_cast<size_t>(w.items) * 8);
+  w.items_q = take(static_cast<size_t>(w.items) * 8);
+  w.count = take(16);
   w.total = off;
   return w;
 }
 
 hipError_t launch_prefill_backward_bf16(int heads, float scale, const void* q, const void* ckv, const void* ks,
-                                        const void* w_kv_b, const void* gate, const int32_t* cu_host, int nseq,
-                                        int64_t ntok, int max_seqlen, const float* out, const float* lse,
-                                        const float* dout, float* dq, float* dckv, float* dks, float* dw,
-                                        float* dgate, void* ws, hipStream_t st) {
-  const BackwardWs W = backward_ws_layout(heads, ntok, max_seqlen);
+                                        const void* w_kv_b, const void* gate, const int32_t* cu, int nseq,
+                                        int64_t ntok, const float* out, const float* lse, const float* dout,
+                                        float* dq, float* dckv, float* dks, float* dw, float* dgate, void* ws,
+                                        hipStream_t st) {
+  const BackwardWs W = backward_ws_layout(heads, ntok, nseq);
   char* base = static_cast<char*>(ws);
   auto b16 = [&](size_t o) { return reinterpret_cast<uint16_t*>(base + o); };
   auto f32 = [&](size_t o) { return reinterpret_cast<float*>(base + o); };
   const int HW = heads * (kN + kV);
   const int64_t Tp = round128(ntok);
   const int T = static_cast<int>(ntok);
+  int2* items_kv = reinterpret_cast<int2*>(base + W.items_kv);
+  int2* items_q = reinterpret_cast<int2*>(base + W.items_q);
+  int32_t* count = reinterpret_cast<int32_t*>(base + W.count);
+  float2* lsed = reinterpret_cast<float2*>(base + W.lsed);
   hipError_t e;
 #define BW_CHECK()                    \
   do {                                \
     e = hipGetLastError();            \
     if (e != hipSuccess) return e;    \
   } while (0)
+  {
+    TimedScope ts_("bw_plan", st);
+    hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, cu, nseq, ntok, items_kv, items_q, count);
+  }
+  BW_CHECK();
   // [K^C | V] of every head: c^KV W_UKV^T-rows
   {
     const GemmSpec p{static_cast<const uint16_t*>(w_kv_b), b16(W.kv), kR, HW, 0, 0, HW};
@@ -214,83 +749,40 @@ hipError_t launch_prefill_backward_bf16(int heads, float scale, const void* q, c
     if (e != hipSuccess) return e;
   }
   {
+    TimedScope ts_("bw_prep", st);
+    const int64_t rows = ntok * heads;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>((rows + 7) / 8)), dim3(256), 0, st, dout, out,
+                       static_cast<const uint16_t*>(gate), lse, heads, ntok, b16(W.dot), lsed, dgate);
+  }
+  BW_CHECK();
+  const unsigned blocks = static_cast<unsigned>(W.items * heads);
+  {
+    TimedScope ts_("bw_dkv", st);
+    hipLaunchKernelGGL(bwd_dkv_kernel, dim3(blocks), dim3(kBwThreads), 0, st, static_cast<const uint16_t*>(q),
+                       b16(W.kv), static_cast<const uint16_t*>(ks), b16(W.dot), lsed, cu, items_kv, count, heads,
+                       ntok, scale, b16(W.dkv), f32(W.dksp));
+  }
+  BW_CHECK();
+  {
+    TimedScope ts_("bw_dq", st);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(blocks), dim3(kBwThreads), 0, st, static_cast<const uint16_t*>(q),
+                       b16(W.kv), static_cast<const uint16_t*>(ks), b16(W.dot), lsed, cu, items_q, count, heads, ntok,
+                       scale, dq);
+  }
+  BW_CHECK();
+  {
+    TimedScope ts_("bw_dks", st);
+    hipLaunchKernelGGL(bwd_dks_kernel, dim3(static_cast<unsigned>((ntok * kS + 255) / 256)), dim3(256), 0, st,
+                       f32(W.dksp), heads, ntok, dks);
+  }
+  BW_CHECK();
+  {
     TimedScope ts_("bw_transpose", st);
     hipLaunchKernelGGL(bw_transpose_kernel, dim3((HW + 63) / 64, kR / 64, 1), dim3(256), 0, st,
                        static_cast<const uint16_t*>(w_kv_b), static_cast<int64_t>(HW), static_cast<int64_t>(HW), kR,
                        int64_t{0}, int64_t{0}, b16(W.wT));
     hipLaunchKernelGGL(bw_transpose_kernel, dim3(static_cast<unsigned>(Tp / 64), kR / 64, 1), dim3(256), 0, st,
                        static_cast<const uint16_t*>(ckv), ntok, Tp, kR, int64_t{0}, int64_t{0}, b16(W.ckvT));
-  }
-  BW_CHECK();
-  hipLaunchKernelGGL(bw_zero_kernel, dim3(static_cast<unsigned>((ntok * kS + 255) / 256)), dim3(256), 0, st, dks,
-                     ntok * kS);
-  BW_CHECK();
-  for (int sidx = 0; sidx < nseq; ++sidx) {
-    const int64_t a = cu_host[sidx];
-    const int L = cu_host[sidx + 1] - cu_host[sidx];
-    if (L <= 0) continue;
-    const int Lp = static_cast<int>(round128(L));
-    const int64_t LL = static_cast<int64_t>(Lp) * Lp;
-    for (int h0 = 0; h0 < heads; h0 += W.hc) {
-      const int hc = std::min(W.hc, heads - h0);
-      {
-        TimedScope ts_("bw_gather", st);
-        hipLaunchKernelGGL(bw_gather_kernel, dim3(Lp, hc), dim3(128), 0, st, static_cast<const uint16_t*>(q),
-                           b16(W.kv), static_cast<const uint16_t*>(ks), static_cast<const uint16_t*>(gate), out, dout,
-                           heads, a, L, Lp, h0, b16(W.qp), b16(W.kp), b16(W.vh), b16(W.dot), f32(W.dv), dgate);
-      }
-      BW_CHECK();
-      {
-        TimedScope ts_("bw_transpose", st);
-        const dim3 g256(Lp / 64, kBwF / 64, hc), g128(Lp / 64, kV / 64, hc);
-        const int64_t s256 = static_cast<int64_t>(Lp) * kBwF, s128 = static_cast<int64_t>(Lp) * kV;
-        hipLaunchKernelGGL(bw_transpose_kernel, g256, dim3(256), 0, st, b16(W.qp), int64_t{Lp}, int64_t{Lp}, kBwF,
-                           s256, s256, b16(W.qpT));
-        hipLaunchKernelGGL(bw_transpose_kernel, g256, dim3(256), 0, st, b16(W.kp), int64_t{Lp}, int64_t{Lp}, kBwF,
-                           s256, s256, b16(W.kpT));
-        hipLaunchKernelGGL(bw_transpose_kernel, g128, dim3(256), 0, st, b16(W.dot), int64_t{Lp}, int64_t{Lp}, kV,
-                           s128, s128, b16(W.dotT));
-      }
-      BW_CHECK();
-      {  // S = Q_h K_h^T with P = causal exp(scale S - lse) in its epilogue: P, P^T (bf16)
-        const GemmSpec ps{b16(W.kp), b16(W.p), kBwF, Lp, static_cast<int64_t>(Lp) * kBwF, LL, Lp};
-        const GemmSoftmaxBwd smp{kGemmEpiP, nullptr, lse, nullptr, nullptr, b16(W.pT), LL, ntok, a, h0, L, scale};
-        e = launch_gemm_bf16(false, b16(W.qp), kBwF, static_cast<int64_t>(Lp) * kBwF, Lp, kBwF, hc, 1, &ps,
-                             "bw_scores", st, kGemmSkipUpper, &smp);
-        if (e != hipSuccess) return e;
-        // dP = dO~_h V_h^T with dS = scale P (dP - D) in its epilogue: dS, dS^T (bf16)
-        const GemmSpec pd{b16(W.vh), b16(W.ds), kV, Lp, static_cast<int64_t>(Lp) * kV, LL, Lp};
-        const GemmSoftmaxBwd sm{kGemmEpiDS, b16(W.p), nullptr, f32(W.dv), b16(W.dsT), nullptr, LL, ntok, a, h0, L,
-                                scale};
-        e = launch_gemm_bf16(false, b16(W.dot), kV, static_cast<int64_t>(Lp) * kV, Lp, kV, hc, 1, &pd, "bw_dp_softmax",
-                             st, kGemmSkipUpper, &sm);
-        if (e != hipSuccess) return e;
-      }
-      {  // dQ = dS K_h, dK = dS^T Q_h, dV = P^T dO~_h (fp32)
-        const GemmSpec pq{b16(W.kpT), f32(W.dqc), Lp, kBwF, static_cast<int64_t>(kBwF) * Lp,
-                          static_cast<int64_t>(Lp) * kBwF, kBwF};
-        e = launch_gemm_bf16(true, b16(W.ds), Lp, LL, Lp, Lp, hc, 1, &pq, "bw_grads", st, kGemmKToRow);
-        if (e != hipSuccess) return e;
-        const GemmSpec pk{b16(W.qpT), f32(W.dkc), Lp, kBwF, static_cast<int64_t>(kBwF) * Lp,
-                          static_cast<int64_t>(Lp) * kBwF, kBwF};
-        e = launch_gemm_bf16(true, b16(W.dsT), Lp, LL, Lp, Lp, hc, 1, &pk, "bw_grads", st, kGemmKFromRow);
-        if (e != hipSuccess) return e;
-        const GemmSpec pv{b16(W.dotT), f32(W.dvc), Lp, kV, static_cast<int64_t>(kV) * Lp,
-                          static_cast<int64_t>(Lp) * kV, kV};
-        e = launch_gemm_bf16(true, b16(W.pT), Lp, LL, Lp, Lp, hc, 1, &pv, "bw_grads", st, kGemmKFromRow);
-        if (e != hipSuccess) return e;
-      }
-      {
-        TimedScope ts_("bw_scatter", st);
-        hipLaunchKernelGGL(bw_scatter_kernel, dim3(L, hc), dim3(128), 0, st, f32(W.dqc), f32(W.dkc), f32(W.dvc),
-                           heads, a, Lp, h0, dq, b16(W.dkv));
-        hipLaunchKernelGGL(bw_dks_kernel, dim3(L), dim3(64), 0, st, f32(W.dkc), hc, a, Lp, dks);
-      }
-      BW_CHECK();
-    }
-  }
-  {
-    TimedScope ts_("bw_transpose", st);
     hipLaunchKernelGGL(bw_transpose_kernel, dim3(static_cast<unsigned>(Tp / 64), (HW + 63) / 64, 1), dim3(256), 0,
                        st, b16(W.dkv), ntok, Tp, HW, int64_t{0}, int64_t{0}, b16(W.dkvT));
   }

@@ -158,15 +158,15 @@ inline LayerWs layer_ws_layout(int heads, int hidden, int q_rank, int64_t ntok, 
   return w;
 }
 
-// Workspace of the bf16 prefill backward: [K^C | V] of every head, the
-// transposed weight and latent, the K^C / V gradients (and their transpose),
-// then one chunk of heads' per-sequence buffers (rows padded to a multiple of
-// 128, Q and K padded to 256 features; Lp x Lp score planes).
+// Workspace of the bf16 prefill backward (all O(T H)): [K^C | V] of every
+// head, dO~ (bf16), {lse log2(e), D} per head and token, [dK^C | dV] (bf16) and
+// its transpose, the transposed weight and latent, the per-head k^S
+// gradients, and the two work-item lists of the attention passes.
 struct BackwardWs {
-  size_t kv, wT, ckvT, dkv, dkvT, qp, qpT, kp, kpT, vh, dot, dotT, dv, p, ds, dsT, pT, dqc, dkc, dvc, total;
-  int hc;   // heads per chunk
+  size_t kv, dot, lsed, dkv, dkvT, wT, ckvT, dksp, items_kv, items_q, count, total;
+  int64_t items;   // capacity of each work-item list: ceil(T / 128) + nseq
 };
-BackwardWs backward_ws_layout(int heads, int64_t ntok, int max_seqlen);
+BackwardWs backward_ws_layout(int heads, int64_t ntok, int nseq);
 
 // QK-norm variant: per-head RMSNorm of the queries over their N + S features,
 // times a per-feature weight shared by the heads (w NULL: ones), the result
@@ -248,10 +248,10 @@ hipError_t launch_layer_bf16(int heads, float scale, int hidden, int q_rank, flo
                              bool init_max_logit, void* ws, hipStream_t st);
 
 hipError_t launch_prefill_backward_bf16(int heads, float scale, const void* q, const void* ckv, const void* ks,
-                                        const void* w_kv_b, const void* gate, const int32_t* cu_host, int nseq,
-                                        int64_t ntok, int max_seqlen, const float* out, const float* lse,
-                                        const float* dout, float* dq, float* dckv, float* dks, float* dw,
-                                        float* dgate, void* ws, hipStream_t st);
+                                        const void* w_kv_b, const void* gate, const int32_t* cu, int nseq,
+                                        int64_t ntok, const float* out, const float* lse, const float* dout,
+                                        float* dq, float* dckv, float* dks, float* dw, float* dgate, void* ws,
+                                        hipStream_t st);
 
 hipError_t launch_absorbed_f32(int heads, int R, int S, int N, int V, float scale,
                                const float* q, const float* cache, int64_t cap, const int32_t* lens,

@@ -181,22 +181,26 @@ def test_linear_norm_layer_and_backward_validation(m):
     assert layer(wsb=16) == m.MLA_ERR_WORKSPACE
     assert m.mla_layer_workspace_size(K3, 7168, 1536, 4096, 1) > 4096 * (1536 + 576 + 12288 + 18432) * 2
     bwd = m.lib.mla_prefill_backward
-    cu = (ctypes.c_int32 * 3)(0, 5, 10)
-    bad = (ctypes.c_int32 * 3)(0, 7, 5)
 
-    def back(cu_=cu, T=10, dq=16, gate=None, dgate=None, wsb=1 << 40):
-        return bwd(ctypes.byref(d), 16, 16, 16, 16, gate, cu_, 2, T, 16, 16, 16, dq, 16, 16, 16, dgate, 16, wsb,
+    def back(cu_=16, nseq=2, T=10, dq=16, gate=None, dgate=None, wsb=1 << 40):
+        return bwd(ctypes.byref(d), 16, 16, 16, 16, gate, cu_, nseq, T, 16, 16, 16, dq, 16, 16, 16, dgate, 16, wsb,
                    None)
-    assert back(T=11) == m.MLA_ERR_INVALID          # cu_seqlens must end at total_tokens
-    assert back(cu_=bad) == m.MLA_ERR_INVALID       # decreasing
     assert back(cu_=None) == m.MLA_ERR_INVALID
+    assert back(cu_=18) == m.MLA_ERR_INVALID        # cu_seqlens (int32) misaligned
+    assert back(nseq=0) == m.MLA_ERR_INVALID        # tokens need a sequence
+    assert back(nseq=-1) == m.MLA_ERR_INVALID
     assert back(dq=None) == m.MLA_ERR_INVALID
     assert back(gate=16, dgate=None) == m.MLA_ERR_INVALID   # a gate needs its gradient buffer
     assert back(wsb=16) == m.MLA_ERR_WORKSPACE
     assert back(T=0) == m.MLA_OK
-    assert bwd(ctypes.byref(d), 16, 16, 16, 16, None, cu, 2, (1 << 20) + 1, 16, 16, 16, 16, 16, 16, 16, None, 16,
-               1 << 40, None) == m.MLA_ERR_UNSUPPORTED
-    assert m.lib.mla_prefill_backward_workspace_size(ctypes.byref(d), 4096, 4096) > 4096 * 4096 * 10
+    assert back(T=(1 << 20) + 1) == m.MLA_ERR_UNSUPPORTED
+    # O(T H) workspace: linear in the token count, independent of the sequence lengths
+    ws = m.lib.mla_prefill_backward_workspace_size
+    w4, w8, w12 = (ws(ctypes.byref(d), t, 1) for t in (4096, 8192, 12288))
+    assert 4096 * 96 * 256 * 2 * 2 < w4 < 4096 * 96 * 2200   # about 2 KB per token and head
+    assert abs((w12 - w8) - (w8 - w4)) < 0.001 * w4       # affine in T (the transposed weight is fixed)
+    assert ws(ctypes.byref(d), 4096, 64) - w4 < 4096
+    assert ws(ctypes.byref(d), 4096, -1) == 0
 
 
 def test_qk_clip_validation(m):
