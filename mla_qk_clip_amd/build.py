@@ -27,6 +27,15 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags. The backward kernels hold their gradient accumulators
+# across a loop next to the score accumulators; with the matrix-core results
+# in architectural VGPRs (and AGPRs left to the register allocator) the loop
+# body avoids most accumulator copies between the two register files.
+EXTRA = {
+    "backward_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -40,7 +49,7 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = (r.stdout + r.stderr).strip()
     # hipcc's host pass does not know the packed-fp32 feature; that warning is harmless

@@ -651,6 +651,30 @@ __global__ void __launch_bounds__(256) bwd_dks_kernel(const float* __restrict__ 
   dks[i] = s;
 }
 
+// out[i] = sum over the split-K partials part[c][i], c < nsplit (n a multiple of 4).
+__global__ void __launch_bounds__(256) bwd_sum_kernel(const float* __restrict__ part, int nsplit, int64_t n,
+                                                      float* __restrict__ out) {
+  const int64_t i = 4 * (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x);
+  if (i >= n) return;
+  float4 s = *reinterpret_cast<const float4*>(part + i);
+  for (int c = 1; c < nsplit; ++c) {
+    const float4 v = *reinterpret_cast<const float4*>(part + c * n + i);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  *reinterpret_cast<float4*>(out + i) = s;
+}
+
+// Split of a long-K GEMM with few 256 x 256 output tiles: enough K chunks
+// (each a multiple of 128) to give about 512 workgroups, at most 16.
+inline int gemm_split(int64_t tiles, int64_t kblocks) {
+  int sp = static_cast<int>(std::min<int64_t>(16, std::max<int64_t>(1, 512 / std::max<int64_t>(tiles, 1))));
+  while (sp > 1 && kblocks % sp) --sp;
+  return sp;
+}
+
 // dst[b][c][r] = r < rvalid ? src[b][r][c] : 0 for r < rp, c < cols (bf16).
 // 64 x 64 tiles through LDS; cols and rp multiples of 4.
 __global__ void __launch_bounds__(256) bw_transpose_kernel(const uint16_t* __restrict__ src, int64_t rvalid,
@@ -708,6 +732,11 @@ BackwardWs backward_ws_layout(int heads, int64_t ntok, int nseq) {
   w.wT = take(HW * kR * 2);
   w.ckvT = take(static_cast<size_t>(kR) * Tp * 2);
   w.dksp = take(H * T * kS * 4);
+  // split-K partials of the two weight products (one at a time)
+  const int64_t tiles_c = (ntok + 255) / 256 * 2, tiles_w = (static_cast<int64_t>(HW) + 255) / 256 * 2;
+  w.split_c = gemm_split(tiles_c, static_cast<int64_t>(HW) / 128);
+  w.split_w = gemm_split(tiles_w, static_cast<int64_t>(Tp) / 128);
+  w.part = take(std::max(w.split_c > 1 ? w.split_c * T * kR * 4 : 0, w.split_w > 1 ? w.split_w * HW * kR * 4 : 0));
   w.items_kv = take(static_cast<size_t>(w.items) * 8);
   w.items_q = take(static_cast<size_t>(w.items) * 8);
   w.count = take(16);
@@ -787,13 +816,30 @@ hipError_t launch_prefill_backward_bf16(int heads, float scale, const void* q, c
                        st, b16(W.dkv), ntok, Tp, HW, int64_t{0}, int64_t{0}, b16(W.dkvT));
   }
   BW_CHECK();
-  {  // dc^KV = dKV W_UKV (through W^T rows) and dW = dKV^T c^KV (fp32)
-    const GemmSpec pc{b16(W.wT), dckv, HW, kR, 0, 0, kR};
-    e = launch_gemm_bf16(true, b16(W.dkv), HW, 0, T, HW, 1, 1, &pc, "bw_weights", st);
+  {  // dc^KV = dKV W_UKV (through W^T rows) and dW = dKV^T c^KV (fp32), split over K into
+     // partials summed afterwards when the outputs have few tiles
+    const int sc = W.split_c, sw = W.split_w;
+    const int64_t kc = HW / sc, kw = Tp / sw;
+    const GemmSpec pc{b16(W.wT), sc > 1 ? f32(W.part) : dckv, HW, kR, kc, ntok * kR, kR};
+    e = launch_gemm_bf16(true, b16(W.dkv), HW, kc, T, static_cast<int>(kc), sc, 1, &pc, "bw_weights", st);
     if (e != hipSuccess) return e;
-    const GemmSpec pw{b16(W.ckvT), dw, Tp, kR, 0, 0, kR};
-    e = launch_gemm_bf16(true, b16(W.dkvT), Tp, 0, HW, static_cast<int>(Tp), 1, 1, &pw, "bw_weights", st);
+    if (sc > 1) {
+      TimedScope ts_("bw_weights", st);
+      const int64_t n = ntok * kR;
+      hipLaunchKernelGGL(bwd_sum_kernel, dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0, st,
+                         f32(W.part), sc, n, dckv);
+      BW_CHECK();
+    }
+    const GemmSpec pw{b16(W.ckvT), sw > 1 ? f32(W.part) : dw, Tp, kR, kw, static_cast<int64_t>(HW) * kR, kR};
+    e = launch_gemm_bf16(true, b16(W.dkvT), Tp, kw, HW, static_cast<int>(kw), sw, 1, &pw, "bw_weights", st);
     if (e != hipSuccess) return e;
+    if (sw > 1) {
+      TimedScope ts_("bw_weights", st);
+      const int64_t n = static_cast<int64_t>(HW) * kR;
+      hipLaunchKernelGGL(bwd_sum_kernel, dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0, st,
+                         f32(W.part), sw, n, dw);
+      BW_CHECK();
+    }
   }
 #undef BW_CHECK
   return hipSuccess;

@@ -161,10 +161,12 @@ inline LayerWs layer_ws_layout(int heads, int hidden, int q_rank, int64_t ntok, 
 // Workspace of the bf16 prefill backward (all O(T H)): [K^C | V] of every
 // head, dO~ (bf16), {lse log2(e), D} per head and token, [dK^C | dV] (bf16) and
 // its transpose, the transposed weight and latent, the per-head k^S
-// gradients, and the two work-item lists of the attention passes.
+// gradients, the two work-item lists of the attention passes, and the
+// split-K partials of the weight products.
 struct BackwardWs {
-  size_t kv, dot, lsed, dkv, dkvT, wT, ckvT, dksp, items_kv, items_q, count, total;
+  size_t kv, dot, lsed, dkv, dkvT, wT, ckvT, dksp, part, items_kv, items_q, count, total;
   int64_t items;   // capacity of each work-item list: ceil(T / 128) + nseq
+  int split_c, split_w;   // K splits of dc^KV and dW
 };
 BackwardWs backward_ws_layout(int heads, int64_t ntok, int nseq);
 

@@ -196,9 +196,10 @@ def test_linear_norm_layer_and_backward_validation(m):
     assert back(T=(1 << 20) + 1) == m.MLA_ERR_UNSUPPORTED
     # O(T H) workspace: linear in the token count, independent of the sequence lengths
     ws = m.lib.mla_prefill_backward_workspace_size
-    w4, w8, w12 = (ws(ctypes.byref(d), t, 1) for t in (4096, 8192, 12288))
-    assert 4096 * 96 * 256 * 2 * 2 < w4 < 4096 * 96 * 2200   # about 2 KB per token and head
-    assert abs((w12 - w8) - (w8 - w4)) < 0.001 * w4       # affine in T (the transposed weight is fixed)
+    for t in (4096, 8192, 65536):
+        # about 2 KB per token and head, plus split-K partials of at most 256 MB
+        assert t * 96 * 1024 < ws(ctypes.byref(d), t, 1) < t * 96 * 2200 + (1 << 28)
+    w4 = ws(ctypes.byref(d), 4096, 1)
     assert ws(ctypes.byref(d), 4096, 64) - w4 < 4096
     assert ws(ctypes.byref(d), 4096, -1) == 0
 
