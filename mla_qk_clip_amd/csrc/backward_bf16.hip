@@ -301,79 +301,53 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const float* __restrict__
 // ---------------------------------------------------------------------------
 __shared__ __align__(1024) char g_bw_lds[2 * kKvStage];
 
-// Score-side products of one tile, shared by both passes: four accumulators
-// (block 0 and 1 of the wide product X = A F^T over 192 features, block 0
-// and 1 of the narrow one Y = B G^T over 128), A and B read as operand rows
-// from LDS (A: the 128-feature region a16 then the 64-feature region a8),
-// F and G held in registers. Issue order: X0, X1, Y0 round-robin over
-// k-steps 0..7, then X0, X1 k-steps 8..11 with Y1 k-steps 0..3, then Y1
-// 4..7, so that block 0 completes first; operand reads run kSW ahead.
-struct ScoreStep {
-  int t, blk, ks;   // t: 0 wide, 1 narrow
+// A tile body is one fixed sequence of matrix-core products ("ops") in four
+// phases, each a scheduling region of its own:
+//   1  score products of block 0: X0 (wide, 12 k-steps) and Y0 (narrow, 8)
+//      alternating, X0's last four alone
+//   2  the same for block 1, while the VALU turns block 0's scores into
+//      bf16 operands (softmax)
+//   3  gradient products of block 0, while the VALU does block 1's softmax
+//   4  gradient products of block 1
+// Each op's LDS operand read is issued kAhead ops earlier in program order
+// (across phase boundaries), and the phases' instruction groups interleave
+// one product with its reads and a share of the VALU work.
+struct TileOp {
+  int kind, blk, ks, cb;   // kind 0: wide score, 1: narrow score, 2 / 3: gradient products
 };
-__host__ __device__ constexpr ScoreStep score_step(int e) {
-  return e < 24   ? ((e % 3) == 2 ? ScoreStep{1, 0, e / 3} : ScoreStep{0, e % 3, e / 3})
-         : e < 36 ? (((e - 24) % 3) == 2 ? ScoreStep{1, 1, (e - 24) / 3} : ScoreStep{0, (e - 24) % 3, 8 + (e - 24) / 3})
-                  : ScoreStep{1, 1, e - 32};
+__host__ __device__ constexpr TileOp score_op(int blk, int r) {
+  return r < 16 ? TileOp{r & 1, blk, r >> 1, 0} : TileOp{0, blk, 8 + (r - 16), 0};
 }
-constexpr int kScoreSteps = 40;
-constexpr int kSW = 6;   // operand reads in flight
+constexpr int kScoreOps = 20;   // per block
+constexpr int kAhead = 4;
 
-__device__ __forceinline__ void score_products(const char* a16, const char* a8, const char* b16, const LaneOff& o,
-                                               const bf16x8 (&f)[12], const bf16x8 (&gv)[8], f32x16 (&x)[2],
-                                               f32x16 (&y)[2]) {
-  auto rd = [&](auto E) -> bf16x8 {
-    constexpr ScoreStep st = score_step(E);
-    if constexpr (st.t == 1) return ld_row16(b16, o, 32 * st.blk, st.ks);
-    else if constexpr (st.ks < 8) return ld_row16(a16, o, 32 * st.blk, st.ks);
-    else return ld_row8(a8, o, 32 * st.blk, st.ks - 8);
-  };
-  static_for<0, 2>([&](auto B) {
-    x[B] = f32x16{};
-    y[B] = f32x16{};
-  });
-  bf16x8 buf[kSW];
-  static_for<0, kSW>([&](auto E) { buf[E] = rd(E); });
-  static_for<0, kScoreSteps>([&](auto E) {
-    constexpr ScoreStep st = score_step(E);
-    const bf16x8 av = buf[E % kSW];
-    if constexpr (E + kSW < kScoreSteps) buf[E % kSW] = rd(std::integral_constant<int, E + kSW>{});
-    if constexpr (st.t == 0) x[st.blk] = mfma32(av, f[st.ks], x[st.blk]);
-    else y[st.blk] = mfma32(av, gv[st.ks], y[st.blk]);
-  });
-}
-
-// Instruction interleave of one tile body (sched groups over the whole
-// block): the score products with their operand reads, then the second
-// half of the softmax VALU work overlapping the last products, then two
-// rounds of gradient products (NG each, operand reads kGW ahead, two
-// transpose reads per product) with the remaining VALU work folded into
-// the first round.
-constexpr int kGW = 3;
-template <int NG, int PRE_READS, int VALU_A, int VALU_B>
-__device__ __forceinline__ void tile_schedule() {
-  __builtin_amdgcn_sched_group_barrier(0x100, kSW, 0);
-  static_for<0, kScoreSteps>([&](auto E) {
+// Instruction groups of one phase: an initial batch of reads, then per
+// product one MFMA, its share of reads and of VALU work.
+template <int NOPS, int FIRST_DS, int DS_PER, int VALU_PER>
+__device__ __forceinline__ void phase_schedule() {
+  if constexpr (FIRST_DS > 0) __builtin_amdgcn_sched_group_barrier(0x100, FIRST_DS, 0);
+  static_for<0, NOPS>([&](auto) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (E + kSW < kScoreSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    if constexpr (E == 30 && PRE_READS > 0) __builtin_amdgcn_sched_group_barrier(0x100, PRE_READS, 0);
-    if constexpr (E >= 34) __builtin_amdgcn_sched_group_barrier(0x002, VALU_A, 0);
+    if constexpr (DS_PER > 0) __builtin_amdgcn_sched_group_barrier(0x100, DS_PER, 0);
+    if constexpr (VALU_PER > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
   });
-  static_for<0, 2>([&](auto R) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kGW + (R == 0 ? PRE_READS : 0), 0);
-    static_for<0, NG>([&](auto M) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if constexpr (M + kGW < NG) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if constexpr (R == 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU_B, 0);
-    });
-  });
+  __builtin_amdgcn_sched_barrier(0);
 }
+
+// dK/dV tile ops: phases 1, 2 score products of blocks 0, 1; phases 3, 4
+// gradient products of blocks 0, 1 (k-step kk of the block, then per kk the
+// four dV column blocks and the six dK column blocks).
+__host__ __device__ constexpr TileOp kv_op(int e) {
+  if (e < 2 * kScoreOps) return score_op(e / kScoreOps, e % kScoreOps);
+  const int blk = (e - 2 * kScoreOps) / 20, r = (e - 2 * kScoreOps) % 20, kk = r / 10, j = r % 10;
+  return j < 4 ? TileOp{2, blk, kk, j} : TileOp{3, blk, kk, j - 4};
+}
+constexpr int kKvOps = 80;
 
 // One query tile for the wave's 32 keys. P is kept where
 // (unsigned)(kd + row) < span for the element's row in the tile: with
 // kd = q0 + 4 g - key and span = max(L - key, 0) that is key <= query < L;
-// tiles with no masked element pass kd = 0, span = 2^31 - 1 (one code path,
-// so the compiler has no common code to hoist out of two variants).
+// tiles with no masked element pass kd = 0, span = 2^31 - 1 (one code path).
 __device__ __forceinline__ void dkv_tile(const char* st, const LaneOff& o, int lane, const bf16x8 (&kf)[12],
                                          const bf16x8 (&vf)[8], f32x16 (&dk)[6], f32x16 (&dv)[4], float c, int kd,
                                          int span) {
@@ -383,49 +357,71 @@ __device__ __forceinline__ void dkv_tile(const char* st, const LaneOff& o, int l
   const char* info = st + 2 * kReg16 + kReg8;
   const int g = lane >> 5;
   f32x16 s[2], dp[2];
-  score_products(qc, qr, od, o, kf, vf, s, dp);
-  // P and dS' = P (dP - D) of both query blocks, as bf16 operands (k-step kk:
-  // elements 8 kk .. 8 kk + 7); {lse log2(e), D} of the rows the lane holds
   bf16x8 pa[2][2], da[2][2];
-  static_for<0, 2>([&](auto QB) {
-    float p[16], d[16];
+  float4 inf[2][8];
+  auto rd = [&](auto E) -> bf16x8 {
+    constexpr TileOp op = kv_op(E);
+    if constexpr (op.kind == 0) {
+      if constexpr (op.ks < 8) return ld_row16(qc, o, 32 * op.blk, op.ks);
+      else return ld_row8(qr, o, 32 * op.blk, op.ks - 8);
+    } else if constexpr (op.kind == 1) {
+      return ld_row16(od, o, 32 * op.blk, op.ks);
+    } else if constexpr (op.kind == 2) {
+      return ld_tr16(od, o, 32 * op.blk + 16 * op.ks, op.cb);
+    } else {
+      if constexpr (op.cb < 4) return ld_tr16(qc, o, 32 * op.blk + 16 * op.ks, op.cb);
+      else return ld_tr8(qr, o, 32 * op.blk + 16 * op.ks, op.cb - 4);
+    }
+  };
+  // {lse log2(e), D} of the 16 rows of block b the lane holds: rows 8 j + 4 g .. +3
+  auto rd_info = [&](auto B) {
     static_for<0, 4>([&](auto J) {
-      const float4* ip = reinterpret_cast<const float4*>(info + 8 * (32 * QB + 8 * J + 4 * g));
-      const float4 xv = ip[0], yv = ip[1];
-      const float l2[4] = {xv.x, xv.z, yv.x, yv.z}, dd[4] = {xv.y, xv.w, yv.y, yv.w};
-      static_for<0, 4>([&](auto E) {
-        constexpr int i = 4 * J + E;
-        constexpr int ci = 32 * QB + arow0(i);
-        float pv = fast_exp2(fmaf(s[QB][i], c, -l2[E]));
-        pv = static_cast<unsigned>(kd + ci) < static_cast<unsigned>(span) ? pv : 0.0f;
-        p[i] = pv;
-        d[i] = pv * (dp[QB][i] - dd[E]);
-      });
+      const float4* ip = reinterpret_cast<const float4*>(info + 8 * (32 * B + 8 * J + 4 * g));
+      inf[B][2 * J] = ip[0];
+      inf[B][2 * J + 1] = ip[1];
     });
-    pa[QB][0] = pack8(p, 0);
-    pa[QB][1] = pack8(p, 1);
-    da[QB][0] = pack8(d, 0);
-    da[QB][1] = pack8(d, 1);
-  });
-  // dV += P^T dO~ and dK += dS'^T Q, query block by query block
-  static_for<0, 2>([&](auto QB) {
-    auto rd = [&](auto M) -> bf16x8 {
-      constexpr int KK = M / 10, j = M % 10, R0 = 32 * QB + 16 * KK;
-      if constexpr (j < 4) return ld_tr16(od, o, R0, j);
-      else if constexpr (j < 8) return ld_tr16(qc, o, R0, j - 4);
-      else return ld_tr8(qr, o, R0, j - 8);
-    };
-    bf16x8 buf[kGW];
-    static_for<0, kGW>([&](auto M) { buf[M] = rd(M); });
-    static_for<0, 20>([&](auto M) {
-      constexpr int KK = M / 10, j = M % 10;
-      const bf16x8 bv = buf[M % kGW];
-      if constexpr (M + kGW < 20) buf[M % kGW] = rd(std::integral_constant<int, M + kGW>{});
-      if constexpr (j < 4) dv[j] = mfma32(pa[QB][KK], bv, dv[j]);
-      else dk[j - 4] = mfma32(da[QB][KK], bv, dk[j - 4]);
+  };
+  // P and dS' = P (dP - D) of block b as bf16 operands (k-step kk: elements 8 kk .. 8 kk + 7)
+  auto softmax = [&](auto B) {
+    float p[16], d[16];
+    static_for<0, 16>([&](auto II) {
+      constexpr int i = II, J = i / 4, E = i % 4;
+      const float4 v = inf[B][2 * J + E / 2];
+      const float l2 = (E & 1) ? v.z : v.x, dd = (E & 1) ? v.w : v.y;
+      constexpr int ci = 32 * B + arow0(i);
+      float pv = fast_exp2(fmaf(s[B][i], c, -l2));
+      pv = static_cast<unsigned>(kd + ci) < static_cast<unsigned>(span) ? pv : 0.0f;
+      p[i] = pv;
+      d[i] = pv * (dp[B][i] - dd);
     });
+    pa[B][0] = pack8(p, 0);
+    pa[B][1] = pack8(p, 1);
+    da[B][0] = pack8(d, 0);
+    da[B][1] = pack8(d, 1);
+  };
+  static_for<0, 2>([&](auto B) {
+    s[B] = f32x16{};
+    dp[B] = f32x16{};
   });
-  tile_schedule<20, 8, 16, 6>();
+  bf16x8 buf[kAhead];
+  static_for<0, kAhead>([&](auto E) { buf[E] = rd(E); });
+  static_for<0, kKvOps>([&](auto E) {
+    constexpr TileOp op = kv_op(E);
+    if constexpr (E == kScoreOps) phase_schedule<kScoreOps, kAhead, 1, 0>();
+    if constexpr (E == 2 * kScoreOps) phase_schedule<kScoreOps, 8, 1, 7>();
+    if constexpr (E == 3 * kScoreOps) phase_schedule<20, 8, 2, 7>();
+    if constexpr (E == kScoreOps) rd_info(std::integral_constant<int, 0>{});
+    if constexpr (E == 2 * kScoreOps) rd_info(std::integral_constant<int, 1>{});
+    const bf16x8 x = buf[E % kAhead];
+    if constexpr (E + kAhead < kKvOps) buf[E % kAhead] = rd(std::integral_constant<int, E + kAhead>{});
+    if constexpr (op.kind == 0) s[op.blk] = mfma32(x, kf[op.ks], s[op.blk]);
+    else if constexpr (op.kind == 1) dp[op.blk] = mfma32(x, vf[op.ks], dp[op.blk]);
+    else if constexpr (op.kind == 2) dv[op.cb] = mfma32(pa[op.blk][op.ks], x, dv[op.cb]);
+    else dk[op.cb] = mfma32(da[op.blk][op.ks], x, dk[op.cb]);
+    if constexpr (E == 2 * kScoreOps - 1) softmax(std::integral_constant<int, 0>{});
+    if constexpr (E == 3 * kScoreOps - 1) softmax(std::integral_constant<int, 1>{});
+  });
+  phase_schedule<20, 0, 2, 0>();
 }
 
 __global__ void __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dkv_kernel(
@@ -521,6 +517,15 @@ __global__ void __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu
 // ---------------------------------------------------------------------------
 // dQ pass. Block x = item * heads + head.
 // ---------------------------------------------------------------------------
+// dQ tile ops: phases 1, 2 score products of key blocks 0, 1; phases 3, 4
+// dQ products of key blocks 0, 1 (k-step kk, then the six column blocks).
+__host__ __device__ constexpr TileOp q_op(int e) {
+  if (e < 2 * kScoreOps) return score_op(e / kScoreOps, e % kScoreOps);
+  const int blk = (e - 2 * kScoreOps) / 12, r = (e - 2 * kScoreOps) % 12;
+  return TileOp{3, blk, r / 6, r % 6};
+}
+constexpr int kQOps = 64;
+
 // One key tile for the wave's 32 queries (this lane's lse log2(e) l2 and
 // D dd). P is kept where the element's row (key) in the tile is <= m: with
 // m = query - k0 - 4 g that is key <= query; tiles with no masked element
@@ -531,37 +536,51 @@ __device__ __forceinline__ void dq_tile(const char* st, const LaneOff& o, const 
   const char* kr = st + kReg16;
   const char* vt = st + kReg16 + kReg8;
   f32x16 s[2], dp[2];
-  score_products(kc, kr, vt, o, qf, of, s, dp);
   bf16x8 da[2][2];
-  static_for<0, 2>([&](auto KB) {
+  auto rd = [&](auto E) -> bf16x8 {
+    constexpr TileOp op = q_op(E);
+    if constexpr (op.kind == 0) {
+      if constexpr (op.ks < 8) return ld_row16(kc, o, 32 * op.blk, op.ks);
+      else return ld_row8(kr, o, 32 * op.blk, op.ks - 8);
+    } else if constexpr (op.kind == 1) {
+      return ld_row16(vt, o, 32 * op.blk, op.ks);
+    } else {
+      if constexpr (op.cb < 4) return ld_tr16(kc, o, 32 * op.blk + 16 * op.ks, op.cb);
+      else return ld_tr8(kr, o, 32 * op.blk + 16 * op.ks, op.cb - 4);
+    }
+  };
+  auto softmax = [&](auto B) {
     float d[16];
     static_for<0, 16>([&](auto II) {
-      constexpr int I = II;
-      constexpr int ci = 32 * KB + arow0(I);
-      float pv = fast_exp2(fmaf(s[KB][I], c, -l2));
+      constexpr int i = II;
+      constexpr int ci = 32 * B + arow0(i);
+      float pv = fast_exp2(fmaf(s[B][i], c, -l2));
       pv = ci <= m ? pv : 0.0f;
-      d[I] = pv * (dp[KB][I] - dd);
+      d[i] = pv * (dp[B][i] - dd);
     });
-    da[KB][0] = pack8(d, 0);
-    da[KB][1] = pack8(d, 1);
+    da[B][0] = pack8(d, 0);
+    da[B][1] = pack8(d, 1);
+  };
+  static_for<0, 2>([&](auto B) {
+    s[B] = f32x16{};
+    dp[B] = f32x16{};
   });
-  // dQ += dS' K, key block by key block
-  static_for<0, 2>([&](auto KB) {
-    auto rd = [&](auto M) -> bf16x8 {
-      constexpr int KK = M / 6, j = M % 6, R0 = 32 * KB + 16 * KK;
-      if constexpr (j < 4) return ld_tr16(kc, o, R0, j);
-      else return ld_tr8(kr, o, R0, j - 4);
-    };
-    bf16x8 buf[kGW];
-    static_for<0, kGW>([&](auto M) { buf[M] = rd(M); });
-    static_for<0, 12>([&](auto M) {
-      constexpr int KK = M / 6, j = M % 6;
-      const bf16x8 bv = buf[M % kGW];
-      if constexpr (M + kGW < 12) buf[M % kGW] = rd(std::integral_constant<int, M + kGW>{});
-      dq[j] = mfma32(da[KB][KK], bv, dq[j]);
-    });
+  bf16x8 buf[kAhead];
+  static_for<0, kAhead>([&](auto E) { buf[E] = rd(E); });
+  static_for<0, kQOps>([&](auto E) {
+    constexpr TileOp op = q_op(E);
+    if constexpr (E == kScoreOps) phase_schedule<kScoreOps, kAhead, 1, 0>();
+    if constexpr (E == 2 * kScoreOps) phase_schedule<kScoreOps, 0, 1, 5>();
+    if constexpr (E == 2 * kScoreOps + 12) phase_schedule<12, 0, 2, 7>();
+    const bf16x8 x = buf[E % kAhead];
+    if constexpr (E + kAhead < kQOps) buf[E % kAhead] = rd(std::integral_constant<int, E + kAhead>{});
+    if constexpr (op.kind == 0) s[op.blk] = mfma32(x, qf[op.ks], s[op.blk]);
+    else if constexpr (op.kind == 1) dp[op.blk] = mfma32(x, of[op.ks], dp[op.blk]);
+    else dq[op.cb] = mfma32(da[op.blk][op.ks], x, dq[op.cb]);
+    if constexpr (E == 2 * kScoreOps - 1) softmax(std::integral_constant<int, 0>{});
+    if constexpr (E == 2 * kScoreOps + 11) softmax(std::integral_constant<int, 1>{});
   });
-  tile_schedule<12, 0, 14, 7>();
+  phase_schedule<12, 0, 2, 0>();
 }
 
 __global__ void __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) bwd_dq_kernel(
