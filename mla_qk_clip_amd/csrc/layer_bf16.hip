@@ -50,53 +50,30 @@ struct GemmArgs {
   int64_t lda, sa;   // row stride and batch stride (elements) of A
   int m, k;
   int nprob, mtiles, ntiles;
-  int kmode;   // kGemmFull, or a causal mode (see mla_internal.h)
   GemmProblem p[kGemmMaxProblems];
-  GemmSoftmaxBwd sm;   // softmax epilogues (kEpi 2 and 3)
 };
 
 // blockIdx.y is the batch index (a separate A, B and C per batch entry).
-// Epilogue kEpi: 0 bf16 C, 1 fp32 C, 2 and 3 the softmax epilogues of a
-// causal score plane (see GemmSoftmaxBwd).
-template <int kEpi>
+// kOutF32: fp32 C, else bf16.
+template <bool kOutF32>
 __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
-  constexpr bool kOutF32 = kEpi == 1;
   __shared__ uint4 As0[kGmUnits], As1[kGmUnits];
   __shared__ uint4 Bs0[kGmUnits], Bs1[kGmUnits];
 
-  int mt, nt;
-  if (args.kmode == kGemmFull) {
-    // items are dealt to the XCDs in contiguous ranges (block b runs on XCD b % 8)
-    const int total = args.mtiles * args.ntiles;
-    const int per_xcd = (total + 7) >> 3;
-    const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    if (item >= total) return;
-    // groups of 8 row tiles x all column tiles, row tile fastest inside a group:
-    // an XCD's 32 concurrent workgroups cover 8 row tiles x 4 column tiles
-    constexpr int kGroupM = 8;
-    const int group = item / (kGroupM * args.ntiles);
-    const int first_m = group * kGroupM;
-    const int gm = min(args.mtiles - first_m, kGroupM);
-    const int in_group = item - group * kGroupM * args.ntiles;
-    mt = first_m + in_group % gm;
-    nt = in_group / gm;
-  } else if (args.kmode == kGemmSkipUpper) {
-    // only the tiles on or below the diagonal (square tile grid), in turn over the XCDs
-    const int item = blockIdx.x;
-    if (item >= args.mtiles * (args.mtiles + 1) / 2) return;
-    mt = static_cast<int>((sqrtf(8.0f * item + 1.0f) - 1.0f) * 0.5f);
-    while ((mt + 1) * (mt + 2) / 2 <= item) ++mt;
-    while (mt * (mt + 1) / 2 > item) --mt;
-    nt = item - mt * (mt + 1) / 2;
-  } else {
-    // causal K ranges: longest tiles first (row tiles in order of decreasing K
-    // range), dealt in turn over the XCDs
-    const int item = blockIdx.x;
-    if (item >= args.mtiles * args.ntiles) return;
-    const int rank = item / args.ntiles;
-    nt = item - rank * args.ntiles;
-    mt = args.kmode == kGemmKToRow ? args.mtiles - 1 - rank : rank;
-  }
+  // items are dealt to the XCDs in contiguous ranges (block b runs on XCD b % 8)
+  const int total = args.mtiles * args.ntiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (item >= total) return;
+  // groups of 8 row tiles x all column tiles, row tile fastest inside a group:
+  // an XCD's 32 concurrent workgroups cover 8 row tiles x 4 column tiles
+  constexpr int kGroupM = 8;
+  const int group = item / (kGroupM * args.ntiles);
+  const int first_m = group * kGroupM;
+  const int gm = min(args.mtiles - first_m, kGroupM);
+  const int in_group = item - group * kGroupM * args.ntiles;
+  const int mt = first_m + in_group % gm;
+  const int nt = in_group / gm;
   // this tile's problem (selected field by field: indexing the argument array
   // would copy it to private memory)
   const bool p1 = args.nprob > 1 && nt >= args.p[1].tile0;
@@ -113,10 +90,6 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
                       p2 ? args.p[2].tile0 : p1 ? args.p[1].tile0 : args.p[0].tile0};
   const uint16_t* a_base = args.a + bz * args.sa;
   const int m0 = mt * kGmT, n0 = (nt - P.tile0) * kGmT;
-  // K range of this tile (a multiple of 128 long in every mode)
-  const int kbeg = args.kmode == kGemmKFromRow ? m0 : 0;
-  const int kend = args.kmode == kGemmKToRow ? min(args.k, m0 + kGmT) : args.k;
-  const uint32_t kbyte = static_cast<uint32_t>(kbeg) * 2;
   const int rows_a = min(kGmT, args.m - m0), rows_b = min(kGmT, P.n - n0);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -139,8 +112,8 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
   auto issue = [&](uint4* ad, uint4* bd, int st) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      dma16_buf(rs_a, voff_a[q], kbyte + 128 * st, ad + 64 * (4 * wave + q));
-      dma16_buf(rs_b, voff_b[q], kbyte + 128 * st, bd + 64 * (4 * wave + q));
+      dma16_buf(rs_a, voff_a[q], 128 * st, ad + 64 * (4 * wave + q));
+      dma16_buf(rs_b, voff_b[q], 128 * st, bd + 64 * (4 * wave + q));
     }
   };
   // Fragment reads: rows r0 .. r0+31 (r0 a multiple of 32), k-units 2 kh + g.
@@ -173,7 +146,7 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
           for (int kb = 0; kb < 2; ++kb) acc[2 * fb + kb] = mfma32(bf[fb], af[kb], acc[2 * fb + kb]);
       }
     };
-    const int nsteps = (kend - kbeg) / 64;
+    const int nsteps = args.k / 64;
     issue(As0, Bs0, 0);
     wait_vmcnt<0>();
     __syncthreads();
@@ -201,54 +174,12 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
     // ---- store: lane = output row l32 of the row block; element i of a tile is
     // column 8 (i / 4) + 4 g + i % 4 of the column block. Lanes l and l + 32 swap
     // runs so that each holds 8 consecutive columns (two 16-byte stores per tile).
-    // softmax epilogues of a causal score plane (kEpi 3: P from S; kEpi 2: dS
-    // from dP): the transposed plane goes through a wave-private 8 KB of LDS
-    // (the operand slots are free once every wave is past the k loop)
-    constexpr bool kSm = kEpi >= 2;
-    uint16_t* tst = nullptr;
-    if constexpr (kSm) {
-      __syncthreads();
-      uint4* slot = wave < 2 ? As0 : wave < 4 ? As1 : wave < 6 ? Bs0 : Bs1;
-      tst = reinterpret_cast<uint16_t*>(slot + (wave & 1) * 1024);   // [128 columns][32 rows] bf16
-    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int m = m0 + 64 * wm + 32 * kb + l32;
-      float lse2 = 0.0f, dv = 0.0f;
-      if constexpr (kEpi == 3) {
-        if (m < args.sm.L) lse2 = args.sm.lse[(args.sm.h0 + bz) * args.sm.ntok + args.sm.a + m] * kLog2e;
-      }
-      if constexpr (kEpi == 2) {
-        if (m < args.sm.L) dv = args.sm.D[bz * args.m + m];
-      }
 #pragma unroll
       for (int fb = 0; fb < 4; ++fb) {
-        f32x16 a = acc[2 * fb + kb];
-        if constexpr (kSm) {
-          const int nb = n0 + 128 * wn + 32 * fb + 4 * g;
-          const float sl2 = args.sm.scale * kLog2e;
-          const uint16_t* prow = args.sm.P + bz * args.sm.plane + static_cast<int64_t>(m) * args.m;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            uint2 pw = make_uint2(0, 0);
-            if constexpr (kEpi == 2) {
-              if (m < args.m) pw = *reinterpret_cast<const uint2*>(prow + nb + 8 * r);
-            }
-            const float pe[4] = {bf16lo(pw.x), bf16hi(pw.x), bf16lo(pw.y), bf16hi(pw.y)};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int n = nb + 8 * r + e;
-              float v;
-              if constexpr (kEpi == 3) {   // P = exp(scale S - lse) on and below the diagonal of the first L rows
-                v = (m < args.sm.L && n <= m) ? fast_exp2(a[4 * r + e] * sl2 - lse2) : 0.0f;
-              } else {                     // dS = scale P (dP - D)
-                v = args.sm.scale * pe[e] * (a[4 * r + e] - dv);
-              }
-              a[4 * r + e] = v;
-              tst[(32 * fb + 8 * r + 4 * g + e) * 32 + l32] = f32_to_bf16(v);
-            }
-          }
-        }
+        const f32x16 a = acc[2 * fb + kb];
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {   // runs 2 pr (kept by g = 0) and 2 pr + 1 (kept by g = 1)
           const int n = n0 + 128 * wn + 32 * fb + 16 * pr + 8 * g;
@@ -282,22 +213,7 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
           }
         }
       }
-      if constexpr (kSm) {
-        // rows of the transposed plane: 32 consecutive t (64 bytes) per column of this row block
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        const int t0 = m0 + 64 * wm + 32 * kb;
-        uint16_t* tout = kEpi == 2 ? args.sm.dST : args.sm.PT;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c = lane + 64 * j, cl = c >> 2, part = c & 3;
-          const int n = n0 + 128 * wn + cl, t = t0 + 8 * part;
-          const uint4 vt = *reinterpret_cast<const uint4*>(tst + cl * 32 + 8 * part);
-          if (n < args.m && t < args.m) stg16(tout + bz * args.sm.plane + static_cast<int64_t>(n) * args.m + t, vt);
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-      }
+
     }
   };
   if (wave < 4) run(std::integral_constant<int, 0>{});
@@ -355,10 +271,8 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(NormJob j0, NormJob j1, in
 }  // namespace
 
 hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_t sa, int m, int k, int batch,
-                            int nprob, const GemmSpec* p, const char* name, hipStream_t st, int kmode,
-                            const GemmSoftmaxBwd* sm) {
+                            int nprob, const GemmSpec* p, const char* name, hipStream_t st) {
   GemmArgs args{};
-  args.kmode = kmode;
   args.a = a;
   args.lda = lda;
   args.sa = sa;
@@ -372,25 +286,15 @@ hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_
     tiles += (p[i].n + kGmT - 1) / kGmT;
   }
   args.ntiles = tiles;
-  const int total = kmode == kGemmSkipUpper ? args.mtiles * (args.mtiles + 1) / 2 : args.mtiles * tiles;
+  const int total = args.mtiles * tiles;
   if (total == 0 || batch == 0) return hipSuccess;
-  if (kmode == kGemmSkipUpper && (tiles != args.mtiles || nprob != 1)) return hipErrorInvalidValue;
   const dim3 grid(((total + 7) / 8) * 8, batch);
   TimedScope ts_(name, st);
-  if (sm) {
-    args.sm = *sm;
-    if (sm->mode == kGemmEpiP) hipLaunchKernelGGL(gemm_nt_kernel<3>, grid, dim3(kGmThreads), 0, st, args);
-    else hipLaunchKernelGGL(gemm_nt_kernel<2>, grid, dim3(kGmThreads), 0, st, args);
-  } else if (out_f32) {
-    hipLaunchKernelGGL(gemm_nt_kernel<1>, grid, dim3(kGmThreads), 0, st, args);
-  } else {
-    hipLaunchKernelGGL(gemm_nt_kernel<0>, grid, dim3(kGmThreads), 0, st, args);
-  }
+  if (out_f32) hipLaunchKernelGGL(gemm_nt_kernel<true>, grid, dim3(kGmThreads), 0, st, args);
+  else hipLaunchKernelGGL(gemm_nt_kernel<false>, grid, dim3(kGmThreads), 0, st, args);
   return hipGetLastError();
 }
 
-namespace {
-}  // namespace
 
 hipError_t launch_linear_bf16(const void* x, int64_t m, int k, const void* w, int n, void* y, hipStream_t st) {
   const GemmSpec p{static_cast<const uint16_t*>(w), y, k, n, 0, 0, n};

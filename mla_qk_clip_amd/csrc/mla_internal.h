@@ -214,32 +214,8 @@ struct GemmSpec {
   int64_t ldb, ldc, sb, sc;
   int n;
 };
-// K ranges for causal products over square row x K planes (m0 = first row of
-// a 256-row tile; K, M multiples of 128):
-//   kGemmSkipUpper  tiles whose columns all lie above the diagonal are skipped
-//   kGemmKToRow     each tile sums k < min(K, m0 + 256)   (C[t] = sum_{s <= t})
-//   kGemmKFromRow   each tile sums k >= m0                (C[s] = sum_{t >= s})
-constexpr int kGemmFull = 0, kGemmSkipUpper = 1, kGemmKToRow = 2, kGemmKFromRow = 3;
-// Softmax epilogues over square causal planes (M = N = the plane width; bf16 C):
-//   kGemmEpiP   on C = S (raw scores): P = exp(scale S - lse[h][a + t]) for row
-//               t < L and column s <= t, else 0; C receives P, PT its transpose
-//   kGemmEpiDS  on C = dP: dS = scale P (dP - D[t]) with P read from the plane
-//               written by kGemmEpiP; C receives dS, dST its transpose
-constexpr int kGemmEpiP = 3, kGemmEpiDS = 2;
-struct GemmSoftmaxBwd {
-  int mode;              // kGemmEpiP or kGemmEpiDS
-  const uint16_t* P;     // [batch][M][M] bf16 (kGemmEpiDS)
-  const float* lse;      // [H][ntok] natural-log LSE of the scaled scores (kGemmEpiP)
-  const float* D;        // [batch][M] rowsum(dO . o) (kGemmEpiDS)
-  uint16_t* dST;         // [batch][M][M] (kGemmEpiDS)
-  uint16_t* PT;          // [batch][M][M] (kGemmEpiP)
-  int64_t plane, ntok, a, h0;   // plane stride, tokens, first token of the sequence, first head of the batch
-  int L;
-  float scale;
-};
 hipError_t launch_gemm_bf16(bool out_f32, const uint16_t* a, int64_t lda, int64_t sa, int m, int k, int batch,
-                            int nprob, const GemmSpec* p, const char* name, hipStream_t st, int kmode = kGemmFull,
-                            const GemmSoftmaxBwd* sm = nullptr);
+                            int nprob, const GemmSpec* p, const char* name, hipStream_t st);
 hipError_t launch_linear_bf16(const void* x, int64_t m, int k, const void* w, int n, void* y, hipStream_t st);
 hipError_t launch_rms_norm_bf16(const void* x, int64_t rows, int n, const void* w, float eps, void* y,
                                 hipStream_t st);
