@@ -107,6 +107,8 @@ DECODE_SOURCES = ("mla_qk_clip_amd/csrc/absorbed_bf16.hip", "mla_qk_clip_amd/csr
                   "mla_qk_clip_amd/csrc/mla_internal.h")
 EXPANDED_SOURCES = ("mla_qk_clip_amd/csrc/expanded_bf16.hip", "mla_qk_clip_amd/csrc/mla_common.h",
                     "mla_qk_clip_amd/csrc/mla_internal.h")
+BACKWARD_SOURCES = ("mla_qk_clip_amd/csrc/backward_bf16.hip", "mla_qk_clip_amd/csrc/mla_common.h",
+                    "mla_qk_clip_amd/csrc/mla_internal.h")
 LAYER_SOURCES = ("mla_qk_clip_amd/csrc/layer_bf16.hip", "mla_qk_clip_amd/csrc/mla_common.h",
                  "mla_qk_clip_amd/csrc/mla_internal.h")
 
@@ -229,11 +231,22 @@ def backward_leg(m, dims, p, q, ckv, ks, w_kv_b, gate, cu, steps: int = 3):
     # dc^KV and dW (each 2 T H 256 R)
     attn = 2.0 * H * pairs * (192 + 128 + 192 + 192 + 128)
     lat = 3 * 2.0 * T * H * 256 * 512
+    # the two attention passes: dK/dV recomputes S and dP (640 MACs per causal pair), dQ recomputes them
+    # again (512); matrix-core busy fraction and HBM bytes from the committed counter tables
+    passes = {}
+    for k, macs in (("bwd_dkv", 640), ("bwd_dq", 512)):
+        kms = kern.get("bw_dkv" if k == "bwd_dkv" else "bw_dq")
+        if kms:
+            tf = 2.0 * H * pairs * macs / (kms * 1e-3) / 1e12
+            traffic = recorded_traffic(k, BACKWARD_SOURCES)
+            passes[k] = {"ms": round(kms, 4), "tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "mfma_busy": recorded_mfma_busy(k, BACKWARD_SOURCES),
+                         "traffic_gb": None if traffic is None else round(traffic / 1e9, 3)}
     return {"workload": "backward of the Kimi K3 prefill, B=1 T=4096 H=96 (bf16 operands, fp32 gradients)",
             "ms": round(ms, 4), "gflop_algorithmic": round((attn + lat) / 1e9, 1),
             "tflops": round((attn + lat) / (ms * 1e-3) / 1e12, 2),
             "frac_mfma_peak": round((attn + lat) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "kernels_ms_per_call": {k: round(v, 4) for k, v in kern.items()}}
+            "kernels_ms_per_call": {k: round(v, 4) for k, v in kern.items()}, "passes": passes}
 
 
 def layer_leg(m, dims, steps: int = 5):
