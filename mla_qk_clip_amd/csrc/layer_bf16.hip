@@ -116,6 +116,12 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
       dma16_buf(rs_b, voff_b[q], 128 * st, bd + 64 * (4 * wave + q));
     }
   };
+  // copy c (0..7) of a step: A block c / 2 or B block c / 2
+  auto issue_one = [&](uint4* ad, uint4* bd, int st, int c) {
+    const int q = c >> 1;
+    if (c & 1) dma16_buf(rs_b, voff_b[q], 128 * st, bd + 64 * (4 * wave + q));
+    else dma16_buf(rs_a, voff_a[q], 128 * st, ad + 64 * (4 * wave + q));
+  };
   // Fragment reads: rows r0 .. r0+31 (r0 a multiple of 32), k-units 2 kh + g.
   // Unit 64 (r/8) + 8 (r%8) + (c ^ (r/2)%8) splits into the wave-uniform
   // 8 r0 and a per-lane part that depends on kh only.
@@ -132,7 +138,9 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
     f32x16 acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
-    auto step = [&](const uint4* as, const uint4* bs) {
+    // one k-step; copy c of the next step goes out after MFMA 4 c + 1 + 2 wn
+    // (the two waves of a SIMD alternate their copy stalls)
+    auto step = [&](const uint4* as, const uint4* bs, auto&& cp) {
 #pragma unroll
       for (int kh = 0; kh < 4; ++kh) {
         bf16x8 af[2], bf[4];
@@ -143,33 +151,37 @@ __global__ void __launch_bounds__(kGmThreads) gemm_nt_kernel(GemmArgs args) {
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) acc[2 * fb + kb] = mfma32(bf[fb], af[kb], acc[2 * fb + kb]);
+          for (int kb = 0; kb < 2; ++kb) {
+            acc[2 * fb + kb] = mfma32(bf[fb], af[kb], acc[2 * fb + kb]);
+            const int m = 8 * kh + 2 * fb + kb;
+            if (m < 16 && (m & 1) == wn) {   // copies in the first half of the step: they land before its end
+              __builtin_amdgcn_sched_barrier(0);
+              cp(m >> 1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
       }
     };
+    auto none = [](int) {};
     const int nsteps = args.k / 64;
     issue(As0, Bs0, 0);
     wait_vmcnt<0>();
     __syncthreads();
     int st = 0;
     for (; st + 2 < nsteps; st += 2) {   // steps st (slot 0) and st + 1 (slot 1), each copying the next
-      issue(As1, Bs1, st + 1);          // slot 1 was last read by step st - 1
-      __builtin_amdgcn_sched_barrier(0);
-      step(As0, Bs0);
+      // (slot 1 was last read by step st - 1)
+      step(As0, Bs0, [&](int c) { issue_one(As1, Bs1, st + 1, c); });
       wait_vmcnt<0>();
       __syncthreads();
-      issue(As0, Bs0, st + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      step(As1, Bs1);
+      step(As1, Bs1, [&](int c) { issue_one(As0, Bs0, st + 2, c); });
       wait_vmcnt<0>();
       __syncthreads();
     }
     // the last two steps (K is a multiple of 128)
-    issue(As1, Bs1, st + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    step(As0, Bs0);
+    step(As0, Bs0, [&](int c) { issue_one(As1, Bs1, st + 1, c); });
     wait_vmcnt<0>();
     __syncthreads();
-    step(As1, Bs1);
+    step(As1, Bs1, none);
 
     // ---- store: lane = output row l32 of the row block; element i of a tile is
     // column 8 (i / 4) + 4 g + i % 4 of the column block. Lanes l and l + 32 swap

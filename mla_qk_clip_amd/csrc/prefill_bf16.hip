@@ -738,18 +738,28 @@ __global__ void __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_
     __syncthreads();
   };
 
-  // ---- prologue: K(0), K(1), V(0) in LDS; S(0) ----
+  // ---- prologue: K(0), V(0), K(1) into LDS; S(0) as soon as the queries and
+  // K(0) have landed (the later copies, issued after them, may still be in
+  // flight), then V(0) and K(1) before the first step ----
   dma_k(K0, 0);
   dma_v(V0, 0);
-  if (nkt > 1) dma_k(K1, 1);
-  wait_vmcnt<0>();
-  __syncthreads();
+  if (nkt > 1) {
+    dma_k(K1, 1);
+    wait_vmcnt<kVtCopies + kKcCopies + kKsCopies>();
+  } else {
+    wait_vmcnt<kVtCopies>();
+  }
+  // a bare barrier: __syncthreads' fence would wait for every copy in flight
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   if (nkt_w > 0) {
     qk(K0, sA);
     if (nkt_w == 1) mask_tile(0, sA);
     mx_cur = tile_max(sA);
   }
-  __syncthreads();   // K0 is refilled by the first step
+  wait_vmcnt<0>();
+  __syncthreads();   // V(0) and K(1) are in; K0 is refilled by the first step
 
   for (int j = 0; j < nkt; j += 2) {
     step(std::integral_constant<int, 0>{}, j);
