@@ -344,13 +344,20 @@ __host__ __device__ constexpr TileOp kv_op(int e) {
 }
 constexpr int kKvOps = 80;
 
-// One query tile for the wave's 32 keys. P is kept where
-// (unsigned)(kd + row) < span for the element's row in the tile: with
-// kd = q0 + 4 g - key and span = max(L - key, 0) that is key <= query < L;
-// tiles with no masked element pass kd = 0, span = 2^31 - 1 (one code path).
-__device__ __forceinline__ void dkv_tile(const char* st, const LaneOff& o, int lane, const bf16x8 (&kf)[12],
-                                         const bf16x8 (&vf)[8], f32x16 (&dk)[6], f32x16 (&dv)[4], float c, int kd,
-                                         int span) {
+// One query tile for the wave's 32 keys. MASK: P is kept where
+// (unsigned)(kd + row) < span for the element's row in the tile; with
+// kd = q0 + 4 g - key and span = max(L - key, 0) that is key <= query < L.
+// Without MASK every element is kept (the tile lies past the block's keys
+// and before L). The leading asm names the variant in the assembly listing.
+template <bool MASK>
+__device__ __forceinline__ void dkv_tile(const char* st, int lane, const bf16x8 (&kf)[12], const bf16x8 (&vf)[8],
+                                         f32x16 (&dk)[6], f32x16 (&dv)[4], float c, int kd, int span) {
+  asm volatile("; dK/dV tile, masked: %0" ::"n"(MASK ? 1 : 0));
+  // the lane's LDS offsets, formed here from an opaque copy of the lane index:
+  // held across the tile loop they were spilled and reloaded behind waits
+  int lane_o = lane;
+  asm volatile("" : "+v"(lane_o));
+  const LaneOff o = lane_offsets(lane_o);
   const char* qc = st;
   const char* qr = st + kReg16;
   const char* od = st + kReg16 + kReg8;
@@ -390,7 +397,7 @@ __device__ __forceinline__ void dkv_tile(const char* st, const LaneOff& o, int l
       const float l2 = (E & 1) ? v.z : v.x, dd = (E & 1) ? v.w : v.y;
       constexpr int ci = 32 * B + arow0(i);
       float pv = fast_exp2(fmaf(s[B][i], c, -l2));
-      pv = static_cast<unsigned>(kd + ci) < static_cast<unsigned>(span) ? pv : 0.0f;
+      if constexpr (MASK) pv = static_cast<unsigned>(kd + ci) < static_cast<unsigned>(span) ? pv : 0.0f;
       p[i] = pv;
       d[i] = pv * (dp[B][i] - dd);
     });
@@ -441,7 +448,6 @@ __global__ void __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu
   const int kb0 = kBwBlock * it.y, kw0 = kb0 + 32 * w;
   const int key = kw0 + l32;   // this lane's key (sequence-relative)
   const int span = max(L - key, 0);
-  const LaneOff o = lane_offsets(lane);
   const int64_t HQ = static_cast<int64_t>(heads) * kD * 2, HO = static_cast<int64_t>(heads) * kV * 2;
 
   const int nq = (L + kBwTile - 1) / kBwTile;
@@ -483,18 +489,31 @@ __global__ void __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu
   const float c = scale * kLog2e;
   wait_vmcnt<0>();
   bw_barrier();
-  for (int j = 0; j < ntiles; ++j) {
+  // query tile j: the next tile's copies, the tile, its landing and the barrier
+  auto run_tile = [&](int j, auto M) {
+    constexpr bool kMask = decltype(M)::value;
     const int stage = j & 1;
     if (j + 1 < ntiles) issue(j + 1, stage ^ 1);
     const int q0 = kBwTile * (nq - 1 - j);
     const char* st = g_bw_lds + stage * kKvStage;
-    if (q0 + kBwTile - 1 >= kw0) {   // else every query of the tile precedes the wave's keys
-      const bool masked = q0 < kw0 + 31 || q0 + kBwTile > L;
-      dkv_tile(st, o, lane, kf, vf, dk, dv, c, masked ? q0 + 4 * g - key : 0, masked ? span : 0x7fffffff);
+    if constexpr (kMask) {
+      if (q0 + kBwTile - 1 >= kw0)   // else every query of the tile precedes the wave's keys
+        dkv_tile<true>(st, lane, kf, vf, dk, dv, c, q0 + 4 * g - key, span);
+    } else {
+      dkv_tile<false>(st, lane, kf, vf, dk, dv, c, 0, 0);
     }
     wait_vmcnt<0>();
     bw_barrier();
-  }
+  };
+  // Tiles 0 .. ntiles - 3 start at or past the block's first key + 128, so
+  // no wave masks them for causality; tile 0 alone can reach past L (when L is
+  // not a multiple of 64) and then takes the masked body. The last two tiles
+  // are the diagonal. The loops are separate so that the main one holds only
+  // the unmasked body (the mask select is 16 VALU ops per accumulator block).
+  int jt = 0;
+  if (ntiles > 0 && kBwTile * nq > L) run_tile(jt++, std::true_type{});
+  for (; jt < ntiles - 2; ++jt) run_tile(jt, std::false_type{});
+  for (; jt < ntiles; ++jt) run_tile(jt, std::true_type{});
   // dV rows (bf16), dK^C rows scaled (bf16), k^S part scaled into the per-head partials (fp32):
   // accumulator block b: lane = column 32 b + l32, element i = key kw0 + acc_row(i, g)
   static_for<0, 16>([&](auto II) {
@@ -527,11 +546,13 @@ __host__ __device__ constexpr TileOp q_op(int e) {
 constexpr int kQOps = 64;
 
 // One key tile for the wave's 32 queries (this lane's lse log2(e) l2 and
-// D dd). P is kept where the element's row (key) in the tile is <= m: with
-// m = query - k0 - 4 g that is key <= query; tiles with no masked element
-// pass a large m.
+// D dd). MASK: P is kept where the element's row (key) in the tile is <= m;
+// with m = query - k0 - 4 g that is key <= query. Without MASK every element
+// is kept (the tile ends before the block's first query).
+template <bool MASK>
 __device__ __forceinline__ void dq_tile(const char* st, const LaneOff& o, const bf16x8 (&qf)[12],
                                         const bf16x8 (&of)[8], f32x16 (&dq)[6], float c, float l2, float dd, int m) {
+  asm volatile("; dQ tile, masked: %0" ::"n"(MASK ? 1 : 0));
   const char* kc = st;
   const char* kr = st + kReg16;
   const char* vt = st + kReg16 + kReg8;
@@ -555,7 +576,7 @@ __device__ __forceinline__ void dq_tile(const char* st, const LaneOff& o, const 
       constexpr int i = II;
       constexpr int ci = 32 * B + arow0(i);
       float pv = fast_exp2(fmaf(s[B][i], c, -l2));
-      pv = ci <= m ? pv : 0.0f;
+      if constexpr (MASK) pv = ci <= m ? pv : 0.0f;
       d[i] = pv * (dp[B][i] - dd);
     });
     da[B][0] = pack8(d, 0);
@@ -637,18 +658,28 @@ __global__ void __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu
   const float c = scale * kLog2e;
   wait_vmcnt<0>();
   bw_barrier();
-  for (int j = 0; j < ntiles; ++j) {
+  // key tile j: the next tile's copies, the tile, its landing and the barrier
+  auto run_tile = [&](int j, auto M) {
+    constexpr bool kMask = decltype(M)::value;
     const int stage = j & 1;
     if (j + 1 < ntiles) issue(j + 1, stage ^ 1);
     const int k0 = kBwTile * j;
     const char* st = g_bw_lds + stage * kQStage;
-    if (k0 <= qw0 + 31) {   // else every key of the tile follows the wave's queries
-      const bool masked = k0 + kBwTile - 1 > qw0;
-      dq_tile(st, o, qf, of, acc, c, l2, dd, masked ? qrow - k0 - 4 * g : 0x3fffffff);
+    if constexpr (kMask) {
+      if (k0 <= qw0 + 31)   // else every key of the tile follows the wave's queries
+        dq_tile<true>(st, o, qf, of, acc, c, l2, dd, qrow - k0 - 4 * g);
+    } else {
+      dq_tile<false>(st, o, qf, of, acc, c, l2, dd, 0);
     }
     wait_vmcnt<0>();
     bw_barrier();
-  }
+  };
+  // key tiles before the block's first query need no mask for any wave; the
+  // last (at most) two are the diagonal
+  const int j_unmasked = min(ntiles, qb0 / kBwTile);
+  int jt = 0;
+  for (; jt < j_unmasked; ++jt) run_tile(jt, std::false_type{});
+  for (; jt < ntiles; ++jt) run_tile(jt, std::true_type{});
   // accumulator block b: lane = feature 32 b + l32, element i = query qw0 + acc_row(i, g)
   static_for<0, 16>([&](auto II) {
     constexpr int I = II;
