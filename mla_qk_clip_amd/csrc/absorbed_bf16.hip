@@ -254,16 +254,17 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
 //    them to LDS in the MFMA B-operand order.
 //  - PV waves 3-7 hold the latent accumulators O_lat^T = C^T P^T for a share
 //    of the 48 (head block, 32 latent columns) blocks: waves 3 and 7 (which
-//    share SIMD 3) 12 blocks each, waves 4-6 (beside an S wave) 8 each, so
-//    every SIMD issues 48 or 52 MFMAs per tile. In phase i they accumulate
-//    tile i-1 with the weights written in phase i-1, C^T read through the
-//    LDS transpose read.
+//    share SIMD 3) 12 blocks each, waves 5 and 6 (beside S waves 1 and 2) 11
+//    each, wave 4 (beside S wave 0, and keeping the max-logit candidate
+//    lists) 2. In phase i they accumulate tile i-1 with the weights written
+//    in phase i-1, C^T read through the LDS transpose read.
 //  - The PV waves also stream the tiles into a ring of kStages LDS stages:
-//    in phase i each issues 8 of the 37 wave-wide 1 KB copies of tile i+2
-//    (buffer loads straight into LDS; the buffer ends at the tile's last row,
-//    so reads past it return zeros) and before the barrier waits for its
-//    copies of tile i+1. A stage is refilled two phases after its tile's S
-//    phase, once the PV phase of that tile has ended.
+//    in phase i they issue the 37 wave-wide 1 KB copies of tile i+2 (waves
+//    3-7: 10, 9, 6, 9 and 3 of them; buffer loads straight into LDS; the
+//    buffer ends at the tile's last row, so reads past it return zeros) and
+//    before the barrier each waits for its copies of tile i+1. A stage is
+//    refilled two phases after its tile's S phase, once the PV phase of that
+//    tile has ended.
 // LDS tile layout: [32 rows][73 chunks of 8 bf16] (72 data chunks and one
 // pad chunk per row, so rows are 36 banks apart and both read patterns are
 // free of bank conflicts). A wave-wide copy fills 64 consecutive chunk
