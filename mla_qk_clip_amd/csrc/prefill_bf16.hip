@@ -872,7 +872,7 @@ __device__ __forceinline__ float refine_threshold(const float* aux, int h, int h
   return M - 2.0f * (1.01f / 256.0f + 3e-5f) * qn * kn;
 }
 
-constexpr int kRefRowSplit = 8;     // workgroups per head scanning row maxima
+constexpr int kRefRowSplit = 4;     // workgroups per head scanning row maxima
 
 __device__ __forceinline__ int seq_of(const int32_t* cu, int nseq, int t) {
   int lo = 0, hi = nseq - 1;
