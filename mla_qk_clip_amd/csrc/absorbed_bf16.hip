@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
                                                        uint16_t* __restrict__ qabs, const int32_t* __restrict__ lens,
                                                        int tq, int64_t* __restrict__ P, int32_t* __restrict__ nflag,
                                                        float* __restrict__ ml_init, float* __restrict__ qn2,
-                                                       float* __restrict__ hmax, uint16_t* __restrict__ qlo,
+                                                       uint16_t* __restrict__ qlo,
                                                        int qnorm, const uint16_t* __restrict__ qn_w, float qn_eps) {
   __shared__ __align__(16) uint16_t Wt[kN * kAqLd];
   __shared__ float qsq[2][64];
@@ -115,8 +115,6 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
     absorbed_prefix_block(lens, tq, bt, P, nflag);
     // max-logit slots start at -inf unless the caller accumulates into them
     if (ml_init && tid < heads) ml_init[tid] = -INFINITY;
-    // state of the max-logit refinement (written by later kernels only)
-    for (int i = tid; i < heads; i += 256) hmax[i] = -INFINITY;
   }
   __syncthreads();
   const lds_u16* wl = (const lds_u16*)(Wt);
@@ -279,7 +277,7 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
 // kernel.
 // Partials per (workgroup, virtual sequence) slot and head:
 //   part_o[slot][h][r] = sum_j p_j c_j[r] (relative to the reference max),
-//   part_ml[slot][h] = {reference max (raw), denominator, true raw max, flag}.
+//   part_ml[slot][h] = {reference max (raw), denominator, 0, flag}.
 // ---------------------------------------------------------------------------
 // Bound on |streamed - exact| logit per unit of ||q_abs|| * ||row||: bf16
 // rounding of q_abs (unit roundoff 2^-8, with 1% slack for the fp32
@@ -442,7 +440,7 @@ __device__ __forceinline__ u32x4 tile_rsrc(const uint16_t* cache, int64_t cap, i
 // ---- S waves ----
 struct SplitState {
   bf16x8 qf[kW / 16];
-  float m_ref, m_true, l_part;
+  float m_ref, l_part;
   bool overflow, first;
 };
 
@@ -498,7 +496,6 @@ __device__ __forceinline__ float split_scores(const char* tb, int nrows, int lan
   for (int e = 0; e < 16; e += 2) mx = fmax3_(mx, sacc[e], sacc[e + 1]);
   mx = xor32_max(mx);
   if (S.first) S.m_ref = mx;
-  S.m_true = fmaxf(S.m_true, mx);
   S.overflow = S.overflow || (mx - S.m_ref) * c2 > 64.0f;
   const float moff = -S.m_ref * c2;
   float psum = 0.0f;
@@ -589,7 +586,6 @@ __device__ __forceinline__ void split_s_wave(int ntiles, int lane, int64_t lo, i
         // 2^64; flagged, and such segments are recomputed by the fix-up
         // kernel).
         S.m_ref = 0.0f;
-        S.m_true = -INFINITY;
         S.l_part = 0.0f;
         S.overflow = false;
         S.first = true;
@@ -618,7 +614,7 @@ __device__ __forceinline__ void split_s_wave(int ntiles, int lane, int64_t lo, i
           const float l_tot = xor32_sum(S.l_part);
           if (g == 0)
             *reinterpret_cast<float4*>(part_ml + (slot * heads + head) * 4) =
-                make_float4(S.m_ref, l_tot, S.m_true, S.overflow ? 1.0f : 0.0f);
+                make_float4(S.m_ref, l_tot, 0.0f, S.overflow ? 1.0f : 0.0f);
         }
         if (__ballot(hvalid && S.overflow) && lane == 0) atomicAdd(nflag, 1);
         seg_new = true;
@@ -914,7 +910,6 @@ __global__ void __launch_bounds__(256) absorbed_fixup_kernel(
       if (lane == 0) {
         ml[0] = m;
         ml[1] = l;
-        ml[2] = m;
         ml[3] = 0.0f;
       }
     }
@@ -968,10 +963,9 @@ template <bool OUT_BF16>
 __global__ void __launch_bounds__(256) absorbed_combine_kernel(
     const int64_t* __restrict__ P, int64_t bt, int heads, float scale, const float* __restrict__ part_o,
     const float* __restrict__ part_ml, const uint16_t* __restrict__ w, const uint16_t* __restrict__ gate,
-    void* __restrict__ out, float* __restrict__ hmax) {
+    void* __restrict__ out) {
   __shared__ __align__(16) uint16_t ohi[kCmbV * kCmbLd];
   __shared__ __align__(16) uint16_t olo[kCmbV * kCmbLd];
-  __shared__ float red[kCmbV];
   const int h = blockIdx.x;
   const int64_t v0 = static_cast<int64_t>(blockIdx.y) * kCmbV;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -996,7 +990,7 @@ __global__ void __launch_bounds__(256) absorbed_combine_kernel(
   float acc[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
-  float den = 1.0f, Mt = -INFINITY;
+  float den = 1.0f;
   if (vs < bt) {
     const int64_t total = P[bt];
     const int wa = split_of_row(total, P[vs]);
@@ -1025,7 +1019,6 @@ __global__ void __launch_bounds__(256) absorbed_combine_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) x1[e] = *reinterpret_cast<const float4*>(p1 + 64 * e);
       }
-      Mt = fmaxf(Mt, fmaxf(m0.z, m1.z));
       const float mnew = fmaxf(M, fmaxf(m0.x, m1.x));
       if (mnew > M) {
         const float corr = fast_exp2((M - mnew) * c2);   // 0 on the first pair (M = -inf)
@@ -1074,13 +1067,7 @@ __global__ void __launch_bounds__(256) absorbed_combine_kernel(
       *reinterpret_cast<uint2*>(olo + off) = make_uint2(lv[0], lv[1]);
     }
   }
-  if (sub == 0) red[vl] = Mt;
-  __syncthreads();
-  if (tid == 0) {
-    float mm = -INFINITY;
-    for (int i = 0; i < kCmbV; ++i) mm = fmaxf(mm, red[i]);
-    if (mm > -INFINITY) atomic_max_float(hmax + h, mm);   // approximate, raw; refined below
-  }
+  __syncthreads();   // o_lat (hi, lo) of the workgroup's sequences is in LDS
 
   // ---- phase 2: O~^T = W_UV_h o_lat^T ----
   static_for<0, 2>([&](auto b) {
@@ -1131,18 +1118,22 @@ __global__ void __launch_bounds__(256) absorbed_combine_kernel(
 // listed tiles that still pass, and re-scores their rows in fp32 against
 // q_abs carried to about 16 significant bits (its bf16 value plus the bf16
 // rounding residual). The head's max logit is the maximum of those scores.
-// If a list overflowed (near-ties: q = 0, repeated rows) the streamed maximum
-// M is folded in as well, which is within max_j delta_j of E.
+// If a list overflowed (near-ties: q = 0, repeated rows), the refine
+// workgroup re-scores instead, per split workgroup, every tile of its row
+// range (its own list overflowed) or its listed tiles that pass against L,
+// so the result is the same exact maximum, only slower to reach.
 // ---------------------------------------------------------------------------
 constexpr int kRefTiles = 128;   // candidate tiles per refine workgroup
 constexpr int kRefSplit = 4;     // refine workgroups per head
 
 // Grid (heads, kRefSplit): workgroup (h, y) takes the lists of the split
-// workgroups w with w % kRefSplit == y. Scoring: one wave per listed tile;
-// lane l takes row l % 32, half l / 32 of its 72 16-byte chunks.
+// workgroups w with w % kRefSplit == y. Scoring: one wave per tile; lane l
+// takes row l % 32, half l / 32 of its 72 16-byte chunks. P (bt + 1 row
+// offsets of the virtual sequences) gives the split workgroups' row ranges
+// for the overflow path.
 __global__ void __launch_bounds__(256) absorbed_refine_kernel(
     int heads, const float* __restrict__ dlb, const int32_t* __restrict__ dcnt, const int4* __restrict__ dent,
-    const float* __restrict__ hmax, const uint16_t* __restrict__ qabs, const uint16_t* __restrict__ qlo,
+    const int64_t* __restrict__ P, int64_t bt, const uint16_t* __restrict__ qabs, const uint16_t* __restrict__ qlo,
     const uint16_t* __restrict__ cache, int64_t cap, int tq, float scale, float* __restrict__ max_logit) {
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   __shared__ i32x4 tl[kRefTiles + 1];
@@ -1150,8 +1141,8 @@ __global__ void __launch_bounds__(256) absorbed_refine_kernel(
   __shared__ int ntile, overflow;
   __shared__ __align__(16) float qe[4][kW];
   const int h = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float M = hmax[h];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar row walk below)
   if (tid == 0) {
     ntile = 0;
     overflow = 0;
@@ -1195,15 +1186,12 @@ __global__ void __launch_bounds__(256) absorbed_refine_kernel(
     if (q > kRefTiles) overflow = 1;
   }
   __syncthreads();
-  if (tid == 0 && overflow) atomic_max_float(max_logit + h, M * scale);   // some list overflowed
-  // ---- rows of the listed tiles, one wave per tile
-  const int nt = min(ntile, kRefTiles);
   float best = -INFINITY;
   float* q = qe[wave];
   const int rw = lane & 31, half = lane >> 5;
-  for (int k = wave; k < nt; k += 4) {
-    const i32x4 ti = tl[k];
-    const int vs = ti[0], row0 = ti[1], nrows = ti[2];
+  // the rows [row0, row0 + nrows) of virtual sequence vs, one per lane pair,
+  // scored in fp32 against q_abs + residual; the maximum goes into best
+  auto score_tile = [&](int vs, int row0, int nrows) {
     const uint16_t* qa = qabs + (static_cast<size_t>(vs) * heads + h) * kW;
     const uint16_t* ql = qlo + (static_cast<size_t>(vs) * heads + h) * kR;
     float qv[kW / 64];
@@ -1236,6 +1224,41 @@ __global__ void __launch_bounds__(256) absorbed_refine_kernel(
     if (rvalid) best = fmaxf(best, sc);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  };
+  if (!overflow) {
+    // ---- the listed tiles that pass, one wave per tile
+    const int nt = min(ntile, kRefTiles);
+    for (int k = wave; k < nt; k += 4) {
+      const i32x4 ti = tl[k];
+      score_tile(ti[0], ti[1], ti[2]);
+    }
+  } else {
+    // ---- a list overflowed: each wave takes every fourth of this
+    // workgroup's split workgroups and scores all tiles of its row range
+    // (walked as the split kernel walks it) when its own list overflowed,
+    // else its listed tiles that pass against L
+    const int64_t total = P[bt];
+    for (int i = wave; kRefSplit * i + static_cast<int>(blockIdx.y) < kDecSplits; i += 4) {
+      const int ws = kRefSplit * i + static_cast<int>(blockIdx.y);
+      const size_t os = static_cast<size_t>(ws) * heads + h;
+      const int cs = dcnt[os];
+      if (cs > kDecList) {
+        const int64_t lo = split_lo(total, ws), hi = split_lo(total, ws + 1);
+        if (lo >= hi) continue;
+        TileCursor cur;
+        cursor_init(cur, P, bt, lo, hi);
+        while (cur.pos < cur.n) {
+          score_tile(static_cast<int>(cur.vs), static_cast<int>(cursor_row0(cur, P)), cursor_rows(cur));
+          cursor_next(cur, P);
+        }
+      } else {
+        const i32x4* es = reinterpret_cast<const i32x4*>(dent) + os * kDecList;
+        for (int k = 0; k < cs; ++k) {
+          const i32x4 ti = es[k];
+          if (__int_as_float(ti[3]) >= L) score_tile(ti[0], ti[1], ti[2]);
+        }
+      }
+    }
   }
   best = wave_max(best);
   if (lane == 0 && best > -INFINITY) atomic_max_float(max_logit + h, best * scale);
@@ -1251,7 +1274,6 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
   int32_t* dcnt = reinterpret_cast<int32_t*>(base + L.dcnt);
   int4* dent = reinterpret_cast<int4*>(base + L.dent);
   float* qn2 = reinterpret_cast<float*>(base + L.qn2);
-  float* hmax = reinterpret_cast<float*>(base + L.hmax);
   uint16_t* qlo = reinterpret_cast<uint16_t*>(base + L.qlo);
   uint16_t* qabs = reinterpret_cast<uint16_t*>(base + L.qabs);
   int64_t* P = reinterpret_cast<int64_t*>(base + L.prefix);
@@ -1265,7 +1287,7 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
     TimedScope ts_("absorb_q", st);
     hipLaunchKernelGGL(absorb_q_kernel, dim3(heads, kR / 128), dim3(256), 0, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(w_kv_b), static_cast<int>(bt), heads, qabs, lens, tq, P, nflag,
-                       init_max_logit ? max_logit : nullptr, qn2, hmax, qlo, qn.on ? 1 : 0,
+                       init_max_logit ? max_logit : nullptr, qn2, qlo, qn.on ? 1 : 0,
                        static_cast<const uint16_t*>(qn.w), qn.eps);
   }
   e = hipGetLastError();
@@ -1292,14 +1314,14 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
       TimedScope ts_("absorbed_combine", st);
       hipLaunchKernelGGL(absorbed_combine_kernel<true>, cg, dim3(256), 0, st, P, bt, heads, scale,
                          part_o, part_ml, static_cast<const uint16_t*>(w_kv_b),
-                         static_cast<const uint16_t*>(gate), out, hmax);
+                         static_cast<const uint16_t*>(gate), out);
     }
   } else {
     {
       TimedScope ts_("absorbed_combine", st);
       hipLaunchKernelGGL(absorbed_combine_kernel<false>, cg, dim3(256), 0, st, P, bt, heads, scale,
                          part_o, part_ml, static_cast<const uint16_t*>(w_kv_b),
-                         static_cast<const uint16_t*>(gate), out, hmax);
+                         static_cast<const uint16_t*>(gate), out);
     }
   }
   e = hipGetLastError();
@@ -1307,7 +1329,7 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
   {
     TimedScope ts_("absorbed_refine", st);
     hipLaunchKernelGGL(absorbed_refine_kernel, dim3(heads, kRefSplit), dim3(256), 0, st, heads, dlb, dcnt, dent,
-                       hmax, qabs, qlo, static_cast<const uint16_t*>(cache), cap, tq, scale, max_logit);
+                       P, bt, qabs, qlo, static_cast<const uint16_t*>(cache), cap, tq, scale, max_logit);
   }
   return hipGetLastError();
 }

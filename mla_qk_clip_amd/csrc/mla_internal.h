@@ -89,10 +89,9 @@ inline size_t prefill_f32_ws(int heads, int64_t ntok, int N, int V) {
 //   qn2  [H][4]      per head and 128-column block of q_abs: max over the
 //                    virtual sequences of the block's squared norm (block 0
 //                    also holds the q^R part)
-//   hmax [H]         approximate max logit (raw) per head
 constexpr int kDecList = 32;   // candidate tiles a split workgroup keeps per head
 struct AbsorbedWs {
-  size_t qabs, qlo, prefix, nflag, part_o, part_ml, dlb, dcnt, dent, qn2, hmax, total;
+  size_t qabs, qlo, prefix, nflag, part_o, part_ml, dlb, dcnt, dent, qn2, total;
   int64_t slots;
 };
 inline AbsorbedWs absorbed_ws_layout(int heads, int batch, int tq) {
@@ -110,7 +109,6 @@ inline AbsorbedWs absorbed_ws_layout(int heads, int batch, int tq) {
   w.dcnt = off; off = align_up(off + static_cast<size_t>(kDecSplits) * heads * 4, 256);
   w.dent = off; off = align_up(off + static_cast<size_t>(kDecSplits) * heads * kDecList * 16, 256);
   w.qn2 = off; off = align_up(off + static_cast<size_t>(heads) * 4 * 4, 256);
-  w.hmax = off; off = align_up(off + static_cast<size_t>(heads) * 4, 256);
   w.total = off;
   return w;
 }

@@ -76,20 +76,6 @@ def test_bf16_decode_fewer_rows_than_splits(lib, tq):
     assert np.all(np.abs(host(ml) - ref_sm) / np.abs(ref_sm) <= SMAX_TOL)
 
 
-def check_smax_qabs_bound(ml, ref_sm, d, rows):
-    """The absorbed form scores against q_abs rounded to bf16 (unit roundoff
-    2^-8), so each logit is off by at most 2^-8 |q_abs| |row| plus the fp32
-    accumulation; a head whose max logit falls back to the streamed value
-    must lie within that bound."""
-    sc = oracle.mla_oracle.scale_of(d.dims)
-    rmax = max(float(np.max(np.linalg.norm(r.astype(np.float64), axis=1))) for r in rows)
-    for h in range(d.dims.heads):
-        qn = max(np.linalg.norm(oracle.mla_oracle.absorb_query(d.q[b, t, h], d.w_kv_b, d.dims, h))
-                 for b in range(d.batch) for t in range(d.tq))
-        bound = (2.0 ** -8 * 1.01 + 4e-5) * qn * rmax * sc
-        assert abs(float(ml[h]) - ref_sm[h]) <= bound, h
-
-
 def test_bf16_decode_max_logit_init_and_accumulate(lib):
     """Without accumulate the max-logit slots are reset (a stale value above
     every logit does not survive); with accumulate the call folds its maxima
@@ -138,11 +124,12 @@ def test_bf16_decode_logit_spike_takes_fixup_path(lib):
     assert np.all(np.abs(host(ml) - ref_sm) / np.abs(ref_sm) <= SMAX_TOL)
 
 
-def test_bf16_decode_max_logit_fallback_on_ties(lib):
+def test_bf16_decode_max_logit_exact_on_ties(lib):
     """Every row of a long sequence identical: every tile of each head is a
-    candidate, more than the refinement lists, so the max logit falls back to
-    the streamed value, which lies within the bf16 rounding bound; the second
-    sequence (ordinary rows) is unaffected in the output."""
+    candidate, more than a refine workgroup lists, so the refinement re-scores
+    the split workgroups' candidate tiles directly and the max logit is still
+    exact (to 1e-3); the second sequence (ordinary rows) is unaffected in the
+    output."""
     import torch
     from tests._gpu import dev, host, log, run_absorbed
     d = synth.decode_inputs(synth.K3, [9000, 700], cap=9024, tq=1, seed=38, bf16=True)
@@ -156,7 +143,30 @@ def test_bf16_decode_max_logit_fallback_on_ties(lib):
     out, ml = run_absorbed(d, cache=cache)
     ref, ref_sm = oracle.absorbed(d.q, rows, d.w_kv_b, d.gate, d.dims)
     assert rel_err(host(out), ref) <= BF16_TOL
-    check_smax_qabs_bound(host(ml), ref_sm, d, rows)
+    assert np.all(np.abs(host(ml) - ref_sm) / np.abs(ref_sm) <= SMAX_TOL)
+
+
+def test_bf16_decode_max_logit_exact_when_every_list_overflows(lib):
+    """Sixteen sequences of 20000 identical rows each (one row drawn per
+    sequence): every split workgroup holds about 39 tied candidate tiles per
+    head, more than its list keeps, so every list overflows and the
+    refinement re-scores all rows of every split workgroup. Identical rows
+    make the exact references those of one row per sequence: the softmax is
+    uniform, the output is the row's value mix and the max logit its logit."""
+    import torch
+    from tests._gpu import dev, host, log, run_absorbed
+    L = 20000
+    d = synth.decode_inputs(synth.K3, [L] * 16, cap=L, tq=1, seed=39, bf16=True)
+    one = [d.cache_rows(b)[:1].copy() for b in range(d.batch)]
+    W = d.dims.kv_rank + d.dims.shared_dim
+    cache = torch.empty((d.batch, d.cap, W), dtype=torch.bfloat16, device="cuda")
+    for b in range(d.batch):
+        cache[b] = dev(one[b], True).expand(L, W)
+    log(f"bf16 absorbed, {d.batch} x {L} identical rows")
+    out, ml = run_absorbed(d, cache=cache)
+    ref, ref_sm = oracle.absorbed(d.q, one, d.w_kv_b, d.gate, d.dims)
+    assert rel_err(host(out), ref) <= BF16_TOL
+    assert np.all(np.abs(host(ml) - ref_sm) / np.abs(ref_sm) <= SMAX_TOL)
 
 
 def test_bf16_decode_matches_prefill_last_row(lib):
