@@ -139,7 +139,14 @@ size_t mla_prefill_workspace_size(const mla_dims* dims, mla_dtype in_dtype,
  *
  * bf16: products in bf16 MFMA with fp32 accumulation, K^C and V rounded to
  * bf16 in the workspace, softmax in fp32, probabilities rounded to bf16 for
- * the value product. fp32: fp32 throughout.
+ * the value product. max_logit is refined: the rows whose streamed row
+ * maximum lies within twice the bound of the bf16 rounding of K^C below the
+ * head's streamed maximum have every logit re-scored in fp32 against q_abs =
+ * W_UK q^C carried to about 16 significant bits, so the result is the exact
+ * maximum up to fp32 rounding. A head with more than 64 such rows (near-ties:
+ * q = 0, repeated queries) takes the streamed maximum instead, within
+ * (1.01 * 2^-8 + 3e-5) * max|q| * max|K| * scale of the exact one.
+ * fp32: fp32 throughout.
  */
 mla_status mla_prefill(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype,
                        const void* q, const void* ckv, const void* ks,
@@ -217,8 +224,9 @@ size_t mla_absorbed_workspace_size(const mla_dims* dims, mla_dtype in_dtype,
  * tile's largest row norm), every tile that could hold the head's exact
  * maximum is re-scored in fp32 against q_abs carried to about 16 significant
  * bits, so the result is the exact maximum up to fp32 rounding. Where more
- * tiles than the refinement lists tie within that bound (q = 0, repeated
- * rows), a head falls back to the streamed maximum, within the bound.
+ * tiles tie within that bound than the refinement lists (q = 0, repeated
+ * rows), it re-scores the rows of the split ranges concerned directly: the
+ * same result, reached more slowly.
  * cap is at most 2^31 - 1.
  */
 mla_status mla_absorbed(const mla_dims* dims, mla_dtype in_dtype, mla_dtype out_dtype,
