@@ -1,5 +1,4 @@
 """GPU parity of QK-Clip (mla_qk_clip) and the QK-Clip stress workload end to end."""
-import math
 
 import numpy as np
 import pytest
