@@ -124,15 +124,17 @@ def test_bf16_decode_logit_spike_takes_fixup_path(lib):
     assert np.all(np.abs(host(ml) - ref_sm) / np.abs(ref_sm) <= SMAX_TOL)
 
 
-def test_bf16_decode_max_logit_exact_on_ties(lib):
+@pytest.mark.parametrize("tq", [1, 2])
+def test_bf16_decode_max_logit_exact_on_ties(lib, tq):
     """Every row of a long sequence identical: every tile of each head is a
     candidate, more than a refine workgroup lists, so the refinement re-scores
     the split workgroups' candidate tiles directly and the max logit is still
     exact (to 1e-3); the second sequence (ordinary rows) is unaffected in the
-    output."""
+    output. With two query tokens per sequence the virtual sequences see
+    different row counts."""
     import torch
     from tests._gpu import dev, host, log, run_absorbed
-    d = synth.decode_inputs(synth.K3, [9000, 700], cap=9024, tq=1, seed=38, bf16=True)
+    d = synth.decode_inputs(synth.K3, [9000, 700], cap=9024, tq=tq, seed=38, bf16=True)
     rows = [d.cache_rows(b).copy() for b in range(d.batch)]
     rows[0][:] = rows[0][0]
     W = d.dims.kv_rank + d.dims.shared_dim
