@@ -9,11 +9,13 @@
 //   O~_h = o_lat W_UV_h,  o = sigma(g) . O~                 (combine kernel)
 //
 // The split kernel is a split-K stream over the concatenation of all
-// sequences' visible rows: workgroup w owns the row range [T*w/G, T*(w+1)/G)
-// (T = all visible rows, G workgroups), so every workgroup reads the same
-// number of cache bytes whatever the length mix. For every (workgroup,
-// sequence) overlap it writes a partial (row max, denominator, unnormalised
-// o_lat) for all heads; the combine kernel merges them by log-sum-exp.
+// sequences' visible rows: the G workgroups own consecutive row ranges of
+// equal cost, where a range's cost is its rows plus kSegCost rows for every
+// sequence start inside it (starting a sequence reloads its queries and
+// writes a partial), so every workgroup does the same work whatever the
+// length mix. For every (workgroup, sequence) overlap it writes a partial
+// (row max, denominator, unnormalised o_lat) for all heads; the combine
+// kernel merges them by log-sum-exp.
 //
 // The per-head max logit is refined to the exact value: the split kernel
 // bounds the bf16 rounding error of every 32-row tile's logits (from the
@@ -58,6 +60,29 @@ __device__ void absorbed_prefix_block(const int32_t* __restrict__ lens, int tq, 
   for (int64_t v = v0; v < v1; ++v) {
     P[v] = acc;
     acc += rows_of(v);
+  }
+}
+
+// Row boundaries of the split workgroups, S[w] for w = 0 .. kDecSplits,
+// stored right after P (S = P + bt + 1). The bt virtual sequences are laid
+// end to end with kSegCost virtual rows before every one but the first (the
+// cost of starting a sequence, in rows); workgroup w takes the cost interval
+// [C w / G, C (w + 1) / G) of the total cost C, and a boundary that falls
+// into such a gap snaps to the sequence start. Called by one workgroup after
+// P is complete.
+constexpr int64_t kSegCost = 192;
+__device__ void absorbed_split_table(int64_t* __restrict__ P, int64_t bt) {
+  int64_t* S = P + bt + 1;
+  const int64_t C = P[bt] + kSegCost * (bt - 1);
+  for (int w = threadIdx.x; w <= kDecSplits; w += blockDim.x) {
+    const int64_t c = C * w / kDecSplits;
+    // the last sequence v whose cost start P[v] + kSegCost v is at most c
+    int64_t lo = 0, hi = bt - 1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (P[mid] + kSegCost * mid <= c) lo = mid; else hi = mid - 1;
+    }
+    S[w] = P[lo] + min(c - (P[lo] + kSegCost * lo), P[lo + 1] - P[lo]);
   }
 }
 
@@ -113,6 +138,8 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const uint16_t* __restric
   }
   if (h == 0 && rc == 0) {
     absorbed_prefix_block(lens, tq, bt, P, nflag);
+    __syncthreads();   // P is complete
+    absorbed_split_table(P, bt);
     // max-logit slots start at -inf unless the caller accumulates into them
     if (ml_init && tid < heads) ml_init[tid] = -INFINITY;
   }
@@ -310,7 +337,7 @@ static_assert(kDecHeadsPerWg == 96 && kDecRows == 32, "three head blocks of 32, 
 
 // Walk over a workgroup's row range [lo, lo + n), tile by tile and segment
 // (virtual sequence) by segment. Positions are row offsets from lo, 32-bit (a
-// range holds total / G rows); the 64-bit prefix P is turned into offsets
+// range holds about total / G rows); the 64-bit prefix P is turned into offsets
 // with 32-bit compares only. (This compiler has been seen to drop the
 // VCC-to-SCC step of a 64-bit scalar select in this kernel, which made a
 // cursor skip to its segment end; 32-bit scalar compares set SCC directly.)
@@ -793,10 +820,8 @@ __global__ void __launch_bounds__(kSplitThreads) absorbed_split_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = gridDim.x;
-  const int64_t total = P[bt];
-  const int64_t lo = total * blockIdx.x / G;
-  const int64_t hi = total * (blockIdx.x + 1) / G;
+  const int64_t* S = P + bt + 1;   // the workgroups' row boundaries
+  const int64_t lo = S[blockIdx.x], hi = S[blockIdx.x + 1];
   if (lo >= hi) {
     // no rows: no bound and no candidates for this workgroup's heads
     for (int h = 96 * static_cast<int>(blockIdx.y) + tid; h < min(heads, 96 * (static_cast<int>(blockIdx.y) + 1));
@@ -854,14 +879,13 @@ __global__ void __launch_bounds__(kSplitThreads) absorbed_split_kernel(
 // workgroup per split workgroup; one wavefront per flagged head at a time.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) absorbed_fixup_kernel(
-    const uint16_t* __restrict__ cache, int64_t cap, int tq, int heads, int64_t bt, int G,
+    const uint16_t* __restrict__ cache, int64_t cap, int tq, int heads, int64_t bt,
     const int64_t* __restrict__ P, const uint16_t* __restrict__ qabs, float scale, float* __restrict__ part_o,
     float* __restrict__ part_ml, const int32_t* __restrict__ nflag) {
   if (*nflag == 0) return;   // nothing was flagged (the common case)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t total = P[bt];
-  const int64_t lo = total * blockIdx.x / G;
-  const int64_t hi = total * (blockIdx.x + 1) / G;
+  const int64_t* S = P + bt + 1;   // the split workgroups' row boundaries
+  const int64_t lo = S[blockIdx.x], hi = S[blockIdx.x + 1];
   if (lo >= hi) return;
   const float c2 = scale * kLog2e;
   TileCursor cur;
@@ -940,15 +964,14 @@ constexpr int kCmbV = 16;
 
 constexpr int kCmbLd = kR + 8;   // LDS row of the o_lat parts (16-byte pad)
 
-// First cache row of split workgroup w (the split kernel's partition).
-__device__ __forceinline__ int64_t split_lo(int64_t total, int w) { return total * w / kDecSplits; }
-
-// The split workgroup whose rows contain `row`: the largest w with split_lo(w) <= row.
-__device__ __forceinline__ int split_of_row(int64_t total, int64_t row) {
+// The split workgroup whose rows contain `row`: the largest w with S[w] <=
+// row (S: the split kernel's row boundaries; empty workgroups share their
+// boundary with the next one).
+__device__ __forceinline__ int split_of_row(const int64_t* S, int64_t row) {
   int lo = 0, hi = kDecSplits - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (split_lo(total, mid) <= row) lo = mid; else hi = mid - 1;
+    if (S[mid] <= row) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -992,10 +1015,10 @@ __global__ void __launch_bounds__(256) absorbed_combine_kernel(
   for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
   float den = 1.0f;
   if (vs < bt) {
-    const int64_t total = P[bt];
-    const int wa = split_of_row(total, P[vs]);
-    const int wb = split_of_row(total, P[vs + 1] - 1);
-    auto nonempty = [&](int s) { return split_lo(total, s) < split_lo(total, s + 1); };
+    const int64_t* S = P + bt + 1;
+    const int wa = split_of_row(S, P[vs]);
+    const int wb = split_of_row(S, P[vs + 1] - 1);
+    auto nonempty = [&](int s) { return S[s] < S[s + 1]; };
     float M = -INFINITY;
     den = 0.0f;
     const float* pb = part_o + static_cast<size_t>(h) * kR + 4 * sub;
@@ -1237,13 +1260,13 @@ __global__ void __launch_bounds__(256) absorbed_refine_kernel(
     // workgroup's split workgroups and scores all tiles of its row range
     // (walked as the split kernel walks it) when its own list overflowed,
     // else its listed tiles that pass against L
-    const int64_t total = P[bt];
+    const int64_t* S = P + bt + 1;
     for (int i = wave; kRefSplit * i + static_cast<int>(blockIdx.y) < kDecSplits; i += 4) {
       const int ws = kRefSplit * i + static_cast<int>(blockIdx.y);
       const size_t os = static_cast<size_t>(ws) * heads + h;
       const int cs = dcnt[os];
       if (cs > kDecList) {
-        const int64_t lo = split_lo(total, ws), hi = split_lo(total, ws + 1);
+        const int64_t lo = S[ws], hi = S[ws + 1];
         if (lo >= hi) continue;
         TileCursor cur;
         cursor_init(cur, P, bt, lo, hi);
@@ -1303,7 +1326,7 @@ hipError_t launch_absorbed_bf16(int heads, float scale, bool out_bf16, const voi
   {
     TimedScope ts_("absorbed_fixup", st);
     hipLaunchKernelGGL(absorbed_fixup_kernel, dim3(kDecSplits), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(cache), cap, tq, heads, bt, kDecSplits, P, qabs, scale, part_o,
+                       static_cast<const uint16_t*>(cache), cap, tq, heads, bt, P, qabs, scale, part_o,
                        part_ml, nflag);
   }
   e = hipGetLastError();

@@ -101,7 +101,9 @@ inline AbsorbedWs absorbed_ws_layout(int heads, int batch, int tq) {
   size_t off = 0;
   w.qabs = off; off = align_up(off + static_cast<size_t>(bt) * heads * (kR + kS) * 2, 256);
   w.qlo = off; off = align_up(off + static_cast<size_t>(bt) * heads * kR * 2, 256);
-  w.prefix = off; off = align_up(off + static_cast<size_t>(bt + 1) * 8, 256);
+  // prefix: bt + 1 row offsets of the virtual sequences, then the split
+  // workgroups' kDecSplits + 1 row boundaries
+  w.prefix = off; off = align_up(off + static_cast<size_t>(bt + 1 + kDecSplits + 1) * 8, 256);
   w.nflag = off; off = align_up(off + 4, 256);   // count of segments the fix-up kernel must redo
   w.part_o = off; off = align_up(off + static_cast<size_t>(w.slots) * heads * kR * 4, 256);
   w.part_ml = off; off = align_up(off + static_cast<size_t>(w.slots) * heads * 4 * 4, 256);
