@@ -70,7 +70,7 @@ __device__ void absorbed_prefix_block(const int32_t* __restrict__ lens, int tq, 
 // [C w / G, C (w + 1) / G) of the total cost C, and a boundary that falls
 // into such a gap snaps to the sequence start. Called by one workgroup after
 // P is complete.
-constexpr int64_t kSegCost = 192;
+constexpr int64_t kSegCost = 256;
 __device__ void absorbed_split_table(int64_t* __restrict__ P, int64_t bt) {
   int64_t* S = P + bt + 1;
   const int64_t C = P[bt] + kSegCost * (bt - 1);
