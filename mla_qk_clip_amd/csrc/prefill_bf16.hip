@@ -118,8 +118,12 @@ __global__ void __launch_bounds__(kExThreads) prefill_expand_kernel(
 
   // ---- work item: groups of kExGroupRows row tiles x kExGroupHeads heads,
   // consecutive groups on the same XCD ----
+  // the row tiles of the padded tokens of this call (hdr[1]), not of the
+  // workspace's bound npad_max: the items are dealt to the XCDs in equal
+  // contiguous ranges, and counting empty tiles would leave the last XCDs
+  // nearly idle
   const int npad = hdr[1];
-  const int nrt = static_cast<int>(npad_max / kExRows);
+  const int nrt = (npad + kExRows - 1) / kExRows;
   const int nrg = (nrt + kExGroupRows - 1) / kExGroupRows, nhg = (heads + kExGroupHeads - 1) / kExGroupHeads;
   const int per_xcd = (nrg * nhg * kExGroup + 7) >> 3;
   const int slot = blockIdx.x >> 3;
