@@ -104,7 +104,7 @@ constexpr int kExRows = 256;      // padded rows per workgroup
 constexpr int kExThreads = 512;
 constexpr int kExSteps = kR / 64;  // k-steps of 64
 constexpr int kExUnits = kExRows * 8;  // 16-byte units per operand slot
-constexpr int kExGroupRows = 2, kExGroupHeads = 16, kExGroup = kExGroupRows * kExGroupHeads;
+constexpr int kExGroupRows = 4, kExGroupHeads = 8, kExGroup = kExGroupRows * kExGroupHeads;
 
 __global__ void __launch_bounds__(kExThreads) prefill_expand_kernel(
     const uint16_t* __restrict__ ckv, const uint16_t* __restrict__ w, const int32_t* __restrict__ cu,
