@@ -1147,13 +1147,14 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
   const int64_t grid = 8 * tiles_max * ((heads + 7) / 8);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   // Heads interleaved per XCD group: as many as keep the K and V that all
-  // eight XCDs' groups read within about 192 MB (the last-level cache holds
-  // 256 MB), between 2 and 12. Measured at 96 heads: 12 at T = 4096 is 1.8 %
-  // faster than 2; at T = 8192 and 16384 the rule's 6 and 3 equal 2, while 12
-  // is 5 % and 12 % slower.
+  // eight XCDs' groups read within about 96 MB (the last-level cache holds
+  // 256 MB), between 2 and 12. Measured at 96 heads: at T = 4096 the rule's 6
+  // is 2-4 % faster than 2 and as fast as 12 with a third less traffic; at
+  // T = 8192 and 16384 groups of 6 and 3 equal 2, while 12 is 5 % and 12 %
+  // slower.
   const int64_t kv_head_bytes = ntok * (kN + kV) * 2;
-  const int hgroup = static_cast<int>(std::min<int64_t>(12, std::max<int64_t>(2, (int64_t{192} << 20) /
-                                                                                      (8 * kv_head_bytes))));
+  const int hgroup = static_cast<int>(std::min<int64_t>(12, std::max<int64_t>(2, (int64_t{96} << 20) /
+                                                                                     (8 * kv_head_bytes))));
   if (out_bf16) {
     {
       TimedScope ts_("prefill_attn", st);
