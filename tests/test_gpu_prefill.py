@@ -76,6 +76,19 @@ def test_bf16_varlen_ragged_tiles(lib, out_bf16):
     _check(p, out, lse, ml, ref, ref_lse, ref_sm, BF16_TOL)
 
 
+def test_bf16_varlen_twenty_heads(lib):
+    """20 heads: the eight XCDs own 2 or 3 heads each (head ranges [x 20 / 8,
+    (x + 1) 20 / 8)), so their head groups differ in size; ragged packed
+    sequences, every output and every head's max logit against the oracle."""
+    from tests._gpu import log, run_prefill
+    dims = synth.Dims(20, 512, 64, 128, 128)
+    p = synth.prefill_inputs(dims, [300, 1, 129, 64, 200], seed=9, bf16=True)
+    log("bf16 varlen prefill, 20 heads")
+    out, lse, ml = run_prefill(p)
+    ref, ref_lse, ref_sm = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims)
+    _check(p, out, lse, ml, ref, ref_lse, ref_sm, BF16_TOL)
+
+
 def test_bf16_no_gate_and_accumulate(lib):
     import torch
     from tests._gpu import host, log, run_prefill
