@@ -22,55 +22,180 @@ namespace mla {
 
 // ---------------------------------------------------------------------------
 // Plan: pcu[s] = start of sequence s in the padded workspace (each sequence
-// rounded up to 64 rows), order[] = sequences by descending length, toff[r] =
-// first query tile of the r-th sequence in that order, hdr = {tiles, padded rows}.
-// The same single workgroup also clears the max-logit refinement state and,
-// unless the caller accumulates, sets the max-logit slots to -inf.
+// rounded up to 64 rows), order[] = sequences by descending length (ties by
+// index), toff[r] = first query tile of the r-th sequence in that order,
+// hdr = {tiles, padded rows}. The same single workgroup also clears the
+// max-logit refinement state and, unless the caller accumulates, sets the
+// max-logit slots to -inf.
+//
+// Up to 64 sequences: one wave, one sequence per lane; the prefixes are wave
+// shuffle scans and the order a rank count over the lanes. Otherwise:
+// lengths are read once per chunk of kPlanSortMax sequences into LDS; both
+// prefixes are block scans over a chunk (16 consecutive values per thread,
+// wave shuffles, one LDS exchange of the four wave totals). Up to
+// kPlanSortMax sequences are ordered by a bitonic sort of 64-bit keys in LDS
+// (high word = length mapped so that ascending keys mean descending lengths,
+// low word = index); past that the sequences keep their index order.
 // ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 256;
+constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanSortMax = 4096;
+constexpr int kPlanPer = kPlanSortMax / kPlanThreads;
+constexpr int kPlanPairs = kPlanSortMax / 2 / kPlanThreads;
 
-__global__ void __launch_bounds__(256) prefill_plan_kernel(const int32_t* __restrict__ cu, int nseq,
-                                                           int32_t* __restrict__ pcu,
-                                                           int32_t* __restrict__ order,
-                                                           int32_t* __restrict__ toff,
-                                                           int32_t* __restrict__ hdr, int heads,
-                                                           float* __restrict__ aux, int32_t* __restrict__ cand,
-                                                           float* __restrict__ ml_init) {
-  __shared__ int s_order[kPlanSortMax];
-  for (int i = threadIdx.x; i < (heads + 1) * kAuxStride; i += blockDim.x)
-    aux[i] = ((i % kAuxStride) == 0 && i < heads * kAuxStride) ? -INFINITY : 0.0f;
-  for (int i = threadIdx.x; i < kCandHeadCount + heads; i += blockDim.x) cand[i] = 0;
-  if (ml_init)
-    for (int i = threadIdx.x; i < heads; i += blockDim.x) ml_init[i] = -INFINITY;
-  const bool sort = nseq <= kPlanSortMax;
-  if (sort) {
-    for (int s = threadIdx.x; s < nseq; s += blockDim.x) {
-      const int L = cu[s + 1] - cu[s];
-      int rank = 0;
-      for (int t = 0; t < nseq; ++t) {
-        const int Lt = cu[t + 1] - cu[t];
-        rank += (Lt > L) || (Lt == L && t < s);
-      }
-      s_order[rank] = s;
-    }
+// Exclusive scan of val(0 .. n-1), n <= kPlanSortMax, offset by carry; calls
+// out(i, prefix_i) and returns carry + the sum. All threads must call it.
+template <class Val, class Out>
+__device__ __forceinline__ int plan_scan(int n, int carry, int* s_wave, Val val, Out out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = tid * kPlanPer;
+  int v[kPlanPer];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < kPlanPer; ++j) {
+    v[j] = b + j < n ? val(b + j) : 0;
+    sum += v[j];
+  }
+  int x = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int run = carry + x - sum, total = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) {
+    const int t = s_wave[w];
+    run += w < wave ? t : 0;
+    total += t;
+  }
+#pragma unroll
+  for (int j = 0; j < kPlanPer; ++j) {
+    if (b + j < n) out(b + j, run);
+    run += v[j];
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int p = 0;
-    for (int s = 0; s < nseq; ++s) {
-      pcu[s] = p;
-      const int L = cu[s + 1] - cu[s];
-      p += (L + kSeqPad - 1) / kSeqPad * kSeqPad;
+  return carry + total;
+}
+
+__global__ void __launch_bounds__(kPlanThreads) prefill_plan_kernel(const int32_t* __restrict__ cu, int nseq,
+                                                                    int32_t* __restrict__ pcu,
+                                                                    int32_t* __restrict__ order,
+                                                                    int32_t* __restrict__ toff,
+                                                                    int32_t* __restrict__ hdr, int heads,
+                                                                    float* __restrict__ aux,
+                                                                    int32_t* __restrict__ cand,
+                                                                    float* __restrict__ ml_init) {
+  __shared__ uint64_t s_key[kPlanSortMax];
+  __shared__ int s_len[kPlanSortMax];
+  __shared__ int s_wave[kPlanWaves];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < (heads + 1) * kAuxStride; i += kPlanThreads)
+    aux[i] = ((i % kAuxStride) == 0 && i < heads * kAuxStride) ? -INFINITY : 0.0f;
+  for (int i = tid; i < kCandHeadCount + heads; i += kPlanThreads) cand[i] = 0;
+  if (ml_init)
+    for (int i = tid; i < heads; i += kPlanThreads) ml_init[i] = -INFINITY;
+  auto pad_rows = [](int L) { return (L + kSeqPad - 1) / kSeqPad * kSeqPad; };
+  auto q_tiles = [](int L) { return (L + kPrefBM - 1) / kPrefBM; };
+
+  if (nseq <= 64) {
+    // One wave, one sequence per lane, everything in registers.
+    if (tid < 64) {
+      const int lane = tid;
+      const int L = lane < nseq ? cu[lane + 1] - cu[lane] : 0;
+      auto incl_scan = [&](int x) {
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(x, off, 64);
+          if (lane >= off) x += y;
+        }
+        return x;
+      };
+      const int a = lane < nseq ? pad_rows(L) : 0, pa = incl_scan(a);
+      if (lane < nseq) pcu[lane] = pa - a;
+      int rank = 0;
+      for (int s = 0; s < nseq; ++s) {
+        const int Ls = __builtin_amdgcn_readlane(L, s);
+        rank += (Ls > L) || (Ls == L && s < lane);
+      }
+      int at = 0;  // the sequence ranked lane-th
+      for (int s = 0; s < nseq; ++s) at = __builtin_amdgcn_readlane(rank, s) == lane ? s : at;
+      const int b = lane < nseq ? q_tiles(__shfl(L, at, 64)) : 0, pb = incl_scan(b);
+      if (lane < nseq) {
+        order[lane] = at;
+        toff[lane] = pb - b;
+      }
+      if (lane == 63) {
+        pcu[nseq] = pa;
+        toff[nseq] = pb;
+        hdr[0] = pb;
+        hdr[1] = pa;
+      }
     }
+    return;
+  }
+
+  const bool sort = nseq <= kPlanSortMax;
+  int p = 0, t = 0;
+  for (int c0 = 0; c0 < nseq; c0 += kPlanSortMax) {
+    const int n = min(kPlanSortMax, nseq - c0);
+    for (int i = tid; i < n; i += kPlanThreads) s_len[i] = cu[c0 + i + 1] - cu[c0 + i];
+    __syncthreads();
+    p = plan_scan(n, p, s_wave, [&](int i) { return pad_rows(s_len[i]); },
+                  [&](int i, int x) { pcu[c0 + i] = x; });
+    if (!sort)
+      t = plan_scan(n, t, s_wave, [&](int i) { return q_tiles(s_len[i]); },
+                    [&](int i, int x) {
+                      order[c0 + i] = c0 + i;
+                      toff[c0 + i] = x;
+                    });
+  }
+  if (sort) {
+    // s_len holds all nseq lengths (one chunk).
+    int n2 = 1;
+    while (n2 < nseq) n2 <<= 1;
+    for (int i = tid; i < n2; i += kPlanThreads) {
+      uint64_t key = ~uint64_t{0};
+      if (i < nseq) {
+        const uint32_t hi = 0xffffffffu - (static_cast<uint32_t>(s_len[i]) ^ 0x80000000u);
+        key = (static_cast<uint64_t>(hi) << 32) | static_cast<uint32_t>(i);
+      }
+      s_key[i] = key;
+    }
+    __syncthreads();
+    // Each step: pair q = tid + 256 m takes keys i (bit j clear) and i + j;
+    // all of a thread's loads are issued before its compare-and-swaps.
+    for (int k = 2, lk = 1; k <= n2; k <<= 1, ++lk)
+      for (int j = k >> 1, lj = lk - 1; j > 0; j >>= 1, --lj) {
+        uint64_t a[kPlanPairs], c[kPlanPairs];
+#pragma unroll
+        for (int m = 0; m < kPlanPairs; ++m) {
+          const int q = tid + m * kPlanThreads, i = ((q >> lj) << (lj + 1)) | (q & (j - 1));
+          if (q < n2 / 2) {
+            a[m] = s_key[i];
+            c[m] = s_key[i + j];
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < kPlanPairs; ++m) {
+          const int q = tid + m * kPlanThreads, i = ((q >> lj) << (lj + 1)) | (q & (j - 1));
+          if (q < n2 / 2 && (a[m] > c[m]) == ((i & k) == 0)) {
+            s_key[i] = c[m];
+            s_key[i + j] = a[m];
+          }
+        }
+        __syncthreads();
+      }
+    auto seq_at = [&](int r) { return static_cast<int>(static_cast<uint32_t>(s_key[r])); };
+    t = plan_scan(nseq, 0, s_wave, [&](int r) { return q_tiles(s_len[seq_at(r)]); },
+                  [&](int r, int x) {
+                    order[r] = seq_at(r);
+                    toff[r] = x;
+                  });
+  }
+  if (tid == 0) {
     pcu[nseq] = p;
-    int t = 0;
-    for (int r = 0; r < nseq; ++r) {
-      const int s = sort ? s_order[r] : r;
-      order[r] = s;
-      toff[r] = t;
-      const int L = cu[s + 1] - cu[s];
-      t += (L + kPrefBM - 1) / kPrefBM;
-    }
     toff[nseq] = t;
     hdr[0] = t;
     hdr[1] = p;
@@ -1124,7 +1249,7 @@ hipError_t launch_prefill_bf16(int heads, float scale, bool out_bf16, const void
 
   {
     TimedScope ts_("prefill_plan", st);
-    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(256), 0, st, cu, nseq, pcu, order, toff, hdr, heads, aux,
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, cu, nseq, pcu, order, toff, hdr, heads, aux,
                        cand, init_max_logit ? max_logit : nullptr);
   }
   hipError_t e = hipGetLastError();

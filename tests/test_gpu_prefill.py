@@ -89,6 +89,24 @@ def test_bf16_varlen_twenty_heads(lib):
     _check(p, out, lse, ml, ref, ref_lse, ref_sm, BF16_TOL)
 
 
+@pytest.mark.parametrize("nseq", [64, 65, 700, 4500])
+def test_bf16_many_short_sequences(lib, nseq):
+    """Tens to thousands of packed sequences of 0 to 6 tokens (many equal
+    lengths, empty ones) around two longer ones: the plan takes up to 64
+    sequences in one wave, sorts up to 4096 by length in LDS and scans past
+    that in chunks of 4096."""
+    from tests._gpu import log, run_prefill
+    rng = np.random.default_rng(nseq)
+    lens = [int(x) for x in rng.integers(0, 7, nseq)]
+    lens[5], lens[nseq - 3] = 130, 200
+    dims = synth.Dims(8, 512, 64, 128, 128)
+    p = synth.prefill_inputs(dims, lens, seed=31, bf16=True)
+    log(f"bf16 varlen prefill, {nseq} sequences, {sum(lens)} tokens")
+    out, lse, ml = run_prefill(p)
+    ref, ref_lse, ref_sm = oracle.prefill(p.q, p.ckv, p.ks, p.w_kv_b, p.gate, p.cu_seqlens, p.dims)
+    _check(p, out, lse, ml, ref, ref_lse, ref_sm, BF16_TOL)
+
+
 def test_bf16_no_gate_and_accumulate(lib):
     import torch
     from tests._gpu import host, log, run_prefill
