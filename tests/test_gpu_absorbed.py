@@ -76,6 +76,24 @@ def test_bf16_decode_fewer_rows_than_splits(lib, tq):
     assert np.all(np.abs(host(ml) - ref_sm) / np.abs(ref_sm) <= SMAX_TOL)
 
 
+@pytest.mark.parametrize("tq", [1, 2])
+def test_bf16_decode_more_sequences_than_splits(lib, tq):
+    """700 sequences, far more than the 256 split workgroups: most hold tq to
+    40 rows, so a split's row range covers many whole sequences (cuts snap to
+    sequence starts), and three long ones are cut over several splits."""
+    from tests._gpu import host, log, run_absorbed
+    rng = np.random.default_rng(700 + tq)
+    lens = rng.integers(tq, 41, 700).astype(np.int32)
+    lens[[3, 350, 699]] = [2900, 1500, 2999]
+    d = synth.decode_inputs(synth.K3, lens, cap=3008, tq=tq, seed=36, bf16=True)
+    log(f"bf16 absorbed, {d.batch} sequences, {int(lens.sum())} rows, tq={tq}")
+    out, ml = run_absorbed(d)
+    rows = [d.cache_rows(b) for b in range(d.batch)]
+    ref, ref_sm = oracle.absorbed(d.q, rows, d.w_kv_b, d.gate, d.dims)
+    assert rel_err(host(out), ref) <= BF16_TOL
+    assert np.all(np.abs(host(ml) - ref_sm) / np.abs(ref_sm) <= SMAX_TOL)
+
+
 def test_bf16_decode_max_logit_init_and_accumulate(lib):
     """Without accumulate the max-logit slots are reset (a stale value above
     every logit does not survive); with accumulate the call folds its maxima
