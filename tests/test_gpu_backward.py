@@ -63,6 +63,18 @@ def test_backward_many_lengths(lib):
     _check(p, 79)
 
 
+@pytest.mark.parametrize("nseq", [600, 5000])
+def test_backward_many_short_sequences(lib, nseq):
+    """Hundreds to thousands of packed sequences of 0 to 6 tokens (empty ones
+    included) around a 300- and a 129-token one: the plan's counting sort
+    lists thousands of one-block work items behind the long ones."""
+    rng = np.random.default_rng(nseq)
+    lens = [int(x) for x in rng.integers(0, 7, nseq)]
+    lens[7], lens[nseq - 10] = 300, 129
+    p = synth.prefill_inputs(synth.Dims(2, 512, 64, 128, 128), lens, seed=83, bf16=True)
+    _check(p, 84)
+
+
 def test_backward_96_heads_2048(lib):
     """96 heads, one sequence of 2048 tokens."""
     p = synth.prefill_inputs(synth.K3, [2048], seed=73, bf16=True)
