@@ -542,7 +542,7 @@ def main():
     kern = {}
     for k in ("fill", "prefill_plan", "prefill_expand", "prefill_attn", "prefill_refine_rows",
               "prefill_refine_score", "qk_clip", "absorb_q", "absorbed_split",
-              "absorbed_fixup", "absorbed_combine", "absorbed_refine"):
+              "absorbed_fixup", "absorbed_finish"):
         tot, n = m.mla_timing_read(k)
         if n:
             kern[k] = tot / n

@@ -392,7 +392,7 @@ const char* mla_version(void);
  * mla_timing_enable(0) stops it. mla_timing_read waits for the recorded
  * events and returns the summed milliseconds and launch count of one kernel
  * ("prefill_expand", "prefill_attn", "absorb_q", "absorbed_split",
- * "absorbed_combine", "expanded_split", "qk_clip", ...); it returns 0 if that kernel has not
+ * "absorbed_finish", "expanded_split", "qk_clip", ...); it returns 0 if that kernel has not
  * run. This is the library's one piece of process-global host state (the
  * pending events and the per-kernel totals, behind a mutex): it is off by
  * default, changes no result, and while on, the events it creates are the
