@@ -45,6 +45,24 @@ def test_fp32_decode_ragged(lib, tq):
     assert np.all(np.abs(host(ml) - ref_sm) / np.abs(ref_sm) <= 1e-5)
 
 
+@pytest.mark.parametrize("heads", [20, 128])
+def test_bf16_decode_other_head_counts(lib, heads):
+    """Head counts other than 96: 20 (one partial block of 32 heads in the
+    split workgroups' single row) and 128 (the largest supported: a second row
+    of split workgroups holding 32 heads). Nine ragged sequences with two query
+    tokens each give 18 virtual sequences, so the finishing kernel's last
+    combine block is partial."""
+    from tests._gpu import host, log, run_absorbed
+    dims = synth.Dims(heads=heads, kv_rank=512, shared_dim=64, nope_dim=128, v_dim=128)
+    d = synth.decode_inputs(dims, [5, 700, 33, 2100, 64, 2, 900, 31, 4097], cap=4104, tq=2, seed=41, bf16=True)
+    log(f"bf16 absorbed heads={heads} batch=9 tq=2")
+    out, ml = run_absorbed(d)
+    rows = [d.cache_rows(b) for b in range(d.batch)]
+    ref, ref_sm = oracle.absorbed(d.q, rows, d.w_kv_b, d.gate, d.dims)
+    assert rel_err(host(out), ref) <= BF16_TOL
+    assert np.all(np.abs(host(ml) - ref_sm) / np.abs(ref_sm) <= SMAX_TOL)
+
+
 @pytest.mark.parametrize("tq", [1, 2])
 def test_bf16_decode_ragged_k3(lib, tq):
     """Lengths that are not multiples of the 32-row tile, shorter than a tile,
